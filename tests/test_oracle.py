@@ -1,0 +1,271 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test names the statement it follows.  The definition comes from the Motif
+2.6B explainer (section "Differential attention" and the figure 1 caption):
+  o = [softmax(Q1 K1^T) - lambda softmax(Q2 K2^T)] V,  y = GroupNorm(o),
+with the readings taken where the pages are silent (1/sqrt(d) scale, causal
+mask, one GroupNorm group per head, biased variance, gain, no bias).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import bruteforce
+
+WL = synth.WORKLOADS["tiny_b1_h2_t128"]
+
+
+def _inputs(B=1, T=32, H=2, seed=11, d_qk=64, d_v=128):
+    from synth.workloads import Workload
+
+    wl = Workload("t", "prefill", B=B, T=T, H=H, seed=seed, lam=0.5, d_qk=d_qk, d_v=d_v)
+    return synth.make_prefill_inputs(wl)
+
+
+def _f64(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _run(x, lam=None, **kw):
+    lam = x["lam"] if lam is None else lam
+    return oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], lam, x["gain"],
+                          x["eps"], x["scale"], **kw)
+
+
+# --- lambda = 0 is ordinary attention (explainer, "Differential attention") ---
+
+def test_lambda0_is_causal_sdpa_plus_group_norm():
+    x = _inputs(B=2, T=48, H=3)
+    o, y = _run(x, lam=0.0)
+    q = torch.from_numpy(_f64(x["q1"])).permute(0, 2, 1, 3)
+    k = torch.from_numpy(_f64(x["k1"])).permute(0, 2, 1, 3)
+    v = torch.from_numpy(_f64(x["v"])).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=x["scale"])
+    ref = ref.permute(0, 2, 1, 3).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    B, T, H, D = o.shape
+    gn = torch.nn.functional.group_norm(torch.from_numpy(ref.reshape(B * T, H * D)), H,
+                                        weight=torch.from_numpy(x["gain"].astype(np.float64).reshape(-1)),
+                                        eps=x["eps"])
+    np.testing.assert_allclose(y, gn.numpy().reshape(B, T, H, D), rtol=0, atol=1e-10)
+
+
+def test_lambda0_ignores_second_map():
+    x = _inputs(T=24)
+    o, y = _run(x, lam=0.0)
+    x2 = dict(x)
+    x2["q2"] = synth.normal_bf16(99, 1, x["q2"].shape)
+    x2["k2"] = synth.normal_bf16(99, 2, x["k2"].shape)
+    o2, y2 = _run(x2, lam=0.0)
+    assert np.array_equal(o, o2) and np.array_equal(y, y2)
+
+
+# --- rows of the difference map sum to 1 - lambda ---
+
+@pytest.mark.parametrize("lam", [0.0, 0.5, 0.8, 1.0, -0.3, 2.5])
+def test_v_ones_gives_one_minus_lambda(lam):
+    x = _inputs(T=40)
+    x["v"] = np.full_like(x["v"], 0x3F80)  # bf16 1.0
+    o, y = _run(x, lam=lam)
+    np.testing.assert_allclose(o, 1.0 - lam, rtol=0, atol=1e-14)
+    assert np.abs(y).max() < 1e-9
+
+
+def test_per_head_lambda_row_sums():
+    x = _inputs(T=20, H=4)
+    x["v"] = np.full_like(x["v"], 0x3F80)
+    lam = np.array([0.2, 0.45, 0.7, 0.9])
+    o, _ = _run(x, lam=lam)
+    for h in range(4):
+        np.testing.assert_allclose(o[:, :, h, :], 1.0 - lam[h], rtol=0, atol=1e-14)
+
+
+# --- identical maps at lambda = 1 cancel exactly ---
+
+def test_identical_maps_lambda1_zero():
+    x = _inputs(T=64)
+    x["q2"], x["k2"] = x["q1"].copy(), x["k1"].copy()
+    o, y = _run(x, lam=1.0)
+    assert np.all(o == 0.0) and np.all(y == 0.0)
+
+
+# --- independent brute force, T <= 16 ---
+
+@pytest.mark.parametrize("T,d_qk,d_v,lam", [(16, 64, 128, 0.8), (9, 8, 16, 0.5), (5, 4, 8, -0.7)])
+def test_bruteforce_decimal(T, d_qk, d_v, lam):
+    x = _inputs(B=2, T=T, H=2, seed=5 + T, d_qk=d_qk, d_v=d_v)
+    lam_h = np.array([lam, 0.3])
+    o, y = _run(x, lam=lam_h)
+    rows = [(0, 0, 0), (0, T - 1, 1), (1, T // 2, 0), (1, T - 1, 0)]
+    for b, i, h in rows:
+        ob, yb = bruteforce.row(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], b, i, h, lam_h[h],
+                                x["gain"], x["eps"], x["scale"])
+        ob = np.array([float(t) for t in ob])
+        yb = np.array([float(t) for t in yb])
+        np.testing.assert_allclose(o[b, i, h], ob, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(y[b, i, h], yb, rtol=1e-12, atol=1e-13)
+
+
+def test_bruteforce_decimal_decode():
+    from synth.workloads import Workload
+
+    wl = Workload("d", "decode", B=2, T=7, H=2, seed=21, lam=0.8, d_qk=16, d_v=32)
+    x = synth.make_decode_inputs(wl)
+    seqlens = np.array([7, 4], dtype=np.int32)
+    o, y = oracle.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"],
+                         x["eps"], x["scale"], seqlens=seqlens)
+    for b in range(2):
+        for h in range(2):
+            q1 = x["q1"][:, None]  # [B, 1, H, d]
+            q2 = x["q2"][:, None]
+            ob, yb = bruteforce.row(q1, q2, x["k1"], x["k2"], x["v"], b, 0, h, x["lam"][h],
+                                    x["gain"], x["eps"], x["scale"], n_keys=int(seqlens[b]))
+            np.testing.assert_allclose(o[b, h], [float(t) for t in ob], rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(y[b, h], [float(t) for t in yb], rtol=1e-12, atol=1e-13)
+
+
+# --- closed forms ---
+
+def test_row0_closed_form():
+    x = _inputs(B=2, T=10, H=2)
+    lam = np.array([0.8, -0.25])
+    o, _ = _run(x, lam=lam)
+    v = _f64(x["v"])
+    for h in range(2):
+        np.testing.assert_allclose(o[:, 0, h], (1 - lam[h]) * v[:, 0, h], rtol=0, atol=1e-14)
+
+
+def test_zero_keys_give_prefix_mean():
+    x = _inputs(T=30)
+    x["k1"] = np.zeros_like(x["k1"])
+    x["k2"] = np.zeros_like(x["k2"])
+    o, _ = _run(x, lam=0.8)
+    v = _f64(x["v"])
+    T = v.shape[1]
+    prefix_mean = np.cumsum(v, axis=1) / np.arange(1, T + 1)[None, :, None, None]
+    np.testing.assert_allclose(o, 0.2 * prefix_mean, rtol=0, atol=1e-14)
+
+
+def test_only_first_map_keys_zero():
+    # K1 = 0: the first map is uniform over j <= i; the second stays a softmax.
+    x = _inputs(T=12, H=1)
+    x["k1"] = np.zeros_like(x["k1"])
+    o, _ = _run(x, lam=0.5)
+    q2, k2, v = _f64(x["q2"]), _f64(x["k2"]), _f64(x["v"])
+    for i in range(12):
+        s = (k2[0, : i + 1, 0] @ q2[0, i, 0]) * x["scale"]
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        ref = v[0, : i + 1, 0].mean(axis=0) - 0.5 * (p @ v[0, : i + 1, 0])
+        np.testing.assert_allclose(o[0, i, 0], ref, rtol=0, atol=1e-13)
+
+
+# --- invariants ---
+
+def test_causality():
+    x = _inputs(T=40)
+    o, y = _run(x)
+    x2 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in x.items()}
+    cut = 17
+    for name in ("k1", "k2", "v", "q1", "q2"):
+        x2[name][:, cut + 1:] = synth.normal_bf16(77, 3, x2[name][:, cut + 1:].shape)
+    o2, y2 = _run(x2)
+    assert np.array_equal(o[:, : cut + 1], o2[:, : cut + 1])
+    assert np.array_equal(y[:, : cut + 1], y2[:, : cut + 1])
+    assert not np.array_equal(o[:, cut + 1:], o2[:, cut + 1:])
+
+
+def test_antisymmetry_lambda1():
+    x = _inputs(T=25)
+    o, _ = _run(x, lam=1.0)
+    xs = dict(x, q1=x["q2"], k1=x["k2"], q2=x["q1"], k2=x["k1"])
+    os_, _ = _run(xs, lam=1.0)
+    np.testing.assert_allclose(os_, -o, rtol=0, atol=1e-15)
+
+
+def test_linearity_in_v():
+    x = _inputs(T=30)
+    o, y = _run(x)
+    x2 = dict(x, v=synth.f32_to_bf16_bits(2.0 * synth.bf16_bits_to_f32(x["v"])))
+    o2, _ = _run(x2)
+    assert np.array_equal(o2, 2.0 * o)  # power-of-two scaling is exact
+    # GroupNorm: (2o - 2mu) / sqrt(4 var + 4 eps) == (o - mu) / sqrt(var + eps)
+    _, y2 = _run(dict(x2, eps=4.0 * x["eps"]))
+    np.testing.assert_allclose(y2, y, rtol=1e-13, atol=1e-13)
+
+
+def test_bh_independence():
+    x = _inputs(B=2, T=20, H=3)
+    o, y = _run(x)
+    x2 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in x.items()}
+    for name in ("q1", "q2", "k1", "k2", "v"):
+        x2[name][1, :, 2] = synth.normal_bf16(55, 4, x2[name][1, :, 2].shape)
+    o2, _ = _run(x2)
+    mask = np.ones(o.shape[:3], bool)
+    mask[1, :, 2] = False
+    assert np.array_equal(o[mask], o2[mask])
+    assert not np.array_equal(o[1, :, 2], o2[1, :, 2])
+
+
+def test_bounds_and_norm_moments():
+    x = _inputs(T=64, H=2)
+    lam = 0.7
+    o, _ = _run(x, lam=lam)
+    v = np.abs(_f64(x["v"]))
+    vmax = np.maximum.accumulate(v, axis=1)
+    assert np.all(np.abs(o) <= (1 + lam) * vmax + 1e-12)
+    x1 = dict(x, gain=np.ones_like(x["gain"]))
+    o, y = _run(x1, lam=lam)
+    mu = y.mean(axis=-1)
+    var = y.var(axis=-1)
+    s2 = o.var(axis=-1)
+    np.testing.assert_allclose(mu, 0.0, atol=1e-12)
+    np.testing.assert_allclose(var, s2 / (s2 + x["eps"]), rtol=1e-12)
+
+
+def test_row_selection_matches_full():
+    x = _inputs(B=2, T=33, H=2)
+    o, y = _run(x)
+    rows = [(1, 32, 1), (0, 0, 0), (1, 5, 0)]
+    ro, ry = _run(x, rows=rows)
+    for n, (b, i, h) in enumerate(rows):
+        assert np.array_equal(ro[n], o[b, i, h]) and np.array_equal(ry[n], y[b, i, h])
+
+
+def test_decode_equals_last_prefill_row():
+    x = _inputs(B=2, T=37, H=2)
+    o, y = _run(x)
+    od, yd = oracle.decode(x["q1"][:, -1], x["q2"][:, -1], x["k1"], x["k2"], x["v"], x["lam"],
+                           x["gain"], x["eps"], x["scale"])
+    np.testing.assert_array_equal(od, o[:, -1])
+    np.testing.assert_array_equal(yd, y[:, -1])
+    # a shorter cached length equals the prefill row at that position
+    sl = np.array([10, 37], dtype=np.int32)
+    od, _ = oracle.decode(x["q1"][:, 9], x["q2"][:, 9], x["k1"], x["k2"], x["v"], x["lam"],
+                          x["gain"], x["eps"], x["scale"], seqlens=sl)
+    np.testing.assert_array_equal(od[0], o[0, 9])
+
+
+def test_decode_empty_cache_is_zero():
+    x = _inputs(B=2, T=8, H=2)
+    od, yd = oracle.decode(x["q1"][:, 0], x["q2"][:, 0], x["k1"], x["k2"], x["v"], x["lam"],
+                           x["gain"], x["eps"], x["scale"], seqlens=np.array([0, 3], np.int32))
+    assert np.all(od[0] == 0) and np.all(yd[0] == 0) and np.any(od[1] != 0)
+
+
+def test_golden_fixture():
+    """Regression anchor: stored oracle values (tests/golden/make_golden.py)."""
+    import json
+    import os
+
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_rows.json")
+    g = json.load(open(path))
+    wl = synth.WORKLOADS[g["workload"]]
+    x = synth.make_prefill_inputs(wl)
+    o, y = _run(x, rows=[tuple(r) for r in g["rows"]])
+    np.testing.assert_allclose(o, np.array(g["o_pre"]), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(y, np.array(g["y"]), rtol=0, atol=1e-13)
