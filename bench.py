@@ -1,0 +1,223 @@
+"""Benchmark of the causal differential-attention forward path on one MI355X.
+
+One step = one pass of the whole path on resident synthetic inputs: the causal
+prefill of the Motif-2.6B-shaped layer (B=1, T=4096, H=16, d_qk=64, d_v=128,
+lambda=0.8, per-head GroupNorm) followed by the split-KV decode of 64 sequences
+against a 4096-long cache (H=16, 8 splits).  Both run through the C ABI on the
+current torch stream; HIP events around each call time the kernels.
+
+Prints ONE JSON line.  `value` is the prefill throughput in TFLOP/s, counting
+768 FLOP per causal (query, key <= query) pair and head: two 64-wide score dot
+products and two 128-wide P V products (the one-pass form has to keep P1 V and
+P2 V apart).  Decode reports HBM GB/s from the bytes it must move.  The roofline
+object covers the prefill kernel against the dense bf16/fp16 MFMA peak; the
+cpu_baseline object times the fp64 oracle on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-calibration     # plain device copy, for HBM counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+FLOP_PER_PAIR = 768
+PREFILL_WL = "prefill_b1_t4096_h16"
+DECODE_WL = "decode_b64_l4096_h16"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_kernel_b1_t4096_h16_hbm_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "differential_attention_causal_amd", "csrc", f)
+                  for f in ("prefill.hip", "kernels.h")]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per prefill launch from the committed counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def decode_bytes(wl) -> int:
+    """Bytes the decode must move: K1, K2, V caches once, both queries, the
+    output (bf16) and the gain."""
+    cache = wl.B * wl.T * wl.H * (2 * wl.d_qk + wl.d_v) * 2
+    q = 2 * wl.B * wl.H * wl.d_qk * 2
+    out = wl.B * wl.H * wl.d_v * 2
+    gain = wl.H * wl.d_v * 4
+    return cache + q + out + gain
+
+
+def cpu_baseline(x, wl):
+    """Time the fp64 oracle on all rows of the prefill workload on this host."""
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"],
+                   nthreads=cores)
+    dt = time.perf_counter() - t0
+    flop = wl.causal_pairs * FLOP_PER_PAIR
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "all %d rows of %s (B=1,T=4096,H=16), fp64, %.2f s wall; FLOP counted at %d per "
+                      "causal pair like the GPU value" % (wl.B * wl.T * wl.H, wl.name, dt, FLOP_PER_PAIR)}
+
+
+def copy_calibration(steps: int) -> None:
+    """A plain device-to-device copy of a known size, for scaling HBM counters."""
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": steps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no sharding or collectives); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return 0
+
+    import differential_attention_causal_amd as da
+    import synth
+
+    def to_dev(bits, device):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+    def f32_dev(a, device):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    dev = "cuda"
+    pw = synth.WORKLOADS[PREFILL_WL]
+    dw = synth.WORKLOADS[DECODE_WL]
+    xp = synth.make_prefill_inputs(pw)
+    xd = synth.make_decode_inputs(dw)
+    P = {n: to_dev(xp[n], dev) for n in ("q1", "q2", "k1", "k2", "v")}
+    P["gain"] = f32_dev(xp["gain"], dev)
+    D = {n: to_dev(xd[n], dev) for n in ("q1", "q2", "k1", "k2", "v")}
+    D["gain"] = f32_dev(xd["gain"], dev)
+    p_out = torch.empty((pw.B, pw.T, pw.H, pw.d_v), dtype=torch.bfloat16, device=dev)
+    d_out = torch.empty((dw.B, dw.H, dw.d_v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(da.diffattn_decode_workspace_bytes(dw.B, dw.H, dw.d_v, dw.num_splits), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        da.diffattn_fwd_prefill(P["q1"], P["q2"], P["k1"], P["k2"], P["v"], pw.lam, P["gain"], eps=pw.eps,
+                                scale=pw.scale, out=p_out)
+
+    def decode():
+        da.diffattn_fwd_decode(D["q1"], D["q2"], D["k1"], D["k2"], D["v"], dw.lam, D["gain"], eps=dw.eps,
+                               scale=dw.scale, num_splits=dw.num_splits, workspace=ws, out=d_out)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record()
+        prefill()
+        ev[k][1].record()
+        decode()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)])
+    d_ms = np.array([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)])
+    step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
+    assert bool(torch.isfinite(p_out.float()).all()) and bool(torch.isfinite(d_out.float()).all())
+
+    p_flop = pw.causal_pairs * FLOP_PER_PAIR
+    p_s = float(p_ms.mean()) / 1e3
+    tflops = p_flop / p_s / 1e12
+    d_bytes = decode_bytes(dw)
+    d_s = float(d_ms.mean()) / 1e3
+    gbs = d_bytes / d_s / 1e9
+    traffic = read_traffic()
+
+    rec = {
+        "metric": "diff-attn fwd TFLOP/s + % bf16 MFMA peak (T=4096,H=16); decode HBM GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": PREFILL_WL, "B": pw.B, "T": pw.T, "H": pw.H, "d_qk": pw.d_qk, "d_v": pw.d_v,
+                   "lambda": pw.lam, "causal": True, "step_also_runs": DECODE_WL},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "prefill_kernel", "algorithmic_flop_per_launch": p_flop},
+        "prefill": {"us_mean": round(p_s * 1e6, 2), "us_min": round(float(p_ms.min()) * 1e3, 2),
+                    "tflops": round(tflops, 2), "tflops_512_per_pair": round(pw.causal_pairs * 512 / p_s / 1e12, 2),
+                    "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4)},
+        "decode": {"workload": DECODE_WL, "us_mean": round(d_s * 1e6, 2), "us_min": round(float(d_ms.min()) * 1e3, 2),
+                   "bytes": d_bytes, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                   "splits": dw.num_splits},
+        "wall_s_timed": round(wall, 3),
+        "kernel_source_sha256_16": kernel_source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(xp, pw)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,198 @@
+"""Python binding of libdiffattn.so (causal differential attention on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/diffattn.h``; this module takes
+torch tensors (device memory) and the current torch stream, checks dtypes and
+shapes, passes raw pointers and strides through ctypes, and raises
+``RuntimeError`` with the library's status text on any nonzero status.
+
+There is no fallback: if the library is missing or fails to load, importing
+this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # first: the HIP runtime torch loads is the one the library binds to
+
+__all__ = [
+    "diffattn_fwd_prefill",
+    "diffattn_fwd_decode",
+    "diffattn_decode_workspace_bytes",
+    "diffattn_status_string",
+    "diffattn_abi_version",
+    "LIB_PATH",
+    "D_QK",
+    "D_V",
+]
+
+D_QK = 64
+D_V = 128
+OUT_BF16 = 0
+OUT_F32 = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdiffattn.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libdiffattn.so is not built; run `python -m differential_attention_causal_amd.build` "
+        "(or __graft_entry__.build()) first"
+    )
+
+
+class _Strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("t", ctypes.c_int64), ("h", ctypes.c_int64)]
+
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P, _I, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+_lib.diffattn_fwd_prefill.restype = _I
+_lib.diffattn_fwd_prefill.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(_Strides), _I, _I, _I, _I, _I,
+                                      _F, _P, _P, _F, _F, _P, _I, _P, _P]
+_lib.diffattn_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.diffattn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I]
+_lib.diffattn_fwd_decode.restype = _I
+_lib.diffattn_fwd_decode.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(_Strides), _P, _I, _I, _I, _I, _I,
+                                     _F, _P, _P, _F, _F, _I, _P, ctypes.c_size_t, _P, _I, _P, _P]
+_lib.diffattn_status_string.restype = ctypes.c_char_p
+_lib.diffattn_status_string.argtypes = [_I]
+_lib.diffattn_abi_version.restype = _I
+_lib.diffattn_abi_version.argtypes = []
+
+
+def diffattn_status_string(status: int) -> str:
+    return _lib.diffattn_status_string(int(status)).decode()
+
+
+def diffattn_abi_version() -> int:
+    return int(_lib.diffattn_abi_version())
+
+
+def diffattn_decode_workspace_bytes(B: int, H: int, d_v: int = D_V, num_splits: int = 0) -> int:
+    return int(_lib.diffattn_decode_workspace_bytes(B, H, d_v, num_splits))
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise RuntimeError(diffattn_status_string(rc))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides4(t: torch.Tensor) -> _Strides:
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B, T, H, D] tensor with a contiguous last dimension")
+    return _Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _lambda_args(lam, H, device):
+    """Scalar lambda -> (value, None); tensor [H] -> (0.0, fp32 device tensor)."""
+    if isinstance(lam, torch.Tensor):
+        if lam.shape != (H,) or lam.dtype != torch.float32 or lam.device != device or not lam.is_contiguous():
+            raise ValueError("per-head lambda must be a contiguous fp32 [H] tensor on the inputs' device")
+        return 0.0, lam
+    return float(lam), None
+
+
+def _out_code(dtype):
+    if dtype == torch.bfloat16:
+        return OUT_BF16
+    if dtype == torch.float32:
+        return OUT_F32
+    raise ValueError("out dtype must be torch.bfloat16 or torch.float32")
+
+
+def diffattn_fwd_prefill(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, out=None,
+                         out_dtype=torch.bfloat16, o_pre=None, stream=None):
+    """Causal differential-attention prefill.
+
+    q1, q2, k1, k2: bf16 [B, T, H, 64]; v: bf16 [B, T, H, 128] (any strides with
+    a contiguous last dimension).  lam: float, or fp32 [H] device tensor.
+    gain: fp32 [H, 128].  out: optional preallocated [B, T, H, 128] output of
+    ``out_dtype``; o_pre: optional fp32 [B, T, H, 128] for the pre-norm output.
+    Returns out.  Runs asynchronously on ``stream`` (default: current stream).
+    """
+    B, T, H, d_qk = q1.shape
+    d_v = v.shape[3]
+    for t in (q1, q2, k1, k2, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError("q1, q2, k1, k2, v must be bf16 device tensors")
+    for t in (q2, k1, k2):
+        if tuple(t.shape) != (B, T, H, d_qk):
+            raise ValueError("q1, q2, k1, k2 must share one shape")
+    if tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError("v must be [B, T, H, d_v]")
+    if gain.dtype != torch.float32 or tuple(gain.shape) != (H, d_v) or not gain.is_contiguous():
+        raise ValueError("gain must be a contiguous fp32 [H, d_v] tensor")
+    if out is None:
+        out = torch.empty((B, T, H, d_v), dtype=out_dtype, device=q1.device)
+    if tuple(out.shape) != (B, T, H, d_v) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, T, H, d_v] tensor")
+    if o_pre is not None and (o_pre.dtype != torch.float32 or tuple(o_pre.shape) != (B, T, H, d_v)
+                              or not o_pre.is_contiguous()):
+        raise ValueError("o_pre must be a contiguous fp32 [B, T, H, d_v] tensor")
+    lam_v, lam_t = _lambda_args(lam, H, q1.device)
+    st = (_Strides * 5)(*[_strides4(t) for t in (q1, q2, k1, k2, v)])
+    rc = _lib.diffattn_fwd_prefill(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, B, T, H, d_qk, d_v,
+                                   lam_v, _ptr(lam_t), _ptr(gain), float(eps), float(scale), _ptr(out),
+                                   _out_code(out.dtype), _ptr(o_pre), _stream(stream))
+    _check(rc)
+    return out
+
+
+def diffattn_fwd_decode(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, seqlens=None, num_splits=0,
+                        workspace=None, out=None, out_dtype=torch.bfloat16, o_pre=None, stream=None):
+    """Single-query decode against a KV cache, split over cache positions.
+
+    q1, q2: bf16 [B, H, 64] contiguous; k1, k2: bf16 cache [B, L, H, 64];
+    v: bf16 cache [B, L, H, 128]; seqlens: optional int32 [B] device tensor.
+    workspace: optional uint8 device tensor of at least
+    ``diffattn_decode_workspace_bytes(B, H, 128, num_splits)`` bytes (allocated
+    here through torch when omitted).  Returns out [B, H, 128].
+    """
+    B, H, d_qk = q1.shape
+    L = k1.shape[1]
+    d_v = v.shape[3]
+    for t in (q1, q2, k1, k2, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError("q1, q2, k1, k2, v must be bf16 device tensors")
+    if tuple(q2.shape) != (B, H, d_qk) or not q1.is_contiguous() or not q2.is_contiguous():
+        raise ValueError("q1, q2 must be contiguous [B, H, d_qk]")
+    if tuple(k1.shape) != (B, L, H, d_qk) or tuple(k2.shape) != (B, L, H, d_qk) or tuple(v.shape[:3]) != (B, L, H):
+        raise ValueError("cache shapes disagree")
+    if gain.dtype != torch.float32 or tuple(gain.shape) != (H, d_v) or not gain.is_contiguous():
+        raise ValueError("gain must be a contiguous fp32 [H, d_v] tensor")
+    if seqlens is not None and (seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,)
+                                or not seqlens.is_cuda):
+        raise ValueError("seqlens must be an int32 [B] device tensor")
+    need = diffattn_decode_workspace_bytes(B, H, d_v, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=out_dtype, device=q1.device)
+    if tuple(out.shape) != (B, H, d_v) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, d_v] tensor")
+    if o_pre is not None and (o_pre.dtype != torch.float32 or tuple(o_pre.shape) != (B, H, d_v)
+                              or not o_pre.is_contiguous()):
+        raise ValueError("o_pre must be a contiguous fp32 [B, H, d_v] tensor")
+    lam_v, lam_t = _lambda_args(lam, H, q1.device)
+    st = (_Strides * 3)(*[_strides4(t) for t in (k1, k2, v)])
+    rc = _lib.diffattn_fwd_decode(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, _ptr(seqlens), B, L, H,
+                                  d_qk, d_v, lam_v, _ptr(lam_t), _ptr(gain), float(eps), float(scale),
+                                  int(num_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _ptr(out), _out_code(out.dtype), _ptr(o_pre), _stream(stream))
+    _check(rc)
+    return out
+
+
+def default_scale(d_qk: int = D_QK) -> float:
+    return 1.0 / math.sqrt(d_qk)

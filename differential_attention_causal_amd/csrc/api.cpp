@@ -1,0 +1,174 @@
+// C-ABI front end of libdiffattn.so: argument validation (before any HIP
+// call), stride defaults and kernel launch.  The operation and every argument
+// are documented in include/diffattn.h.
+#include "diffattn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace {
+
+using diffattn::kDqk;
+using diffattn::kDv;
+using diffattn::Strides;
+
+constexpr int kDefaultSplits = 8;
+constexpr int kMaxSplits = 64;
+constexpr int64_t kMaxWorkgroups = int64_t(1) << 23;
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool strides_ok(const diffattn_strides& s) {
+  return s.b >= 0 && s.t >= 0 && s.h >= 0 && s.b % 8 == 0 && s.t % 8 == 0 && s.h % 8 == 0;
+}
+
+Strides to_internal(const diffattn_strides& s) { return Strides{s.b, s.t, s.h}; }
+
+diffattn_strides contiguous(int T, int H, int D) {
+  return diffattn_strides{(int64_t)T * H * D, (int64_t)H * D, (int64_t)D};
+}
+
+int check_common(int B, int H, int d_qk, int d_v, float lambda, float eps, float scale, int out_dtype) {
+  if (B <= 0 || H <= 0) return DIFFATTN_ERR_SHAPE;
+  if ((int64_t)B * H > (int64_t(1) << 24)) return DIFFATTN_ERR_SHAPE;
+  if (d_qk != kDqk || d_v != kDv) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(lambda) || !std::isfinite(eps) || eps < 0.f || std::isnan(scale) || std::isinf(scale))
+    return DIFFATTN_ERR_VALUE;
+  if (out_dtype != DIFFATTN_OUT_BF16 && out_dtype != DIFFATTN_OUT_F32) return DIFFATTN_ERR_VALUE;
+  return DIFFATTN_OK;
+}
+
+float score_factor(float scale) {
+  const float s = scale > 0.f ? scale : 1.0f / std::sqrt((float)kDqk);
+  return s * kLog2e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int diffattn_abi_version(void) { return 100; }
+
+const char* diffattn_status_string(int status) {
+  switch (status) {
+    case DIFFATTN_OK: return "ok";
+    case DIFFATTN_ERR_NULL: return "diffattn: a required pointer is NULL";
+    case DIFFATTN_ERR_SHAPE: return "diffattn: a size is non-positive or beyond the supported range";
+    case DIFFATTN_ERR_UNSUPPORTED: return "diffattn: unsupported head size (needs d_qk=64, d_v=128)";
+    case DIFFATTN_ERR_LAYOUT: return "diffattn: pointer not 16-byte aligned or stride not a multiple of 8 elements";
+    case DIFFATTN_ERR_WORKSPACE: return "diffattn: decode workspace missing, misaligned or too small";
+    case DIFFATTN_ERR_HIP: return "diffattn: the HIP runtime refused the kernel launch";
+    case DIFFATTN_ERR_VALUE: return "diffattn: invalid scalar argument (lambda, eps, scale, dtype or split count)";
+    default: return "diffattn: unknown status";
+  }
+}
+
+int diffattn_fwd_prefill(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
+                         const diffattn_strides* strides, int B, int T, int H, int d_qk, int d_v,
+                         float lambda, const float* lambda_per_head, const float* gain, float gn_eps,
+                         float scale, void* out, int out_dtype, float* o_pre, void* stream) {
+  if (!q1 || !q2 || !k1 || !k2 || !v || !gain || !out) return DIFFATTN_ERR_NULL;
+  int rc = check_common(B, H, d_qk, d_v, lambda, gn_eps, scale, out_dtype);
+  if (rc != DIFFATTN_OK) return rc;
+  if (T <= 0 || T > (1 << 22)) return DIFFATTN_ERR_SHAPE;
+  // One 256-thread workgroup per 128 queries of each (b, h); the launch must
+  // stay below 2^32 threads.
+  if ((int64_t)((T + 127) / 128) * B * H > kMaxWorkgroups) return DIFFATTN_ERR_SHAPE;
+  const void* ptrs[5] = {q1, q2, k1, k2, v};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return DIFFATTN_ERR_LAYOUT;
+  if (!aligned16(out) || !aligned16(gain) || (o_pre && !aligned16(o_pre))) return DIFFATTN_ERR_LAYOUT;
+  diffattn_strides st[5];
+  for (int i = 0; i < 5; ++i) {
+    st[i] = strides ? strides[i] : contiguous(T, H, i == 4 ? d_v : d_qk);
+    if (!strides_ok(st[i])) return DIFFATTN_ERR_LAYOUT;
+  }
+
+  diffattn::PrefillArgs a{};
+  a.q1 = static_cast<const uint16_t*>(q1);
+  a.q2 = static_cast<const uint16_t*>(q2);
+  a.k1 = static_cast<const uint16_t*>(k1);
+  a.k2 = static_cast<const uint16_t*>(k2);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sq1 = to_internal(st[0]);
+  a.sq2 = to_internal(st[1]);
+  a.sk1 = to_internal(st[2]);
+  a.sk2 = to_internal(st[3]);
+  a.sv = to_internal(st[4]);
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.c = score_factor(scale);
+  a.lambda = lambda;
+  a.lambda_h = lambda_per_head;
+  a.gain = gain;
+  a.eps = gn_eps;
+  a.out = out;
+  a.out_f32 = out_dtype == DIFFATTN_OUT_F32;
+  a.o_pre = o_pre;
+  if (diffattn::launch_prefill(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
+  return DIFFATTN_OK;
+}
+
+size_t diffattn_decode_workspace_bytes(int B, int H, int d_v, int num_splits) {
+  if (num_splits <= 0) num_splits = kDefaultSplits;
+  if (B <= 0 || H <= 0 || d_v != kDv || num_splits > kMaxSplits) return 0;
+  if ((int64_t)B * H > (int64_t(1) << 24)) return 0;
+  return (size_t)B * H * num_splits * 2 * diffattn::kPartialStride * sizeof(float);
+}
+
+int diffattn_fwd_decode(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
+                        const diffattn_strides* cache_strides, const int32_t* seqlens, int B, int L, int H,
+                        int d_qk, int d_v, float lambda, const float* lambda_per_head, const float* gain,
+                        float gn_eps, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                        void* out, int out_dtype, float* o_pre, void* stream) {
+  if (!q1 || !q2 || !k1 || !k2 || !v || !gain || !out) return DIFFATTN_ERR_NULL;
+  int rc = check_common(B, H, d_qk, d_v, lambda, gn_eps, scale, out_dtype);
+  if (rc != DIFFATTN_OK) return rc;
+  if (L <= 0 || L > (1 << 26)) return DIFFATTN_ERR_SHAPE;
+  if (num_splits <= 0) num_splits = kDefaultSplits;
+  if (num_splits > kMaxSplits) return DIFFATTN_ERR_VALUE;
+  if ((int64_t)B * H * num_splits > kMaxWorkgroups) return DIFFATTN_ERR_SHAPE;
+  const void* ptrs[5] = {q1, q2, k1, k2, v};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return DIFFATTN_ERR_LAYOUT;
+  if (!aligned16(out) || !aligned16(gain) || (o_pre && !aligned16(o_pre))) return DIFFATTN_ERR_LAYOUT;
+  if (!workspace || !aligned16(workspace)) return DIFFATTN_ERR_WORKSPACE;
+  if (workspace_bytes < diffattn_decode_workspace_bytes(B, H, d_v, num_splits)) return DIFFATTN_ERR_WORKSPACE;
+  diffattn_strides st[3];
+  for (int i = 0; i < 3; ++i) {
+    st[i] = cache_strides ? cache_strides[i] : contiguous(L, H, i == 2 ? d_v : d_qk);
+    if (!strides_ok(st[i])) return DIFFATTN_ERR_LAYOUT;
+  }
+
+  diffattn::DecodeArgs a{};
+  a.q1 = static_cast<const uint16_t*>(q1);
+  a.q2 = static_cast<const uint16_t*>(q2);
+  a.k1 = static_cast<const uint16_t*>(k1);
+  a.k2 = static_cast<const uint16_t*>(k2);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sk1 = to_internal(st[0]);
+  a.sk2 = to_internal(st[1]);
+  a.sv = to_internal(st[2]);
+  a.seqlens = seqlens;
+  a.B = B;
+  a.L = L;
+  a.H = H;
+  a.splits = num_splits;
+  a.c = score_factor(scale);
+  a.lambda = lambda;
+  a.lambda_h = lambda_per_head;
+  a.gain = gain;
+  a.eps = gn_eps;
+  a.partial = static_cast<float*>(workspace);
+  a.out = out;
+  a.out_f32 = out_dtype == DIFFATTN_OUT_F32;
+  a.o_pre = o_pre;
+  if (diffattn::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
+  return DIFFATTN_OK;
+}
+
+}  // extern "C"

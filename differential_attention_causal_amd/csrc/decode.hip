@@ -1,0 +1,286 @@
+// Split-KV single-query decode for causal differential attention on gfx950.
+//
+// One query per (b, h) attends every cached position of its sequence (the
+// cache includes the current token).  The cache is HBM-bound work: each byte
+// of K1, K2 and V is read once.  The positions are cut into `splits` equal
+// ranges; a workgroup per (b, h, split) keeps BOTH maps' softmax states (running
+// max, sum, unnormalised 128-channel output) and writes them to the workspace.
+// A merge kernel per (b, h) rescales the splits to a common max per map, keeps
+// the maps apart until o = O1/L1 - lambda O2/L2, then applies the per-head
+// GroupNorm (Motif 2.6B explainer, "Differential attention", figure 1 caption).
+//
+// Inside a split, keys go in blocks of kKB: scores (8 lanes per key, exact
+// bf16 products, fp32 accumulation) -> LDS; block max and exp2 in fp32 (P stays
+// fp32 here; there is no matrix product to feed); then the P V pass with 16
+// lanes per 256-byte V row.  Scores are kept in base-2 units (c = scale log2 e).
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kKB = 512;                   // keys per block inside a split
+constexpr int kPerThread = kKB / kThreads; // scores each thread reduces
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Dot product of 8 bf16 pairs: products are exact in fp32, sums in fp32.
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = __builtin_fmaf(bf16_lo(a[i]), bf16_lo(b[i]), acc);
+    acc = __builtin_fmaf(bf16_hi(a[i]), bf16_hi(b[i]), acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
+  int n = a.seqlens ? a.seqlens[b] : a.L;
+  return n > a.L ? a.L : n;
+}
+
+__global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
+  __shared__ float sc[2][kKB];          // scores, then probabilities
+  __shared__ float red[2][kWaves][2];   // per-wave max / sum of each map
+  __shared__ float acc[kWaves][2][kDv]; // per-wave partial outputs
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int split = (int)(blockIdx.x % a.splits);
+  const int bh = (int)(blockIdx.x / a.splits);
+  const int head = bh % a.H, b = bh / a.H;
+
+  const int n = seq_len(a, b);
+  const int chunk = n > 0 ? (n + a.splits - 1) / a.splits : 0;
+  const int s0 = split * chunk;
+  const int s1 = min(n, s0 + chunk);
+  float* rec = a.partial + ((int64_t)bh * a.splits + split) * 2 * kPartialStride;
+
+  // Query chunks: lane e of a key group holds dims 8e .. 8e+7 of q1 and q2.
+  const int e = tid & 7, ks = tid >> 3;
+  const u32x4 q1 = *reinterpret_cast<const u32x4*>(a.q1 + (int64_t)bh * kDqk + 8 * e);
+  const u32x4 q2 = *reinterpret_cast<const u32x4*>(a.q2 + (int64_t)bh * kDqk + 8 * e);
+  const uint16_t* k1b = a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h + 8 * e;
+  const uint16_t* k2b = a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h + 8 * e;
+  const int cg = tid & 15, kq = tid >> 4;
+  const uint16_t* vb = a.v + (int64_t)b * a.sv.b + (int64_t)head * a.sv.h + 8 * cg;
+
+  float m1 = -__builtin_inff(), m2 = -__builtin_inff(), l1 = 0.f, l2 = 0.f;
+  float o1[8], o2[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o1[k] = o2[k] = 0.f;
+
+  for (int kb = s0; kb < s1; kb += kKB) {
+    const int cnt = min(kKB, s1 - kb);
+    // Scores of both maps for this block (32 keys per pass, 8 lanes per key).
+#pragma unroll 4
+    for (int p = 0; p < kKB / 32; ++p) {
+      const int kk = p * 32 + ks;
+      float d1 = 0.f, d2 = 0.f;
+      if (kk < cnt) {
+        const int64_t pos = kb + kk;
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(k1b + pos * a.sk1.t);
+        const u32x4 x2 = *reinterpret_cast<const u32x4*>(k2b + pos * a.sk2.t);
+        d1 = dot8(q1, x1, 0.f);
+        d2 = dot8(q2, x2, 0.f);
+      }
+      d1 += __shfl_xor(d1, 1);
+      d2 += __shfl_xor(d2, 1);
+      d1 += __shfl_xor(d1, 2);
+      d2 += __shfl_xor(d2, 2);
+      d1 += __shfl_xor(d1, 4);
+      d2 += __shfl_xor(d2, 4);
+      if (e == 0) {
+        sc[0][kk] = kk < cnt ? d1 * a.c : -__builtin_inff();
+        sc[1][kk] = kk < cnt ? d2 * a.c : -__builtin_inff();
+      }
+    }
+    __syncthreads();
+    // Block max per map, raise the running max, rescale.
+    float t1[kPerThread], t2[kPerThread];
+    float bm1 = -__builtin_inff(), bm2 = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      t1[i] = sc[0][tid + i * kThreads];
+      t2[i] = sc[1][tid + i * kThreads];
+      bm1 = fmaxf(bm1, t1[i]);
+      bm2 = fmaxf(bm2, t2[i]);
+    }
+    bm1 = wave_max(bm1);
+    bm2 = wave_max(bm2);
+    if (lane == 0) {
+      red[0][wave][0] = bm1;
+      red[1][wave][0] = bm2;
+    }
+    __syncthreads();
+    bm1 = red[0][0][0];
+    bm2 = red[1][0][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      bm1 = fmaxf(bm1, red[0][w][0]);
+      bm2 = fmaxf(bm2, red[1][w][0]);
+    }
+    const float nm1 = fmaxf(m1, bm1), nm2 = fmaxf(m2, bm2);
+    const float al1 = __builtin_amdgcn_exp2f(m1 - nm1), al2 = __builtin_amdgcn_exp2f(m2 - nm2);
+    m1 = nm1;
+    m2 = nm2;
+    float ps1 = 0.f, ps2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const float p1 = __builtin_amdgcn_exp2f(t1[i] - m1), p2 = __builtin_amdgcn_exp2f(t2[i] - m2);
+      sc[0][tid + i * kThreads] = p1;
+      sc[1][tid + i * kThreads] = p2;
+      ps1 += p1;
+      ps2 += p2;
+    }
+    ps1 = wave_sum(ps1);
+    ps2 = wave_sum(ps2);
+    if (lane == 0) {
+      red[0][wave][1] = ps1;
+      red[1][wave][1] = ps2;
+    }
+    __syncthreads();
+    float bs1 = 0.f, bs2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      bs1 += red[0][w][1];
+      bs2 += red[1][w][1];
+    }
+    l1 = l1 * al1 + bs1;
+    l2 = l2 * al2 + bs2;
+    // P V for both maps (16 keys per pass, 16 lanes per V row).
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o1[k] *= al1;
+      o2[k] *= al2;
+    }
+#pragma unroll 8
+    for (int p = 0; p < kKB / 16; ++p) {
+      const int kk = p * 16 + kq;
+      if (kk < cnt) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(vb + (int64_t)(kb + kk) * a.sv.t);
+        const float p1 = sc[0][kk], p2 = sc[1][kk];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float lo = bf16_lo(x[w]), hi = bf16_hi(x[w]);
+          o1[2 * w] = __builtin_fmaf(p1, lo, o1[2 * w]);
+          o1[2 * w + 1] = __builtin_fmaf(p1, hi, o1[2 * w + 1]);
+          o2[2 * w] = __builtin_fmaf(p2, lo, o2[2 * w]);
+          o2[2 * w + 1] = __builtin_fmaf(p2, hi, o2[2 * w + 1]);
+        }
+      }
+    }
+    __syncthreads();  // sc is rewritten by the next block
+  }
+
+  // Sum the 16 key groups: 4 per wave by shuffles, then the 4 waves in LDS.
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    o1[k] += __shfl_xor(o1[k], 16);
+    o2[k] += __shfl_xor(o2[k], 16);
+    o1[k] += __shfl_xor(o1[k], 32);
+    o2[k] += __shfl_xor(o2[k], 32);
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc[wave][0][8 * cg + k] = o1[k];
+      acc[wave][1][8 * cg + k] = o2[k];
+    }
+  }
+  __syncthreads();
+  {
+    const int map = tid >> 7, ch = tid & 127;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += acc[w][map][ch];
+    float* r = rec + map * kPartialStride;
+    r[2 + ch] = s;
+    if (ch == 0) {
+      r[0] = map ? m2 : m1;
+      r[1] = map ? l2 : l1;
+    }
+  }
+}
+
+// Merge the splits of one (b, h): one thread per channel.
+__global__ void __launch_bounds__(kDv) decode_merge_kernel(DecodeArgs a) {
+  __shared__ float red[2][2];
+  const int ch = threadIdx.x;
+  const int wave = ch >> 6;
+  const int bh = blockIdx.x;
+  const int head = bh % a.H, b = bh / a.H;
+  const float* rec = a.partial + (int64_t)bh * a.splits * 2 * kPartialStride;
+
+  float O[2], Lsum[2];
+  bool empty = false;
+#pragma unroll
+  for (int map = 0; map < 2; ++map) {
+    float M = -__builtin_inff();
+    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, rec[(s * 2 + map) * kPartialStride]);
+    if (M == -__builtin_inff()) empty = true;
+    float L = 0.f, o = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+      const float* r = rec + (s * 2 + map) * kPartialStride;
+      const float w = __builtin_amdgcn_exp2f(r[0] - M);
+      L += w * r[1];
+      o += w * r[2 + ch];
+    }
+    O[map] = o;
+    Lsum[map] = L;
+  }
+  const int64_t row = (int64_t)bh * kDv + ch;
+  float o = 0.f, y = 0.f;
+  if (!empty) {
+    const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
+    {
+#pragma clang fp contract(off)
+      o = O[0] / Lsum[0] - lam * (O[1] / Lsum[1]);
+    }
+    float s = wave_sum(o);
+    if ((ch & 63) == 0) red[0][wave] = s;
+    __syncthreads();
+    const float mu = (red[0][0] + red[0][1]) * (1.0f / kDv);
+    const float d = o - mu;
+    float v = wave_sum(d * d);
+    if ((ch & 63) == 0) red[1][wave] = v;
+    __syncthreads();
+    const float var = (red[1][0] + red[1][1]) * (1.0f / kDv);
+    y = d * (1.0f / __builtin_sqrtf(var + a.eps)) * a.gain[(int64_t)head * kDv + ch];
+  }
+  (void)b;
+  if (a.o_pre) a.o_pre[row] = o;
+  if (a.out_f32)
+    static_cast<float*>(a.out)[row] = y;
+  else
+    static_cast<__bf16*>(a.out)[row] = (__bf16)y;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t bh = (int64_t)a.B * a.H;
+  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)(bh * a.splits)), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)bh), dim3(kDv), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace diffattn

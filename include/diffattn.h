@@ -1,0 +1,140 @@
+/*
+ * diffattn.h - C ABI of the MI355X (gfx950) causal differential-attention
+ * forward library, libdiffattn.so.
+ *
+ * The operation (Motif 2.6B explainer, section "Differential attention" and
+ * the figure 1 caption of section "The block"): per batch row b and head h,
+ *
+ *     o = [ softmax(Q1 K1^T * scale) - lambda_h * softmax(Q2 K2^T * scale) ] V
+ *     y = GroupNorm(o)   (one group per head over its d_v channels:
+ *                         y = (o - mean) / sqrt(var + eps) * gain[h, c],
+ *                         biased variance, no bias)
+ *
+ * with a causal mask (the model is decoder-only, per the edgentiq article on
+ * Motif-2.6B): query i attends to keys j <= i.  Decode attends a single query
+ * to every cached position of its sequence.  scale defaults to 1/sqrt(d_qk).
+ *
+ * Supported head sizes: d_qk = 64, d_v = 128 (Motif 2.6B: 16 heads, hidden
+ * 2048, no grouped-query sharing; explainer section "The block").
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are device memory owned by the caller.  The library allocates
+ *     nothing, keeps no pointer after it returns, and has no global mutable
+ *     state; calls are thread-safe.  Keep buffers alive until the stream work
+ *     has finished.
+ *   - Inputs Q1, Q2, K1, K2, V are bf16 (raw 16-bit patterns).  V is converted
+ *     exactly to fp16 on chip, so its magnitudes must stay below 65504;
+ *     values below 2^-14 lose precision as fp16 subnormals (below 2^-24 they
+ *     flush to zero).
+ *   - Layout [B, T, H, D] with element strides given per tensor by
+ *     diffattn_strides {b, t, h}; the innermost dimension D is contiguous.  A
+ *     NULL strides pointer means C-contiguous [B, T, H, D].  Base pointers
+ *     must be 16-byte aligned and every stride a multiple of 8 elements.
+ *   - Outputs are C-contiguous.  out: bf16 (round to nearest even) or fp32,
+ *     chosen by out_dtype.  o_pre: optional fp32 copy of o before the norm
+ *     (NULL to skip).
+ *   - lambda: one finite value for all heads, or lambda_per_head (device fp32
+ *     [H]) when non-NULL.  No clamping.  gain: device fp32 [H, d_v].
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     returns immediately.  Arguments are validated on the host before any
+ *     HIP call: on an invalid argument the call returns a nonzero status and
+ *     touches no memory.  A failed launch returns DIFFATTN_ERR_HIP.  Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Results are bitwise reproducible run to run (no atomics).
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DIFFATTN_API __attribute__((visibility("default")))
+#else
+#define DIFFATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum diffattn_status {
+    DIFFATTN_OK = 0,
+    DIFFATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+    DIFFATTN_ERR_SHAPE = 2,       /* a size is non-positive or too large */
+    DIFFATTN_ERR_UNSUPPORTED = 3, /* head sizes other than d_qk=64, d_v=128 */
+    DIFFATTN_ERR_LAYOUT = 4,      /* misaligned pointer or stride */
+    DIFFATTN_ERR_WORKSPACE = 5,   /* decode workspace missing or too small */
+    DIFFATTN_ERR_HIP = 6,         /* the HIP runtime refused a launch */
+    DIFFATTN_ERR_VALUE = 7        /* non-finite lambda/eps/scale, eps < 0, bad dtype or split count */
+};
+
+enum diffattn_out_dtype { DIFFATTN_OUT_BF16 = 0, DIFFATTN_OUT_F32 = 1 };
+
+/* Element strides of the three outer dimensions of a [B, T, H, D] tensor. */
+typedef struct {
+    int64_t b, t, h;
+} diffattn_strides;
+
+/*
+ * Causal prefill over T tokens (a square causal map per (b, h)).
+ *   q1, q2, k1, k2 : bf16 [B, T, H, d_qk]
+ *   v              : bf16 [B, T, H, d_v]
+ *   strides        : 5 entries, for q1, q2, k1, k2, v in that order; or NULL
+ *   lambda, lambda_per_head, gain, gn_eps : as above (gn_eps >= 0)
+ *   scale          : score factor; <= 0 selects 1/sqrt(d_qk)
+ *   out            : [B, T, H, d_v], bf16 or fp32 per out_dtype
+ *   o_pre          : fp32 [B, T, H, d_v] or NULL
+ * Limits: B*H <= 2^24, T <= 2^22, ceil(T/128)*B*H <= 2^23.
+ */
+DIFFATTN_API int diffattn_fwd_prefill(const void* q1, const void* q2, const void* k1, const void* k2,
+                         const void* v, const diffattn_strides* strides, int B, int T, int H,
+                         int d_qk, int d_v, float lambda, const float* lambda_per_head,
+                         const float* gain, float gn_eps, float scale, void* out, int out_dtype,
+                         float* o_pre, void* stream);
+
+/*
+ * Bytes of device workspace that diffattn_fwd_decode needs for these sizes:
+ * per (b, h, split) and per map, the split's running max, sum and d_v
+ * unnormalised outputs, in fp32.  num_splits <= 0 means the default (8).
+ * Returns 0 for invalid sizes.
+ */
+DIFFATTN_API size_t diffattn_decode_workspace_bytes(int B, int H, int d_v, int num_splits);
+
+/*
+ * Single-query decode against a KV cache, split over the cached positions
+ * (each split keeps both maps' softmax states; a second kernel merges the
+ * splits, keeping the two maps apart until o = O1/L1 - lambda O2/L2, then
+ * applies the GroupNorm).
+ *   q1, q2         : bf16 [B, H, d_qk], C-contiguous
+ *   k1, k2         : bf16 cache [B, L, H, d_qk]
+ *   v              : bf16 cache [B, L, H, d_v]
+ *   cache_strides  : 3 entries, for k1, k2, v (t = cache position); or NULL
+ *   seqlens        : device int32 [B] cached lengths, or NULL for L.  Values
+ *                    above L count as L; values <= 0 give all-zero output.
+ *   num_splits     : 1..64, or <= 0 for the default (8)
+ *   workspace      : device buffer of >= diffattn_decode_workspace_bytes()
+ *                    bytes, 16-byte aligned; contents need no initialisation
+ *   out            : [B, H, d_v], bf16 or fp32 per out_dtype
+ *   o_pre          : fp32 [B, H, d_v] or NULL
+ * Limits: B*H <= 2^24, L <= 2^26, B*H*num_splits <= 2^23.
+ */
+DIFFATTN_API int diffattn_fwd_decode(const void* q1, const void* q2, const void* k1, const void* k2,
+                        const void* v, const diffattn_strides* cache_strides,
+                        const int32_t* seqlens, int B, int L, int H, int d_qk, int d_v,
+                        float lambda, const float* lambda_per_head, const float* gain,
+                        float gn_eps, float scale, int num_splits, void* workspace,
+                        size_t workspace_bytes, void* out, int out_dtype, float* o_pre,
+                        void* stream);
+
+/* Static text for a status code (never NULL). */
+DIFFATTN_API const char* diffattn_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+DIFFATTN_API int diffattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

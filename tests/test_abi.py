@@ -1,0 +1,100 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, and rejects every invalid argument with its status code before any
+HIP call (so nothing here needs a GPU: the fake pointers are never touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import differential_attention_causal_amd as da
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "diffattn.h")
+
+OK, ENULL, ESHAPE, EUNSUP, ELAYOUT, EWS, EHIP, EVALUE = range(8)
+A = 0x10000  # 16-byte aligned fake device address, never dereferenced
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return re.findall(r"DIFFATTN_API\s+[\w\s\*]+?\b(diffattn_\w+)\s*\(", txt)
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert set(names) == {"diffattn_fwd_prefill", "diffattn_fwd_decode", "diffattn_decode_workspace_bytes",
+                          "diffattn_status_string", "diffattn_abi_version"}
+    lib = ctypes.CDLL(da.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert da.diffattn_abi_version() == 100
+
+
+def test_status_strings():
+    for rc in range(8):
+        s = da.diffattn_status_string(rc)
+        assert s and (rc == 0) == (s == "ok")
+    assert "unknown" in da.diffattn_status_string(99)
+
+
+def _prefill(**kw):
+    args = dict(q1=A, q2=A, k1=A, k2=A, v=A, st=None, B=1, T=128, H=2, dqk=64, dv=128, lam=0.5, lamh=None,
+                gain=A, eps=1e-5, scale=0.0, out=A, odt=0, opre=None, stream=None)
+    args.update(kw)
+    st = args["st"]
+    return da._lib.diffattn_fwd_prefill(args["q1"], args["q2"], args["k1"], args["k2"], args["v"], st,
+                                        args["B"], args["T"], args["H"], args["dqk"], args["dv"], args["lam"],
+                                        args["lamh"], args["gain"], args["eps"], args["scale"], args["out"],
+                                        args["odt"], args["opre"], args["stream"])
+
+
+def _decode(**kw):
+    need = da.diffattn_decode_workspace_bytes(4, 2, 128, 8)
+    args = dict(q1=A, q2=A, k1=A, k2=A, v=A, st=None, sl=None, B=4, L=100, H=2, dqk=64, dv=128, lam=0.8,
+                lamh=None, gain=A, eps=1e-5, scale=0.0, splits=8, ws=A, wsb=need, out=A, odt=0, opre=None,
+                stream=None)
+    args.update(kw)
+    return da._lib.diffattn_fwd_decode(args["q1"], args["q2"], args["k1"], args["k2"], args["v"], args["st"],
+                                       args["sl"], args["B"], args["L"], args["H"], args["dqk"], args["dv"],
+                                       args["lam"], args["lamh"], args["gain"], args["eps"], args["scale"],
+                                       args["splits"], args["ws"], args["wsb"], args["out"], args["odt"],
+                                       args["opre"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(q1=None), ENULL), (dict(v=None), ENULL), (dict(gain=None), ENULL), (dict(out=None), ENULL),
+    (dict(B=0), ESHAPE), (dict(T=0), ESHAPE), (dict(H=-1), ESHAPE), (dict(T=(1 << 22) + 1), ESHAPE),
+    (dict(B=1 << 13, H=1 << 12), ESHAPE), (dict(B=4096, H=16, T=1 << 20), ESHAPE),
+    (dict(dqk=128), EUNSUP), (dict(dv=64), EUNSUP),
+    (dict(k2=A + 2), ELAYOUT), (dict(out=A + 8), ELAYOUT), (dict(opre=A + 4), ELAYOUT),
+    (dict(lam=float("nan")), EVALUE), (dict(lam=float("inf")), EVALUE), (dict(eps=-1.0), EVALUE),
+    (dict(eps=float("nan")), EVALUE), (dict(scale=float("nan")), EVALUE), (dict(odt=2), EVALUE),
+])
+def test_prefill_rejects(kw, rc):
+    assert _prefill(**kw) == rc
+
+
+def test_prefill_rejects_bad_strides():
+    st = (da._Strides * 5)(*[da._Strides(128 * 2 * 64, 2 * 64, 64) for _ in range(5)])
+    st[4] = da._Strides(128 * 2 * 128, 2 * 128, 124)  # not a multiple of 8
+    assert _prefill(st=st) == ELAYOUT
+    st[4] = da._Strides(-8, 256, 128)
+    assert _prefill(st=st) == ELAYOUT
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(q2=None), ENULL), (dict(L=0), ESHAPE), (dict(L=(1 << 26) + 1), ESHAPE), (dict(dqk=32), EUNSUP),
+    (dict(splits=65), EVALUE), (dict(ws=None), EWS), (dict(ws=A + 4), EWS), (dict(wsb=16), EWS),
+    (dict(k1=A + 6), ELAYOUT), (dict(lam=float("nan")), EVALUE), (dict(odt=-1), EVALUE),
+])
+def test_decode_rejects(kw, rc):
+    assert _decode(**kw) == rc
+
+
+def test_workspace_bytes():
+    assert da.diffattn_decode_workspace_bytes(64, 16, 128, 8) == 64 * 16 * 8 * 2 * 130 * 4
+    assert da.diffattn_decode_workspace_bytes(64, 16, 128, 0) == da.diffattn_decode_workspace_bytes(64, 16, 128, 8)
+    assert da.diffattn_decode_workspace_bytes(0, 16, 128, 8) == 0
+    assert da.diffattn_decode_workspace_bytes(1, 1, 64, 8) == 0
+    assert da.diffattn_decode_workspace_bytes(1, 1, 128, 65) == 0
