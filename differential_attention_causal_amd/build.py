@@ -22,6 +22,9 @@ COMMON = [
     # packed fp32 VALU forms stay off: plain fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # keep MFMA accumulators in VGPRs: the O rescale and the epilogue touch them
+    # with VALU ops, and AGPR accumulators cost a copy each way per key tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 SOURCES = ["prefill.hip", "decode.hip", "api.cpp"]
 

@@ -6,10 +6,17 @@
 //   y_i = GroupNorm(o_i)  (one group = the head's 128 channels, with gain)
 // in one pass over the keys, with two independent online-softmax states.
 //
-// Work split.  A workgroup owns 128 consecutive queries of one (b, h): four
-// wave64s with 32 queries each.  Keys stream through LDS in tiles of 32; tiles
-// past the causal diagonal are never loaded, and a wave skips tiles past its
-// own diagonal.
+// Work split.  A workgroup owns 128 consecutive queries of one (b, h); within
+// a group of four wave64s, wave w takes queries 32w .. 32w+31.  Keys stream
+// through LDS in 32-key tiles; tiles past the causal diagonal are never
+// loaded, and a wave skips tiles past its own diagonal.  Two launch shapes:
+//   - one group (4 waves): the default; two workgroups share a CU, and a grid
+//     larger than the chip balances itself in longest-first order;
+//   - two groups (8 waves) that take alternate tiles of the causal range
+//     (group 0 the even ones, group 1 the odd ones), each with its own softmax
+//     states and accumulators, merged through LDS at the end.  For a grid that
+//     fits on the chip in one round, this halves the run time of the longest
+//     query blocks, which would otherwise finish alone.
 //
 // Transposed products.  Each wave computes S^T = K Q^T (32 keys x 32 queries)
 // on v_mfma_f32_32x32x16_bf16 with K from LDS and Q^T held in registers for the
@@ -41,15 +48,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;            // queries per workgroup
-constexpr int kBN = 32;                     // keys per LDS tile
+constexpr int kGroupWaves = 4;              // waves per group, 32 queries each
+constexpr int kBM = 32 * kGroupWaves;       // queries per workgroup
+constexpr int kBN = 32;                     // keys per tile (one tile per group per step)
 constexpr int kKRow = kDqk * 2;             // 128 bytes per key row
 constexpr int kKBytes = kBN * kKRow;        // 4 KiB per K tile
 constexpr int kVRow = (kBN + 8) * 2;        // 80 bytes per V^T channel row (16-byte pad)
 constexpr int kVBytes = kDv * kVRow;        // 10 KiB per V^T tile
-constexpr int kStage = 2 * kKBytes + kVBytes;
+constexpr int kTile = 2 * kKBytes + kVBytes;
+constexpr int kTileThreads = 256;           // threads that stage one tile
+// End-of-loop merge buffer (reuses the stage memory): one map's O^T of the four
+// group-1 waves stored [wave][register][lane], then their (max, sum) pairs.
+constexpr int kMergeO = kGroupWaves * 64 * 64 * 4;
+constexpr int kMergeML = kGroupWaves * 64 * 2 * 4;
+static_assert(kMergeO + kMergeML <= 2 * 2 * kTile, "merge buffer must fit in the stage memory");
 constexpr float kSlack = 8.0f;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -62,6 +74,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // holds in its score accumulator.  That is a swap of bits 0 and 1 of kg.
 __device__ __forceinline__ int kVPos(int kg) { return (kg & 4) | ((kg & 1) << 1) | ((kg >> 1) & 1); }
 
+// 16-byte chunk swizzle of K rows: row r's chunk c sits at c ^ kSwz(r).  Any 8
+// consecutive rows, and the 8 even or the 8 odd rows of any 16, read the same
+// logical chunk from 8 distinct chunk slots, so a 16-byte read by 8 or 16
+// lanes (one key row each) is free of bank conflicts on 32 or 64 banks.
+__device__ __forceinline__ int kSwz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 load8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 
@@ -70,36 +88,43 @@ struct Staged {
   u32x2 v[4];
 };
 
-// Global -> registers for key tile starting at k0.  Thread t loads 16 bytes of
-// K1 and K2 (key t/8, chunk t%8) and a 4-key x 4-channel block of V.
+// Global -> registers for one step: one 32-key tile per group, keys from k0 on
+// (keys at or past kend read as zero).  Threads 256g .. 256g+255 stage group
+// g's tile.  Within a tile, thread t loads 16 bytes of K1 and K2 (key t/8,
+// chunk t%8) and a 4-key x 4-channel block of V (keys 4(t%8).., channels
+// 4(t/8)..).
 __device__ __forceinline__ void stage_load(Staged& st, const PrefillArgs& a, int b, int head, int k0,
-                                           int tid) {
-  const int kr = tid >> 3, ch = tid & 7;
-  const int key = k0 + kr;
-  if (key < a.T) {
+                                           int kend, int tid) {
+  const int tile = tid / kTileThreads, t = tid % kTileThreads;
+  const int kbase = k0 + tile * kBN;
+  const int kr = t >> 3, ch = t & 7;
+  const int key = kbase + kr;
+  if (key < kend) {
     st.k1 = load16(a.k1 + (int64_t)b * a.sk1.b + (int64_t)key * a.sk1.t + (int64_t)head * a.sk1.h + 8 * ch);
     st.k2 = load16(a.k2 + (int64_t)b * a.sk2.b + (int64_t)key * a.sk2.t + (int64_t)head * a.sk2.h + 8 * ch);
   } else {
     st.k1 = u32x4{0, 0, 0, 0};
     st.k2 = u32x4{0, 0, 0, 0};
   }
-  const int kg = tid & 7, cg = tid >> 3;
+  const int kg = t & 7, cg = t >> 3;
   const uint16_t* vb = a.v + (int64_t)b * a.sv.b + (int64_t)head * a.sv.h + 4 * cg;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int kv = k0 + 4 * kg + r;
-    st.v[r] = (kv < a.T) ? load8(vb + (int64_t)kv * a.sv.t) : u32x2{0, 0};
+    const int kv = kbase + 4 * kg + r;
+    st.v[r] = (kv < kend) ? load8(vb + (int64_t)kv * a.sv.t) : u32x2{0, 0};
   }
 }
 
-// Registers -> LDS: K rows with the 16-byte chunk index XOR-swizzled by the
-// row, V transposed to [channel][key] in fp16 with the kVPos key order.
+// Registers -> LDS: K rows with swizzled 16-byte chunks, V transposed to
+// [channel][key] in fp16 with the kVPos key order.
 __device__ __forceinline__ void stage_store(const Staged& st, char* stage, int tid) {
-  const int kr = tid >> 3, ch = tid & 7;
-  const int koff = kr * kKRow + ((ch ^ (kr & 7)) << 4);
-  *reinterpret_cast<u32x4*>(stage + koff) = st.k1;
-  *reinterpret_cast<u32x4*>(stage + kKBytes + koff) = st.k2;
-  const int kg = tid & 7, cg = tid >> 3;
+  const int tile = tid / kTileThreads, t = tid % kTileThreads;
+  char* base = stage + tile * kTile;
+  const int kr = t >> 3, ch = t & 7;
+  const int koff = kr * kKRow + ((ch ^ kSwz(kr)) << 4);
+  *reinterpret_cast<u32x4*>(base + koff) = st.k1;
+  *reinterpret_cast<u32x4*>(base + kKBytes + koff) = st.k2;
+  const int kg = t & 7, cg = t >> 3;
   float e[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -108,7 +133,7 @@ __device__ __forceinline__ void stage_store(const Staged& st, char* stage, int t
     e[r][2] = bf16_lo(st.v[r].y);
     e[r][3] = bf16_hi(st.v[r].y);
   }
-  char* vt = stage + 2 * kKBytes + kVPos(kg) * 8;
+  char* vt = base + 2 * kKBytes + kVPos(kg) * 8;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     f16x4 h = {(_Float16)e[0][c], (_Float16)e[1][c], (_Float16)e[2][c], (_Float16)e[3][c]};
@@ -117,19 +142,23 @@ __device__ __forceinline__ void stage_store(const Staged& st, char* stage, int t
 }
 
 // One map's online-softmax step on a 32x32 score tile held as S^T (lane: one
-// query, 16 keys).  Updates the running max m (base-2 units) and the lane's
-// partial sum l, rescales that map's O^T when the max is raised, and returns
-// the tile's probabilities as the two f16 operands of the P^T V^T product.
+// query, 16 keys).  Keeps the running reference max m (base-2 units) unless
+// a score lies more than kSlack above it: only when some lane of the wave sees
+// one are the two lanes of each query pair reconciled, and the queries over
+// the bound raise m to their tile max and rescale that map's O^T and partial
+// sum l.  Returns the tile's probabilities
+// 2^(c s - m) <= 2^kSlack as the two f16 operands of the P^T V^T product.
 __device__ __forceinline__ void softmax_step(f32x16& s, float c, float& m, float& l, f32x16 (&O)[4],
                                              f16x8& p0, f16x8& p1) {
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mc = mx * c;
-  const bool need = mc > m + kSlack;
-  if (__any(need)) {
-    const float mn = need ? mc : m;
+  if (__any(mx * c > m + kSlack)) {
+    // Each query decides from its own scores only (its two lanes agree after
+    // the exchange), so a row's result never depends on other rows' data.
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mc = mx * c;
+    const float mn = mc > m + kSlack ? mc : m;  // finite: every query sees a key in its first tile
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     l *= alpha;
 #pragma unroll
@@ -151,11 +180,50 @@ __device__ __forceinline__ void softmax_step(f32x16& s, float c, float& m, float
   }
 }
 
-__global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
+// Merge one map's (m, l, O^T) of a group-1 wave into the matching group-0 wave
+// through LDS.  Every thread of the workgroup calls it (it holds two barriers).
+__device__ __forceinline__ void merge_map(char* smem, int grp, int wq, int lane, bool live, float& m, float& l,
+                                          f32x16 (&O)[4]) {
+  float* mo = reinterpret_cast<float*>(smem);
+  float* ml = reinterpret_cast<float*>(smem + kMergeO);
+  if (grp == 1 && live) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mo[((wq * 64) + cb * 16 + i) * 64 + lane] = O[cb][i];
+    ml[(wq * 64 + lane) * 2 + 0] = m;
+    ml[(wq * 64 + lane) * 2 + 1] = l;
+  }
+  __syncthreads();
+  if (grp == 0 && live) {
+    const float mb = ml[(wq * 64 + lane) * 2 + 0];
+    const float lb = ml[(wq * 64 + lane) * 2 + 1];
+    const float mn = fmaxf(m, mb);  // finite: group 0 always holds tile 0
+    const float aa = __builtin_amdgcn_exp2f(m - mn);
+    const float ab = __builtin_amdgcn_exp2f(mb - mn);
+    l = l * aa + lb * ab;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[cb][i] = O[cb][i] * aa + mo[((wq * 64) + cb * 16 + i) * 64 + lane] * ab;
+    m = mn;
+  }
+  __syncthreads();
+}
+
+// kGroups wave groups of four waves share a workgroup's 128 queries and split
+// its key tiles.  Two waves per SIMD (<= 256 VGPRs each): one wave's softmax
+// VALU work overlaps the other's matrix products.
+template <int kGroups>
+__global__ void __launch_bounds__(64 * kGroupWaves * kGroups) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_kernel(PrefillArgs a) {
+  constexpr int kStage = kGroups * kTile;  // one step: a tile for each group
   __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int grp = wave / kGroupWaves;  // which half of the key tiles
+  const int wq = wave % kGroupWaves;   // which 32 queries
   const int lane = tid & 63;
   const int hf = lane >> 5;  // lane half
   const int lq = lane & 31;  // query within the wave
@@ -170,10 +238,12 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   const int head = bh % a.H;
   const int b = bh / a.H;
 
-  const int q_first = qb * kBM + 32 * wave;  // first query of this wave
-  const int q = q_first + lq;                // this lane's query
+  const int q_first = qb * kBM + 32 * wq;  // first query of this wave
+  const int q = q_first + lq;              // this lane's query
   const bool wave_live = q_first < a.T;
-  const int last_tile = min(qb * (kBM / kBN) + (kBM / kBN) - 1, (a.T - 1) / kBN);
+  const int ntiles = min(qb * (kBM / kBN) + (kBM / kBN), (a.T + kBN - 1) / kBN);
+  const int kend = min(a.T, ntiles * kBN);
+  const int nsteps = (ntiles + kGroups - 1) / kGroups;
   const int wave_last_tile = q_first / kBN;  // the wave's diagonal tile
 
   // Q1^T, Q2^T operands: lane holds query lq, dims 16s + 8hf .. +7.
@@ -199,26 +269,29 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   }
   float m1 = -__builtin_inff(), m2 = -__builtin_inff(), l1 = 0.f, l2 = 0.f;
   const float c = a.c;
+  const int ksw = kSwz(lq);
 
   Staged st;
-  stage_load(st, a, b, head, 0, tid);
+  stage_load(st, a, b, head, 0, kend, tid);
   stage_store(st, smem, tid);
   __syncthreads();
 
-  for (int j = 0; j <= last_tile; ++j) {
-    char* cur = smem + (j & 1) * kStage;
-    char* nxt = smem + ((j + 1) & 1) * kStage;
-    const bool more = j < last_tile;
-    if (more) stage_load(st, a, b, head, (j + 1) * kBN, tid);
+  for (int it = 0; it < nsteps; ++it) {
+    char* cur = smem + (it & 1) * kStage;
+    char* nxt = smem + ((it + 1) & 1) * kStage;
+    const bool more = it + 1 < nsteps;
+    if (more) stage_load(st, a, b, head, (it + 1) * kGroups * kBN, kend, tid);
 
+    const int j = it * kGroups + grp;  // this group's tile
     if (wave_live && j <= wave_last_tile) {
+      const char* kt = cur + grp * kTile;
       f32x16 s1 = f32x16{}, s2 = f32x16{};
       const int krow = lq * kKRow;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int off = krow + (((2 * s + hf) ^ (lq & 7)) << 4);
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(cur + off);
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(cur + kKBytes + off);
+        const int off = krow + (((2 * s + hf) ^ ksw) << 4);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + off);
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kt + kKBytes + off);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qa[s], s1, 0, 0, 0);
         s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qb2[s], s2, 0, 0, 0);
       }
@@ -237,7 +310,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
       f16x8 p1a, p1b, p2a, p2b;
       softmax_step(s1, c, m1, l1, O1, p1a, p1b);
       softmax_step(s2, c, m2, l2, O2, p2a, p2b);
-      const char* vt = cur + 2 * kKBytes + lq * kVRow + hf * 16;
+      const char* vt = kt + 2 * kKBytes + lq * kVRow + hf * 16;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const f16x8 va0 = *reinterpret_cast<const f16x8*>(vt + cb * 32 * kVRow);
@@ -253,7 +326,13 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  if (!wave_live) return;
+  // Fold group 1's states into group 0 (the stage memory is free: the last
+  // loop iteration ended with a barrier after every read of it).
+  if constexpr (kGroups == 2) {
+    merge_map(smem, grp, wq, lane, wave_live, m1, l1, O1);
+    merge_map(smem, grp, wq, lane, wave_live, m2, l2, O2);
+  }
+  if (grp != 0 || !wave_live) return;
 
   // Combine the two maps, then GroupNorm over the 128 channels of the query.
   // Lane (hf, lq) holds channels 32cb + 8(i/4) + 4hf + i%4; its partner lane
@@ -322,7 +401,19 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int nqb = (a.T + kBM - 1) / kBM;
   const int64_t grid = (int64_t)nqb * a.B * a.H;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  // A grid that fits on the chip in one round (two 4-wave workgroups per CU)
+  // leaves the CUs holding the longest query blocks working alone at the end;
+  // splitting each workgroup's key range over two wave groups halves that
+  // tail.  Larger grids balance by themselves in longest-first order and run
+  // better as independent 4-wave workgroups.
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (grid <= 2 * (int64_t)cus)
+    hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)grid), dim3(64 * kGroupWaves * 2), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<1>, dim3((unsigned)grid), dim3(64 * kGroupWaves), 0, stream, a);
   return hipGetLastError();
 }
 
