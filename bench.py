@@ -33,30 +33,33 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FLOP_PER_PAIR = 768
 PREFILL_WL = "prefill_b1_t4096_h16"
 DECODE_WL = "decode_b64_l4096_h16"
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_kernel_b1_t4096_h16_hbm_counters.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "differential_attention_causal_amd", "csrc", f)
-                  for f in ("prefill.hip", "kernels.h")]
+CSRC = os.path.join(ROOT, "differential_attention_causal_amd", "csrc")
+PREFILL_PMC = os.path.join(ROOT, "profiles", "prefill_kernel_b1_t4096_h16_hbm_counters.txt")
+PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("prefill.hip", "kernels.h")]
+DECODE_PMC = os.path.join(ROOT, "profiles", "decode_split_kernel_b64_l4096_h16_hbm_counters.txt")
+DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode.hip", "kernels.h")]
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(sources=PREFILL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per prefill launch from the committed counter summary, or None
-    when there is none or the kernel source changed since it was taken."""
-    if not os.path.exists(PMC_SUMMARY):
+def read_traffic(summary=PREFILL_PMC, sources=PREFILL_SOURCES):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's readings), or None when there is none
+    or the kernel source changed since the counters were taken."""
+    if not os.path.exists(summary):
         return None
     kv = {}
-    for line in open(PMC_SUMMARY):
+    for line in open(summary):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_digest():
+    if kv.get("kernel_source_sha256_16") != kernel_source_digest(sources):
         return None
     try:
         return int(float(kv["hbm_bytes_per_dispatch"]))
@@ -209,7 +212,7 @@ def main() -> int:
                     "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4)},
         "decode": {"workload": DECODE_WL, "us_mean": round(d_s * 1e6, 2), "us_min": round(float(d_ms.min()) * 1e3, 2),
                    "bytes": d_bytes, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                   "splits": dw.num_splits},
+                   "splits": dw.num_splits, "traffic": read_traffic(DECODE_PMC, DECODE_SOURCES)},
         "wall_s_timed": round(wall, 3),
         "kernel_source_sha256_16": kernel_source_digest(),
     }
