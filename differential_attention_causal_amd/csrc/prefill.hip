@@ -88,31 +88,47 @@ struct Staged {
   u32x2 v[4];
 };
 
+// Buffer resource over key rows k0 .. kend-1 of one (b, h) (row stride
+// `stride` elements, rows of `row` elements): loads past the last valid row
+// return zero in hardware, so tile loads need no per-row branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t stride, int k0, int kend,
+                                                             int row) {
+  const uint16_t* p = base + (int64_t)k0 * stride;
+  const int nrec = kend > k0 ? (int)(((int64_t)(kend - k0 - 1) * stride + row) * 2) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, nrec, 0x00020000);
+}
+
+// Per-thread byte offsets of the staging loads inside a tile (see stage_load).
+struct StageOffsets {
+  uint32_t k1, k2, v;
+};
+
+__device__ __forceinline__ StageOffsets stage_offsets(const PrefillArgs& a, int tid) {
+  const int t = tid % kTileThreads;
+  const int kr = t >> 3, ch = t & 7, kg = t & 7, cg = t >> 3;
+  StageOffsets o;
+  o.k1 = (uint32_t)((kr * a.sk1.t + 8 * ch) * 2);
+  o.k2 = (uint32_t)((kr * a.sk2.t + 8 * ch) * 2);
+  o.v = (uint32_t)((4 * kg * a.sv.t + 4 * cg) * 2);
+  return o;
+}
+
 // Global -> registers for one step: one 32-key tile per group, keys from k0 on
 // (keys at or past kend read as zero).  Threads 256g .. 256g+255 stage group
 // g's tile.  Within a tile, thread t loads 16 bytes of K1 and K2 (key t/8,
 // chunk t%8) and a 4-key x 4-channel block of V (keys 4(t%8).., channels
-// 4(t/8)..).
-__device__ __forceinline__ void stage_load(Staged& st, const PrefillArgs& a, int b, int head, int k0,
-                                           int kend, int tid) {
-  const int tile = tid / kTileThreads, t = tid % kTileThreads;
+// 4(t/8)..).  kb1, kb2, vb point at key 0 of this (b, h).
+__device__ __forceinline__ void stage_load(Staged& st, const PrefillArgs& a, const uint16_t* kb1,
+                                           const uint16_t* kb2, const uint16_t* vb, const StageOffsets& off,
+                                           int k0, int kend, int tid) {
+  const int tile = __builtin_amdgcn_readfirstlane(tid / kTileThreads);
   const int kbase = k0 + tile * kBN;
-  const int kr = t >> 3, ch = t & 7;
-  const int key = kbase + kr;
-  if (key < kend) {
-    st.k1 = load16(a.k1 + (int64_t)b * a.sk1.b + (int64_t)key * a.sk1.t + (int64_t)head * a.sk1.h + 8 * ch);
-    st.k2 = load16(a.k2 + (int64_t)b * a.sk2.b + (int64_t)key * a.sk2.t + (int64_t)head * a.sk2.h + 8 * ch);
-  } else {
-    st.k1 = u32x4{0, 0, 0, 0};
-    st.k2 = u32x4{0, 0, 0, 0};
-  }
-  const int kg = t & 7, cg = t >> 3;
-  const uint16_t* vb = a.v + (int64_t)b * a.sv.b + (int64_t)head * a.sv.h + 4 * cg;
+  st.k1 = __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc(kb1, a.sk1.t, kbase, kend, kDqk), off.k1, 0, 0);
+  st.k2 = __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc(kb2, a.sk2.t, kbase, kend, kDqk), off.k2, 0, 0);
+  const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vb, a.sv.t, kbase, kend, kDv);
+  const int vrow = (int)(a.sv.t * 2);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int kv = kbase + 4 * kg + r;
-    st.v[r] = (kv < kend) ? load8(vb + (int64_t)kv * a.sv.t) : u32x2{0, 0};
-  }
+  for (int r = 0; r < 4; ++r) st.v[r] = __builtin_amdgcn_raw_buffer_load_b64(rv, off.v, r * vrow, 0);
 }
 
 // Registers -> LDS: K rows with swizzled 16-byte chunks, V transposed to
@@ -271,8 +287,13 @@ prefill_kernel(PrefillArgs a) {
   const float c = a.c;
   const int ksw = kSwz(lq);
 
+  const uint16_t* kb1 = a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h;
+  const uint16_t* kb2 = a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h;
+  const uint16_t* vbase = a.v + (int64_t)b * a.sv.b + (int64_t)head * a.sv.h;
+  const StageOffsets soff = stage_offsets(a, tid);
+
   Staged st;
-  stage_load(st, a, b, head, 0, kend, tid);
+  stage_load(st, a, kb1, kb2, vbase, soff, 0, kend, tid);
   stage_store(st, smem, tid);
   __syncthreads();
 
@@ -280,7 +301,7 @@ prefill_kernel(PrefillArgs a) {
     char* cur = smem + (it & 1) * kStage;
     char* nxt = smem + ((it + 1) & 1) * kStage;
     const bool more = it + 1 < nsteps;
-    if (more) stage_load(st, a, b, head, (it + 1) * kGroups * kBN, kend, tid);
+    if (more) stage_load(st, a, kb1, kb2, vbase, soff, (it + 1) * kGroups * kBN, kend, tid);
 
     const int j = it * kGroups + grp;  // this group's tile
     if (wave_live && j <= wave_last_tile) {
