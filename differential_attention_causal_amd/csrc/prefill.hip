@@ -43,6 +43,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -182,18 +183,23 @@ __device__ __forceinline__ void softmax_step(f32x16& s, float c, float& m, float
     m = mn;
   }
   float p[16];
-  float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m));
-    sum += p[i];
-  }
-  l += sum;
+  for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m));
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     p0[j] = (_Float16)p[j];
     p1[j] = (_Float16)p[8 + j];
   }
+  // The sum runs over the rounded f16 values the product uses, two per
+  // instruction (dot product with (1, 1), fp32 accumulation).
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  float sum = l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sum = __builtin_amdgcn_fdot2(f16x2{p0[2 * j], p0[2 * j + 1]}, one, sum, false);
+    sum = __builtin_amdgcn_fdot2(f16x2{p1[2 * j], p1[2 * j + 1]}, one, sum, false);
+  }
+  l = sum;
 }
 
 // Merge one map's (m, l, O^T) of a group-1 wave into the matching group-0 wave
