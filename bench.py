@@ -14,6 +14,9 @@ object covers the prefill kernel against the dense bf16/fp16 MFMA peak; the
 cpu_baseline object times the fp64 oracle on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+
+The default warm-up (2000 steps, about a second of GPU work) lets the GPU reach
+its steady clocks before the timed region; the timed region is 200 steps.
     python bench.py --copy-calibration     # plain device copy, for HBM counter scaling
 """
 from __future__ import annotations
@@ -109,8 +112,8 @@ def copy_calibration(steps: int) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()

@@ -219,39 +219,61 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the splits of one (b, h): one thread per channel.
+// Merge the splits of one (b, h): one thread per channel.  Every split
+// record's (max, sum, O[channel]) is loaded up front, kMergeChunk splits at a
+// time with independent loads, so the kernel waits for memory once per chunk.
+constexpr int kMergeChunk = 8;
+
 __global__ void __launch_bounds__(kDv) decode_merge_kernel(DecodeArgs a) {
   __shared__ float red[2][2];
   const int ch = threadIdx.x;
   const int wave = ch >> 6;
   const int bh = blockIdx.x;
-  const int head = bh % a.H, b = bh / a.H;
+  const int head = bh % a.H;
   const float* rec = a.partial + (int64_t)bh * a.splits * 2 * kPartialStride;
 
-  float O[2], Lsum[2];
-  bool empty = false;
+  float M[2] = {-__builtin_inff(), -__builtin_inff()};
+  float L[2] = {0.f, 0.f}, O[2] = {0.f, 0.f};
+  for (int s0 = 0; s0 < a.splits; s0 += kMergeChunk) {
+    float m[kMergeChunk][2], l[kMergeChunk][2], o[kMergeChunk][2];
 #pragma unroll
-  for (int map = 0; map < 2; ++map) {
-    float M = -__builtin_inff();
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, rec[(s * 2 + map) * kPartialStride]);
-    if (M == -__builtin_inff()) empty = true;
-    float L = 0.f, o = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float* r = rec + (s * 2 + map) * kPartialStride;
-      const float w = __builtin_amdgcn_exp2f(r[0] - M);
-      L += w * r[1];
-      o += w * r[2 + ch];
+    for (int u = 0; u < kMergeChunk; ++u) {
+#pragma unroll
+      for (int map = 0; map < 2; ++map) {
+        const bool ok = s0 + u < a.splits;
+        const float* r = rec + ((s0 + u) * 2 + map) * kPartialStride;
+        m[u][map] = ok ? r[0] : -__builtin_inff();
+        l[u][map] = ok ? r[1] : 0.f;
+        o[u][map] = ok ? r[2 + ch] : 0.f;
+      }
     }
-    O[map] = o;
-    Lsum[map] = L;
+#pragma unroll
+    for (int map = 0; map < 2; ++map) {
+      float mn = M[map];
+#pragma unroll
+      for (int u = 0; u < kMergeChunk; ++u) mn = fmaxf(mn, m[u][map]);
+      if (mn == -__builtin_inff()) continue;  // nothing seen yet (uniform)
+      const float sc = __builtin_amdgcn_exp2f(M[map] - mn);
+      float Ls = L[map] * sc, Os = O[map] * sc;
+#pragma unroll
+      for (int u = 0; u < kMergeChunk; ++u) {
+        const float w = __builtin_amdgcn_exp2f(m[u][map] - mn);
+        Ls += w * l[u][map];
+        Os += w * o[u][map];
+      }
+      M[map] = mn;
+      L[map] = Ls;
+      O[map] = Os;
+    }
   }
+  const bool empty = M[0] == -__builtin_inff();  // no cached position (uniform)
   const int64_t row = (int64_t)bh * kDv + ch;
   float o = 0.f, y = 0.f;
   if (!empty) {
     const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
     {
 #pragma clang fp contract(off)
-      o = O[0] / Lsum[0] - lam * (O[1] / Lsum[1]);
+      o = O[0] / L[0] - lam * (O[1] / L[1]);
     }
     float s = wave_sum(o);
     if ((ch & 63) == 0) red[0][wave] = s;
@@ -264,7 +286,6 @@ __global__ void __launch_bounds__(kDv) decode_merge_kernel(DecodeArgs a) {
     const float var = (red[1][0] + red[1][1]) * (1.0f / kDv);
     y = d * (1.0f / __builtin_sqrtf(var + a.eps)) * a.gain[(int64_t)head * kDv + ch];
   }
-  (void)b;
   if (a.o_pre) a.o_pre[row] = o;
   if (a.out_f32)
     static_cast<float*>(a.out)[row] = y;
