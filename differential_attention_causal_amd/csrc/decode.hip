@@ -13,6 +13,8 @@
 // bf16 products, fp32 accumulation) -> LDS; block max and exp2 in fp32 (P stays
 // fp32 here; there is no matrix product to feed); then the P V pass with 16
 // lanes per 256-byte V row.  Scores are kept in base-2 units (c = scale log2 e).
+// Every cache byte is read exactly once, so the cache loads are non-temporal:
+// they stream past the caches instead of evicting other data.
 #include "kernels.h"
 
 namespace diffattn {
@@ -95,8 +97,8 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
       float d1 = 0.f, d2 = 0.f;
       if (kk < cnt) {
         const int64_t pos = kb + kk;
-        const u32x4 x1 = *reinterpret_cast<const u32x4*>(k1b + pos * a.sk1.t);
-        const u32x4 x2 = *reinterpret_cast<const u32x4*>(k2b + pos * a.sk2.t);
+        const u32x4 x1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k1b + pos * a.sk1.t));
+        const u32x4 x2 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k2b + pos * a.sk2.t));
         d1 = dot8(q1, x1, 0.f);
         d2 = dot8(q2, x2, 0.f);
       }
@@ -174,7 +176,7 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
     for (int p = 0; p < kKB / 16; ++p) {
       const int kk = p * 16 + kq;
       if (kk < cnt) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(vb + (int64_t)(kb + kk) * a.sv.t);
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (int64_t)(kb + kk) * a.sv.t));
         const float p1 = sc[0][kk], p2 = sc[1][kk];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
