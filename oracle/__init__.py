@@ -36,19 +36,25 @@ def build() -> str:
     return _LIB_PATH
 
 
+def _bind(path):
+    """ctypes handle of an oracle library at `path` (the tests also bind
+    deliberately broken copies, to check that the pins catch them)."""
+    lib = ctypes.CDLL(path)
+    P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+    lib.oracle_prefill.restype = I
+    lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P, D, D, P,
+                                   ctypes.c_int64, P, P, I]
+    lib.oracle_decode.restype = I
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, D, D, P, P, I]
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build()
-        lib = ctypes.CDLL(_LIB_PATH)
-        P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
-        lib.oracle_prefill.restype = I
-        lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P, D, D, P,
-                                       ctypes.c_int64, P, P, I]
-        lib.oracle_decode.restype = I
-        lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, D, D, P, P, I]
-        _lib = lib
+        _lib = _bind(_LIB_PATH)
     return _lib
 
 
@@ -68,7 +74,7 @@ def _lam(lam, H):
     return np.ascontiguousarray(lam)
 
 
-def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0):
+def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib=None):
     """Causal prefill in fp64.
 
     q1, q2, k1, k2: bf16 bits [B, T, H, d_qk]; v: bf16 bits [B, T, H, d_v].
@@ -99,7 +105,7 @@ def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0):
         n = flat.shape[0]
     o = np.empty((n, d_v), dtype=np.float64)
     y = np.empty((n, d_v), dtype=np.float64)
-    rc = _load().oracle_prefill(q1.ctypes.data, q2.ctypes.data, k1.ctypes.data, k2.ctypes.data,
+    rc = (lib or _load()).oracle_prefill(q1.ctypes.data, q2.ctypes.data, k1.ctypes.data, k2.ctypes.data,
                                 v.ctypes.data, B, T, H, d_qk, d_v, lam.ctypes.data,
                                 gain.ctypes.data, float(eps), float(scale),
                                 None if flat is None else flat.ctypes.data, n,
@@ -111,7 +117,7 @@ def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0):
     return o, y
 
 
-def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0):
+def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0, lib=None):
     """Single-query decode in fp64: q [B, H, d_qk] against caches [B, L, H, d].
 
     seqlens: optional [B] cached lengths (above L counts as L; <= 0 gives zeros).
@@ -133,7 +139,7 @@ def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0):
             raise ValueError("seqlens must be [B]")
     o = np.empty((B, H, d_v), dtype=np.float64)
     y = np.empty((B, H, d_v), dtype=np.float64)
-    rc = _load().oracle_decode(q1.ctypes.data, q2.ctypes.data, k1.ctypes.data, k2.ctypes.data,
+    rc = (lib or _load()).oracle_decode(q1.ctypes.data, q2.ctypes.data, k1.ctypes.data, k2.ctypes.data,
                                v.ctypes.data, None if sl is None else sl.ctypes.data,
                                B, L, H, d_qk, d_v, lam.ctypes.data, gain.ctypes.data,
                                float(eps), float(scale), o.ctypes.data, y.ctypes.data,

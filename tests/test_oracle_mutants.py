@@ -1,0 +1,114 @@
+"""Planted mistakes: each mutant copy of the oracle's C source carries one
+plausible bug, is built on the CPU, and must fail at least one of the pins
+(the same checks tests/test_oracle.py applies to the real oracle).  This is
+how the pins are shown to catch a dropped term, a wrong sign or index, or a
+transposed operand."""
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.workloads import Workload
+from tests import bruteforce
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "diffattn_oracle.c")
+
+MUTANTS = {
+    "scale dropped": ("p1[j] = scale * a;", "p1[j] = a;"),
+    "not causal": ("(int64_t)H * d_qk, (int64_t)H * d_v, i + 1, d_qk, d_v,",
+                   "(int64_t)H * d_qk, (int64_t)H * d_v, T, d_qk, d_v,"),
+    "lambda sign": ("p1[j] = p1[j] - lam * p2[j];", "p1[j] = p1[j] + lam * p2[j];"),
+    "second map uses K1": ("b += bf16_to_f64(q2[c]) * bf16_to_f64(k2[j * kstride + c]);",
+                           "b += bf16_to_f64(q2[c]) * bf16_to_f64(k1[j * kstride + c]);"),
+    "unbiased variance": ("    var /= d_v;", "    var /= (d_v - 1);"),
+    "eps outside sqrt": ("double inv = 1.0 / sqrt(var + eps);", "double inv = 1.0 / (sqrt(var) + eps);"),
+    "gain dropped": ("y[c] = (o[c] - mu) * inv * (double)gain[c];", "y[c] = (o[c] - mu) * inv;"),
+    "lambda of head 0": ("scale, lam[h], gain + (int64_t)h * d_v, eps, p1, p2,\n                                   o_pre + r * d_v",
+                         "scale, lam[0], gain + (int64_t)h * d_v, eps, p1, p2,\n                                   o_pre + r * d_v"),
+    "V read with K stride": ("(int64_t)H * d_qk, (int64_t)H * d_v, i + 1, d_qk, d_v,",
+                             "(int64_t)H * d_qk, (int64_t)H * d_qk, i + 1, d_qk, d_v,"),
+    "mean over wrong count": ("    mu /= d_v;", "    mu /= (d_v + 1);"),
+    "second softmax short": ("    softmax_inplace(p2, n_keys);", "    softmax_inplace(p2, n_keys > 1 ? n_keys - 1 : 1);"),
+}
+
+
+def _build(src_text, tmp, name):
+    c = os.path.join(tmp, name + ".c")
+    so = os.path.join(tmp, name + ".so")
+    with open(c, "w") as f:
+        f.write(src_text)
+    subprocess.check_call(["gcc", "-O1", "-fopenmp", "-shared", "-fPIC", "-o", so, c, "-lm"])
+    return oracle._bind(so)
+
+
+def _inputs(B=2, T=12, H=2, seed=31, d_qk=8, d_v=16):
+    wl = Workload("m", "prefill", B=B, T=T, H=H, seed=seed, lam=0.5, d_qk=d_qk, d_v=d_v)
+    return synth.make_prefill_inputs(wl)
+
+
+def _f64(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _pins(lib):
+    """Names of the pins this library fails (empty for a correct oracle)."""
+    failed = []
+
+    def run(x, lam, **kw):
+        return oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], lam, x["gain"], x["eps"],
+                              x["scale"], lib=lib, **kw)
+
+    x = _inputs()
+    # lambda = 0: causal SDPA + group_norm
+    o, y = run(x, 0.0)
+    q = torch.from_numpy(_f64(x["q1"])).permute(0, 2, 1, 3)
+    k = torch.from_numpy(_f64(x["k1"])).permute(0, 2, 1, 3)
+    v = torch.from_numpy(_f64(x["v"])).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=x["scale"])
+    ref = ref.permute(0, 2, 1, 3).numpy()
+    B, T, H, D = ref.shape
+    gn = torch.nn.functional.group_norm(torch.from_numpy(ref.reshape(B * T, H * D)), H,
+                                        weight=torch.from_numpy(x["gain"].astype(np.float64).reshape(-1)),
+                                        eps=x["eps"]).numpy().reshape(B, T, H, D)
+    if not (np.allclose(o, ref, rtol=0, atol=1e-12) and np.allclose(y, gn, rtol=0, atol=1e-10)):
+        failed.append("lambda0")
+    # V = ones: o = 1 - lambda_h
+    lam = np.array([0.3, 0.9])
+    xo = dict(x, v=np.full_like(x["v"], 0x3F80))
+    o, _ = run(xo, lam)
+    if not all(np.allclose(o[:, :, h], 1 - lam[h], atol=1e-12) for h in range(2)):
+        failed.append("row sums")
+    # brute force at T <= 16 (a few rows)
+    lam = np.array([0.8, -0.4])
+    o, y = run(x, lam)
+    for b, i, h in [(0, 0, 0), (1, 11, 1), (0, 6, 1)]:
+        ob, yb = bruteforce.row(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], b, i, h, lam[h], x["gain"],
+                                x["eps"], x["scale"])
+        if not (np.allclose(o[b, i, h], [float(t) for t in ob], rtol=1e-12, atol=1e-14)
+                and np.allclose(y[b, i, h], [float(t) for t in yb], rtol=1e-10, atol=1e-12)):
+            failed.append("brute force")
+            break
+    # identical maps at lambda = 1 cancel
+    xi = dict(x, q2=x["q1"], k2=x["k1"])
+    o, _ = run(xi, 1.0)
+    if not np.all(o == 0):
+        failed.append("identical maps")
+    return failed
+
+
+def test_real_oracle_passes_all_pins():
+    assert _pins(oracle._load()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, "mutation site not found: " + name
+    lib = _build(src.replace(old, new), str(tmp_path), "mutant")
+    assert _pins(lib), "no pin caught the planted mistake: " + name
