@@ -36,6 +36,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FLOP_PER_PAIR = 768
 PREFILL_WL = "prefill_b1_t4096_h16"
 DECODE_WL = "decode_b64_l4096_h16"
+SWA_PREFILL_WL = "swa_b1_t16384_h16_w128"
+SWA_DECODE_WL = "swa_decode_b64_l4096_h16_w128"
 CSRC = os.path.join(ROOT, "differential_attention_causal_amd", "csrc")
 PREFILL_PMC = os.path.join(ROOT, "profiles", "prefill_kernel_b1_t4096_h16_hbm_counters.txt")
 PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("prefill.hip", "kernels.h")]
@@ -71,9 +73,10 @@ def read_traffic(summary=PREFILL_PMC, sources=PREFILL_SOURCES):
 
 
 def decode_bytes(wl) -> int:
-    """Bytes the decode must move: K1, K2, V caches once, both queries, the
-    output (bf16) and the gain."""
-    cache = wl.B * wl.T * wl.H * (2 * wl.d_qk + wl.d_v) * 2
+    """Bytes the decode must move: the visible K1, K2, V cache positions once
+    (all L, or the last `window`), both queries, the output (bf16) and the gain."""
+    positions = min(wl.T, wl.window) if wl.window > 0 else wl.T
+    cache = wl.B * positions * wl.H * (2 * wl.d_qk + wl.d_v) * 2
     q = 2 * wl.B * wl.H * wl.d_qk * 2
     out = wl.B * wl.H * wl.d_v * 2
     gain = wl.H * wl.d_v * 4
@@ -107,6 +110,63 @@ def copy_calibration(steps: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": steps}))
+
+
+def _time_calls(torch, np, fn, warmup: int, iters: int):
+    """Mean and minimum microseconds of fn() between events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return float(ms.mean()) * 1e3, float(ms.min()) * 1e3
+
+
+def sliding_window_variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
+    """Motif 3's sliding-window layer type (128-token windows): the windowed
+    prefill at T=16384 and the windowed decode over the 4096-long caches.
+    Timed after, and outside, the step's timed region."""
+    import synth
+
+    pw = synth.WORKLOADS[SWA_PREFILL_WL]
+    dw = synth.WORKLOADS[SWA_DECODE_WL]
+    xp = synth.make_prefill_inputs(pw)
+    xd = synth.make_decode_inputs(dw)
+    P = {n: to_dev(xp[n], dev) for n in ("q1", "q2", "k1", "k2", "v")}
+    D = {n: to_dev(xd[n], dev) for n in ("q1", "q2", "k1", "k2", "v")}
+    pg, dg = f32_dev(xp["gain"], dev), f32_dev(xd["gain"], dev)
+    p_out = torch.empty((pw.B, pw.T, pw.H, pw.d_v), dtype=torch.bfloat16, device=dev)
+    d_out = torch.empty((dw.B, dw.H, dw.d_v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(da.diffattn_decode_workspace_bytes(dw.B, dw.H, dw.d_v, dw.num_splits), dtype=torch.uint8,
+                     device=dev)
+
+    def prefill():
+        da.diffattn_fwd_prefill_ex(P["q1"], P["q2"], P["k1"], P["k2"], P["v"], pw.lam, pg, eps=pw.eps,
+                                   scale=pw.scale, out=p_out, window=pw.window)
+
+    def decode():
+        da.diffattn_fwd_decode_ex(D["q1"], D["q2"], D["k1"], D["k2"], D["v"], dw.lam, dg, eps=dw.eps,
+                                  scale=dw.scale, num_splits=dw.num_splits, workspace=ws, out=d_out,
+                                  window=dw.window)
+
+    p_us, p_min = _time_calls(torch, np, prefill, warmup, iters)
+    d_us, d_min = _time_calls(torch, np, decode, warmup, iters)
+    assert bool(torch.isfinite(p_out.float()).all()) and bool(torch.isfinite(d_out.float()).all())
+    p_flop = pw.causal_pairs * FLOP_PER_PAIR
+    d_bytes = decode_bytes(dw)
+    return {
+        "prefill": {"workload": SWA_PREFILL_WL, "window": pw.window, "us_mean": round(p_us, 2),
+                    "us_min": round(p_min, 2), "visible_pairs": pw.causal_pairs,
+                    "tflops": round(p_flop / p_us / 1e6, 2),
+                    "frac_mfma_peak": round(p_flop / p_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},
+        "decode": {"workload": SWA_DECODE_WL, "window": dw.window, "us_mean": round(d_us, 2),
+                   "us_min": round(d_min, 2), "bytes": d_bytes, "gbs": round(d_bytes / d_us / 1e3, 1),
+                   "frac_hbm_peak": round(d_bytes / d_us / 1e3 / HBM_PEAK_GBS, 4), "splits": dw.num_splits},
+    }
 
 
 def main() -> int:
@@ -184,6 +244,8 @@ def main() -> int:
     step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
     assert bool(torch.isfinite(p_out.float()).all()) and bool(torch.isfinite(d_out.float()).all())
 
+    variants = sliding_window_variants(da, torch, np, to_dev, f32_dev, dev)
+
     p_flop = pw.causal_pairs * FLOP_PER_PAIR
     p_s = float(p_ms.mean()) / 1e3
     tflops = p_flop / p_s / 1e12
@@ -216,6 +278,7 @@ def main() -> int:
         "decode": {"workload": DECODE_WL, "us_mean": round(d_s * 1e6, 2), "us_min": round(float(d_ms.min()) * 1e3, 2),
                    "bytes": d_bytes, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                    "splits": dw.num_splits, "traffic": read_traffic(DECODE_PMC, DECODE_SOURCES)},
+        "sliding_window": variants,
         "wall_s_timed": round(wall, 3),
         "kernel_source_sha256_16": kernel_source_digest(),
     }

@@ -19,7 +19,9 @@ import torch  # first: the HIP runtime torch loads is the one the library binds 
 
 __all__ = [
     "diffattn_fwd_prefill",
+    "diffattn_fwd_prefill_ex",
     "diffattn_fwd_decode",
+    "diffattn_fwd_decode_ex",
     "diffattn_decode_workspace_bytes",
     "diffattn_status_string",
     "diffattn_abi_version",
@@ -41,8 +43,18 @@ if not os.path.exists(LIB_PATH):
     )
 
 
+ROPE_NONE = 0
+ROPE_HALF = 1
+ROPE_INTERLEAVED = 2
+
+
 class _Strides(ctypes.Structure):
     _fields_ = [("b", ctypes.c_int64), ("t", ctypes.c_int64), ("h", ctypes.c_int64)]
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("kv_ring", ctypes.c_int32), ("rope", ctypes.c_int32),
+                ("rope_pos0", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("reserved", ctypes.c_int32 * 3)]
 
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -55,6 +67,10 @@ _lib.diffattn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I]
 _lib.diffattn_fwd_decode.restype = _I
 _lib.diffattn_fwd_decode.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(_Strides), _P, _I, _I, _I, _I, _I,
                                      _F, _P, _P, _F, _F, _I, _P, ctypes.c_size_t, _P, _I, _P, _P]
+_lib.diffattn_fwd_prefill_ex.restype = _I
+_lib.diffattn_fwd_prefill_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffattn_fwd_prefill.argtypes
+_lib.diffattn_fwd_decode_ex.restype = _I
+_lib.diffattn_fwd_decode_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffattn_fwd_decode.argtypes
 _lib.diffattn_status_string.restype = ctypes.c_char_p
 _lib.diffattn_status_string.argtypes = [_I]
 _lib.diffattn_abi_version.restype = _I
@@ -113,6 +129,19 @@ def _out_code(dtype):
 
 def diffattn_fwd_prefill(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, out=None,
                          out_dtype=torch.bfloat16, o_pre=None, stream=None):
+    return _prefill(None, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream)
+
+
+def diffattn_fwd_prefill_ex(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, out=None,
+                            out_dtype=torch.bfloat16, o_pre=None, stream=None, window=0, rope=ROPE_NONE,
+                            rope_theta=0.0, rope_pos0=0):
+    """diffattn_fwd_prefill with variants: window > 0 is a sliding window
+    (query i attends keys i-window+1 .. i); rope selects the rotary prologue."""
+    opt = _Options(window=int(window), rope=int(rope), rope_pos0=int(rope_pos0), rope_theta=float(rope_theta))
+    return _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream)
+
+
+def _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream):
     """Causal differential-attention prefill.
 
     q1, q2, k1, k2: bf16 [B, T, H, 64]; v: bf16 [B, T, H, 128] (any strides with
@@ -142,15 +171,33 @@ def diffattn_fwd_prefill(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, out=
         raise ValueError("o_pre must be a contiguous fp32 [B, T, H, d_v] tensor")
     lam_v, lam_t = _lambda_args(lam, H, q1.device)
     st = (_Strides * 5)(*[_strides4(t) for t in (q1, q2, k1, k2, v)])
-    rc = _lib.diffattn_fwd_prefill(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, B, T, H, d_qk, d_v,
-                                   lam_v, _ptr(lam_t), _ptr(gain), float(eps), float(scale), _ptr(out),
-                                   _out_code(out.dtype), _ptr(o_pre), _stream(stream))
+    args = (_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, B, T, H, d_qk, d_v, lam_v, _ptr(lam_t),
+            _ptr(gain), float(eps), float(scale), _ptr(out), _out_code(out.dtype), _ptr(o_pre), _stream(stream))
+    rc = _lib.diffattn_fwd_prefill(*args) if opt is None else _lib.diffattn_fwd_prefill_ex(ctypes.byref(opt), *args)
     _check(rc)
     return out
 
 
 def diffattn_fwd_decode(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, seqlens=None, num_splits=0,
                         workspace=None, out=None, out_dtype=torch.bfloat16, o_pre=None, stream=None):
+    return _decode(None, q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens, num_splits, workspace, out,
+                   out_dtype, o_pre, stream)
+
+
+def diffattn_fwd_decode_ex(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, seqlens=None, num_splits=0,
+                           workspace=None, out=None, out_dtype=torch.bfloat16, o_pre=None, stream=None,
+                           window=0, kv_ring=False, rope=ROPE_NONE, rope_theta=0.0, rope_pos0=0):
+    """diffattn_fwd_decode with variants: window > 0 attends only the last
+    `window` positions; kv_ring treats each sequence's L cache slots as a ring
+    (position p in slot p % L, seqlens may exceed L)."""
+    opt = _Options(window=int(window), kv_ring=int(bool(kv_ring)), rope=int(rope), rope_pos0=int(rope_pos0),
+                   rope_theta=float(rope_theta))
+    return _decode(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens, num_splits, workspace, out,
+                   out_dtype, o_pre, stream)
+
+
+def _decode(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens, num_splits, workspace, out, out_dtype,
+            o_pre, stream):
     """Single-query decode against a KV cache, split over cache positions.
 
     q1, q2: bf16 [B, H, 64] contiguous; k1, k2: bf16 cache [B, L, H, 64];
@@ -186,10 +233,11 @@ def diffattn_fwd_decode(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, seqle
         raise ValueError("o_pre must be a contiguous fp32 [B, H, d_v] tensor")
     lam_v, lam_t = _lambda_args(lam, H, q1.device)
     st = (_Strides * 3)(*[_strides4(t) for t in (k1, k2, v)])
-    rc = _lib.diffattn_fwd_decode(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, _ptr(seqlens), B, L, H,
-                                  d_qk, d_v, lam_v, _ptr(lam_t), _ptr(gain), float(eps), float(scale),
-                                  int(num_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _ptr(out), _out_code(out.dtype), _ptr(o_pre), _stream(stream))
+    args = (_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, _ptr(seqlens), B, L, H, d_qk, d_v, lam_v,
+            _ptr(lam_t), _ptr(gain), float(eps), float(scale), int(num_splits), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(out), _out_code(out.dtype), _ptr(o_pre),
+            _stream(stream))
+    rc = _lib.diffattn_fwd_decode(*args) if opt is None else _lib.diffattn_fwd_decode_ex(ctypes.byref(opt), *args)
     _check(rc)
     return out
 

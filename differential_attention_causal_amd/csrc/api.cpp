@@ -41,6 +41,18 @@ int check_common(int B, int H, int d_qk, int d_v, float lambda, float eps, float
   return DIFFATTN_OK;
 }
 
+// Options shared by prefill and decode; the kv_ring field is checked by the
+// caller (it is meaningful for decode only).
+int check_options(const diffattn_options* opt) {
+  if (!opt) return DIFFATTN_OK;
+  if (opt->window < 0) return DIFFATTN_ERR_VALUE;
+  for (int r : opt->reserved)
+    if (r != 0) return DIFFATTN_ERR_VALUE;
+  if (opt->rope < DIFFATTN_ROPE_NONE || opt->rope > DIFFATTN_ROPE_INTERLEAVED) return DIFFATTN_ERR_VALUE;
+  if (opt->rope != DIFFATTN_ROPE_NONE) return DIFFATTN_ERR_UNSUPPORTED;
+  return DIFFATTN_OK;
+}
+
 float score_factor(float scale) {
   const float s = scale > 0.f ? scale : 1.0f / std::sqrt((float)kDqk);
   return s * kLog2e;
@@ -50,7 +62,7 @@ float score_factor(float scale) {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 100; }
+int diffattn_abi_version(void) { return 101; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -66,13 +78,16 @@ const char* diffattn_status_string(int status) {
   }
 }
 
-int diffattn_fwd_prefill(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
-                         const diffattn_strides* strides, int B, int T, int H, int d_qk, int d_v,
-                         float lambda, const float* lambda_per_head, const float* gain, float gn_eps,
-                         float scale, void* out, int out_dtype, float* o_pre, void* stream) {
+int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,
+                            const void* k2, const void* v, const diffattn_strides* strides, int B, int T, int H,
+                            int d_qk, int d_v, float lambda, const float* lambda_per_head, const float* gain,
+                            float gn_eps, float scale, void* out, int out_dtype, float* o_pre, void* stream) {
   if (!q1 || !q2 || !k1 || !k2 || !v || !gain || !out) return DIFFATTN_ERR_NULL;
   int rc = check_common(B, H, d_qk, d_v, lambda, gn_eps, scale, out_dtype);
   if (rc != DIFFATTN_OK) return rc;
+  rc = check_options(opt);
+  if (rc != DIFFATTN_OK) return rc;
+  if (opt && opt->kv_ring != 0) return DIFFATTN_ERR_VALUE;
   if (T <= 0 || T > (1 << 22)) return DIFFATTN_ERR_SHAPE;
   // One 256-thread workgroup per 128 queries of each (b, h); the launch must
   // stay below 2^32 threads.
@@ -101,6 +116,7 @@ int diffattn_fwd_prefill(const void* q1, const void* q2, const void* k1, const v
   a.B = B;
   a.T = T;
   a.H = H;
+  a.window = opt ? opt->window : 0;
   a.c = score_factor(scale);
   a.lambda = lambda;
   a.lambda_h = lambda_per_head;
@@ -113,6 +129,14 @@ int diffattn_fwd_prefill(const void* q1, const void* q2, const void* k1, const v
   return DIFFATTN_OK;
 }
 
+int diffattn_fwd_prefill(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
+                         const diffattn_strides* strides, int B, int T, int H, int d_qk, int d_v,
+                         float lambda, const float* lambda_per_head, const float* gain, float gn_eps,
+                         float scale, void* out, int out_dtype, float* o_pre, void* stream) {
+  return diffattn_fwd_prefill_ex(nullptr, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda,
+                                 lambda_per_head, gain, gn_eps, scale, out, out_dtype, o_pre, stream);
+}
+
 size_t diffattn_decode_workspace_bytes(int B, int H, int d_v, int num_splits) {
   if (num_splits <= 0) num_splits = kDefaultSplits;
   if (B <= 0 || H <= 0 || d_v != kDv || num_splits > kMaxSplits) return 0;
@@ -120,15 +144,20 @@ size_t diffattn_decode_workspace_bytes(int B, int H, int d_v, int num_splits) {
   return (size_t)B * H * num_splits * 2 * diffattn::kPartialStride * sizeof(float);
 }
 
-int diffattn_fwd_decode(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
-                        const diffattn_strides* cache_strides, const int32_t* seqlens, int B, int L, int H,
-                        int d_qk, int d_v, float lambda, const float* lambda_per_head, const float* gain,
-                        float gn_eps, float scale, int num_splits, void* workspace, size_t workspace_bytes,
-                        void* out, int out_dtype, float* o_pre, void* stream) {
+int diffattn_fwd_decode_ex(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,
+                           const void* k2, const void* v, const diffattn_strides* cache_strides,
+                           const int32_t* seqlens, int B, int L, int H, int d_qk, int d_v, float lambda,
+                           const float* lambda_per_head, const float* gain, float gn_eps, float scale,
+                           int num_splits, void* workspace, size_t workspace_bytes, void* out, int out_dtype,
+                           float* o_pre, void* stream) {
   if (!q1 || !q2 || !k1 || !k2 || !v || !gain || !out) return DIFFATTN_ERR_NULL;
   int rc = check_common(B, H, d_qk, d_v, lambda, gn_eps, scale, out_dtype);
   if (rc != DIFFATTN_OK) return rc;
+  rc = check_options(opt);
+  if (rc != DIFFATTN_OK) return rc;
   if (L <= 0 || L > (1 << 26)) return DIFFATTN_ERR_SHAPE;
+  const bool ring = opt && opt->kv_ring != 0;
+  if (ring && opt->window > L) return DIFFATTN_ERR_VALUE;
   if (num_splits <= 0) num_splits = kDefaultSplits;
   if (num_splits > kMaxSplits) return DIFFATTN_ERR_VALUE;
   if ((int64_t)B * H * num_splits > kMaxWorkgroups) return DIFFATTN_ERR_SHAPE;
@@ -158,6 +187,9 @@ int diffattn_fwd_decode(const void* q1, const void* q2, const void* k1, const vo
   a.L = L;
   a.H = H;
   a.splits = num_splits;
+  a.window = opt ? opt->window : 0;
+  a.ring = ring;
+  if (ring && a.window == 0) a.window = L;
   a.c = score_factor(scale);
   a.lambda = lambda;
   a.lambda_h = lambda_per_head;
@@ -169,6 +201,16 @@ int diffattn_fwd_decode(const void* q1, const void* q2, const void* k1, const vo
   a.o_pre = o_pre;
   if (diffattn::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
   return DIFFATTN_OK;
+}
+
+int diffattn_fwd_decode(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
+                        const diffattn_strides* cache_strides, const int32_t* seqlens, int B, int L, int H,
+                        int d_qk, int d_v, float lambda, const float* lambda_per_head, const float* gain,
+                        float gn_eps, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                        void* out, int out_dtype, float* o_pre, void* stream) {
+  return diffattn_fwd_decode_ex(nullptr, q1, q2, k1, k2, v, cache_strides, seqlens, B, L, H, d_qk, d_v, lambda,
+                                lambda_per_head, gain, gn_eps, scale, num_splits, workspace, workspace_bytes, out,
+                                out_dtype, o_pre, stream);
 }
 
 }  // extern "C"

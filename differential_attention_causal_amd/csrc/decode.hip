@@ -52,9 +52,11 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Positions 0 .. n-1 of sequence b have been cached.  A linear cache holds at
+// most L of them; a ring cache keeps the last L, so n may exceed L there.
 __device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
   int n = a.seqlens ? a.seqlens[b] : a.L;
-  return n > a.L ? a.L : n;
+  return (!a.ring && n > a.L) ? a.L : n;
 }
 
 __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
@@ -69,9 +71,16 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
   const int head = bh % a.H, b = bh / a.H;
 
   const int n = seq_len(a, b);
-  const int chunk = n > 0 ? (n + a.splits - 1) / a.splits : 0;
-  const int s0 = split * chunk;
-  const int s1 = min(n, s0 + chunk);
+  const int lo = (a.window > 0 && n > a.window) ? n - a.window : 0;  // oldest visible position
+  const int nvis = n - lo;  // visible positions lo .. n-1 (at most L)
+  // This split takes visible positions lo + r for r in [r0, r1).
+  const int chunk = nvis > 0 ? (nvis + a.splits - 1) / a.splits : 0;
+  const int r0 = split * chunk;
+  const int r1 = min(nvis, r0 + chunk);
+  // Slot of position lo + r: slot0 + r, less L if that reaches L (the visible
+  // positions span at most L slots, so they wrap at most once).  A linear
+  // cache has n <= L and slot = position.
+  const int slot0 = a.ring ? lo % a.L : lo;
   float* rec = a.partial + ((int64_t)bh * a.splits + split) * 2 * kPartialStride;
 
   // Query chunks: lane e of a key group holds dims 8e .. 8e+7 of q1 and q2.
@@ -88,15 +97,17 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) o1[k] = o2[k] = 0.f;
 
-  for (int kb = s0; kb < s1; kb += kKB) {
-    const int cnt = min(kKB, s1 - kb);
+  for (int kb = r0; kb < r1; kb += kKB) {
+    const int cnt = min(kKB, r1 - kb);
     // Scores of both maps for this block (32 keys per pass, 8 lanes per key).
 #pragma unroll 4
     for (int p = 0; p < kKB / 32; ++p) {
       const int kk = p * 32 + ks;
       float d1 = 0.f, d2 = 0.f;
       if (kk < cnt) {
-        const int64_t pos = kb + kk;
+        int slot = slot0 + kb + kk;
+        slot -= slot >= a.L ? a.L : 0;
+        const int64_t pos = slot;
         const u32x4 x1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k1b + pos * a.sk1.t));
         const u32x4 x2 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k2b + pos * a.sk2.t));
         d1 = dot8(q1, x1, 0.f);
@@ -176,7 +187,9 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
     for (int p = 0; p < kKB / 16; ++p) {
       const int kk = p * 16 + kq;
       if (kk < cnt) {
-        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (int64_t)(kb + kk) * a.sv.t));
+        int slot = slot0 + kb + kk;
+        slot -= slot >= a.L ? a.L : 0;
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (int64_t)slot * a.sv.t));
         const float p1 = sc[0][kk], p2 = sc[1][kk];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {

@@ -22,6 +22,7 @@ struct PrefillArgs {
   const uint16_t* v;
   Strides sq1, sq2, sk1, sk2, sv;
   int B, T, H;
+  int window;             // > 0: query i sees keys i-window+1 .. i; 0: every key <= i
   float c;                // scale * log2(e): scores are kept in base-2 units
   float lambda;           // used when lambda_h is null
   const float* lambda_h;  // [H] or null
@@ -41,6 +42,8 @@ struct DecodeArgs {
   Strides sk1, sk2, sv;
   const int32_t* seqlens;  // [B] or null
   int B, L, H, splits;
+  int window;              // > 0: attend only the last `window` positions
+  int ring;                // cache of L slots is a ring: position p in slot p % L
   float c;
   float lambda;
   const float* lambda_h;
@@ -51,6 +54,10 @@ struct DecodeArgs {
   int out_f32;
   float* o_pre;
 };
+
+// Initial reference max of a softmax state: finite, so a query whose first
+// tile holds none of its keys (sliding window) gets P = 2^(-inf) = 0, not NaN.
+constexpr float kNoMax = -1.0e30f;
 
 // Floats per (b, h, split, map) record in the decode workspace: max, sum, O[kDv].
 constexpr int kPartialStride = kDv + 2;

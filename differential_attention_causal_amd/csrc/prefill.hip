@@ -175,7 +175,7 @@ __device__ __forceinline__ void softmax_step(f32x16& s, float c, float& m, float
     // the exchange), so a row's result never depends on other rows' data.
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mc = mx * c;
-    const float mn = mc > m + kSlack ? mc : m;  // finite: every query sees a key in its first tile
+    const float mn = mc > m + kSlack ? mc : m;
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     l *= alpha;
 #pragma unroll
@@ -220,7 +220,7 @@ __device__ __forceinline__ void merge_map(char* smem, int grp, int wq, int lane,
   if (grp == 0 && live) {
     const float mb = ml[(wq * 64 + lane) * 2 + 0];
     const float lb = ml[(wq * 64 + lane) * 2 + 1];
-    const float mn = fmaxf(m, mb);  // finite: group 0 always holds tile 0
+    const float mn = fmaxf(m, mb);  // every query sees at least itself
     const float aa = __builtin_amdgcn_exp2f(m - mn);
     const float ab = __builtin_amdgcn_exp2f(mb - mn);
     l = l * aa + lb * ab;
@@ -265,8 +265,11 @@ prefill_kernel(PrefillArgs a) {
   const bool wave_live = q_first < a.T;
   const int ntiles = min(qb * (kBM / kBN) + (kBM / kBN), (a.T + kBN - 1) / kBN);
   const int kend = min(a.T, ntiles * kBN);
-  const int nsteps = (ntiles + kGroups - 1) / kGroups;
+  // With a sliding window, tiles below every query's window are skipped.
+  const int tile0 = a.window > 0 ? max(0, qb * kBM - a.window + 1) / kBN : 0;
+  const int nsteps = (ntiles - tile0 + kGroups - 1) / kGroups;
   const int wave_last_tile = q_first / kBN;  // the wave's diagonal tile
+  const int wave_first_tile = a.window > 0 ? max(0, q_first - a.window + 1) / kBN : 0;
 
   // Q1^T, Q2^T operands: lane holds query lq, dims 16s + 8hf .. +7.
   bf16x8 qa[4], qb2[4];
@@ -289,7 +292,7 @@ prefill_kernel(PrefillArgs a) {
     O1[cb] = f32x16{};
     O2[cb] = f32x16{};
   }
-  float m1 = -__builtin_inff(), m2 = -__builtin_inff(), l1 = 0.f, l2 = 0.f;
+  float m1 = kNoMax, m2 = kNoMax, l1 = 0.f, l2 = 0.f;
   const float c = a.c;
   const int ksw = kSwz(lq);
 
@@ -299,7 +302,7 @@ prefill_kernel(PrefillArgs a) {
   const StageOffsets soff = stage_offsets(a, tid);
 
   Staged st;
-  stage_load(st, a, kb1, kb2, vbase, soff, 0, kend, tid);
+  stage_load(st, a, kb1, kb2, vbase, soff, tile0 * kBN, kend, tid);
   stage_store(st, smem, tid);
   __syncthreads();
 
@@ -307,10 +310,10 @@ prefill_kernel(PrefillArgs a) {
     char* cur = smem + (it & 1) * kStage;
     char* nxt = smem + ((it + 1) & 1) * kStage;
     const bool more = it + 1 < nsteps;
-    if (more) stage_load(st, a, kb1, kb2, vbase, soff, (it + 1) * kGroups * kBN, kend, tid);
+    if (more) stage_load(st, a, kb1, kb2, vbase, soff, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
 
-    const int j = it * kGroups + grp;  // this group's tile
-    if (wave_live && j <= wave_last_tile) {
+    const int j = tile0 + it * kGroups + grp;  // this group's tile
+    if (wave_live && j >= wave_first_tile && j <= wave_last_tile) {
       const char* kt = cur + grp * kTile;
       f32x16 s1 = f32x16{}, s2 = f32x16{};
       const int krow = lq * kKRow;
@@ -329,6 +332,18 @@ prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < 16; ++i) {
           const int kr = 8 * (i >> 2) + 4 * hf + (i & 3);
           if (kr > lq) {
+            s1[i] = -__builtin_inff();
+            s2[i] = -__builtin_inff();
+          }
+        }
+      }
+      if (a.window > 0 && j * kBN < q_first + 32 - a.window) {
+        // Lower window edge: key k is visible to query q iff k > q - window.
+        const int lim = q - a.window - j * kBN;  // key rows <= lim are too old
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kr = 8 * (i >> 2) + 4 * hf + (i & 3);
+          if (kr <= lim) {
             s1[i] = -__builtin_inff();
             s2[i] = -__builtin_inff();
           }

@@ -71,6 +71,41 @@ enum diffattn_status {
 
 enum diffattn_out_dtype { DIFFATTN_OUT_BF16 = 0, DIFFATTN_OUT_F32 = 1 };
 
+/* Rotary position embedding on Q1, Q2, K1, K2 (diffattn_options.rope). */
+enum diffattn_rope {
+    DIFFATTN_ROPE_NONE = 0,
+    DIFFATTN_ROPE_HALF = 1,        /* pairs (i, i + 32) of each 64-dim vector */
+    DIFFATTN_ROPE_INTERLEAVED = 2  /* pairs (2i, 2i + 1) */
+};
+
+/*
+ * Variants of the operation, for the *_ex entry points.  Zero-initialise and
+ * set what is needed: all fields zero is exactly the plain causal operation.
+ *   window     : > 0 gives a sliding window: query i attends keys
+ *                i-window+1 .. i (decode: the last `window` positions of the
+ *                sequence); 0 attends every key <= i.  Motif 3 alternates one
+ *                full causal layer with three sliding-window layers (picx.dev
+ *                summary of the Motif 3 report, section 2.1).
+ *   kv_ring    : decode only (prefill requires 0).  Nonzero: each sequence's
+ *                cache of L slots is a ring buffer, position p in slot p % L,
+ *                so seqlens may exceed L; the query attends the last
+ *                min(seqlen, window) positions, and window = 0 means window =
+ *                L.  A window larger than L is an error (the ring no longer
+ *                holds those positions).  Zero: slot p holds position p and
+ *                seqlens above L count as L.
+ *   rope, rope_theta, rope_pos0 : reserved for the rotary prologue; rope must
+ *                be DIFFATTN_ROPE_NONE in this version.
+ *   reserved   : must be zero.
+ */
+typedef struct {
+    int32_t window;
+    int32_t kv_ring;
+    int32_t rope;
+    int32_t rope_pos0;
+    float rope_theta;
+    int32_t reserved[3];
+} diffattn_options;
+
 /* Element strides of the three outer dimensions of a [B, T, H, D] tensor. */
 typedef struct {
     int64_t b, t, h;
@@ -127,10 +162,34 @@ DIFFATTN_API int diffattn_fwd_decode(const void* q1, const void* q2, const void*
                         size_t workspace_bytes, void* out, int out_dtype, float* o_pre,
                         void* stream);
 
+/* diffattn_fwd_prefill with variants (opt may be NULL: plain causal).  A
+ * negative window, a nonzero kv_ring or reserved field, or an unknown rope mode
+ * returns DIFFATTN_ERR_VALUE; a rope mode this version lacks returns
+ * DIFFATTN_ERR_UNSUPPORTED. */
+DIFFATTN_API int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void* q1, const void* q2,
+                                         const void* k1, const void* k2, const void* v,
+                                         const diffattn_strides* strides, int B, int T, int H, int d_qk,
+                                         int d_v, float lambda, const float* lambda_per_head,
+                                         const float* gain, float gn_eps, float scale, void* out,
+                                         int out_dtype, float* o_pre, void* stream);
+
+/* diffattn_fwd_decode with variants (opt may be NULL: every cached position).
+ * Errors as for diffattn_fwd_prefill_ex, and DIFFATTN_ERR_VALUE for a ring
+ * cache with window > L.  With a ring cache, seqlens may exceed L (up to
+ * 2^31 - 1). */
+DIFFATTN_API int diffattn_fwd_decode_ex(const diffattn_options* opt, const void* q1, const void* q2,
+                                        const void* k1, const void* k2, const void* v,
+                                        const diffattn_strides* cache_strides, const int32_t* seqlens,
+                                        int B, int L, int H, int d_qk, int d_v, float lambda,
+                                        const float* lambda_per_head, const float* gain, float gn_eps,
+                                        float scale, int num_splits, void* workspace,
+                                        size_t workspace_bytes, void* out, int out_dtype, float* o_pre,
+                                        void* stream);
+
 /* Static text for a status code (never NULL). */
 DIFFATTN_API const char* diffattn_status_string(int status);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor): 101 adds the *_ex entry points. */
 DIFFATTN_API int diffattn_abi_version(void);
 
 #ifdef __cplusplus

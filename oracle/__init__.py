@@ -42,10 +42,10 @@ def _bind(path):
     lib = ctypes.CDLL(path)
     P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
     lib.oracle_prefill.restype = I
-    lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P, D, D, P,
+    lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P, D, D, I, P,
                                    ctypes.c_int64, P, P, I]
     lib.oracle_decode.restype = I
-    lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, D, D, P, P, I]
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, D, D, I, I, P, P, I]
     return lib
 
 
@@ -74,12 +74,14 @@ def _lam(lam, H):
     return np.ascontiguousarray(lam)
 
 
-def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib=None):
+def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib=None, window=0):
     """Causal prefill in fp64.
 
     q1, q2, k1, k2: bf16 bits [B, T, H, d_qk]; v: bf16 bits [B, T, H, d_v].
     lam: scalar or [H]; gain: [H, d_v] (fp32 values); eps, scale: floats.
     rows: optional sequence of (b, i, h) triples; default all rows.
+    window: > 0 for a sliding window of that many keys (query i sees
+    i-window+1 .. i), 0 for every key <= i.
     Returns (o_pre, y) as fp64 arrays of shape [B, T, H, d_v], or [n_rows, d_v]
     when rows are given.
     """
@@ -107,7 +109,7 @@ def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib
     y = np.empty((n, d_v), dtype=np.float64)
     rc = (lib or _load()).oracle_prefill(q1.ctypes.data, q2.ctypes.data, k1.ctypes.data, k2.ctypes.data,
                                 v.ctypes.data, B, T, H, d_qk, d_v, lam.ctypes.data,
-                                gain.ctypes.data, float(eps), float(scale),
+                                gain.ctypes.data, float(eps), float(scale), int(window),
                                 None if flat is None else flat.ctypes.data, n,
                                 o.ctypes.data, y.ctypes.data, int(nthreads))
     if rc != 0:
@@ -117,10 +119,13 @@ def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib
     return o, y
 
 
-def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0, lib=None):
+def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0, lib=None, window=0, ring=False):
     """Single-query decode in fp64: q [B, H, d_qk] against caches [B, L, H, d].
 
     seqlens: optional [B] cached lengths (above L counts as L; <= 0 gives zeros).
+    window: > 0 attends only the last `window` positions.
+    ring: the L cache slots are a ring buffer (position p in slot p % L;
+    seqlens may exceed L; window 0 means L; window > L is an error).
     Returns (o_pre, y), fp64 [B, H, d_v].
     """
     q1, q2, k1, k2, v = (_u16(a) for a in (q1, q2, k1, k2, v))
@@ -142,7 +147,8 @@ def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0, l
     rc = (lib or _load()).oracle_decode(q1.ctypes.data, q2.ctypes.data, k1.ctypes.data, k2.ctypes.data,
                                v.ctypes.data, None if sl is None else sl.ctypes.data,
                                B, L, H, d_qk, d_v, lam.ctypes.data, gain.ctypes.data,
-                               float(eps), float(scale), o.ctypes.data, y.ctypes.data,
+                               float(eps), float(scale), int(window), int(bool(ring)), o.ctypes.data,
+                               y.ctypes.data,
                                int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_decode failed")

@@ -17,6 +17,9 @@
  *   - scores carry the usual 1/sqrt(d_qk) factor (passed in as `scale`);
  *   - the model is decoder-only (edgentiq article on Motif-2.6B), so query i
  *     attends to keys j <= i; decode attends to all n cached keys;
+ *   - sliding window (Motif 3's sliding-window layers, picx.dev summary of the
+ *     Motif 3 report, section 2.1): with window W > 0, query i attends keys
+ *     i-W+1 .. i, and decode the last W cached keys;
  *   - lambda is an input (scalar or one value per head) that scales the
  *     normalised second map; no clamping;
  *   - "GroupNorm" acts on the head output (after the product with V), with one
@@ -99,7 +102,8 @@ static void diff_attention_row(const uint16_t* q1, const uint16_t* q2,
 
 /*
  * Causal prefill.  q1, q2, k1, k2: bf16 [B, T, H, d_qk]; v: bf16 [B, T, H, d_v],
- * all C-contiguous.  lam: fp64 [H].  gain: fp32 [H, d_v].
+ * all C-contiguous.  lam: fp64 [H].  gain: fp32 [H, d_v].  window: > 0 for a
+ * sliding window of that many keys, 0 for every key <= i.
  * rows: n_rows flat indices ((b * T + i) * H + h), or NULL for every row in
  * that order (then n_rows must be B*T*H).  o_pre, y: fp64 [n_rows, d_v].
  * nthreads <= 0 uses the OpenMP default.  Returns 0, or -1 on bad arguments
@@ -108,9 +112,9 @@ static void diff_attention_row(const uint16_t* q1, const uint16_t* q2,
 int oracle_prefill(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
                    const uint16_t* k2, const uint16_t* v, int B, int T, int H,
                    int d_qk, int d_v, const double* lam, const float* gain,
-                   double eps, double scale, const int64_t* rows, int64_t n_rows,
+                   double eps, double scale, int window, const int64_t* rows, int64_t n_rows,
                    double* o_pre, double* y, int nthreads) {
-    if (B <= 0 || T <= 0 || H <= 0 || d_qk <= 0 || d_v <= 0) return -1;
+    if (B <= 0 || T <= 0 || H <= 0 || d_qk <= 0 || d_v <= 0 || window < 0) return -1;
     if (!rows && n_rows != (int64_t)B * T * H) return -1;
     int bad = 0;
 #ifdef _OPENMP
@@ -132,11 +136,12 @@ int oracle_prefill(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
                 int h = (int)(flat % H);
                 int64_t i = (flat / H) % T;
                 int64_t b = flat / ((int64_t)H * T);
+                int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0;
                 int64_t qoff = ((b * T + i) * H + h) * d_qk;
-                int64_t koff = (b * T * H + h) * (int64_t)d_qk;
-                int64_t voff = (b * T * H + h) * (int64_t)d_v;
+                int64_t koff = ((b * T + first) * H + h) * (int64_t)d_qk;
+                int64_t voff = ((b * T + first) * H + h) * (int64_t)d_v;
                 diff_attention_row(q1 + qoff, q2 + qoff, k1 + koff, k2 + koff, v + voff,
-                                   (int64_t)H * d_qk, (int64_t)H * d_v, i + 1, d_qk, d_v,
+                                   (int64_t)H * d_qk, (int64_t)H * d_v, i + 1 - first, d_qk, d_v,
                                    scale, lam[h], gain + (int64_t)h * d_v, eps, p1, p2,
                                    o_pre + r * d_v, y + r * d_v);
             }
@@ -150,16 +155,24 @@ int oracle_prefill(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
 /*
  * Decode: one query per (b, h) against a cache of length L.
  * q1, q2: bf16 [B, H, d_qk]; k1, k2: bf16 [B, L, H, d_qk]; v: bf16 [B, L, H, d_v].
- * seqlens: [B] cached lengths (NULL = L for all).  A length above L counts as
- * L; a length <= 0 leaves no key to attend to and gives all-zero outputs.
+ * seqlens: [B] cached lengths (NULL = L for all).  A length <= 0 leaves no
+ * key to attend to and gives all-zero outputs.
+ * window: > 0 attends only the last `window` positions.
+ * ring = 0: slot p holds position p; a length above L counts as L.
+ * ring != 0: the L slots are a ring buffer, position p in slot p % L, so the
+ * length may exceed L; window 0 then means window L, and window > L is an
+ * error (those positions are overwritten).  The visible positions are
+ * gathered, oldest first, into a contiguous copy before the row is computed.
  * o_pre, y: fp64 [B, H, d_v].
  */
 int oracle_decode(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
                   const uint16_t* k2, const uint16_t* v, const int32_t* seqlens,
                   int B, int L, int H, int d_qk, int d_v, const double* lam,
-                  const float* gain, double eps, double scale, double* o_pre,
-                  double* y, int nthreads) {
-    if (B <= 0 || L <= 0 || H <= 0 || d_qk <= 0 || d_v <= 0) return -1;
+                  const float* gain, double eps, double scale, int window, int ring,
+                  double* o_pre, double* y, int nthreads) {
+    if (B <= 0 || L <= 0 || H <= 0 || d_qk <= 0 || d_v <= 0 || window < 0) return -1;
+    if (ring && window > L) return -1;
+    if (ring && window == 0) window = L;
     int bad = 0;
 #ifdef _OPENMP
     if (nthreads <= 0) nthreads = omp_get_max_threads();
@@ -168,7 +181,10 @@ int oracle_decode(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
     {
         double* p1 = (double*)malloc(sizeof(double) * (size_t)L);
         double* p2 = (double*)malloc(sizeof(double) * (size_t)L);
-        if (!p1 || !p2) {
+        uint16_t* g1 = ring ? (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L * d_qk) : NULL;
+        uint16_t* g2 = ring ? (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L * d_qk) : NULL;
+        uint16_t* gv = ring ? (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L * d_v) : NULL;
+        if (!p1 || !p2 || (ring && (!g1 || !g2 || !gv))) {
             bad = 1;
         } else {
 #ifdef _OPENMP
@@ -178,22 +194,38 @@ int oracle_decode(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
                 int h = (int)(r % H);
                 int64_t b = r / H;
                 int64_t n = seqlens ? seqlens[b] : L;
-                if (n > L) n = L;
+                if (!ring && n > L) n = L;
                 if (n <= 0) {
                     for (int c = 0; c < d_v; ++c) { o_pre[r * d_v + c] = 0.0; y[r * d_v + c] = 0.0; }
                     continue;
                 }
+                int64_t first = (window > 0 && n > window) ? n - window : 0;
                 int64_t qoff = (b * H + h) * (int64_t)d_qk;
-                int64_t koff = (b * L * H + h) * (int64_t)d_qk;
-                int64_t voff = (b * L * H + h) * (int64_t)d_v;
+                if (ring) {
+                    for (int64_t p = first; p < n; ++p) {
+                        int64_t slot = p % L;
+                        memcpy(g1 + (p - first) * d_qk, k1 + ((b * L + slot) * H + h) * d_qk, 2 * (size_t)d_qk);
+                        memcpy(g2 + (p - first) * d_qk, k2 + ((b * L + slot) * H + h) * d_qk, 2 * (size_t)d_qk);
+                        memcpy(gv + (p - first) * d_v, v + ((b * L + slot) * H + h) * d_v, 2 * (size_t)d_v);
+                    }
+                    diff_attention_row(q1 + qoff, q2 + qoff, g1, g2, gv, d_qk, d_v, n - first, d_qk, d_v,
+                                       scale, lam[h], gain + (int64_t)h * d_v, eps, p1, p2,
+                                       o_pre + r * d_v, y + r * d_v);
+                    continue;
+                }
+                int64_t koff = ((b * L + first) * H + h) * (int64_t)d_qk;
+                int64_t voff = ((b * L + first) * H + h) * (int64_t)d_v;
                 diff_attention_row(q1 + qoff, q2 + qoff, k1 + koff, k2 + koff, v + voff,
-                                   (int64_t)H * d_qk, (int64_t)H * d_v, n, d_qk, d_v, scale,
+                                   (int64_t)H * d_qk, (int64_t)H * d_v, n - first, d_qk, d_v, scale,
                                    lam[h], gain + (int64_t)h * d_v, eps, p1, p2,
                                    o_pre + r * d_v, y + r * d_v);
             }
         }
         free(p1);
         free(p2);
+        free(g1);
+        free(g2);
+        free(gv);
     }
     return bad ? -1 : 0;
 }

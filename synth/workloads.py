@@ -32,6 +32,7 @@ class Workload:
     d_v: int = 128
     num_splits: int = 0  # decode only
     eps: float = float(np.float32(1e-5))
+    window: int = 0      # > 0: sliding window of that many keys (Motif 3's sliding-window layers)
 
     @property
     def scale(self) -> float:
@@ -39,9 +40,13 @@ class Workload:
 
     @property
     def causal_pairs(self) -> int:
+        """(query, visible key) pairs over all rows and heads."""
+        W = self.window if self.window > 0 else self.T
         if self.kind == "prefill":
-            return self.B * self.H * self.T * (self.T + 1) // 2
-        return self.B * self.H * self.T
+            if W >= self.T:
+                return self.B * self.H * self.T * (self.T + 1) // 2
+            return self.B * self.H * (W * (W + 1) // 2 + (self.T - W) * W)
+        return self.B * self.H * min(self.T, W)
 
 
 WORKLOADS = {
@@ -52,5 +57,10 @@ WORKLOADS = {
         Workload("batch_b8_t4096_h16", "prefill", B=8, T=4096, H=16, seed=3, lam_range=(0.2, 0.9)),
         Workload("longctx_b1_t16384_h16", "prefill", B=1, T=16384, H=16, seed=4, lam=0.8),
         Workload("decode_b64_l4096_h16", "decode", B=64, T=4096, H=16, seed=5, lam=0.8, num_splits=8),
+        # Sliding-window layers: 128-token windows are the window size the
+        # picx.dev summary of the Motif 3 report quotes (section "Practical Implications").
+        Workload("swa_b1_t16384_h16_w128", "prefill", B=1, T=16384, H=16, seed=6, lam=0.8, window=128),
+        Workload("swa_decode_b64_l4096_h16_w128", "decode", B=64, T=4096, H=16, seed=7, lam=0.8,
+                 num_splits=1, window=128),
     ]
 }

@@ -24,11 +24,12 @@ def _declared():
 def test_header_symbols_exported():
     names = _declared()
     assert set(names) == {"diffattn_fwd_prefill", "diffattn_fwd_decode", "diffattn_decode_workspace_bytes",
+                          "diffattn_fwd_prefill_ex", "diffattn_fwd_decode_ex",
                           "diffattn_status_string", "diffattn_abi_version"}
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 100
+    assert da.diffattn_abi_version() == 101
 
 
 def test_status_strings():
@@ -38,28 +39,31 @@ def test_status_strings():
     assert "unknown" in da.diffattn_status_string(99)
 
 
-def _prefill(**kw):
+def _opt_call(fn, fn_ex, opt, args):
+    if opt is None:
+        return fn(*args)
+    if opt == "null":
+        return fn_ex(None, *args)
+    o = da._Options(**{k: v for k, v in opt.items() if k != "reserved"})
+    for i, r in enumerate(opt.get("reserved", ())):
+        o.reserved[i] = r
+    return fn_ex(ctypes.byref(o), *args)
+
+
+def _prefill(opt=None, **kw):
     args = dict(q1=A, q2=A, k1=A, k2=A, v=A, st=None, B=1, T=128, H=2, dqk=64, dv=128, lam=0.5, lamh=None,
                 gain=A, eps=1e-5, scale=0.0, out=A, odt=0, opre=None, stream=None)
     args.update(kw)
-    st = args["st"]
-    return da._lib.diffattn_fwd_prefill(args["q1"], args["q2"], args["k1"], args["k2"], args["v"], st,
-                                        args["B"], args["T"], args["H"], args["dqk"], args["dv"], args["lam"],
-                                        args["lamh"], args["gain"], args["eps"], args["scale"], args["out"],
-                                        args["odt"], args["opre"], args["stream"])
+    return _opt_call(da._lib.diffattn_fwd_prefill, da._lib.diffattn_fwd_prefill_ex, opt, list(args.values()))
 
 
-def _decode(**kw):
+def _decode(opt=None, **kw):
     need = da.diffattn_decode_workspace_bytes(4, 2, 128, 8)
     args = dict(q1=A, q2=A, k1=A, k2=A, v=A, st=None, sl=None, B=4, L=100, H=2, dqk=64, dv=128, lam=0.8,
                 lamh=None, gain=A, eps=1e-5, scale=0.0, splits=8, ws=A, wsb=need, out=A, odt=0, opre=None,
                 stream=None)
     args.update(kw)
-    return da._lib.diffattn_fwd_decode(args["q1"], args["q2"], args["k1"], args["k2"], args["v"], args["st"],
-                                       args["sl"], args["B"], args["L"], args["H"], args["dqk"], args["dv"],
-                                       args["lam"], args["lamh"], args["gain"], args["eps"], args["scale"],
-                                       args["splits"], args["ws"], args["wsb"], args["out"], args["odt"],
-                                       args["opre"], args["stream"])
+    return _opt_call(da._lib.diffattn_fwd_decode, da._lib.diffattn_fwd_decode_ex, opt, list(args.values()))
 
 
 @pytest.mark.parametrize("kw,rc", [
@@ -98,3 +102,34 @@ def test_workspace_bytes():
     assert da.diffattn_decode_workspace_bytes(0, 16, 128, 8) == 0
     assert da.diffattn_decode_workspace_bytes(1, 1, 64, 8) == 0
     assert da.diffattn_decode_workspace_bytes(1, 1, 128, 65) == 0
+
+
+# Options of the *_ex entry points.  Cases expected to pass validation are
+# given an invalid shape instead, so every call stops before any HIP call.
+@pytest.mark.parametrize("opt,rc", [
+    (dict(window=-1), EVALUE), (dict(rope=3), EVALUE), (dict(rope=-1), EVALUE),
+    (dict(kv_ring=1), EVALUE), (dict(reserved=(0, 0, 1)), EVALUE),
+    (dict(window=5), ESHAPE), (dict(window=1 << 30), ESHAPE), ("null", ESHAPE), (dict(), ESHAPE),
+])
+def test_prefill_ex_options(opt, rc):
+    assert (_prefill(opt=opt, T=0) if rc == ESHAPE else _prefill(opt=opt)) == rc
+
+
+@pytest.mark.parametrize("opt,rc", [
+    (dict(window=-7), EVALUE), (dict(rope=9), EVALUE), (dict(reserved=(2, 0, 0)), EVALUE),
+    (dict(kv_ring=1, window=101), EVALUE),
+    (dict(window=3), ESHAPE), (dict(kv_ring=1), ESHAPE), (dict(kv_ring=1, window=100), ESHAPE), ("null", ESHAPE),
+])
+def test_decode_ex_options(opt, rc):
+    assert (_decode(opt=opt, L=0) if rc == ESHAPE else _decode(opt=opt)) == rc
+
+
+def test_options_layout():
+    # The C struct: five 4-byte fields then int32 reserved[3], 32 bytes.
+    assert ctypes.sizeof(da._Options) == 32
+    assert [f[0] for f in da._Options._fields_] == ["window", "kv_ring", "rope", "rope_pos0", "rope_theta",
+                                                    "reserved"]
+    txt = open(HEADER).read()
+    body = txt[txt.index("typedef struct {\n    int32_t window;"):txt.index("} diffattn_options;")]
+    assert re.findall(r"(\w+)(?:\[\d\])?;", body) == ["window", "kv_ring", "rope", "rope_pos0", "rope_theta",
+                                                       "reserved"]

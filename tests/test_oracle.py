@@ -269,3 +269,119 @@ def test_golden_fixture():
     o, y = _run(x, rows=[tuple(r) for r in g["rows"]])
     np.testing.assert_allclose(o, np.array(g["o_pre"]), rtol=0, atol=1e-15)
     np.testing.assert_allclose(y, np.array(g["y"]), rtol=0, atol=1e-13)
+
+
+# --- sliding window (picx.dev summary of the Motif 3 report, section 2.1:
+# sliding-window layers; query i sees the last `window` keys up to itself) ---
+
+@pytest.mark.parametrize("window", [37, 38, 1000])
+def test_window_at_least_T_is_causal(window):
+    x = _inputs(B=2, T=37, H=2)
+    o, y = _run(x)
+    ow, yw = _run(x, window=window)
+    np.testing.assert_array_equal(ow, o)
+    np.testing.assert_array_equal(yw, y)
+
+
+def test_window1_is_own_value():
+    # one key: both softmax rows are exactly 1, so o_i = (1 - lambda_h) v_i
+    x = _inputs(B=2, T=20, H=2)
+    lam = np.array([0.8, -0.3])
+    o, _ = _run(x, lam=lam, window=1)
+    v = _f64(x["v"])
+    for h in range(2):
+        np.testing.assert_array_equal(o[:, :, h], (1.0 - lam[h]) * v[:, :, h])
+
+
+@pytest.mark.parametrize("window", [2, 5, 11])
+def test_window_bruteforce_decimal(window):
+    x = _inputs(B=2, T=14, H=2, seed=41, d_qk=8, d_v=16)
+    lam_h = np.array([0.7, -0.2])
+    o, y = _run(x, lam=lam_h, window=window)
+    for b, i, h in [(0, 0, 0), (0, window - 1, 1), (1, window, 0), (1, 13, 1), (0, 9, 0)]:
+        ob, yb = bruteforce.row(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], b, i, h, lam_h[h],
+                                x["gain"], x["eps"], x["scale"], window=window)
+        np.testing.assert_allclose(o[b, i, h], [float(t) for t in ob], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(y[b, i, h], [float(t) for t in yb], rtol=1e-12, atol=1e-13)
+
+
+def test_window_row_is_last_row_of_slice():
+    # Query i under window W sees exactly what the last query of the sequence
+    # slice [i-W+1, i] sees under the plain causal mask.
+    x = _inputs(B=1, T=40, H=2, seed=17)
+    W = 9
+    o, y = _run(x, window=W)
+    for i in [W - 1, W, 23, 39]:
+        sl = {k: (x[k][:, i - W + 1:i + 1] if k in ("q1", "q2", "k1", "k2", "v") else x[k]) for k in x}
+        os_, ys = _run(sl)
+        np.testing.assert_array_equal(o[:, i], os_[:, -1])
+        np.testing.assert_array_equal(y[:, i], ys[:, -1])
+
+
+def test_window_decode_equals_last_prefill_row():
+    x = _inputs(B=2, T=30, H=2)
+    for W in [1, 7, 29, 30, 64]:
+        o, y = _run(x, window=W)
+        od, yd = oracle.decode(x["q1"][:, -1], x["q2"][:, -1], x["k1"], x["k2"], x["v"], x["lam"],
+                               x["gain"], x["eps"], x["scale"], window=W)
+        np.testing.assert_array_equal(od, o[:, -1])
+        np.testing.assert_array_equal(yd, y[:, -1])
+    # with a shorter cached length the window ends at that length
+    o, _ = _run(x, window=5)
+    od, _ = oracle.decode(x["q1"][:, 11], x["q2"][:, 11], x["k1"], x["k2"], x["v"], x["lam"],
+                          x["gain"], x["eps"], x["scale"], seqlens=np.array([12, 30], np.int32), window=5)
+    np.testing.assert_array_equal(od[0], o[0, 11])
+
+
+def test_window_negative_rejected():
+    x = _inputs(B=1, T=4, H=2)
+    with pytest.raises(RuntimeError):
+        _run(x, window=-1)
+
+
+# --- ring-buffer cache for sliding-window decode: a cache of L slots keeps
+# the last L positions, position p in slot p % L ---
+
+def _ring_from_linear(t, n, L):
+    """Ring image of a linear [B, N, H, D] cache after n[b] positions."""
+    B = t.shape[0]
+    r = np.zeros((B, L) + t.shape[2:], t.dtype)
+    for b in range(B):
+        for p in range(int(n[b])):
+            r[b, p % L] = t[b, p]
+    return r
+
+
+def test_ring_matches_linear_cache():
+    from synth.workloads import Workload
+
+    L, N = 8, 40
+    wl = Workload("r", "decode", B=5, T=N, H=2, seed=33, lam=0.6, d_qk=16, d_v=32)
+    x = synth.make_decode_inputs(wl)
+    n = np.array([3, 8, 9, 21, 40], np.int32)
+    ring = {k: _ring_from_linear(x[k], n, L) for k in ("k1", "k2", "v")}
+    for W in [0, 1, 3, 7, 8]:
+        o_r, y_r = oracle.decode(x["q1"], x["q2"], ring["k1"], ring["k2"], ring["v"], x["lam"], x["gain"],
+                                 x["eps"], x["scale"], seqlens=n, window=W, ring=True)
+        o_l, y_l = oracle.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"],
+                                 x["eps"], x["scale"], seqlens=n, window=W if W else L)
+        np.testing.assert_array_equal(o_r, o_l)
+        np.testing.assert_array_equal(y_r, y_l)
+
+
+def test_ring_without_wrap_is_linear():
+    from synth.workloads import Workload
+
+    wl = Workload("r", "decode", B=3, T=12, H=2, seed=34, lam=0.6, d_qk=16, d_v=32)
+    x = synth.make_decode_inputs(wl)
+    n = np.array([0, 5, 12], np.int32)
+    for W in [0, 4]:
+        a = oracle.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"],
+                          x["scale"], seqlens=n, window=W, ring=True)
+        b = oracle.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"],
+                          x["scale"], seqlens=n, window=W)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+    with pytest.raises(RuntimeError):
+        oracle.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"],
+                      x["scale"], seqlens=n, window=13, ring=True)

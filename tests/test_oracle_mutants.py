@@ -20,8 +20,8 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "diffattn_oracle.c")
 
 MUTANTS = {
     "scale dropped": ("p1[j] = scale * a;", "p1[j] = a;"),
-    "not causal": ("(int64_t)H * d_qk, (int64_t)H * d_v, i + 1, d_qk, d_v,",
-                   "(int64_t)H * d_qk, (int64_t)H * d_v, T, d_qk, d_v,"),
+    "not causal": ("(int64_t)H * d_qk, (int64_t)H * d_v, i + 1 - first, d_qk, d_v,",
+                   "(int64_t)H * d_qk, (int64_t)H * d_v, T - first, d_qk, d_v,"),
     "lambda sign": ("p1[j] = p1[j] - lam * p2[j];", "p1[j] = p1[j] + lam * p2[j];"),
     "second map uses K1": ("b += bf16_to_f64(q2[c]) * bf16_to_f64(k2[j * kstride + c]);",
                            "b += bf16_to_f64(q2[c]) * bf16_to_f64(k1[j * kstride + c]);"),
@@ -30,8 +30,14 @@ MUTANTS = {
     "gain dropped": ("y[c] = (o[c] - mu) * inv * (double)gain[c];", "y[c] = (o[c] - mu) * inv;"),
     "lambda of head 0": ("scale, lam[h], gain + (int64_t)h * d_v, eps, p1, p2,\n                                   o_pre + r * d_v",
                          "scale, lam[0], gain + (int64_t)h * d_v, eps, p1, p2,\n                                   o_pre + r * d_v"),
-    "V read with K stride": ("(int64_t)H * d_qk, (int64_t)H * d_v, i + 1, d_qk, d_v,",
-                             "(int64_t)H * d_qk, (int64_t)H * d_qk, i + 1, d_qk, d_v,"),
+    "V read with K stride": ("(int64_t)H * d_qk, (int64_t)H * d_v, i + 1 - first, d_qk, d_v,",
+                             "(int64_t)H * d_qk, (int64_t)H * d_qk, i + 1 - first, d_qk, d_v,"),
+    "window one key short": ("int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0;",
+                             "int64_t first = (window > 0 && i + 1 > window) ? i + 2 - window : 0;"),
+    "window ignored": ("int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0;",
+                       "int64_t first = 0;"),
+    "window keys not shifted": ("int64_t koff = ((b * T + first) * H + h) * (int64_t)d_qk;",
+                                "int64_t koff = ((b * T) * H + h) * (int64_t)d_qk;"),
     "mean over wrong count": ("    mu /= d_v;", "    mu /= (d_v + 1);"),
     "second softmax short": ("    softmax_inplace(p2, n_keys);", "    softmax_inplace(p2, n_keys > 1 ? n_keys - 1 : 1);"),
 }
@@ -98,6 +104,19 @@ def _pins(lib):
     o, _ = run(xi, 1.0)
     if not np.all(o == 0):
         failed.append("identical maps")
+    # sliding window: brute force with the window, and window 1 = (1 - lambda) v_i
+    W = 4
+    o, y = run(x, lam, window=W)
+    for b, i, h in [(0, 2, 0), (1, 11, 1), (0, 7, 1)]:
+        ob, yb = bruteforce.row(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], b, i, h, lam[h], x["gain"],
+                                x["eps"], x["scale"], window=W)
+        if not (np.allclose(o[b, i, h], [float(t) for t in ob], rtol=1e-12, atol=1e-14)
+                and np.allclose(y[b, i, h], [float(t) for t in yb], rtol=1e-10, atol=1e-12)):
+            failed.append("window brute force")
+            break
+    o, _ = run(x, lam, window=1)
+    if not all(np.array_equal(o[:, :, h], (1.0 - lam[h]) * _f64(x["v"])[:, :, h]) for h in range(2)):
+        failed.append("window 1")
     return failed
 
 
