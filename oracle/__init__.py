@@ -42,10 +42,13 @@ def _bind(path):
     lib = ctypes.CDLL(path)
     P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
     lib.oracle_prefill.restype = I
-    lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P, D, D, I, P,
-                                   ctypes.c_int64, P, P, I]
+    I64 = ctypes.c_int64
+    lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P, D, D, I, I, D, I64, P,
+                                   I64, P, P, I]
     lib.oracle_decode.restype = I
-    lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, D, D, I, I, P, P, I]
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, D, D, I, I, I, D, I64, P, P, I]
+    lib.oracle_rope.restype = I
+    lib.oracle_rope.argtypes = [P, P, I, I, I, I, I, D, I64, P]
     return lib
 
 
@@ -74,7 +77,36 @@ def _lam(lam, H):
     return np.ascontiguousarray(lam)
 
 
-def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib=None, window=0):
+ROPE_NONE, ROPE_HALF, ROPE_INTERLEAVED = 0, 1, 2
+
+
+def _rope_args(rope, theta):
+    rope = int(rope)
+    if rope not in (ROPE_NONE, ROPE_HALF, ROPE_INTERLEAVED):
+        raise ValueError("rope must be 0 (none), 1 (split-half) or 2 (interleaved)")
+    if rope and not float(theta) > 0:
+        raise ValueError("rope_theta must be > 0")
+    return rope, float(theta)
+
+
+def rope(x, mode, theta, pos0=0, pos_start=None, lib=None):
+    """Rotary embedding of bf16 bits x [B, T, H, d] in fp64: token t of batch
+    row b at position pos0 + pos_start[b] + t (pos_start optional).  Returns
+    the rotated fp64 array."""
+    x = _u16(x)
+    B, T, H, d = x.shape
+    mode, theta = _rope_args(mode, theta)
+    ps = None if pos_start is None else np.ascontiguousarray(pos_start, dtype=np.int32).reshape(B)
+    out = np.empty(x.shape, dtype=np.float64)
+    rc = (lib or _load()).oracle_rope(x.ctypes.data, out.ctypes.data, B, T, H, d, mode, theta, int(pos0),
+                                      None if ps is None else ps.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_rope failed")
+    return out
+
+
+def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib=None, window=0,
+            rope=ROPE_NONE, rope_theta=0.0, rope_pos0=0):
     """Causal prefill in fp64.
 
     q1, q2, k1, k2: bf16 bits [B, T, H, d_qk]; v: bf16 bits [B, T, H, d_v].
@@ -82,6 +114,8 @@ def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib
     rows: optional sequence of (b, i, h) triples; default all rows.
     window: > 0 for a sliding window of that many keys (query i sees
     i-window+1 .. i), 0 for every key <= i.
+    rope: ROPE_HALF or ROPE_INTERLEAVED rotates Q1, Q2, K1, K2 (base
+    rope_theta), token t at position rope_pos0 + t.
     Returns (o_pre, y) as fp64 arrays of shape [B, T, H, d_v], or [n_rows, d_v]
     when rows are given.
     """
@@ -95,6 +129,7 @@ def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib
         raise ValueError("v must be [B, T, H, d_v]")
     gain = np.ascontiguousarray(gain, dtype=np.float32).reshape(H, d_v)
     lam = _lam(lam, H)
+    rope, rope_theta = _rope_args(rope, rope_theta)
     if rows is None:
         flat = None
         n = B * T * H
@@ -110,6 +145,7 @@ def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib
     rc = (lib or _load()).oracle_prefill(q1.ctypes.data, q2.ctypes.data, k1.ctypes.data, k2.ctypes.data,
                                 v.ctypes.data, B, T, H, d_qk, d_v, lam.ctypes.data,
                                 gain.ctypes.data, float(eps), float(scale), int(window),
+                                rope, rope_theta, int(rope_pos0),
                                 None if flat is None else flat.ctypes.data, n,
                                 o.ctypes.data, y.ctypes.data, int(nthreads))
     if rc != 0:
@@ -119,13 +155,16 @@ def prefill(q1, q2, k1, k2, v, lam, gain, eps, scale, rows=None, nthreads=0, lib
     return o, y
 
 
-def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0, lib=None, window=0, ring=False):
+def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0, lib=None, window=0, ring=False,
+           rope=ROPE_NONE, rope_theta=0.0, rope_pos0=0):
     """Single-query decode in fp64: q [B, H, d_qk] against caches [B, L, H, d].
 
     seqlens: optional [B] cached lengths (above L counts as L; <= 0 gives zeros).
     window: > 0 attends only the last `window` positions.
     ring: the L cache slots are a ring buffer (position p in slot p % L;
     seqlens may exceed L; window 0 means L; window > L is an error).
+    rope: rotates q1, q2 at position rope_pos0 + n - 1 (n = the sequence's
+    length); the cache is taken as already rotated.
     Returns (o_pre, y), fp64 [B, H, d_v].
     """
     q1, q2, k1, k2, v = (_u16(a) for a in (q1, q2, k1, k2, v))
@@ -137,6 +176,7 @@ def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0, l
         raise ValueError("decode shapes disagree")
     gain = np.ascontiguousarray(gain, dtype=np.float32).reshape(H, d_v)
     lam = _lam(lam, H)
+    rope, rope_theta = _rope_args(rope, rope_theta)
     sl = None
     if seqlens is not None:
         sl = np.ascontiguousarray(seqlens, dtype=np.int32)
@@ -147,7 +187,8 @@ def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0, l
     rc = (lib or _load()).oracle_decode(q1.ctypes.data, q2.ctypes.data, k1.ctypes.data, k2.ctypes.data,
                                v.ctypes.data, None if sl is None else sl.ctypes.data,
                                B, L, H, d_qk, d_v, lam.ctypes.data, gain.ctypes.data,
-                               float(eps), float(scale), int(window), int(bool(ring)), o.ctypes.data,
+                               float(eps), float(scale), int(window), int(bool(ring)), rope, rope_theta,
+                               int(rope_pos0), o.ctypes.data,
                                y.ctypes.data,
                                int(nthreads))
     if rc != 0:

@@ -20,6 +20,13 @@
  *   - sliding window (Motif 3's sliding-window layers, picx.dev summary of the
  *     Motif 3 report, section 2.1): with window W > 0, query i attends keys
  *     i-W+1 .. i, and decode the last W cached keys;
+ *   - rotary position embedding (Motif 2.6B explainer, section "The block":
+ *     RoPE with base 500,000; the pages fix neither the pairing nor where it
+ *     is applied): each d_qk-wide vector of Q1, Q2, K1, K2 is rotated on its
+ *     own, pair c turning by the angle pos * theta^(-2c/d_qk), with either
+ *     the split-half pairing (c, c + d_qk/2) or the interleaved pairing
+ *     (2c, 2c + 1); token t of a prefill sits at position pos0 + t, and a
+ *     decode query at pos0 + n - 1 (the cache holds keys already rotated);
  *   - lambda is an input (scalar or one value per head) that scales the
  *     normalised second map; no clamping;
  *   - "GroupNorm" acts on the head output (after the product with V), with one
@@ -47,6 +54,49 @@ static inline double bf16_to_f64(uint16_t bits) {
     return (double)f;
 }
 
+/*
+ * Rotary position embedding of one d-vector x (fp64, in place) at position
+ * pos: pair c = (i0, i1) turns by the angle pos * theta^(-2c/d), i.e.
+ * (x[i0], x[i1]) -> (x[i0] cos a - x[i1] sin a, x[i0] sin a + x[i1] cos a).
+ * mode 1 pairs (c, c + d/2), mode 2 pairs (2c, 2c + 1); mode 0 leaves x.
+ */
+static void rope_rotate(double* x, int d, int mode, double theta, double pos) {
+    if (mode == 0) return;
+    for (int c = 0; c < d / 2; ++c) {
+        double a = pos * pow(theta, -2.0 * c / d);
+        double cs = cos(a), sn = sin(a);
+        int i0 = mode == 1 ? c : 2 * c;
+        int i1 = mode == 1 ? c + d / 2 : 2 * c + 1;
+        double x0 = x[i0], x1 = x[i1];
+        x[i0] = x0 * cs - x1 * sn;
+        x[i1] = x0 * sn + x1 * cs;
+    }
+}
+
+/* One d-vector of bf16 bits widened to fp64 and rotated at position pos. */
+static void load_rotated(const uint16_t* src, double* dst, int d, int mode, double theta, double pos) {
+    for (int c = 0; c < d; ++c) dst[c] = bf16_to_f64(src[c]);
+    rope_rotate(dst, d, mode, theta, pos);
+}
+
+/*
+ * Standalone rotation of x: bf16 [B, T, H, d] -> fp64 out [B, T, H, d], token
+ * t of batch row b at position pos0 + (pos_start ? pos_start[b] : 0) + t.
+ */
+int oracle_rope(const uint16_t* x, double* out, int B, int T, int H, int d, int mode,
+                double theta, int64_t pos0, const int32_t* pos_start) {
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || d % 2 || mode < 0 || mode > 2) return -1;
+    if (mode && !(theta > 0)) return -1;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t h = 0; h < H; ++h) {
+                int64_t off = ((b * T + t) * H + h) * d;
+                double pos = (double)(pos0 + (pos_start ? pos_start[b] : 0) + t);
+                load_rotated(x + off, out + off, d, mode, theta, pos);
+            }
+    return 0;
+}
+
 /* Softmax of x[0..n) in place: exp(x - max) / sum (the textbook definition). */
 static void softmax_inplace(double* x, int64_t n) {
     double m = -INFINITY;
@@ -57,13 +107,24 @@ static void softmax_inplace(double* x, int64_t n) {
 }
 
 /*
- * One query row.  q1, q2 point at the row's d_qk-vectors; k1, k2, v at key
- * position 0 of this (b, h), with `kstride`/`vstride` elements between
- * consecutive positions.  p1 and p2 are scratch of length >= n_keys.
- * Writes o[d_v] (pre-norm) and y[d_v] (after GroupNorm).
+ * Keys of one (b, h): either bf16 bits (b16) or, when rotated, fp64 values
+ * (f64); element (j, c) at [j * stride + c].
  */
-static void diff_attention_row(const uint16_t* q1, const uint16_t* q2,
-                               const uint16_t* k1, const uint16_t* k2, const uint16_t* v,
+typedef struct {
+    const uint16_t* b16;
+    const double* f64;
+} keys_t;
+
+static inline double key_at(keys_t k, int64_t idx) { return k.f64 ? k.f64[idx] : bf16_to_f64(k.b16[idx]); }
+
+/*
+ * One query row.  q1, q2: the row's d_qk-vectors in fp64 (already rotated
+ * when RoPE is on); k1, k2, v at key position 0 of this (b, h), with
+ * `kstride`/`vstride` elements between consecutive positions.  p1 and p2 are
+ * scratch of length >= n_keys.  Writes o[d_v] (pre-norm) and y[d_v] (after
+ * GroupNorm).
+ */
+static void diff_attention_row(const double* q1, const double* q2, keys_t k1, keys_t k2, const uint16_t* v,
                                int64_t kstride, int64_t vstride, int64_t n_keys,
                                int d_qk, int d_v, double scale, double lam,
                                const float* gain, double eps,
@@ -72,8 +133,8 @@ static void diff_attention_row(const uint16_t* q1, const uint16_t* q2,
     for (int64_t j = 0; j < n_keys; ++j) {
         double a = 0.0, b = 0.0;
         for (int c = 0; c < d_qk; ++c) {
-            a += bf16_to_f64(q1[c]) * bf16_to_f64(k1[j * kstride + c]);
-            b += bf16_to_f64(q2[c]) * bf16_to_f64(k2[j * kstride + c]);
+            a += q1[c] * key_at(k1, j * kstride + c);
+            b += q2[c] * key_at(k2, j * kstride + c);
         }
         p1[j] = scale * a;
         p2[j] = scale * b;
@@ -103,7 +164,8 @@ static void diff_attention_row(const uint16_t* q1, const uint16_t* q2,
 /*
  * Causal prefill.  q1, q2, k1, k2: bf16 [B, T, H, d_qk]; v: bf16 [B, T, H, d_v],
  * all C-contiguous.  lam: fp64 [H].  gain: fp32 [H, d_v].  window: > 0 for a
- * sliding window of that many keys, 0 for every key <= i.
+ * sliding window of that many keys, 0 for every key <= i.  rope: 0 none,
+ * 1 split-half, 2 interleaved pairs, base theta, token t at position pos0 + t.
  * rows: n_rows flat indices ((b * T + i) * H + h), or NULL for every row in
  * that order (then n_rows must be B*T*H).  o_pre, y: fp64 [n_rows, d_v].
  * nthreads <= 0 uses the OpenMP default.  Returns 0, or -1 on bad arguments
@@ -112,10 +174,22 @@ static void diff_attention_row(const uint16_t* q1, const uint16_t* q2,
 int oracle_prefill(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
                    const uint16_t* k2, const uint16_t* v, int B, int T, int H,
                    int d_qk, int d_v, const double* lam, const float* gain,
-                   double eps, double scale, int window, const int64_t* rows, int64_t n_rows,
-                   double* o_pre, double* y, int nthreads) {
+                   double eps, double scale, int window, int rope, double theta, int64_t pos0,
+                   const int64_t* rows, int64_t n_rows, double* o_pre, double* y, int nthreads) {
     if (B <= 0 || T <= 0 || H <= 0 || d_qk <= 0 || d_v <= 0 || window < 0) return -1;
+    if (rope < 0 || rope > 2 || (rope && (!(theta > 0) || d_qk % 2))) return -1;
     if (!rows && n_rows != (int64_t)B * T * H) return -1;
+    /* With RoPE, every key is rotated once, up front, into fp64 copies. */
+    double* k1r = NULL;
+    double* k2r = NULL;
+    if (rope) {
+        size_t n = (size_t)B * T * H * d_qk;
+        k1r = (double*)malloc(sizeof(double) * n);
+        k2r = (double*)malloc(sizeof(double) * n);
+        if (!k1r || !k2r) { free(k1r); free(k2r); return -1; }
+        oracle_rope(k1, k1r, B, T, H, d_qk, rope, theta, pos0, NULL);
+        oracle_rope(k2, k2r, B, T, H, d_qk, rope, theta, pos0, NULL);
+    }
     int bad = 0;
 #ifdef _OPENMP
     if (nthreads <= 0) nthreads = omp_get_max_threads();
@@ -124,9 +198,11 @@ int oracle_prefill(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
     {
         double* p1 = (double*)malloc(sizeof(double) * (size_t)T);
         double* p2 = (double*)malloc(sizeof(double) * (size_t)T);
-        if (!p1 || !p2) {
+        double* qa = (double*)malloc(sizeof(double) * 2 * (size_t)d_qk);
+        if (!p1 || !p2 || !qa) {
             bad = 1;
         } else {
+            double* qb = qa + d_qk;
 #ifdef _OPENMP
 #pragma omp for schedule(dynamic, 16)
 #endif
@@ -140,7 +216,11 @@ int oracle_prefill(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
                 int64_t qoff = ((b * T + i) * H + h) * d_qk;
                 int64_t koff = ((b * T + first) * H + h) * (int64_t)d_qk;
                 int64_t voff = ((b * T + first) * H + h) * (int64_t)d_v;
-                diff_attention_row(q1 + qoff, q2 + qoff, k1 + koff, k2 + koff, v + voff,
+                load_rotated(q1 + qoff, qa, d_qk, rope, theta, (double)(pos0 + i));
+                load_rotated(q2 + qoff, qb, d_qk, rope, theta, (double)(pos0 + i));
+                keys_t kk1 = {k1 + koff, rope ? k1r + koff : NULL};
+                keys_t kk2 = {k2 + koff, rope ? k2r + koff : NULL};
+                diff_attention_row(qa, qb, kk1, kk2, v + voff,
                                    (int64_t)H * d_qk, (int64_t)H * d_v, i + 1 - first, d_qk, d_v,
                                    scale, lam[h], gain + (int64_t)h * d_v, eps, p1, p2,
                                    o_pre + r * d_v, y + r * d_v);
@@ -148,7 +228,10 @@ int oracle_prefill(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
         }
         free(p1);
         free(p2);
+        free(qa);
     }
+    free(k1r);
+    free(k2r);
     return bad ? -1 : 0;
 }
 
@@ -163,14 +246,17 @@ int oracle_prefill(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
  * length may exceed L; window 0 then means window L, and window > L is an
  * error (those positions are overwritten).  The visible positions are
  * gathered, oldest first, into a contiguous copy before the row is computed.
+ * rope, theta, pos0: the query of sequence b is rotated at position
+ * pos0 + n - 1; cached keys are used as given (already rotated).
  * o_pre, y: fp64 [B, H, d_v].
  */
 int oracle_decode(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
                   const uint16_t* k2, const uint16_t* v, const int32_t* seqlens,
                   int B, int L, int H, int d_qk, int d_v, const double* lam,
                   const float* gain, double eps, double scale, int window, int ring,
-                  double* o_pre, double* y, int nthreads) {
+                  int rope, double theta, int64_t pos0, double* o_pre, double* y, int nthreads) {
     if (B <= 0 || L <= 0 || H <= 0 || d_qk <= 0 || d_v <= 0 || window < 0) return -1;
+    if (rope < 0 || rope > 2 || (rope && (!(theta > 0) || d_qk % 2))) return -1;
     if (ring && window > L) return -1;
     if (ring && window == 0) window = L;
     int bad = 0;
@@ -184,9 +270,11 @@ int oracle_decode(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
         uint16_t* g1 = ring ? (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L * d_qk) : NULL;
         uint16_t* g2 = ring ? (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L * d_qk) : NULL;
         uint16_t* gv = ring ? (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L * d_v) : NULL;
-        if (!p1 || !p2 || (ring && (!g1 || !g2 || !gv))) {
+        double* qa = (double*)malloc(sizeof(double) * 2 * (size_t)d_qk);
+        if (!p1 || !p2 || !qa || (ring && (!g1 || !g2 || !gv))) {
             bad = 1;
         } else {
+            double* qb = qa + d_qk;
 #ifdef _OPENMP
 #pragma omp for schedule(dynamic, 1)
 #endif
@@ -201,6 +289,8 @@ int oracle_decode(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
                 }
                 int64_t first = (window > 0 && n > window) ? n - window : 0;
                 int64_t qoff = (b * H + h) * (int64_t)d_qk;
+                load_rotated(q1 + qoff, qa, d_qk, rope, theta, (double)(pos0 + n - 1));
+                load_rotated(q2 + qoff, qb, d_qk, rope, theta, (double)(pos0 + n - 1));
                 if (ring) {
                     for (int64_t p = first; p < n; ++p) {
                         int64_t slot = p % L;
@@ -208,14 +298,16 @@ int oracle_decode(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
                         memcpy(g2 + (p - first) * d_qk, k2 + ((b * L + slot) * H + h) * d_qk, 2 * (size_t)d_qk);
                         memcpy(gv + (p - first) * d_v, v + ((b * L + slot) * H + h) * d_v, 2 * (size_t)d_v);
                     }
-                    diff_attention_row(q1 + qoff, q2 + qoff, g1, g2, gv, d_qk, d_v, n - first, d_qk, d_v,
+                    keys_t kk1 = {g1, NULL}, kk2 = {g2, NULL};
+                    diff_attention_row(qa, qb, kk1, kk2, gv, d_qk, d_v, n - first, d_qk, d_v,
                                        scale, lam[h], gain + (int64_t)h * d_v, eps, p1, p2,
                                        o_pre + r * d_v, y + r * d_v);
                     continue;
                 }
                 int64_t koff = ((b * L + first) * H + h) * (int64_t)d_qk;
                 int64_t voff = ((b * L + first) * H + h) * (int64_t)d_v;
-                diff_attention_row(q1 + qoff, q2 + qoff, k1 + koff, k2 + koff, v + voff,
+                keys_t kk1 = {k1 + koff, NULL}, kk2 = {k2 + koff, NULL};
+                diff_attention_row(qa, qb, kk1, kk2, v + voff,
                                    (int64_t)H * d_qk, (int64_t)H * d_v, n - first, d_qk, d_v, scale,
                                    lam[h], gain + (int64_t)h * d_v, eps, p1, p2,
                                    o_pre + r * d_v, y + r * d_v);
@@ -226,6 +318,7 @@ int oracle_decode(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
         free(g1);
         free(g2);
         free(gv);
+        free(qa);
     }
     return bad ? -1 : 0;
 }

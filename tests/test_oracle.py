@@ -385,3 +385,144 @@ def test_ring_without_wrap_is_linear():
     with pytest.raises(RuntimeError):
         oracle.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"],
                       x["scale"], seqlens=n, window=13, ring=True)
+
+
+# --- rotary position embedding (Motif 2.6B explainer, section "The block":
+# RoPE with base 500,000).  The pairing is a reading: split-half pairs
+# (c, c + 32) as in the Hugging Face Llama code, or interleaved pairs
+# (2c, 2c + 1); each 64-wide Q1, Q2, K1, K2 vector is rotated on its own. ---
+
+THETA = 500000.0
+
+
+def _rope_x(B=2, T=40, H=2, d=64, seed=51):
+    return synth.normal_bf16(seed, 1, (B, T, H, d))
+
+
+def test_rope_half_matches_transformers_llama():
+    from transformers import LlamaConfig
+    from transformers.models.llama.modeling_llama import LlamaRotaryEmbedding, apply_rotary_pos_emb
+
+    x = _rope_x()
+    B, T, H, d = x.shape
+    cfg = LlamaConfig(hidden_size=H * d, num_attention_heads=H, head_dim=d, rope_theta=THETA)
+    emb = LlamaRotaryEmbedding(cfg)
+    pos0 = 7
+    xt = torch.from_numpy(_f64(x)).permute(0, 2, 1, 3)  # [B, H, T, d]
+    cos, sin = emb(xt, (pos0 + torch.arange(T))[None].expand(B, T))
+    ref, _ = apply_rotary_pos_emb(xt, xt, cos, sin)
+    got = oracle.rope(x, oracle.ROPE_HALF, THETA, pos0=pos0)
+    # the library forms its angles in fp32: about 1e-5 at these positions
+    np.testing.assert_allclose(got, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=2e-4)
+
+
+def test_rope_interleaved_is_half_on_permuted_dims():
+    # Interleaved pair (2c, 2c+1) is split-half pair (c, c+32) after moving
+    # dim 2c to c and dim 2c+1 to c+32.
+    x = _rope_x()
+    perm = np.concatenate([np.arange(0, 64, 2), np.arange(1, 64, 2)])
+    half = oracle.rope(np.ascontiguousarray(x[..., perm]), oracle.ROPE_HALF, THETA, pos0=3)
+    inter = oracle.rope(x, oracle.ROPE_INTERLEAVED, THETA, pos0=3)
+    back = np.empty_like(half)
+    back[..., perm] = half
+    np.testing.assert_array_equal(inter, back)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_rope_closed_forms(mode):
+    x = _rope_x(B=1, T=1, H=1)
+    xf = _f64(x)[0, 0, 0]
+    # position 0 is the identity
+    np.testing.assert_array_equal(oracle.rope(x, mode, THETA, pos0=0)[0, 0, 0], xf)
+    # pair 0 turns by exactly `pos` radians (frequency theta^0 = 1)
+    i0, i1 = (0, 32) if mode == 1 else (0, 1)
+    for pos in (1, 2, 100, 12345, 1 << 20):
+        r = oracle.rope(x, mode, THETA, pos0=pos)[0, 0, 0]
+        c, s = math.cos(pos), math.sin(pos)
+        assert abs(r[i0] - (xf[i0] * c - xf[i1] * s)) < 1e-12
+        assert abs(r[i1] - (xf[i0] * s + xf[i1] * c)) < 1e-12
+    # the last pair turns by pos * theta^(-62/64)
+    j0, j1 = (31, 63) if mode == 1 else (62, 63)
+    pos = 5000
+    a = pos * THETA ** (-62 / 64)
+    r = oracle.rope(x, mode, THETA, pos0=pos)[0, 0, 0]
+    assert abs(r[j0] - (xf[j0] * math.cos(a) - xf[j1] * math.sin(a))) < 1e-12
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_rope_is_a_rotation_by_relative_position(mode):
+    q = _rope_x(B=1, T=1, H=3, seed=52)
+    k = _rope_x(B=1, T=1, H=3, seed=53)
+    qf, kf = _f64(q), _f64(k)
+    # each pair keeps its length
+    rq = oracle.rope(q, mode, THETA, pos0=777)
+    pairs = (lambda a: (a[..., :32], a[..., 32:])) if mode == 1 else (lambda a: (a[..., 0::2], a[..., 1::2]))
+    a0, a1 = pairs(rq)
+    b0, b1 = pairs(qf)
+    np.testing.assert_allclose(a0 ** 2 + a1 ** 2, b0 ** 2 + b1 ** 2, rtol=1e-12)
+    # scores depend only on the distance between the two positions
+    def score(pq, pk):
+        return np.sum(oracle.rope(q, mode, THETA, pos0=pq) * oracle.rope(k, mode, THETA, pos0=pk), axis=-1)
+    ref = score(40, 13)
+    for shift in (1, 1000, 300000):
+        np.testing.assert_allclose(score(40 + shift, 13 + shift), ref, rtol=0, atol=1e-10)
+    assert np.abs(score(41, 13) - ref).max() > 1e-3
+
+
+def test_rope_pos_start_per_batch_row():
+    x = _rope_x(B=3, T=5, H=2)
+    got = oracle.rope(x, 1, THETA, pos0=10, pos_start=np.array([0, 4, 100]))
+    for b, st in enumerate((0, 4, 100)):
+        np.testing.assert_array_equal(got[b], oracle.rope(x[b:b + 1], 1, THETA, pos0=10 + st)[0])
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_rope_prefill_lambda0_is_sdpa_on_rotated(mode):
+    x = _inputs(B=2, T=33, H=2)
+    pos0 = 11
+    o, y = _run(x, lam=0.0, rope=mode, rope_theta=THETA, rope_pos0=pos0)
+    q = torch.from_numpy(oracle.rope(x["q1"], mode, THETA, pos0)).permute(0, 2, 1, 3)
+    k = torch.from_numpy(oracle.rope(x["k1"], mode, THETA, pos0)).permute(0, 2, 1, 3)
+    v = torch.from_numpy(_f64(x["v"])).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=x["scale"])
+    np.testing.assert_allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_rope_prefill_shift_invariant(mode):
+    # every score depends on i - j only, so moving all tokens changes nothing
+    x = _inputs(B=1, T=30, H=2)
+    a = _run(x, rope=mode, rope_theta=THETA, rope_pos0=0)
+    b = _run(x, rope=mode, rope_theta=THETA, rope_pos0=4321)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-10)
+    c = _run(x)
+    assert np.abs(a[0] - c[0]).max() > 1e-3  # and it is not the plain result
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_rope_decode_rotates_query_at_last_position(mode):
+    from synth.workloads import Workload
+
+    wl = Workload("d", "decode", B=3, T=20, H=2, seed=61, lam=0.0)
+    x = synth.make_decode_inputs(wl)
+    n = np.array([20, 7, 1], np.int32)
+    pos0 = 5
+    o, _ = oracle.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], 0.0, x["gain"], x["eps"], x["scale"],
+                         seqlens=n, rope=mode, rope_theta=THETA, rope_pos0=pos0)
+    for b in range(3):
+        q = oracle.rope(x["q1"][b:b + 1, None], mode, THETA, pos0 + int(n[b]) - 1)[0, 0]  # [H, d]
+        k = _f64(x["k1"][b, : n[b]])  # cache used as given
+        v = _f64(x["v"][b, : n[b]])
+        for h in range(2):
+            s = k[:, h] @ q[h] * x["scale"]
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            np.testing.assert_allclose(o[b, h], p @ v[:, h], rtol=0, atol=1e-12)
+
+
+def test_rope_rejects_bad_arguments():
+    x = _inputs(B=1, T=4, H=2)
+    with pytest.raises(ValueError):
+        _run(x, rope=3, rope_theta=THETA)
+    with pytest.raises(ValueError):
+        _run(x, rope=1, rope_theta=0.0)

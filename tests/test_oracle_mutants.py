@@ -23,8 +23,8 @@ MUTANTS = {
     "not causal": ("(int64_t)H * d_qk, (int64_t)H * d_v, i + 1 - first, d_qk, d_v,",
                    "(int64_t)H * d_qk, (int64_t)H * d_v, T - first, d_qk, d_v,"),
     "lambda sign": ("p1[j] = p1[j] - lam * p2[j];", "p1[j] = p1[j] + lam * p2[j];"),
-    "second map uses K1": ("b += bf16_to_f64(q2[c]) * bf16_to_f64(k2[j * kstride + c]);",
-                           "b += bf16_to_f64(q2[c]) * bf16_to_f64(k1[j * kstride + c]);"),
+    "second map uses K1": ("b += q2[c] * key_at(k2, j * kstride + c);",
+                           "b += q2[c] * key_at(k1, j * kstride + c);"),
     "unbiased variance": ("    var /= d_v;", "    var /= (d_v - 1);"),
     "eps outside sqrt": ("double inv = 1.0 / sqrt(var + eps);", "double inv = 1.0 / (sqrt(var) + eps);"),
     "gain dropped": ("y[c] = (o[c] - mu) * inv * (double)gain[c];", "y[c] = (o[c] - mu) * inv;"),
@@ -40,6 +40,16 @@ MUTANTS = {
                                 "int64_t koff = ((b * T) * H + h) * (int64_t)d_qk;"),
     "mean over wrong count": ("    mu /= d_v;", "    mu /= (d_v + 1);"),
     "second softmax short": ("    softmax_inplace(p2, n_keys);", "    softmax_inplace(p2, n_keys > 1 ? n_keys - 1 : 1);"),
+    "rope not a rotation": ("x[i1] = x0 * sn + x1 * cs;", "x[i1] = -x0 * sn + x1 * cs;"),
+    "rope turns backwards": ("        x[i0] = x0 * cs - x1 * sn;\n        x[i1] = x0 * sn + x1 * cs;",
+                             "        x[i0] = x0 * cs + x1 * sn;\n        x[i1] = -x0 * sn + x1 * cs;"),
+    "rope frequency exponent": ("pow(theta, -2.0 * c / d)", "pow(theta, -1.0 * c / d)"),
+    "rope pairs adjacent in half mode": ("int i1 = mode == 1 ? c + d / 2 : 2 * c + 1;",
+                                         "int i1 = mode == 1 ? 2 * c + 1 : 2 * c + 1;"),
+    "rope query one position late": ("load_rotated(q1 + qoff, qa, d_qk, rope, theta, (double)(pos0 + i));",
+                                     "load_rotated(q1 + qoff, qa, d_qk, rope, theta, (double)(pos0 + i + 1));"),
+    "rope decode query at n": ("load_rotated(q1 + qoff, qa, d_qk, rope, theta, (double)(pos0 + n - 1));",
+                               "load_rotated(q1 + qoff, qa, d_qk, rope, theta, (double)(pos0 + n));"),
 }
 
 
@@ -117,6 +127,50 @@ def _pins(lib):
     o, _ = run(x, lam, window=1)
     if not all(np.array_equal(o[:, :, h], (1.0 - lam[h]) * _f64(x["v"])[:, :, h]) for h in range(2)):
         failed.append("window 1")
+    failed += _rope_pins(lib)
+    return failed
+
+
+def _rope_pins(lib):
+    """The RoPE pins of tests/test_oracle.py, on 64-wide vectors."""
+    from transformers import LlamaConfig
+    from transformers.models.llama.modeling_llama import LlamaRotaryEmbedding, apply_rotary_pos_emb
+
+    failed = []
+    theta = 500000.0
+    xr = synth.normal_bf16(51, 1, (1, 12, 2, 64))
+    emb = LlamaRotaryEmbedding(LlamaConfig(hidden_size=128, num_attention_heads=2, head_dim=64, rope_theta=theta))
+    xt = torch.from_numpy(_f64(xr)).permute(0, 2, 1, 3)
+    cos, sin = emb(xt, (3 + torch.arange(12))[None])
+    ref, _ = apply_rotary_pos_emb(xt, xt, cos, sin)
+    got = oracle.rope(xr, 1, theta, pos0=3, lib=lib)
+    if not np.allclose(got, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=2e-4):
+        failed.append("rope vs transformers")
+    perm = np.concatenate([np.arange(0, 64, 2), np.arange(1, 64, 2)])
+    half = oracle.rope(np.ascontiguousarray(xr[..., perm]), 1, theta, pos0=3, lib=lib)
+    back = np.empty_like(half)
+    back[..., perm] = half
+    if not np.array_equal(oracle.rope(xr, 2, theta, pos0=3, lib=lib), back):
+        failed.append("rope interleaved permutation")
+    # lambda = 0 prefill with RoPE is SDPA on the rotated vectors
+    x = _inputs(B=1, T=10, H=2, d_qk=64, d_v=16)
+    o, _ = oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], 0.0, x["gain"], x["eps"], x["scale"],
+                          lib=lib, rope=1, rope_theta=theta, rope_pos0=5)
+    q = torch.from_numpy(oracle.rope(x["q1"], 1, theta, 5)).permute(0, 2, 1, 3)
+    k = torch.from_numpy(oracle.rope(x["k1"], 1, theta, 5)).permute(0, 2, 1, 3)
+    v = torch.from_numpy(_f64(x["v"])).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=x["scale"])
+    if not np.allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12):
+        failed.append("rope prefill sdpa")
+    # decode rotates the query at position pos0 + n - 1
+    n = np.array([10], np.int32)
+    od, _ = oracle.decode(x["q1"][:, 9], x["q2"][:, 9], x["k1"], x["k2"], x["v"], 0.0, x["gain"], x["eps"],
+                          x["scale"], seqlens=n, lib=lib, rope=1, rope_theta=theta, rope_pos0=5)
+    qd = torch.from_numpy(oracle.rope(x["q1"][:, 9:10], 1, theta, 14)).permute(0, 2, 1, 3)
+    kd = torch.from_numpy(_f64(x["k1"])).permute(0, 2, 1, 3)
+    refd = torch.nn.functional.scaled_dot_product_attention(qd, kd, v, scale=x["scale"])
+    if not np.allclose(od, refd.permute(0, 2, 1, 3).numpy()[:, 0], rtol=0, atol=1e-12):
+        failed.append("rope decode position")
     return failed
 
 
