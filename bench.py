@@ -38,6 +38,7 @@ PREFILL_WL = "prefill_b1_t4096_h16"
 DECODE_WL = "decode_b64_l4096_h16"
 SWA_PREFILL_WL = "swa_b1_t16384_h16_w128"
 SWA_DECODE_WL = "swa_decode_b64_l4096_h16_w128"
+ROPE_THETA = 500000.0        # Motif 2.6B's RoPE base
 CSRC = os.path.join(ROOT, "differential_attention_causal_amd", "csrc")
 PREFILL_PMC = os.path.join(ROOT, "profiles", "prefill_kernel_b1_t4096_h16_hbm_counters.txt")
 PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("prefill.hip", "kernels.h")]
@@ -126,10 +127,11 @@ def _time_calls(torch, np, fn, warmup: int, iters: int):
     return float(ms.mean()) * 1e3, float(ms.min()) * 1e3
 
 
-def sliding_window_variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
-    """Motif 3's sliding-window layer type (128-token windows): the windowed
-    prefill at T=16384 and the windowed decode over the 4096-long caches.
-    Timed after, and outside, the step's timed region."""
+def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
+    """The variant rows, timed after, and outside, the step's timed region:
+    Motif 3's sliding-window layer type (128-token windows) as the windowed
+    prefill at T=16384 and the windowed decode over the 4096-long caches, and
+    the T=4096 prefill with the fused RoPE prologue."""
     import synth
 
     pw = synth.WORKLOADS[SWA_PREFILL_WL]
@@ -153,12 +155,30 @@ def sliding_window_variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, ite
                                   scale=dw.scale, num_splits=dw.num_splits, workspace=ws, out=d_out,
                                   window=dw.window)
 
+    def prefill_rope():
+        # the Motif 2.6B layer itself: RoPE with base 500,000 fused in front
+        da.diffattn_fwd_prefill_ex(R["q1"], R["q2"], R["k1"], R["k2"], R["v"], rw.lam, rg, eps=rw.eps,
+                                   scale=rw.scale, out=r_out, rope=da.ROPE_HALF, rope_theta=ROPE_THETA)
+
+    rw = synth.WORKLOADS[PREFILL_WL]
+    xr = synth.make_prefill_inputs(rw)
+    R = {n: to_dev(xr[n], dev) for n in ("q1", "q2", "k1", "k2", "v")}
+    rg = f32_dev(xr["gain"], dev)
+    r_out = torch.empty((rw.B, rw.T, rw.H, rw.d_v), dtype=torch.bfloat16, device=dev)
+
     p_us, p_min = _time_calls(torch, np, prefill, warmup, iters)
     d_us, d_min = _time_calls(torch, np, decode, warmup, iters)
+    r_us, r_min = _time_calls(torch, np, prefill_rope, warmup, iters)
+    assert bool(torch.isfinite(r_out.float()).all())
+    r_flop = rw.causal_pairs * FLOP_PER_PAIR
     assert bool(torch.isfinite(p_out.float()).all()) and bool(torch.isfinite(d_out.float()).all())
     p_flop = pw.causal_pairs * FLOP_PER_PAIR
     d_bytes = decode_bytes(dw)
     return {
+        "rope_prefill": {"workload": PREFILL_WL, "rope": "split-half", "theta": ROPE_THETA,
+                         "us_mean": round(r_us, 2), "us_min": round(r_min, 2),
+                         "tflops": round(r_flop / r_us / 1e6, 2),
+                         "frac_mfma_peak": round(r_flop / r_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},
         "prefill": {"workload": SWA_PREFILL_WL, "window": pw.window, "us_mean": round(p_us, 2),
                     "us_min": round(p_min, 2), "visible_pairs": pw.causal_pairs,
                     "tflops": round(p_flop / p_us / 1e6, 2),
@@ -244,7 +264,7 @@ def main() -> int:
     step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
     assert bool(torch.isfinite(p_out.float()).all()) and bool(torch.isfinite(d_out.float()).all())
 
-    variants = sliding_window_variants(da, torch, np, to_dev, f32_dev, dev)
+    var = variants(da, torch, np, to_dev, f32_dev, dev)
 
     p_flop = pw.causal_pairs * FLOP_PER_PAIR
     p_s = float(p_ms.mean()) / 1e3
@@ -278,7 +298,7 @@ def main() -> int:
         "decode": {"workload": DECODE_WL, "us_mean": round(d_s * 1e6, 2), "us_min": round(float(d_ms.min()) * 1e3, 2),
                    "bytes": d_bytes, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                    "splits": dw.num_splits, "traffic": read_traffic(DECODE_PMC, DECODE_SOURCES)},
-        "sliding_window": variants,
+        "variants": var,
         "wall_s_timed": round(wall, 3),
         "kernel_source_sha256_16": kernel_source_digest(),
     }

@@ -22,6 +22,7 @@ __all__ = [
     "diffattn_fwd_prefill_ex",
     "diffattn_fwd_decode",
     "diffattn_fwd_decode_ex",
+    "diffattn_rope_apply",
     "diffattn_decode_workspace_bytes",
     "diffattn_status_string",
     "diffattn_abi_version",
@@ -71,6 +72,9 @@ _lib.diffattn_fwd_prefill_ex.restype = _I
 _lib.diffattn_fwd_prefill_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffattn_fwd_prefill.argtypes
 _lib.diffattn_fwd_decode_ex.restype = _I
 _lib.diffattn_fwd_decode_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffattn_fwd_decode.argtypes
+_lib.diffattn_rope_apply.restype = _I
+_lib.diffattn_rope_apply.argtypes = [_P, ctypes.POINTER(_Strides), _P, ctypes.POINTER(_Strides), _I, _I, _I, _I,
+                                     _I, ctypes.c_float, _I, _P, _P]
 _lib.diffattn_status_string.restype = ctypes.c_char_p
 _lib.diffattn_status_string.argtypes = [_I]
 _lib.diffattn_abi_version.restype = _I
@@ -238,6 +242,28 @@ def _decode(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens, num_splits, 
             workspace.numel() * workspace.element_size(), _ptr(out), _out_code(out.dtype), _ptr(o_pre),
             _stream(stream))
     rc = _lib.diffattn_fwd_decode(*args) if opt is None else _lib.diffattn_fwd_decode_ex(ctypes.byref(opt), *args)
+    _check(rc)
+    return out
+
+
+def diffattn_rope_apply(x, mode, theta, pos0=0, pos_start=None, out=None, stream=None):
+    """Rotary embedding of a bf16 [B, T, H, 64] device tensor, the rotation the
+    *_ex entry points apply with ``rope=mode``: token t of batch row b at
+    position pos0 + pos_start[b] + t.  pos_start: optional int32 [B] device
+    tensor.  out: optional destination (may be x, for in place); returns out."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 4:
+        raise ValueError("x must be a bf16 [B, T, H, d] device tensor")
+    B, T, H, d = x.shape
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, T, H, d):
+        raise ValueError("out must be a bf16 tensor shaped like x")
+    if pos_start is not None and (pos_start.dtype != torch.int32 or tuple(pos_start.shape) != (B,)
+                                  or not pos_start.is_cuda):
+        raise ValueError("pos_start must be an int32 [B] device tensor")
+    sx, so = _strides4(x), _strides4(out)
+    rc = _lib.diffattn_rope_apply(_ptr(x), ctypes.byref(sx), _ptr(out), ctypes.byref(so), B, T, H, d, int(mode),
+                                  float(theta), int(pos0), _ptr(pos_start), _stream(stream))
     _check(rc)
     return out
 

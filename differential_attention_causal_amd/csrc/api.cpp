@@ -49,8 +49,20 @@ int check_options(const diffattn_options* opt) {
   for (int r : opt->reserved)
     if (r != 0) return DIFFATTN_ERR_VALUE;
   if (opt->rope < DIFFATTN_ROPE_NONE || opt->rope > DIFFATTN_ROPE_INTERLEAVED) return DIFFATTN_ERR_VALUE;
-  if (opt->rope != DIFFATTN_ROPE_NONE) return DIFFATTN_ERR_UNSUPPORTED;
+  if (opt->rope != DIFFATTN_ROPE_NONE && (!std::isfinite(opt->rope_theta) || !(opt->rope_theta > 0.f) ||
+                                          opt->rope_pos0 < 0))
+    return DIFFATTN_ERR_VALUE;
   return DIFFATTN_OK;
+}
+
+diffattn::RopeArgs rope_args(const diffattn_options* opt) {
+  diffattn::RopeArgs r{};
+  if (opt && opt->rope != DIFFATTN_ROPE_NONE) {
+    r.mode = opt->rope;
+    r.pos0 = (uint32_t)opt->rope_pos0;
+    diffattn::rope_phases(opt->rope_theta, r);
+  }
+  return r;
 }
 
 float score_factor(float scale) {
@@ -62,7 +74,7 @@ float score_factor(float scale) {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 101; }
+int diffattn_abi_version(void) { return 102; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -73,7 +85,8 @@ const char* diffattn_status_string(int status) {
     case DIFFATTN_ERR_LAYOUT: return "diffattn: pointer not 16-byte aligned or stride not a multiple of 8 elements";
     case DIFFATTN_ERR_WORKSPACE: return "diffattn: decode workspace missing, misaligned or too small";
     case DIFFATTN_ERR_HIP: return "diffattn: the HIP runtime refused the kernel launch";
-    case DIFFATTN_ERR_VALUE: return "diffattn: invalid scalar argument (lambda, eps, scale, dtype or split count)";
+    case DIFFATTN_ERR_VALUE:
+      return "diffattn: invalid scalar argument (lambda, eps, scale, dtype, split count or option)";
     default: return "diffattn: unknown status";
   }
 }
@@ -117,6 +130,7 @@ int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void* q1, const v
   a.T = T;
   a.H = H;
   a.window = opt ? opt->window : 0;
+  a.rope = rope_args(opt);
   a.c = score_factor(scale);
   a.lambda = lambda;
   a.lambda_h = lambda_per_head;
@@ -190,6 +204,7 @@ int diffattn_fwd_decode_ex(const diffattn_options* opt, const void* q1, const vo
   a.window = opt ? opt->window : 0;
   a.ring = ring;
   if (ring && a.window == 0) a.window = L;
+  a.rope = rope_args(opt);
   a.c = score_factor(scale);
   a.lambda = lambda;
   a.lambda_h = lambda_per_head;
@@ -211,6 +226,35 @@ int diffattn_fwd_decode(const void* q1, const void* q2, const void* k1, const vo
   return diffattn_fwd_decode_ex(nullptr, q1, q2, k1, k2, v, cache_strides, seqlens, B, L, H, d_qk, d_v, lambda,
                                 lambda_per_head, gain, gn_eps, scale, num_splits, workspace, workspace_bytes, out,
                                 out_dtype, o_pre, stream);
+}
+
+int diffattn_rope_apply(const void* x, const diffattn_strides* x_strides, void* out,
+                        const diffattn_strides* out_strides, int B, int T, int H, int d, int mode, float theta,
+                        int pos0, const int32_t* pos_start, void* stream) {
+  if (!x || !out) return DIFFATTN_ERR_NULL;
+  if (B <= 0 || T <= 0 || H <= 0 || (int64_t)B * T * H > (int64_t(1) << 34)) return DIFFATTN_ERR_SHAPE;
+  if (d != kDqk) return DIFFATTN_ERR_UNSUPPORTED;
+  if ((mode != DIFFATTN_ROPE_HALF && mode != DIFFATTN_ROPE_INTERLEAVED) || !std::isfinite(theta) ||
+      !(theta > 0.f) || pos0 < 0)
+    return DIFFATTN_ERR_VALUE;
+  if (!aligned16(x) || !aligned16(out)) return DIFFATTN_ERR_LAYOUT;
+  const diffattn_strides sx = x_strides ? *x_strides : contiguous(T, H, d);
+  const diffattn_strides so = out_strides ? *out_strides : contiguous(T, H, d);
+  if (!strides_ok(sx) || !strides_ok(so)) return DIFFATTN_ERR_LAYOUT;
+  diffattn::RopeApplyArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.out = static_cast<uint16_t*>(out);
+  a.sx = to_internal(sx);
+  a.so = to_internal(so);
+  a.pos_start = pos_start;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.rope.mode = mode;
+  a.rope.pos0 = (uint32_t)pos0;
+  diffattn::rope_phases(theta, a.rope);
+  if (diffattn::launch_rope_apply(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
+  return DIFFATTN_OK;
 }
 
 }  // extern "C"

@@ -16,6 +16,7 @@
 // Every cache byte is read exactly once, so the cache loads are non-temporal:
 // they stream past the caches instead of evicting other data.
 #include "kernels.h"
+#include "rope.h"
 
 namespace diffattn {
 namespace {
@@ -32,11 +33,12 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Dot product of 8 bf16 pairs: products are exact in fp32, sums in fp32.
-__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc) {
+// q (8 floats, dims in order) . b (8 packed bf16), fp32 FMAs in dim order.
+__device__ __forceinline__ float dot8(const float (&q)[8], const u32x4& b, float acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    acc = __builtin_fmaf(bf16_lo(a[i]), bf16_lo(b[i]), acc);
-    acc = __builtin_fmaf(bf16_hi(a[i]), bf16_hi(b[i]), acc);
+    acc = __builtin_fmaf(q[2 * i], bf16_lo(b[i]), acc);
+    acc = __builtin_fmaf(q[2 * i + 1], bf16_hi(b[i]), acc);
   }
   return acc;
 }
@@ -85,8 +87,21 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
 
   // Query chunks: lane e of a key group holds dims 8e .. 8e+7 of q1 and q2.
   const int e = tid & 7, ks = tid >> 3;
-  const u32x4 q1 = *reinterpret_cast<const u32x4*>(a.q1 + (int64_t)bh * kDqk + 8 * e);
-  const u32x4 q2 = *reinterpret_cast<const u32x4*>(a.q2 + (int64_t)bh * kDqk + 8 * e);
+  float q[2][8];
+  rope_unpack(*reinterpret_cast<const u32x4*>(a.q1 + (int64_t)bh * kDqk + 8 * e), q[0]);
+  rope_unpack(*reinterpret_cast<const u32x4*>(a.q2 + (int64_t)bh * kDqk + 8 * e), q[1]);
+  if (a.rope.mode != 0) {
+    // The query is the sequence's last token, rotated in fp32 (no rounding);
+    // cached keys are already rotated.
+    __shared__ uint64_t rope_tab[32];
+    if (tid < 32) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if (c == tid) rope_tab[c] = a.rope.phase[c];
+    }
+    __syncthreads();
+    rope_floats<2>(q, e, a.rope.pos0 + (uint32_t)(n - 1), a.rope.mode, rope_tab);
+  }
   const uint16_t* k1b = a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h + 8 * e;
   const uint16_t* k2b = a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h + 8 * e;
   const int cg = tid & 15, kq = tid >> 4;
@@ -110,8 +125,8 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
         const int64_t pos = slot;
         const u32x4 x1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k1b + pos * a.sk1.t));
         const u32x4 x2 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k2b + pos * a.sk2.t));
-        d1 = dot8(q1, x1, 0.f);
-        d2 = dot8(q2, x2, 0.f);
+        d1 = dot8(q[0], x1, 0.f);
+        d2 = dot8(q[1], x2, 0.f);
       }
       d1 += __shfl_xor(d1, 1);
       d2 += __shfl_xor(d2, 1);

@@ -14,6 +14,14 @@ struct Strides {
   int64_t b, t, h;  // element strides; the innermost dimension is contiguous
 };
 
+// Rotary position embedding of the 64-wide Q1, Q2, K1, K2 vectors: pair c
+// turns by pos * theta^(-c/32) radians.
+struct RopeArgs {
+  int mode;            // 0 none, 1 split-half pairs (c, c + 32), 2 interleaved pairs (2c, 2c + 1)
+  uint32_t pos0;       // position of token 0
+  uint64_t phase[32];  // pair c: theta^(-c/32) / (2 pi) revolutions per position, 0.64 fixed point
+};
+
 struct PrefillArgs {
   const uint16_t* q1;
   const uint16_t* q2;
@@ -23,6 +31,7 @@ struct PrefillArgs {
   Strides sq1, sq2, sk1, sk2, sv;
   int B, T, H;
   int window;             // > 0: query i sees keys i-window+1 .. i; 0: every key <= i
+  RopeArgs rope;          // token t at position rope.pos0 + t
   float c;                // scale * log2(e): scores are kept in base-2 units
   float lambda;           // used when lambda_h is null
   const float* lambda_h;  // [H] or null
@@ -44,6 +53,7 @@ struct DecodeArgs {
   int B, L, H, splits;
   int window;              // > 0: attend only the last `window` positions
   int ring;                // cache of L slots is a ring: position p in slot p % L
+  RopeArgs rope;           // the query of a sequence of n tokens sits at rope.pos0 + n - 1
   float c;
   float lambda;
   const float* lambda_h;
@@ -62,7 +72,23 @@ constexpr float kNoMax = -1.0e30f;
 // Floats per (b, h, split, map) record in the decode workspace: max, sum, O[kDv].
 constexpr int kPartialStride = kDv + 2;
 
+// Standalone rotation of a [B, T, H, 64] bf16 tensor (for writing rotated
+// keys into a decode cache): token t of batch row b at position
+// rope.pos0 + pos_start[b] + t.
+struct RopeApplyArgs {
+  const uint16_t* x;
+  uint16_t* out;
+  Strides sx, so;
+  const int32_t* pos_start;  // [B] or null
+  int B, T, H;
+  RopeArgs rope;
+};
+
+// Fills rope.phase for base theta (host).
+void rope_phases(float theta, RopeArgs& r);
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t stream);
 
 }  // namespace diffattn

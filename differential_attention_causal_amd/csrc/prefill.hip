@@ -36,6 +36,7 @@
 // by more than kSlack (base 2), so P <= 2^kSlack stays far inside fp16 range and
 // the O rescale is rare after the first tiles.
 #include "kernels.h"
+#include "rope.h"
 
 namespace diffattn {
 namespace {
@@ -87,6 +88,7 @@ __device__ __forceinline__ u32x2 load8(const uint16_t* p) { return *reinterpret_
 struct Staged {
   u32x4 k1, k2;
   u32x2 v[4];
+  uint32_t kpos;  // position of this thread's key row (rotary embedding)
 };
 
 // Buffer resource over key rows k0 .. kend-1 of one (b, h) (row stride
@@ -104,14 +106,26 @@ struct StageOffsets {
   uint32_t k1, k2, v;
 };
 
+// K columns a thread stages: 16 bytes (dims 8ch .. 8ch+7), or with the
+// split-half rotary embedding 8 + 8 bytes (dims 4ch .. 4ch+3 and their pair
+// partners 32 + 4ch ..), so that every rotation pair stays in one thread.
+template <int kRope>
 __device__ __forceinline__ StageOffsets stage_offsets(const PrefillArgs& a, int tid) {
   const int t = tid % kTileThreads;
   const int kr = t >> 3, ch = t & 7, kg = t & 7, cg = t >> 3;
+  const int col = kRope == 1 ? 4 * ch : 8 * ch;
   StageOffsets o;
-  o.k1 = (uint32_t)((kr * a.sk1.t + 8 * ch) * 2);
-  o.k2 = (uint32_t)((kr * a.sk2.t + 8 * ch) * 2);
+  o.k1 = (uint32_t)((kr * a.sk1.t + col) * 2);
+  o.k2 = (uint32_t)((kr * a.sk2.t + col) * 2);
   o.v = (uint32_t)((4 * kg * a.sv.t + 4 * cg) * 2);
   return o;
+}
+
+__device__ __forceinline__ u32x4 load_krow(__amdgpu_buffer_rsrc_t r, uint32_t off, bool split) {
+  if (!split) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(r, off + 64, 0, 0);  // 32 dims further
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
 // Global -> registers for one step: one 32-key tile per group, keys from k0 on
@@ -119,28 +133,70 @@ __device__ __forceinline__ StageOffsets stage_offsets(const PrefillArgs& a, int 
 // g's tile.  Within a tile, thread t loads 16 bytes of K1 and K2 (key t/8,
 // chunk t%8) and a 4-key x 4-channel block of V (keys 4(t%8).., channels
 // 4(t/8)..).  kb1, kb2, vb point at key 0 of this (b, h).
+template <int kRope>
 __device__ __forceinline__ void stage_load(Staged& st, const PrefillArgs& a, const uint16_t* kb1,
                                            const uint16_t* kb2, const uint16_t* vb, const StageOffsets& off,
                                            int k0, int kend, int tid) {
   const int tile = __builtin_amdgcn_readfirstlane(tid / kTileThreads);
   const int kbase = k0 + tile * kBN;
-  st.k1 = __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc(kb1, a.sk1.t, kbase, kend, kDqk), off.k1, 0, 0);
-  st.k2 = __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc(kb2, a.sk2.t, kbase, kend, kDqk), off.k2, 0, 0);
+  st.kpos = a.rope.pos0 + (uint32_t)(kbase + ((tid % kTileThreads) >> 3));
+  st.k1 = load_krow(rows_rsrc(kb1, a.sk1.t, kbase, kend, kDqk), off.k1, kRope == 1);
+  st.k2 = load_krow(rows_rsrc(kb2, a.sk2.t, kbase, kend, kDqk), off.k2, kRope == 1);
   const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vb, a.sv.t, kbase, kend, kDv);
   const int vrow = (int)(a.sv.t * 2);
 #pragma unroll
   for (int r = 0; r < 4; ++r) st.v[r] = __builtin_amdgcn_raw_buffer_load_b64(rv, off.v, r * vrow, 0);
 }
 
-// Registers -> LDS: K rows with swizzled 16-byte chunks, V transposed to
-// [channel][key] in fp16 with the kVPos key order.
-__device__ __forceinline__ void stage_store(const Staged& st, char* stage, int tid) {
+// Split-half rotation of a staged key row piece: words 0-1 hold dims
+// 4j .. 4j+3 of K1 (K2), words 2-3 the pair partners 32 + 4j .., so pairs
+// c = 4j .. 4j+3 are complete in the thread.  Packs the result as fp16.
+__device__ __forceinline__ void rope_split_half(u32x4& k1, u32x4& k2, int j, uint32_t pos, const uint64_t* tab) {
+  float a[2][8];
+  rope_unpack(k1, a[0]);
+  rope_unpack(k2, a[1]);
+  const uint64_t* f = tab + 4 * j;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float c, sn;
+    rope_cos_sin(pos, f[e], c, sn);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float lo = a[k][e], hi = a[k][4 + e];
+      a[k][e] = lo * c - hi * sn;
+      a[k][4 + e] = lo * sn + hi * c;
+    }
+  }
+  k1 = rope_pack<true>(a[0]);
+  k2 = rope_pack<true>(a[1]);
+}
+
+// Registers -> LDS: K rows with swizzled 16-byte chunks (rotated first when
+// the rotary embedding is on), V transposed to [channel][key] in fp16 with the
+// kVPos key order.
+template <int kRope>
+__device__ __forceinline__ void stage_store(const Staged& st, char* stage, int tid, const uint64_t* rope_tab) {
   const int tile = tid / kTileThreads, t = tid % kTileThreads;
   char* base = stage + tile * kTile;
   const int kr = t >> 3, ch = t & 7;
-  const int koff = kr * kKRow + ((ch ^ kSwz(kr)) << 4);
-  *reinterpret_cast<u32x4*>(base + koff) = st.k1;
-  *reinterpret_cast<u32x4*>(base + kKBytes + koff) = st.k2;
+  if constexpr (kRope == 1) {
+    // dims 4ch .. 4ch+3 (words 0, 1) and their partners 32 + 4ch .. (words 2, 3)
+    u32x4 k1 = st.k1, k2 = st.k2;
+    rope_split_half(k1, k2, ch, st.kpos, rope_tab);
+    const int c0 = ch >> 1, half = (ch & 1) * 8, sw = kSwz(kr);
+    const int off_lo = kr * kKRow + ((c0 ^ sw) << 4) + half;
+    const int off_hi = kr * kKRow + (((c0 + 4) ^ sw) << 4) + half;
+    *reinterpret_cast<u32x2*>(base + off_lo) = u32x2{k1.x, k1.y};
+    *reinterpret_cast<u32x2*>(base + off_hi) = u32x2{k1.z, k1.w};
+    *reinterpret_cast<u32x2*>(base + kKBytes + off_lo) = u32x2{k2.x, k2.y};
+    *reinterpret_cast<u32x2*>(base + kKBytes + off_hi) = u32x2{k2.z, k2.w};
+  } else {
+    const int koff = kr * kKRow + ((ch ^ kSwz(kr)) << 4);
+    rope_u32x4 kk[2] = {st.k1, st.k2};
+    if constexpr (kRope == 2) rope_chunks<2, true>(kk, ch, st.kpos, kRope, rope_tab);
+    *reinterpret_cast<u32x4*>(base + koff) = kk[0];
+    *reinterpret_cast<u32x4*>(base + kKBytes + koff) = kk[1];
+  }
   const int kg = t & 7, cg = t >> 3;
   float e[4][4];
 #pragma unroll
@@ -155,6 +211,63 @@ __device__ __forceinline__ void stage_store(const Staged& st, char* stage, int t
   for (int c = 0; c < 4; ++c) {
     f16x4 h = {(_Float16)e[0][c], (_Float16)e[1][c], (_Float16)e[2][c], (_Float16)e[3][c]};
     *reinterpret_cast<f16x4*>(vt + (4 * cg + c) * kVRow) = h;
+  }
+}
+
+// Rotary embedding of the lane's query vectors, held as the score product's
+// operand: chunk s holds dims 16s + 8hf .. +7.  Split-half pairs (c, c + 32)
+// join chunks s and s + 2 of the same lane; interleaved pairs stay inside a
+// chunk.  Both maps' queries share the angles.  The rotated values are stored
+// as fp16 bits (the key tiles are rotated to fp16 as well, and the score
+// product then runs on fp16 operands: eight times finer than bf16, which keeps
+// the rounding of rotated operands well inside the error budget).
+__device__ __forceinline__ void rope_query(bf16x8 (&q1)[4], bf16x8 (&q2)[4], int hf, uint32_t pos, int mode,
+                                           const RopeArgs& r) {
+  float x1[4][8], x2[4][8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    rope_unpack(__builtin_bit_cast(rope_u32x4, q1[s]), x1[s]);
+    rope_unpack(__builtin_bit_cast(rope_u32x4, q2[s]), x2[s]);
+  }
+  if (mode == 1) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c0 = 16 * s + e;  // pair index in lane half 0; half 1 adds 8
+        const uint64_t f = hf ? r.phase[c0 + 8] : r.phase[c0];
+        float c, sn;
+        rope_cos_sin(pos, f, c, sn);
+        float a = x1[s][e], b = x1[s + 2][e];
+        x1[s][e] = a * c - b * sn;
+        x1[s + 2][e] = a * sn + b * c;
+        a = x2[s][e];
+        b = x2[s + 2][e];
+        x2[s][e] = a * c - b * sn;
+        x2[s + 2][e] = a * sn + b * c;
+      }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c0 = 8 * s + e;  // pair index in lane half 0; half 1 adds 4
+        const uint64_t f = hf ? r.phase[c0 + 4] : r.phase[c0];
+        float c, sn;
+        rope_cos_sin(pos, f, c, sn);
+        float a = x1[s][2 * e], b = x1[s][2 * e + 1];
+        x1[s][2 * e] = a * c - b * sn;
+        x1[s][2 * e + 1] = a * sn + b * c;
+        a = x2[s][2 * e];
+        b = x2[s][2 * e + 1];
+        x2[s][2 * e] = a * c - b * sn;
+        x2[s][2 * e + 1] = a * sn + b * c;
+      }
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    q1[s] = __builtin_bit_cast(bf16x8, rope_pack<true>(x1[s]));
+    q2[s] = __builtin_bit_cast(bf16x8, rope_pack<true>(x2[s]));
   }
 }
 
@@ -236,11 +349,14 @@ __device__ __forceinline__ void merge_map(char* smem, int grp, int wq, int lane,
 // kGroups wave groups of four waves share a workgroup's 128 queries and split
 // its key tiles.  Two waves per SIMD (<= 256 VGPRs each): one wave's softmax
 // VALU work overlaps the other's matrix products.
-template <int kGroups>
+// kRope: the rotary embedding mode (0 none, 1 split-half, 2 interleaved),
+// fixed at compile time so the plain kernel carries none of its registers.
+template <int kGroups, int kRope>
 __global__ void __launch_bounds__(64 * kGroupWaves * kGroups) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillArgs a) {
   constexpr int kStage = kGroups * kTile;  // one step: a tile for each group
   __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  __shared__ uint64_t rope_tab[32];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -285,6 +401,16 @@ prefill_kernel(PrefillArgs a) {
       qb2[s] = __builtin_bit_cast(bf16x8, x2);
     }
   }
+  if constexpr (kRope != 0) {
+    // Phase table for the key tiles, then the lane's own query in registers.
+    if (tid < 32) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if (c == tid) rope_tab[c] = a.rope.phase[c];
+    }
+    rope_query(qa, qb2, hf, a.rope.pos0 + (uint32_t)q, kRope, a.rope);
+    __syncthreads();
+  }
 
   f32x16 O1[4], O2[4];
 #pragma unroll
@@ -299,18 +425,18 @@ prefill_kernel(PrefillArgs a) {
   const uint16_t* kb1 = a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h;
   const uint16_t* kb2 = a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h;
   const uint16_t* vbase = a.v + (int64_t)b * a.sv.b + (int64_t)head * a.sv.h;
-  const StageOffsets soff = stage_offsets(a, tid);
+  const StageOffsets soff = stage_offsets<kRope>(a, tid);
 
   Staged st;
-  stage_load(st, a, kb1, kb2, vbase, soff, tile0 * kBN, kend, tid);
-  stage_store(st, smem, tid);
+  stage_load<kRope>(st, a, kb1, kb2, vbase, soff, tile0 * kBN, kend, tid);
+  stage_store<kRope>(st, smem, tid, rope_tab);
   __syncthreads();
 
   for (int it = 0; it < nsteps; ++it) {
     char* cur = smem + (it & 1) * kStage;
     char* nxt = smem + ((it + 1) & 1) * kStage;
     const bool more = it + 1 < nsteps;
-    if (more) stage_load(st, a, kb1, kb2, vbase, soff, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
+    if (more) stage_load<kRope>(st, a, kb1, kb2, vbase, soff, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
 
     const int j = tile0 + it * kGroups + grp;  // this group's tile
     if (wave_live && j >= wave_first_tile && j <= wave_last_tile) {
@@ -322,8 +448,16 @@ prefill_kernel(PrefillArgs a) {
         const int off = krow + (((2 * s + hf) ^ ksw) << 4);
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + off);
         const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kt + kKBytes + off);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qa[s], s1, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qb2[s], s2, 0, 0, 0);
+        if constexpr (kRope != 0) {
+          // rotated operands are fp16 (see rope_query)
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, ka),
+                                                      __builtin_bit_cast(f16x8, qa[s]), s1, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kb),
+                                                      __builtin_bit_cast(f16x8, qb2[s]), s2, 0, 0, 0);
+        } else {
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qa[s], s1, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qb2[s], s2, 0, 0, 0);
+        }
       }
       if (j == wave_last_tile) {
         // Diagonal tile (its first key is the wave's first query): key row
@@ -364,7 +498,7 @@ prefill_kernel(PrefillArgs a) {
       }
     }
 
-    if (more) stage_store(st, nxt, tid);
+    if (more) stage_store<kRope>(st, nxt, tid, rope_tab);
     __syncthreads();
   }
 
@@ -452,10 +586,17 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (grid <= 2 * (int64_t)cus)
-    hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)grid), dim3(64 * kGroupWaves * 2), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<1>, dim3((unsigned)grid), dim3(64 * kGroupWaves), 0, stream, a);
+  const bool split = grid <= 2 * (int64_t)cus;
+  const dim3 g((unsigned)grid), b1(64 * kGroupWaves), b2(64 * kGroupWaves * 2);
+  switch (a.rope.mode * 2 + (split ? 1 : 0)) {
+    case 0: hipLaunchKernelGGL((prefill_kernel<1, 0>), g, b1, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<2, 0>), g, b2, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<1, 1>), g, b1, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((prefill_kernel<2, 1>), g, b2, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<1, 2>), g, b1, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((prefill_kernel<2, 2>), g, b2, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

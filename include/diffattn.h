@@ -93,8 +93,22 @@ enum diffattn_rope {
  *                L.  A window larger than L is an error (the ring no longer
  *                holds those positions).  Zero: slot p holds position p and
  *                seqlens above L count as L.
- *   rope, rope_theta, rope_pos0 : reserved for the rotary prologue; rope must
- *                be DIFFATTN_ROPE_NONE in this version.
+ *   rope       : rotary position embedding applied to Q1, Q2, K1, K2 inside
+ *                the kernels before the score products (Motif 2.6B explainer,
+ *                section "The block": RoPE with base 500,000).  Each 64-wide
+ *                vector is rotated on its own: pair c turns by the angle
+ *                pos * rope_theta^(-c/32), pairing dims (c, c + 32) for
+ *                DIFFATTN_ROPE_HALF or (2c, 2c + 1) for
+ *                DIFFATTN_ROPE_INTERLEAVED, computed in fp32.  Prefill: token
+ *                t sits at position rope_pos0 + t; the rotated Q and K are
+ *                rounded to fp16 for the score products (eight times finer
+ *                than bf16), so their magnitudes must stay below 65504.
+ *                Decode: only the query is rotated (kept in fp32), at position
+ *                rope_pos0 + n - 1 for a sequence of n cached tokens (n as
+ *                counted after the clamp to L of a linear cache); the cache
+ *                must hold keys already rotated (diffattn_rope_apply).
+ *   rope_theta : base, finite and > 0 when rope is on.
+ *   rope_pos0  : >= 0; positions must stay below 2^32.
  *   reserved   : must be zero.
  */
 typedef struct {
@@ -163,9 +177,9 @@ DIFFATTN_API int diffattn_fwd_decode(const void* q1, const void* q2, const void*
                         void* stream);
 
 /* diffattn_fwd_prefill with variants (opt may be NULL: plain causal).  A
- * negative window, a nonzero kv_ring or reserved field, or an unknown rope mode
- * returns DIFFATTN_ERR_VALUE; a rope mode this version lacks returns
- * DIFFATTN_ERR_UNSUPPORTED. */
+ * negative window, a nonzero kv_ring or reserved field, an unknown rope mode,
+ * or with rope on a non-finite or non-positive rope_theta or a negative
+ * rope_pos0 returns DIFFATTN_ERR_VALUE. */
 DIFFATTN_API int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void* q1, const void* q2,
                                          const void* k1, const void* k2, const void* v,
                                          const diffattn_strides* strides, int B, int T, int H, int d_qk,
@@ -186,10 +200,26 @@ DIFFATTN_API int diffattn_fwd_decode_ex(const diffattn_options* opt, const void*
                                         size_t workspace_bytes, void* out, int out_dtype, float* o_pre,
                                         void* stream);
 
+/*
+ * Rotary embedding of a bf16 [B, T, H, 64] tensor, the same rotation the *_ex
+ * entry points apply (see diffattn_options.rope), for writing rotated keys
+ * into a decode cache.  Token t of batch row b sits at position
+ * pos0 + pos_start[b] + t (pos_start: device int32 [B], values >= 0, or NULL
+ * for 0).  out may be x itself (in place, same strides).  Strides and
+ * alignment as for the other entry points (NULL = C-contiguous).
+ *   mode  : DIFFATTN_ROPE_HALF or DIFFATTN_ROPE_INTERLEAVED
+ *   theta : finite, > 0;  pos0 >= 0
+ * Limits: B*T*H <= 2^34.
+ */
+DIFFATTN_API int diffattn_rope_apply(const void* x, const diffattn_strides* x_strides, void* out,
+                                     const diffattn_strides* out_strides, int B, int T, int H, int d, int mode,
+                                     float theta, int pos0, const int32_t* pos_start, void* stream);
+
 /* Static text for a status code (never NULL). */
 DIFFATTN_API const char* diffattn_status_string(int status);
 
-/* Library ABI version (major * 100 + minor): 101 adds the *_ex entry points. */
+/* Library ABI version (major * 100 + minor): 101 adds the *_ex entry points,
+ * 102 the rotary embedding (diffattn_options.rope, diffattn_rope_apply). */
 DIFFATTN_API int diffattn_abi_version(void);
 
 #ifdef __cplusplus

@@ -24,12 +24,12 @@ def _declared():
 def test_header_symbols_exported():
     names = _declared()
     assert set(names) == {"diffattn_fwd_prefill", "diffattn_fwd_decode", "diffattn_decode_workspace_bytes",
-                          "diffattn_fwd_prefill_ex", "diffattn_fwd_decode_ex",
+                          "diffattn_fwd_prefill_ex", "diffattn_fwd_decode_ex", "diffattn_rope_apply",
                           "diffattn_status_string", "diffattn_abi_version"}
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 101
+    assert da.diffattn_abi_version() == 102
 
 
 def test_status_strings():
@@ -109,7 +109,10 @@ def test_workspace_bytes():
 @pytest.mark.parametrize("opt,rc", [
     (dict(window=-1), EVALUE), (dict(rope=3), EVALUE), (dict(rope=-1), EVALUE),
     (dict(kv_ring=1), EVALUE), (dict(reserved=(0, 0, 1)), EVALUE),
+    (dict(rope=1), EVALUE), (dict(rope=2, rope_theta=-1.0), EVALUE), (dict(rope=1, rope_theta=float("inf")), EVALUE),
+    (dict(rope=1, rope_theta=float("nan")), EVALUE), (dict(rope=1, rope_theta=1e4, rope_pos0=-1), EVALUE),
     (dict(window=5), ESHAPE), (dict(window=1 << 30), ESHAPE), ("null", ESHAPE), (dict(), ESHAPE),
+    (dict(rope=1, rope_theta=5e5), ESHAPE), (dict(rope=2, rope_theta=1e4, rope_pos0=77, window=9), ESHAPE),
 ])
 def test_prefill_ex_options(opt, rc):
     assert (_prefill(opt=opt, T=0) if rc == ESHAPE else _prefill(opt=opt)) == rc
@@ -118,7 +121,9 @@ def test_prefill_ex_options(opt, rc):
 @pytest.mark.parametrize("opt,rc", [
     (dict(window=-7), EVALUE), (dict(rope=9), EVALUE), (dict(reserved=(2, 0, 0)), EVALUE),
     (dict(kv_ring=1, window=101), EVALUE),
+    (dict(rope=1, rope_theta=0.0), EVALUE),
     (dict(window=3), ESHAPE), (dict(kv_ring=1), ESHAPE), (dict(kv_ring=1, window=100), ESHAPE), ("null", ESHAPE),
+    (dict(rope=1, rope_theta=5e5, kv_ring=1), ESHAPE),
 ])
 def test_decode_ex_options(opt, rc):
     assert (_decode(opt=opt, L=0) if rc == ESHAPE else _decode(opt=opt)) == rc
@@ -133,3 +138,24 @@ def test_options_layout():
     body = txt[txt.index("typedef struct {\n    int32_t window;"):txt.index("} diffattn_options;")]
     assert re.findall(r"(\w+)(?:\[\d\])?;", body) == ["window", "kv_ring", "rope", "rope_pos0", "rope_theta",
                                                        "reserved"]
+
+
+def _rope_apply(**kw):
+    args = dict(x=A, sx=None, out=A, so=None, B=2, T=5, H=3, d=64, mode=1, theta=5e5, pos0=0, ps=None, stream=None)
+    args.update(kw)
+    return da._lib.diffattn_rope_apply(*args.values())
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(x=None), ENULL), (dict(out=None), ENULL), (dict(B=0), ESHAPE), (dict(T=-1), ESHAPE),
+    (dict(B=1 << 12, T=1 << 12, H=1 << 11), ESHAPE), (dict(d=128), EUNSUP), (dict(mode=0), EVALUE),
+    (dict(mode=3), EVALUE), (dict(theta=0.0), EVALUE), (dict(theta=float("nan")), EVALUE), (dict(pos0=-5), EVALUE),
+    (dict(x=A + 2), ELAYOUT), (dict(out=A + 8), ELAYOUT),
+])
+def test_rope_apply_rejects(kw, rc):
+    assert _rope_apply(**kw) == rc
+
+
+def test_rope_apply_rejects_bad_strides():
+    assert _rope_apply(sx=ctypes.byref(da._Strides(960, 192, 60))) == ELAYOUT
+    assert _rope_apply(so=ctypes.byref(da._Strides(960, -64, 64))) == ELAYOUT
