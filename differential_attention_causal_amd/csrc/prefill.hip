@@ -109,16 +109,38 @@ struct StageOffsets {
 // K columns a thread stages: 16 bytes (dims 8ch .. 8ch+7), or with the
 // split-half rotary embedding 8 + 8 bytes (dims 4ch .. 4ch+3 and their pair
 // partners 32 + 4ch ..), so that every rotation pair stays in one thread.
+// Without the rotary embedding, key tiles go from memory straight to LDS
+// (buffer loads with an LDS destination: lane i of a wave writes the 16 bytes
+// at its wave's base + 16 i), so thread t fetches the chunk that belongs at
+// chunk position t of the swizzled tile: key t/8, logical chunk
+// (t % 8) ^ kSwz(t / 8).
 template <int kRope>
 __device__ __forceinline__ StageOffsets stage_offsets(const PrefillArgs& a, int tid) {
   const int t = tid % kTileThreads;
   const int kr = t >> 3, ch = t & 7, kg = t & 7, cg = t >> 3;
-  const int col = kRope == 1 ? 4 * ch : 8 * ch;
+  const int col = kRope == 1 ? 4 * ch : kRope == 2 ? 8 * ch : 8 * (ch ^ kSwz(kr));
   StageOffsets o;
   o.k1 = (uint32_t)((kr * a.sk1.t + col) * 2);
   o.k2 = (uint32_t)((kr * a.sk2.t + col) * 2);
   o.v = (uint32_t)((4 * kg * a.sv.t + 4 * cg) * 2);
   return o;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Memory -> LDS for the key tiles of one step (no registers involved): each
+// wave moves 64 chunks of K1 and of K2 into its quarter of its group's tile.
+// Completion is counted by vmcnt; the step's barrier follows a wait for it.
+__device__ __forceinline__ void stage_dma_k(const PrefillArgs& a, const uint16_t* kb1, const uint16_t* kb2,
+                                            const StageOffsets& off, char* stage, int k0, int kend, int tid) {
+  const int tile = __builtin_amdgcn_readfirstlane(tid / kTileThreads);
+  const int part = __builtin_amdgcn_readfirstlane((tid % kTileThreads) >> 6);  // wave within the tile's group
+  const int kbase = k0 + tile * kBN;
+  char* dst = stage + tile * kTile + part * 1024;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(kb1, a.sk1.t, kbase, kend, kDqk), (lds_ptr_t)dst, 16, off.k1,
+                                           0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(kb2, a.sk2.t, kbase, kend, kDqk), (lds_ptr_t)(dst + kKBytes),
+                                           16, off.k2, 0, 0, 0);
 }
 
 __device__ __forceinline__ u32x4 load_krow(__amdgpu_buffer_rsrc_t r, uint32_t off, bool split) {
@@ -139,14 +161,20 @@ __device__ __forceinline__ void stage_load(Staged& st, const PrefillArgs& a, con
                                            int k0, int kend, int tid) {
   const int tile = __builtin_amdgcn_readfirstlane(tid / kTileThreads);
   const int kbase = k0 + tile * kBN;
-  st.kpos = a.rope.pos0 + (uint32_t)(kbase + ((tid % kTileThreads) >> 3));
-  st.k1 = load_krow(rows_rsrc(kb1, a.sk1.t, kbase, kend, kDqk), off.k1, kRope == 1);
-  st.k2 = load_krow(rows_rsrc(kb2, a.sk2.t, kbase, kend, kDqk), off.k2, kRope == 1);
+  if constexpr (kRope != 0) {
+    st.kpos = a.rope.pos0 + (uint32_t)(kbase + ((tid % kTileThreads) >> 3));
+    st.k1 = load_krow(rows_rsrc(kb1, a.sk1.t, kbase, kend, kDqk), off.k1, kRope == 1);
+    st.k2 = load_krow(rows_rsrc(kb2, a.sk2.t, kbase, kend, kDqk), off.k2, kRope == 1);
+  }
   const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vb, a.sv.t, kbase, kend, kDv);
   const int vrow = (int)(a.sv.t * 2);
 #pragma unroll
   for (int r = 0; r < 4; ++r) st.v[r] = __builtin_amdgcn_raw_buffer_load_b64(rv, off.v, r * vrow, 0);
 }
+
+// Waits for this wave's outstanding memory loads, the LDS-destination ones
+// included (vmcnt 0; export and LDS counters left alone).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Split-half rotation of a staged key row piece: words 0-1 hold dims
 // 4j .. 4j+3 of K1 (K2), words 2-3 the pair partners 32 + 4j .., so pairs
@@ -190,13 +218,13 @@ __device__ __forceinline__ void stage_store(const Staged& st, char* stage, int t
     *reinterpret_cast<u32x2*>(base + off_hi) = u32x2{k1.z, k1.w};
     *reinterpret_cast<u32x2*>(base + kKBytes + off_lo) = u32x2{k2.x, k2.y};
     *reinterpret_cast<u32x2*>(base + kKBytes + off_hi) = u32x2{k2.z, k2.w};
-  } else {
+  } else if constexpr (kRope == 2) {
     const int koff = kr * kKRow + ((ch ^ kSwz(kr)) << 4);
     rope_u32x4 kk[2] = {st.k1, st.k2};
-    if constexpr (kRope == 2) rope_chunks<2, true>(kk, ch, st.kpos, kRope, rope_tab);
+    rope_chunks<2, true>(kk, ch, st.kpos, kRope, rope_tab);
     *reinterpret_cast<u32x4*>(base + koff) = kk[0];
     *reinterpret_cast<u32x4*>(base + kKBytes + koff) = kk[1];
-  }
+  }  // without the rotary embedding the key tile came by DMA
   const int kg = t & 7, cg = t >> 3;
   float e[4][4];
 #pragma unroll
@@ -428,15 +456,20 @@ prefill_kernel(PrefillArgs a) {
   const StageOffsets soff = stage_offsets<kRope>(a, tid);
 
   Staged st;
+  if constexpr (kRope == 0) stage_dma_k(a, kb1, kb2, soff, smem, tile0 * kBN, kend, tid);
   stage_load<kRope>(st, a, kb1, kb2, vbase, soff, tile0 * kBN, kend, tid);
   stage_store<kRope>(st, smem, tid, rope_tab);
+  if constexpr (kRope == 0) wait_dma();
   __syncthreads();
 
   for (int it = 0; it < nsteps; ++it) {
     char* cur = smem + (it & 1) * kStage;
     char* nxt = smem + ((it + 1) & 1) * kStage;
     const bool more = it + 1 < nsteps;
-    if (more) stage_load<kRope>(st, a, kb1, kb2, vbase, soff, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
+    if (more) {
+      if constexpr (kRope == 0) stage_dma_k(a, kb1, kb2, soff, nxt, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
+      stage_load<kRope>(st, a, kb1, kb2, vbase, soff, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
+    }
 
     const int j = tile0 + it * kGroups + grp;  // this group's tile
     if (wave_live && j >= wave_first_tile && j <= wave_last_tile) {
@@ -499,6 +532,7 @@ prefill_kernel(PrefillArgs a) {
     }
 
     if (more) stage_store<kRope>(st, nxt, tid, rope_tab);
+    if constexpr (kRope == 0) wait_dma();
     __syncthreads();
   }
 
