@@ -41,9 +41,9 @@ SWA_DECODE_WL = "swa_decode_b64_l4096_h16_w128"
 ROPE_THETA = 500000.0        # Motif 2.6B's RoPE base
 CSRC = os.path.join(ROOT, "differential_attention_causal_amd", "csrc")
 PREFILL_PMC = os.path.join(ROOT, "profiles", "prefill_kernel_b1_t4096_h16_hbm_counters.txt")
-PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("prefill.hip", "kernels.h")]
+PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("prefill.hip", "kernels.h", "rope.h")]
 DECODE_PMC = os.path.join(ROOT, "profiles", "decode_split_kernel_b64_l4096_h16_hbm_counters.txt")
-DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode.hip", "kernels.h")]
+DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode.hip", "kernels.h", "rope.h")]
 
 
 def kernel_source_digest(sources=PREFILL_SOURCES) -> str:
@@ -196,6 +196,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the sliding-window and RoPE timings")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -264,7 +265,7 @@ def main() -> int:
     step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
     assert bool(torch.isfinite(p_out.float()).all()) and bool(torch.isfinite(d_out.float()).all())
 
-    var = variants(da, torch, np, to_dev, f32_dev, dev)
+    var = None if args.no_variants else variants(da, torch, np, to_dev, f32_dev, dev)
 
     p_flop = pw.causal_pairs * FLOP_PER_PAIR
     p_s = float(p_ms.mean()) / 1e3

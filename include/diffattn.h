@@ -66,7 +66,7 @@ enum diffattn_status {
     DIFFATTN_ERR_LAYOUT = 4,      /* misaligned pointer or stride */
     DIFFATTN_ERR_WORKSPACE = 5,   /* decode workspace missing or too small */
     DIFFATTN_ERR_HIP = 6,         /* the HIP runtime refused a launch */
-    DIFFATTN_ERR_VALUE = 7        /* non-finite lambda/eps/scale, eps < 0, bad dtype or split count */
+    DIFFATTN_ERR_VALUE = 7        /* non-finite lambda/eps/scale, eps < 0, bad dtype, split count or option */
 };
 
 enum diffattn_out_dtype { DIFFATTN_OUT_BF16 = 0, DIFFATTN_OUT_F32 = 1 };
