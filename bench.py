@@ -34,6 +34,9 @@ sys.path.insert(0, ROOT)
 MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FLOP_PER_PAIR = 768
+# Backward: recomputed scores (2 x 128) + dP (256, shared by the maps since
+# dO_2 = -lambda dO_1) + dV (256) + dQ (2 x 128) + dK (2 x 128) per pair.
+BWD_FLOP_PER_PAIR = 1280
 PREFILL_WL = "prefill_b1_t4096_h16"
 DECODE_WL = "decode_b64_l4096_h16"
 SWA_PREFILL_WL = "swa_b1_t16384_h16_w128"
@@ -130,8 +133,8 @@ def _time_calls(torch, np, fn, warmup: int, iters: int):
 def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     """The variant rows, timed after, and outside, the step's timed region:
     Motif 3's sliding-window layer type (128-token windows) as the windowed
-    prefill at T=16384 and the windowed decode over the 4096-long caches, and
-    the T=4096 prefill with the fused RoPE prologue."""
+    prefill at T=16384 and the windowed decode over the 4096-long caches, the
+    T=4096 prefill with the fused RoPE prologue, and the T=4096 backward."""
     import synth
 
     pw = synth.WORKLOADS[SWA_PREFILL_WL]
@@ -166,15 +169,37 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     rg = f32_dev(xr["gain"], dev)
     r_out = torch.empty((rw.B, rw.T, rw.H, rw.d_v), dtype=torch.bfloat16, device=dev)
 
+    # backward of the T=4096 layer: training forward once, then the timed
+    # backward (dy ~ N(0,1) bf16, seeded like the inputs)
+    bx = synth.make_prefill_inputs(rw)
+    B_ = {n: to_dev(bx[n], dev) for n in ("q1", "q2", "k1", "k2", "v")}
+    bgain = f32_dev(bx["gain"], dev)
+    _, bo1, bo2, blse = da.diffattn_fwd_prefill_train(B_["q1"], B_["q2"], B_["k1"], B_["k2"], B_["v"], rw.lam, bgain,
+                                                      eps=rw.eps, scale=rw.scale)
+    bdy = to_dev(synth.normal_bf16(rw.seed, 9, (rw.B, rw.T, rw.H, rw.d_v)), dev)
+    bws = torch.empty(da.diffattn_bwd_workspace_bytes(rw.B, rw.T, rw.H, rw.d_v), dtype=torch.uint8, device=dev)
+    bgr = da.diffattn_bwd_prefill(B_["q1"], B_["q2"], B_["k1"], B_["k2"], B_["v"], rw.lam, bgain, bo1, bo2, blse, bdy,
+                                  eps=rw.eps, scale=rw.scale, workspace=bws)
+
+    def backward():
+        da.diffattn_bwd_prefill(B_["q1"], B_["q2"], B_["k1"], B_["k2"], B_["v"], rw.lam, bgain, bo1, bo2, blse, bdy,
+                                eps=rw.eps, scale=rw.scale, workspace=bws, grads=bgr)
+
     p_us, p_min = _time_calls(torch, np, prefill, warmup, iters)
     d_us, d_min = _time_calls(torch, np, decode, warmup, iters)
     r_us, r_min = _time_calls(torch, np, prefill_rope, warmup, iters)
+    bw_us, bw_min = _time_calls(torch, np, backward, warmup // 3, iters)
+    assert all(bool(torch.isfinite(t).all()) for t in bgr.values())
+    bw_flop = rw.causal_pairs * BWD_FLOP_PER_PAIR
     assert bool(torch.isfinite(r_out.float()).all())
     r_flop = rw.causal_pairs * FLOP_PER_PAIR
     assert bool(torch.isfinite(p_out.float()).all()) and bool(torch.isfinite(d_out.float()).all())
     p_flop = pw.causal_pairs * FLOP_PER_PAIR
     d_bytes = decode_bytes(dw)
     return {
+        "backward": {"workload": PREFILL_WL, "us_mean": round(bw_us, 2), "us_min": round(bw_min, 2),
+                     "flop_per_pair": BWD_FLOP_PER_PAIR, "tflops": round(bw_flop / bw_us / 1e6, 2),
+                     "frac_mfma_peak": round(bw_flop / bw_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},
         "rope_prefill": {"workload": PREFILL_WL, "rope": "split-half", "theta": ROPE_THETA,
                          "us_mean": round(r_us, 2), "us_min": round(r_min, 2),
                          "tflops": round(r_flop / r_us / 1e6, 2),

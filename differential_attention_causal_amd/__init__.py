@@ -23,6 +23,9 @@ __all__ = [
     "diffattn_fwd_decode",
     "diffattn_fwd_decode_ex",
     "diffattn_rope_apply",
+    "diffattn_fwd_prefill_train",
+    "diffattn_bwd_workspace_bytes",
+    "diffattn_bwd_prefill",
     "diffattn_decode_workspace_bytes",
     "diffattn_status_string",
     "diffattn_abi_version",
@@ -75,6 +78,14 @@ _lib.diffattn_fwd_decode_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffatt
 _lib.diffattn_rope_apply.restype = _I
 _lib.diffattn_rope_apply.argtypes = [_P, ctypes.POINTER(_Strides), _P, ctypes.POINTER(_Strides), _I, _I, _I, _I,
                                      _I, ctypes.c_float, _I, _P, _P]
+_lib.diffattn_fwd_prefill_train.restype = _I
+_lib.diffattn_fwd_prefill_train.argtypes = _lib.diffattn_fwd_prefill.argtypes[:-1] + [_P, _P, _P, _P]
+_lib.diffattn_bwd_workspace_bytes.restype = ctypes.c_size_t
+_lib.diffattn_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
+_lib.diffattn_bwd_prefill.restype = _I
+_lib.diffattn_bwd_prefill.argtypes = ([_P, _P, _P, _P, _P, ctypes.POINTER(_Strides), _I, _I, _I, _I, _I, ctypes.c_float,
+                                      _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P, _I]
+                                     + [_P] * 7 + [_P, ctypes.c_size_t, _P])
 _lib.diffattn_status_string.restype = ctypes.c_char_p
 _lib.diffattn_status_string.argtypes = [_I]
 _lib.diffattn_abi_version.restype = _I
@@ -145,7 +156,7 @@ def diffattn_fwd_prefill_ex(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, o
     return _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream)
 
 
-def _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream):
+def _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream, train=None):
     """Causal differential-attention prefill.
 
     q1, q2, k1, k2: bf16 [B, T, H, 64]; v: bf16 [B, T, H, 128] (any strides with
@@ -177,7 +188,12 @@ def _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pr
     st = (_Strides * 5)(*[_strides4(t) for t in (q1, q2, k1, k2, v)])
     args = (_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, B, T, H, d_qk, d_v, lam_v, _ptr(lam_t),
             _ptr(gain), float(eps), float(scale), _ptr(out), _out_code(out.dtype), _ptr(o_pre), _stream(stream))
-    rc = _lib.diffattn_fwd_prefill(*args) if opt is None else _lib.diffattn_fwd_prefill_ex(ctypes.byref(opt), *args)
+    if train is not None:
+        rc = _lib.diffattn_fwd_prefill_train(*args[:-1], *(_ptr(t) for t in train), args[-1])
+    elif opt is None:
+        rc = _lib.diffattn_fwd_prefill(*args)
+    else:
+        rc = _lib.diffattn_fwd_prefill_ex(ctypes.byref(opt), *args)
     _check(rc)
     return out
 
@@ -266,6 +282,64 @@ def diffattn_rope_apply(x, mode, theta, pos0=0, pos_start=None, out=None, stream
                                   float(theta), int(pos0), _ptr(pos_start), _stream(stream))
     _check(rc)
     return out
+
+
+def diffattn_fwd_prefill_train(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, out=None,
+                               out_dtype=torch.bfloat16, o_pre=None, stream=None):
+    """Causal prefill that also returns what diffattn_bwd_prefill needs:
+    (out, o1, o2, lse) with o1, o2 fp32 [B, T, H, 128] (each map's normalised
+    output) and lse fp32 [B, T, H, 2] (base-2 log-sum-exp per map)."""
+    B, T, H, _ = q1.shape
+    o1 = torch.empty((B, T, H, D_V), dtype=torch.float32, device=q1.device)
+    o2 = torch.empty_like(o1)
+    lse = torch.empty((B, T, H, 2), dtype=torch.float32, device=q1.device)
+    out = _prefill(None, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream,
+                   train=(o1, o2, lse))
+    return out, o1, o2, lse
+
+
+def diffattn_bwd_workspace_bytes(B: int, T: int, H: int, d_v: int = D_V) -> int:
+    return int(_lib.diffattn_bwd_workspace_bytes(B, T, H, d_v))
+
+
+def diffattn_bwd_prefill(q1, q2, k1, k2, v, lam, gain, o1, o2, lse, dy, eps=1e-5, scale=0.0, workspace=None,
+                         grads=None, stream=None):
+    """Gradients of sum(y * dy) for the causal prefill.  dy: bf16 or fp32
+    [B, T, H, 128], contiguous.  o1, o2, lse: diffattn_fwd_prefill_train's
+    outputs.  Returns a dict of fp32 tensors dq1, dq2, dk1, dk2 ([B, T, H, 64]),
+    dv ([B, T, H, 128]), dlam ([H], per head) and dgain ([H, 128]); pass
+    `grads` (such a dict) to write into preallocated tensors."""
+    B, T, H, d_qk = q1.shape
+    d_v = v.shape[3]
+    for t in (q1, q2, k1, k2, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError("q1, q2, k1, k2, v must be bf16 device tensors")
+    if dy.dtype not in (torch.bfloat16, torch.float32) or tuple(dy.shape) != (B, T, H, d_v) or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous bf16 or fp32 [B, T, H, d_v] tensor")
+    for t, shp in ((o1, (B, T, H, d_v)), (o2, (B, T, H, d_v)), (lse, (B, T, H, 2))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError("o1, o2, lse must be diffattn_fwd_prefill_train's outputs")
+    if gain.dtype != torch.float32 or tuple(gain.shape) != (H, d_v) or not gain.is_contiguous():
+        raise ValueError("gain must be a contiguous fp32 [H, d_v] tensor")
+    if grads is None:
+        f = dict(dtype=torch.float32, device=q1.device)
+        grads = {"dq1": torch.empty((B, T, H, d_qk), **f), "dq2": torch.empty((B, T, H, d_qk), **f),
+                 "dk1": torch.empty((B, T, H, d_qk), **f), "dk2": torch.empty((B, T, H, d_qk), **f),
+                 "dv": torch.empty((B, T, H, d_v), **f), "dlam": torch.empty((H,), **f),
+                 "dgain": torch.empty((H, d_v), **f)}
+    need = diffattn_bwd_workspace_bytes(B, T, H, d_v)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q1.device)
+    lam_v, lam_t = _lambda_args(lam, H, q1.device)
+    st = (_Strides * 5)(*[_strides4(t) for t in (q1, q2, k1, k2, v)])
+    g = grads
+    rc = _lib.diffattn_bwd_prefill(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, B, T, H, d_qk, d_v, lam_v,
+                                   _ptr(lam_t), _ptr(gain), float(eps), float(scale), _ptr(o1), _ptr(o2), _ptr(lse),
+                                   _ptr(dy), _out_code(dy.dtype), _ptr(g["dq1"]), _ptr(g["dq2"]), _ptr(g["dk1"]),
+                                   _ptr(g["dk2"]), _ptr(g["dv"]), _ptr(g["dlam"]), _ptr(g["dgain"]),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+    return grads
 
 
 def default_scale(d_qk: int = D_QK) -> float:

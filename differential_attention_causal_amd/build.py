@@ -26,7 +26,7 @@ COMMON = [
     # with VALU ops, and AGPR accumulators cost a copy each way per key tile
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
-SOURCES = ["prefill.hip", "decode.hip", "rope.hip", "api.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "rope.hip", "backward.hip", "api.cpp"]
 
 
 def _compile(src: str) -> str:

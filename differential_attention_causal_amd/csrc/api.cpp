@@ -74,7 +74,7 @@ float score_factor(float scale) {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 102; }
+int diffattn_abi_version(void) { return 103; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -91,10 +91,14 @@ const char* diffattn_status_string(int status) {
   }
 }
 
-int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,
-                            const void* k2, const void* v, const diffattn_strides* strides, int B, int T, int H,
-                            int d_qk, int d_v, float lambda, const float* lambda_per_head, const float* gain,
-                            float gn_eps, float scale, void* out, int out_dtype, float* o_pre, void* stream) {
+namespace {
+
+// Shared by diffattn_fwd_prefill_ex and diffattn_fwd_prefill_train; `train`
+// holds the three training outputs or nulls.
+int prefill_impl(const diffattn_options* opt, const void* q1, const void* q2, const void* k1, const void* k2,
+                 const void* v, const diffattn_strides* strides, int B, int T, int H, int d_qk, int d_v,
+                 float lambda, const float* lambda_per_head, const float* gain, float gn_eps, float scale, void* out,
+                 int out_dtype, float* o_pre, float* const train[3], void* stream) {
   if (!q1 || !q2 || !k1 || !k2 || !v || !gain || !out) return DIFFATTN_ERR_NULL;
   int rc = check_common(B, H, d_qk, d_v, lambda, gn_eps, scale, out_dtype);
   if (rc != DIFFATTN_OK) return rc;
@@ -139,7 +143,130 @@ int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void* q1, const v
   a.out = out;
   a.out_f32 = out_dtype == DIFFATTN_OUT_F32;
   a.o_pre = o_pre;
+  if (train) {
+    a.o1n = train[0];
+    a.o2n = train[1];
+    a.lse = train[2];
+  }
   if (diffattn::launch_prefill(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
+  return DIFFATTN_OK;
+}
+
+}  // namespace
+
+int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,
+                            const void* k2, const void* v, const diffattn_strides* strides, int B, int T, int H,
+                            int d_qk, int d_v, float lambda, const float* lambda_per_head, const float* gain,
+                            float gn_eps, float scale, void* out, int out_dtype, float* o_pre, void* stream) {
+  return prefill_impl(opt, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head, gain, gn_eps,
+                      scale, out, out_dtype, o_pre, nullptr, stream);
+}
+
+int diffattn_fwd_prefill_train(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
+                               const diffattn_strides* strides, int B, int T, int H, int d_qk, int d_v,
+                               float lambda, const float* lambda_per_head, const float* gain, float gn_eps,
+                               float scale, void* out, int out_dtype, float* o_pre, float* o1, float* o2,
+                               float* lse, void* stream) {
+  if (!o1 || !o2 || !lse) return DIFFATTN_ERR_NULL;
+  if (!aligned16(o1) || !aligned16(o2) || !aligned16(lse)) return DIFFATTN_ERR_LAYOUT;
+  float* const train[3] = {o1, o2, lse};
+  return prefill_impl(nullptr, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head, gain,
+                      gn_eps, scale, out, out_dtype, o_pre, train, stream);
+}
+
+namespace {
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+struct BwdLayout {
+  size_t dO, dstat, partial, total;
+  int nchunks;
+};
+
+// Workspace of the backward pass: dO fp16 [B,T,H,d_v], D fp32 [B,T,H,2],
+// gain/lambda partials fp32 [H, nchunks, d_v + 1].
+BwdLayout bwd_layout(int B, int T, int H) {
+  BwdLayout l;
+  const size_t rows = (size_t)B * T * H;
+  l.nchunks = (int)(((int64_t)B * T + diffattn::kBwdRowsPerChunk - 1) / diffattn::kBwdRowsPerChunk);
+  l.dO = 0;
+  l.dstat = align256(rows * kDv * 2);
+  l.partial = l.dstat + align256(rows * 2 * sizeof(float));
+  l.total = l.partial + align256((size_t)H * l.nchunks * (kDv + 1) * sizeof(float));
+  return l;
+}
+
+}  // namespace
+
+size_t diffattn_bwd_workspace_bytes(int B, int T, int H, int d_v) {
+  if (B <= 0 || T <= 0 || H <= 0 || d_v != kDv || T > (1 << 22)) return 0;
+  if ((int64_t)B * H > (int64_t(1) << 24) || (int64_t)((T + 127) / 128) * B * H > kMaxWorkgroups) return 0;
+  return bwd_layout(B, T, H).total;
+}
+
+int diffattn_bwd_prefill(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
+                         const diffattn_strides* strides, int B, int T, int H, int d_qk, int d_v, float lambda,
+                         const float* lambda_per_head, const float* gain, float gn_eps, float scale, const float* o1,
+                         const float* o2, const float* lse, const void* dy, int dy_dtype, float* dq1, float* dq2,
+                         float* dk1, float* dk2, float* dv, float* dlambda, float* dgain, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!q1 || !q2 || !k1 || !k2 || !v || !gain || !o1 || !o2 || !lse || !dy || !dq1 || !dq2 || !dk1 || !dk2 ||
+      !dv || !dlambda || !dgain)
+    return DIFFATTN_ERR_NULL;
+  int rc = check_common(B, H, d_qk, d_v, lambda, gn_eps, scale, dy_dtype);
+  if (rc != DIFFATTN_OK) return rc;
+  if (T <= 0 || T > (1 << 22)) return DIFFATTN_ERR_SHAPE;
+  if ((int64_t)((T + 127) / 128) * B * H > kMaxWorkgroups) return DIFFATTN_ERR_SHAPE;
+  const void* ptrs[] = {q1, q2, k1, k2, v, gain, o1, o2, lse, dy, dq1, dq2, dk1, dk2, dv, dgain};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return DIFFATTN_ERR_LAYOUT;
+  diffattn_strides st[5];
+  for (int i = 0; i < 5; ++i) {
+    st[i] = strides ? strides[i] : contiguous(T, H, i == 4 ? d_v : d_qk);
+    if (!strides_ok(st[i])) return DIFFATTN_ERR_LAYOUT;
+  }
+  const BwdLayout lay = bwd_layout(B, T, H);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DIFFATTN_ERR_WORKSPACE;
+  if (workspace_bytes < lay.total) return DIFFATTN_ERR_WORKSPACE;
+
+  diffattn::BackwardArgs a{};
+  a.q1 = static_cast<const uint16_t*>(q1);
+  a.q2 = static_cast<const uint16_t*>(q2);
+  a.k1 = static_cast<const uint16_t*>(k1);
+  a.k2 = static_cast<const uint16_t*>(k2);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sq1 = to_internal(st[0]);
+  a.sq2 = to_internal(st[1]);
+  a.sk1 = to_internal(st[2]);
+  a.sk2 = to_internal(st[3]);
+  a.sv = to_internal(st[4]);
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.c = score_factor(scale);
+  a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)kDqk);
+  a.lambda = lambda;
+  a.lambda_h = lambda_per_head;
+  a.gain = gain;
+  a.eps = gn_eps;
+  a.o1n = o1;
+  a.o2n = o2;
+  a.lse = lse;
+  a.dy = dy;
+  a.dy_f32 = dy_dtype == DIFFATTN_OUT_F32;
+  a.dq1 = dq1;
+  a.dq2 = dq2;
+  a.dk1 = dk1;
+  a.dk2 = dk2;
+  a.dv = dv;
+  a.dlam = dlambda;
+  a.dgain = dgain;
+  char* ws = static_cast<char*>(workspace);
+  a.dO = reinterpret_cast<uint16_t*>(ws + lay.dO);
+  a.dstat = reinterpret_cast<float*>(ws + lay.dstat);
+  a.partial = reinterpret_cast<float*>(ws + lay.partial);
+  a.nchunks = lay.nchunks;
+  if (diffattn::launch_backward(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
   return DIFFATTN_OK;
 }
 

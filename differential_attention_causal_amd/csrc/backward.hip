@@ -1,0 +1,663 @@
+// Backward pass of causal differential attention for gfx950 (MI355X).
+//
+// Forward (Motif 2.6B explainer, "Differential attention" and the figure 1
+// caption): P_m = softmax(scale * Q_m K_m^T) causally, O_m = P_m V,
+// o = O_1 - lambda O_2, y = GroupNorm(o) * gain.  Given dy, the calculus of
+// that definition is, per (b, h):
+//   GroupNorm:  x = (o - mu) / sigma, dgain += dy x,
+//               do = (g - mean(g) - x mean(g x)) / sigma  with g = dy gain
+//   combine:    dO_1 = do, dO_2 = -lambda do, dlambda += -sum(do O_2)
+//   each map:   dP_m = dO_m V^T, dS_m = P_m (dP_m - D_m), D_m = rowsum(dO_m O_m)
+//               dQ_m = scale dS_m K_m, dK_m = scale dS_m^T Q_m
+//   values:     dV = P_1^T dO_1 + P_2^T dO_2 = (P_1 - lambda P_2)^T do
+// Since both maps share V and dO_2 = -lambda dO_1, dP_2 = -lambda dP_1: one
+// product serves both maps.
+//
+// Kernels (all deterministic, no atomics):
+//   bwd_pre_kernel     per row: do (fp16), D_1, D_2; gain/lambda partials
+//   bwd_reduce_kernel  per head: sum of the partials
+//   bwd_dq_kernel      queries own lanes (the forward's orientation): recompute
+//                      S^T, P^T from the saved log-sum-exp, dP^T = V dO^T,
+//                      dQ^T += K^T dS^T
+//   bwd_dk_kernel      keys own lanes: S = Q K^T, dP = dO V^T, dK^T += Q^T dS
+//   bwd_dv_kernel      keys own lanes: S = Q K^T, dV^T += dO^T (P_1 - lambda P_2)
+// The last three use v_mfma_f32_32x32x16 like the prefill: a 32x32 accumulator
+// held by a wave is used directly as the next product's operand, with the
+// transposed LDS tiles stored in the matching (kVPos) order.  Scores are bf16
+// products of the exact inputs; dO, P, dS, V^T, K^T and Q^T enter the other
+// products as fp16 (inputs converted exactly, |x| in [2^-14, 65504)).
+#include "kernels.h"
+#include "tile.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRows = 32 * kWaves;      // queries (dQ) or keys (dK, dV) per workgroup
+constexpr int kKRow = kDqk * 2;         // 128-byte bf16 rows of Q or K
+constexpr int kQKTile = 32 * kKRow;     // 4 KiB: one map's 32-row bf16 tile
+constexpr int kD16Row = kDv * 2;        // 256-byte fp16 rows of dO or V
+constexpr int kD16Tile = 32 * kD16Row;  // 8 KiB
+constexpr int kTRow = (32 + 8) * 2;     // 80-byte transposed fp16 rows (16-byte pad)
+constexpr int kQKT = kDqk * kTRow;      // 5 KiB: one map's transposed 64 x 32 tile
+constexpr int kDT = kDv * kTRow;        // 10 KiB: transposed 128 x 32 tile
+
+// 16-byte chunk swizzle of 256-byte rows (16 chunks): rows r and r ^ 16 share
+// it, so a 16-byte read by 32 lanes of consecutive rows is at most 2-way
+// conflicted.
+__device__ __forceinline__ int swz16(int r) { return r & 15; }
+
+__device__ __forceinline__ f32x2 load_dy(const BackwardArgs& a, int64_t off) {
+  if (a.dy_f32) return *reinterpret_cast<const f32x2*>(static_cast<const float*>(a.dy) + off);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.dy) + off);
+  return f32x2{bf16_lo(w), bf16_hi(w)};
+}
+
+// ---------------------------------------------------------------------------
+// Per row: the GroupNorm backward, do, D_1 = rowsum(do O_1),
+// D_2 = rowsum(-lambda do O_2), and partial sums of dgain and dlambda over a
+// chunk of kBwdRowsPerChunk rows of one head.  One wave per row, two channels
+// per lane.
+__global__ void __launch_bounds__(256) bwd_pre_kernel(BackwardArgs a) {
+  __shared__ float red[kWaves][kDv + 1];
+  const int chunk = blockIdx.x, h = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int BT = a.B * a.T;
+  const float lam = a.lambda_h ? a.lambda_h[h] : a.lambda;
+  const f32x2 g = *reinterpret_cast<const f32x2*>(a.gain + (int64_t)h * kDv + 2 * lane);
+  float dg0 = 0.f, dg1 = 0.f, dl = 0.f;
+  for (int k = wave; k < kBwdRowsPerChunk; k += kWaves) {
+    const int rbt = chunk * kBwdRowsPerChunk + k;
+    if (rbt >= BT) break;
+    const int64_t row = (int64_t)rbt * a.H + h;
+    const int64_t off = row * kDv + 2 * lane;
+    const f32x2 o1 = *reinterpret_cast<const f32x2*>(a.o1n + off);
+    const f32x2 o2 = *reinterpret_cast<const f32x2*>(a.o2n + off);
+    const f32x2 dy = load_dy(a, off);
+    const float x0 = o1.x - lam * o2.x, x1 = o1.y - lam * o2.y;
+    const float mu = wave_sum(x0 + x1) * (1.0f / kDv);
+    const float d0 = x0 - mu, d1 = x1 - mu;
+    const float var = wave_sum(d0 * d0 + d1 * d1) * (1.0f / kDv);
+    const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
+    const float xh0 = d0 * rs, xh1 = d1 * rs;
+    dg0 += dy.x * xh0;
+    dg1 += dy.y * xh1;
+    const float g0 = dy.x * g.x, g1 = dy.y * g.y;
+    const float mg = wave_sum(g0 + g1) * (1.0f / kDv);
+    const float mgx = wave_sum(g0 * xh0 + g1 * xh1) * (1.0f / kDv);
+    const float do0 = rs * (g0 - mg - xh0 * mgx), do1 = rs * (g1 - mg - xh1 * mgx);
+    dl -= wave_sum(do0 * o2.x + do1 * o2.y);
+    // D_m from the fp16 dO the products use, so that sum_j P_ij dP_ij = D_i
+    // holds up to fp32 rounding (at T = 1, dS is then 0 as it must be).
+    const f16x2 hv = {(_Float16)do0, (_Float16)do1};
+    const float h0 = (float)hv[0], h1 = (float)hv[1];
+    const float dd1 = wave_sum(h0 * o1.x + h1 * o1.y);
+    const float s2 = wave_sum(h0 * o2.x + h1 * o2.y);
+    *reinterpret_cast<f16x2*>(a.dO + off) = hv;
+    if (lane == 0) *reinterpret_cast<f32x2*>(a.dstat + row * 2) = f32x2{dd1, -lam * s2};
+  }
+  red[wave][2 * lane] = dg0;
+  red[wave][2 * lane + 1] = dg1;
+  if (lane == 0) red[wave][kDv] = dl;
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t <= kDv) {
+    const float s = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+    a.partial[((int64_t)h * a.nchunks + chunk) * (kDv + 1) + t] = s;
+  }
+}
+
+// dgain[h, c] and dlambda[h]: the partials summed in chunk order.
+__global__ void __launch_bounds__(192) bwd_reduce_kernel(BackwardArgs a) {
+  const int h = blockIdx.x, t = threadIdx.x;
+  if (t > kDv) return;
+  const float* p = a.partial + (int64_t)h * a.nchunks * (kDv + 1) + t;
+  float s = 0.f;
+  for (int c = 0; c < a.nchunks; ++c) s += p[(int64_t)c * (kDv + 1)];
+  if (t < kDv)
+    a.dgain[(int64_t)h * kDv + t] = s;
+  else
+    a.dlam[h] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Tile staging shared by the three product kernels.  A tile is 32 rows
+// (keys or queries) of one (b, h), rows r0 .. r0+31, rows at or past `end`
+// reading as zero.  Threads 0..255 of the workgroup take part.
+
+// Row-major bf16 tiles of both maps (Q or K) by DMA into [map][32][128 B]
+// with the kSwz chunk swizzle: thread t fetches row t/8, logical chunk
+// (t % 8) ^ kSwz(t / 8), landing at chunk position t.
+__device__ __forceinline__ void dma_qk(const uint16_t* b1, const uint16_t* b2, int64_t st1, int64_t st2, int r0,
+                                       int end, char* dst, int tid) {
+  const int r = tid >> 3, c = (tid & 7) ^ kSwz(r);
+  char* d = dst + (tid >> 6) * 1024;  // each wave fills 1 KiB of each map's tile
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(b1, st1, r0, end, kDqk), (lds_ptr_t)d, 16,
+                                           (uint32_t)((r * st1 + 8 * c) * 2), 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(b2, st2, r0, end, kDqk), (lds_ptr_t)(d + kQKTile), 16,
+                                           (uint32_t)((r * st2 + 8 * c) * 2), 0, 0, 0);
+}
+
+// Row-major fp16 dO tile by DMA into [32][256 B] with the swz16 swizzle: the
+// tile's 512 chunks, two per thread (chunk positions t and t + 256).
+__device__ __forceinline__ void dma_do(const uint16_t* base, int64_t stride, int r0, int end, char* dst, int tid) {
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(base, stride, r0, end, kDv);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int p = tid + 256 * k;
+    const int r = p >> 4, c = (p & 15) ^ swz16(r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + 1024 * (p >> 6)), 16,
+                                             (uint32_t)((r * stride + 8 * c) * 2), 0, 0, 0);
+  }
+}
+
+// Transposed fp16 tiles of both maps (Q^T or K^T): [map][64 dims][80 B], row
+// d holding rows r0..r0+31 of dim d in kVPos order.  Thread t loads rows
+// 4(t%8) .. +3, dims 2(t/8), 2(t/8)+1 of each map (4-byte loads) ...
+struct StagedT {
+  uint32_t w[2][4];
+};
+
+__device__ __forceinline__ void load_qkT(StagedT& s, const uint16_t* b1, const uint16_t* b2, int64_t st1,
+                                         int64_t st2, int r0, int end, int tid) {
+  const int kg = tid & 7, dg = tid >> 3;
+  const __amdgpu_buffer_rsrc_t x1 = rows_rsrc(b1, st1, r0, end, kDqk);
+  const __amdgpu_buffer_rsrc_t x2 = rows_rsrc(b2, st2, r0, end, kDqk);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s.w[0][r] = __builtin_amdgcn_raw_buffer_load_b32(x1, (uint32_t)(((4 * kg + r) * st1 + 2 * dg) * 2), 0, 0);
+    s.w[1][r] = __builtin_amdgcn_raw_buffer_load_b32(x2, (uint32_t)(((4 * kg + r) * st2 + 2 * dg) * 2), 0, 0);
+  }
+}
+
+// ... and writes them converted to fp16.
+__device__ __forceinline__ void store_qkT(const StagedT& s, char* dst, int tid) {
+  const int kg = tid & 7, dg = tid >> 3;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const f16x4 lo = {(_Float16)bf16_lo(s.w[m][0]), (_Float16)bf16_lo(s.w[m][1]), (_Float16)bf16_lo(s.w[m][2]),
+                      (_Float16)bf16_lo(s.w[m][3])};
+    const f16x4 hi = {(_Float16)bf16_hi(s.w[m][0]), (_Float16)bf16_hi(s.w[m][1]), (_Float16)bf16_hi(s.w[m][2]),
+                      (_Float16)bf16_hi(s.w[m][3])};
+    char* d = dst + m * kQKT + kVPos(kg) * 8;
+    *reinterpret_cast<f16x4*>(d + (2 * dg) * kTRow) = lo;
+    *reinterpret_cast<f16x4*>(d + (2 * dg + 1) * kTRow) = hi;
+  }
+}
+
+// Transposed fp16 dO tile: [128 channels][80 B], channel row holding rows
+// r0..r0+31 in kVPos order.  Thread t loads rows 4(t%8) .. +3, channels
+// 4(t/8) .. +3 (8-byte loads of fp16).
+struct StagedDT {
+  u32x2 w[4];
+};
+
+__device__ __forceinline__ void load_doT(StagedDT& s, const uint16_t* base, int64_t stride, int r0, int end,
+                                         int tid) {
+  const int kg = tid & 7, cg = tid >> 3;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(base, stride, r0, end, kDv);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    s.w[r] = __builtin_amdgcn_raw_buffer_load_b64(rs, (uint32_t)(((4 * kg + r) * stride + 4 * cg) * 2), 0, 0);
+}
+
+__device__ __forceinline__ void store_doT(const StagedDT& s, char* dst, int tid) {
+  const int kg = tid & 7, cg = tid >> 3;
+  char* d = dst + kVPos(kg) * 8;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // channel 4cg + c of rows 4kg .. 4kg+3
+    const int word = c >> 1, shift = (c & 1) * 16;
+    uint32_t e[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[r] = (s.w[r][word] >> shift) & 0xffffu;
+    const u32x2 pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+    *reinterpret_cast<u32x2*>(d + (4 * cg + c) * kTRow) = pk;
+  }
+}
+
+// Row-major fp16 V tile (keys x 128 channels) through registers: thread t
+// takes row t/8, channels 16(t%8) .. +15 (two 16-byte loads), stores them
+// converted at logical chunks 2(t%8), 2(t%8)+1 with the swz16 swizzle.
+struct StagedV {
+  u32x4 w[2];
+};
+
+__device__ __forceinline__ void load_v(StagedV& s, const uint16_t* base, int64_t stride, int r0, int end, int tid) {
+  const int r = tid >> 3, p = tid & 7;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(base, stride, r0, end, kDv);
+  s.w[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((r * stride + 16 * p) * 2), 0, 0);
+  s.w[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((r * stride + 16 * p + 8) * 2), 0, 0);
+}
+
+__device__ __forceinline__ void store_v(const StagedV& s, char* dst, int tid) {
+  const int r = tid >> 3, p = tid & 7;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[2 * i] = (_Float16)bf16_lo(s.w[k][i]);
+      h[2 * i + 1] = (_Float16)bf16_hi(s.w[k][i]);
+    }
+    *reinterpret_cast<f16x8*>(dst + r * kD16Row + (((2 * p + k) ^ swz16(r)) << 4)) = h;
+  }
+}
+
+// Packs a 32x32 accumulator (16 values per lane) as the two fp16 operands of
+// the next product's k-steps: registers 0..7, then 8..15.
+__device__ __forceinline__ void pack16(const f32x16& v, f16x8& p0, f16x8& p1) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p0[j] = (_Float16)v[j];
+    p1[j] = (_Float16)v[8 + j];
+  }
+}
+
+// acc (32 rows x 32 lanes' columns) += T^T(rows 32blk.., kVPos-ordered 32)
+// * B for one 32-row block of a transposed fp16 tile.
+__device__ __forceinline__ f32x16 mfma_T(const char* tT, int blk, int lq, int hf, const f16x8& b0, const f16x8& b1,
+                                         f32x16 acc) {
+  const char* t = tT + (32 * blk + lq) * kTRow + hf * 16;
+  const f16x8 a0 = *reinterpret_cast<const f16x8*>(t);
+  const f16x8 a1 = *reinterpret_cast<const f16x8*>(t + 32);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc, 0, 0, 0);
+}
+
+// Stores a lane's column of a 32-row accumulator block (rows 32blk + 8(i/4) +
+// 4hf + i%4), times f, into dst[rows] (fp32, 16-byte stores).
+__device__ __forceinline__ void store_col(float* dst, const f32x16& acc, int blk, int hf, float f) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    f32x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = acc[4 * r4 + r] * f;
+    *reinterpret_cast<f32x4*>(dst + 32 * blk + 8 * r4 + 4 * hf) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ_1, dQ_2: a workgroup owns 128 queries of one (b, h); wave w queries
+// 32w .. 32w+31, lane (hf, lq) query lq.  Key tiles stream through LDS:
+// K_1, K_2 row-major bf16 (score operands), V row-major fp16 (dP^T operand),
+// K_1^T, K_2^T fp16 (dQ^T operands).
+constexpr int kDqStage = 2 * kQKTile + kD16Tile + 2 * kQKT;
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BackwardArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kDqStage];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, lq = lane & 31;
+  const int nqb = (a.T + kRows - 1) / kRows, BH = a.B * a.H;
+  const int qb = nqb - 1 - (int)(blockIdx.x / BH);  // longest rows first
+  const int bh = (int)(blockIdx.x % BH), head = bh % a.H, b = bh / a.H;
+  const int q_first = qb * kRows + 32 * wave, q = q_first + lq;
+  const bool wave_live = q_first < a.T, ok = q < a.T;
+  const int ntiles = min(qb * (kRows / 32) + kRows / 32, (a.T + 31) / 32);
+  const int kend = min(a.T, ntiles * 32);
+  const int last_tile = q_first / 32;
+
+  // Operands held for the whole kernel: Q_m^T (score B operands, bf16) and
+  // dO^T (dP^T B operand, fp16), both for this lane's query.
+  bf16x8 qa[4], qb2[4];
+  f16x8 dot[8];
+  const int64_t rq = ((int64_t)b * a.T + q) * a.H + head;
+  {
+    const uint16_t* p1 = a.q1 + (int64_t)b * a.sq1.b + (int64_t)q * a.sq1.t + (int64_t)head * a.sq1.h + 8 * hf;
+    const uint16_t* p2 = a.q2 + (int64_t)b * a.sq2.b + (int64_t)q * a.sq2.t + (int64_t)head * a.sq2.h + 8 * hf;
+    const uint16_t* pd = a.dO + rq * kDv + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qa[s] = ok ? *reinterpret_cast<const bf16x8*>(p1 + 16 * s) : bf16x8{};
+      qb2[s] = ok ? *reinterpret_cast<const bf16x8*>(p2 + 16 * s) : bf16x8{};
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) dot[s] = ok ? *reinterpret_cast<const f16x8*>(pd + 16 * s) : f16x8{};
+  }
+  const float lse1 = ok ? a.lse[rq * 2] : 0.f, lse2 = ok ? a.lse[rq * 2 + 1] : 0.f;
+  const float D1 = ok ? a.dstat[rq * 2] : 0.f, D2 = ok ? a.dstat[rq * 2 + 1] : 0.f;
+  const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
+  const float c = a.c;
+
+  const uint16_t* kb1 = a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h;
+  const uint16_t* kb2 = a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h;
+  const uint16_t* vb = a.v + (int64_t)b * a.sv.b + (int64_t)head * a.sv.h;
+
+  f32x16 dq1[2] = {f32x16{}, f32x16{}}, dq2[2] = {f32x16{}, f32x16{}};
+  const int ksw = kSwz(lq);
+
+  StagedV sv;
+  StagedT sk;
+  auto stage_issue = [&](int j, char* st) {
+    dma_qk(kb1, kb2, a.sk1.t, a.sk2.t, 32 * j, kend, st, tid);
+    load_v(sv, vb, a.sv.t, 32 * j, kend, tid);
+    load_qkT(sk, kb1, kb2, a.sk1.t, a.sk2.t, 32 * j, kend, tid);
+  };
+  auto stage_store = [&](char* st) {
+    store_v(sv, st + 2 * kQKTile, tid);
+    store_qkT(sk, st + 2 * kQKTile + kD16Tile, tid);
+  };
+  stage_issue(0, smem);
+  stage_store(smem);
+  wait_dma();
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    char* cur = smem + (j & 1) * kDqStage;
+    char* nxt = smem + ((j + 1) & 1) * kDqStage;
+    const bool more = j + 1 < ntiles;
+    if (more) stage_issue(j + 1, nxt);
+    if (wave_live && j <= last_tile) {
+      // S_m^T = K_m Q_m^T (32 keys x 32 queries)
+      f32x16 s1 = f32x16{}, s2 = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int off = lq * kKRow + (((2 * s + hf) ^ ksw) << 4);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(cur + off), qa[s], s1, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(cur + kQKTile + off), qb2[s],
+                                                     s2, 0, 0, 0);
+      }
+      // dP^T = V dO^T
+      f32x16 dp = f32x16{};
+      const char* vt = cur + 2 * kQKTile + lq * kD16Row;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            *reinterpret_cast<const f16x8*>(vt + (((2 * s + hf) ^ swz16(lq)) << 4)), dot[s], dp, 0, 0, 0);
+      // P_m^T from the saved log-sum-exp, then dS_m^T; the diagonal tile
+      // keeps keys <= query only (register i is key 8(i/4) + 4hf + i%4).
+      const bool diag = j == last_tile;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool vis = !diag || 8 * (i >> 2) + 4 * hf + (i & 3) <= lq;
+        const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lse1)) : 0.f;
+        const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -lse2)) : 0.f;
+        s1[i] = p1 * (dp[i] - D1);
+        s2[i] = p2 * (-lam * dp[i] - D2);
+      }
+      f16x8 a0, a1, b0, b1;
+      pack16(s1, a0, a1);
+      pack16(s2, b0, b1);
+      // dQ_m^T += K_m^T dS_m^T
+      const char* kt = cur + 2 * kQKTile + kD16Tile;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        dq1[blk] = mfma_T(kt, blk, lq, hf, a0, a1, dq1[blk]);
+        dq2[blk] = mfma_T(kt + kQKT, blk, lq, hf, b0, b1, dq2[blk]);
+      }
+    }
+    if (more) stage_store(nxt);
+    wait_dma();
+    __syncthreads();
+  }
+  if (!ok) return;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    store_col(a.dq1 + rq * kDqk, dq1[blk], blk, hf, a.scale);
+    store_col(a.dq2 + rq * kDqk, dq2[blk], blk, hf, a.scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV: a workgroup owns 128 keys of one (b, h); wave w keys 32w ..
+// 32w+31, lane (hf, lk) key lk.  Query tiles from the workgroup's diagonal on
+// stream through LDS.  Scores are S = Q K^T (32 queries x 32 keys), so the
+// accumulator's columns are this lane's key and its rows queries.
+
+// Per-query statistics of a query tile in LDS: [lse_1, lse_2, D_1, D_2][32].
+// Rows past T get lse = +inf, so their probabilities are 0.
+__device__ __forceinline__ void stage_stats(const BackwardArgs& a, int b, int head, int q0, float* st, int tid) {
+  if (tid < 32) {
+    const int q = q0 + tid;
+    f32x2 l = {__builtin_inff(), __builtin_inff()}, d = {0.f, 0.f};
+    if (q < a.T) {
+      const int64_t r = ((int64_t)b * a.T + q) * a.H + head;
+      l = *reinterpret_cast<const f32x2*>(a.lse + r * 2);
+      d = *reinterpret_cast<const f32x2*>(a.dstat + r * 2);
+    }
+    st[tid] = l.x;
+    st[32 + tid] = l.y;
+    st[64 + tid] = d.x;
+    st[96 + tid] = d.y;
+  }
+}
+
+// S_m = Q_m K_m^T for one map from a row-major bf16 Q tile.
+__device__ __forceinline__ f32x16 scores_qk(const char* qt, const bf16x8 (&kt)[4], int lq, int hf) {
+  f32x16 acc = f32x16{};
+  const int sw = kSwz(lq);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        *reinterpret_cast<const bf16x8*>(qt + lq * kKRow + (((2 * s + hf) ^ sw) << 4)), kt[s], acc, 0, 0, 0);
+  return acc;
+}
+
+// Loads this lane's key row as the score B operand (K_m^T: dims 16s + 8hf ..).
+__device__ __forceinline__ void load_krow(bf16x8 (&kt)[4], const uint16_t* base, int64_t stride, int key, bool ok,
+                                          int hf) {
+  const uint16_t* p = base + (int64_t)key * stride + 8 * hf;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) kt[s] = ok ? *reinterpret_cast<const bf16x8*>(p + 16 * s) : bf16x8{};
+}
+
+constexpr int kDkStage = 2 * kQKTile + kD16Tile + 2 * kQKT + 4 * 32 * 4;
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dk_kernel(BackwardArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kDkStage];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, lk = lane & 31;
+  const int BH = a.B * a.H;
+  const int kb = (int)(blockIdx.x / BH);  // longest column blocks first
+  const int bh = (int)(blockIdx.x % BH), head = bh % a.H, b = bh / a.H;
+  const int k_first = kb * kRows + 32 * wave, key = k_first + lk;
+  const bool wave_live = k_first < a.T, ok = key < a.T;
+  const int nqt = (a.T + 31) / 32, qt0 = kb * (kRows / 32);
+  const int diag = k_first / 32;  // this wave's first (diagonal) query tile
+
+  bf16x8 k1t[4], k2t[4];
+  f16x8 vt[8];
+  load_krow(k1t, a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h, a.sk1.t, key, ok, hf);
+  load_krow(k2t, a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h, a.sk2.t, key, ok, hf);
+  {
+    const uint16_t* p = a.v + (int64_t)b * a.sv.b + (int64_t)key * a.sv.t + (int64_t)head * a.sv.h + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 w = ok ? *reinterpret_cast<const u32x4*>(p + 16 * s) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vt[s][2 * i] = (_Float16)bf16_lo(w[i]);
+        vt[s][2 * i + 1] = (_Float16)bf16_hi(w[i]);
+      }
+    }
+  }
+  const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
+  const float c = a.c;
+  const uint16_t* qb1 = a.q1 + (int64_t)b * a.sq1.b + (int64_t)head * a.sq1.h;
+  const uint16_t* qb2 = a.q2 + (int64_t)b * a.sq2.b + (int64_t)head * a.sq2.h;
+  const uint16_t* dob = a.dO + (int64_t)b * a.T * a.H * kDv + (int64_t)head * kDv;
+  const int64_t sdo = (int64_t)a.H * kDv;
+
+  f32x16 dk1[2] = {f32x16{}, f32x16{}}, dk2[2] = {f32x16{}, f32x16{}};
+  StagedT sq;
+  auto stage_issue = [&](int qt, char* st) {
+    dma_qk(qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, st, tid);
+    dma_do(dob, sdo, 32 * qt, a.T, st + 2 * kQKTile, tid);
+    load_qkT(sq, qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, tid);
+  };
+  auto stage_store = [&](int qt, char* st) {
+    store_qkT(sq, st + 2 * kQKTile + kD16Tile, tid);
+    stage_stats(a, b, head, 32 * qt, reinterpret_cast<float*>(st + 2 * kQKTile + kD16Tile + 2 * kQKT), tid);
+  };
+  if (qt0 < nqt) {
+    stage_issue(qt0, smem);
+    stage_store(qt0, smem);
+  }
+  wait_dma();
+  __syncthreads();
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int it = qt - qt0;
+    char* cur = smem + (it & 1) * kDkStage;
+    char* nxt = smem + ((it + 1) & 1) * kDkStage;
+    const bool more = qt + 1 < nqt;
+    if (more) stage_issue(qt + 1, nxt);
+    if (wave_live && qt >= diag) {
+      f32x16 s1 = scores_qk(cur, k1t, lk, hf);
+      f32x16 s2 = scores_qk(cur + kQKTile, k2t, lk, hf);
+      // dP = dO V^T (32 queries x 32 keys)
+      f32x16 dp = f32x16{};
+      const char* dt = cur + 2 * kQKTile + lk * kD16Row;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            *reinterpret_cast<const f16x8*>(dt + (((2 * s + hf) ^ swz16(lk)) << 4)), vt[s], dp, 0, 0, 0);
+      const float* stats = reinterpret_cast<const float*>(cur + 2 * kQKTile + kD16Tile + 2 * kQKT);
+      const bool dg = qt == diag;  // rows are queries 8(i/4) + 4hf + i%4 of the tile, the column key lk
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // statistics of rows 8g + 4hf .. +3, four registers at a time
+        const int r0 = 8 * g + 4 * hf;
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(stats + r0);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 32 + r0);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(stats + 64 + r0);
+        const f32x4 d2 = *reinterpret_cast<const f32x4*>(stats + 96 + r0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * g + r;
+          const bool vis = !dg || lk <= r0 + r;
+          const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r])) : 0.f;
+          const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r])) : 0.f;
+          s1[i] = p1 * (dp[i] - d1[r]);
+          s2[i] = p2 * (-lam * dp[i] - d2[r]);
+        }
+      }
+      f16x8 a0, a1, b0, b1;
+      pack16(s1, a0, a1);
+      pack16(s2, b0, b1);
+      // dK_m^T += Q_m^T dS_m
+      const char* qtT = cur + 2 * kQKTile + kD16Tile;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        dk1[blk] = mfma_T(qtT, blk, lk, hf, a0, a1, dk1[blk]);
+        dk2[blk] = mfma_T(qtT + kQKT, blk, lk, hf, b0, b1, dk2[blk]);
+      }
+    }
+    if (more) stage_store(qt + 1, nxt);
+    wait_dma();
+    __syncthreads();
+  }
+  if (!ok) return;
+  const int64_t rk = ((int64_t)b * a.T + key) * a.H + head;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    store_col(a.dk1 + rk * kDqk, dk1[blk], blk, hf, a.scale);
+    store_col(a.dk2 + rk * kDqk, dk2[blk], blk, hf, a.scale);
+  }
+}
+
+constexpr int kDvStage = 2 * kQKTile + kDT + 2 * 32 * 4;
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dv_kernel(BackwardArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kDvStage];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, lk = lane & 31;
+  const int BH = a.B * a.H;
+  const int kb = (int)(blockIdx.x / BH);
+  const int bh = (int)(blockIdx.x % BH), head = bh % a.H, b = bh / a.H;
+  const int k_first = kb * kRows + 32 * wave, key = k_first + lk;
+  const bool wave_live = k_first < a.T, ok = key < a.T;
+  const int nqt = (a.T + 31) / 32, qt0 = kb * (kRows / 32);
+  const int diag = k_first / 32;
+
+  bf16x8 k1t[4], k2t[4];
+  load_krow(k1t, a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h, a.sk1.t, key, ok, hf);
+  load_krow(k2t, a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h, a.sk2.t, key, ok, hf);
+  const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
+  const float c = a.c;
+  const uint16_t* qb1 = a.q1 + (int64_t)b * a.sq1.b + (int64_t)head * a.sq1.h;
+  const uint16_t* qb2 = a.q2 + (int64_t)b * a.sq2.b + (int64_t)head * a.sq2.h;
+  const uint16_t* dob = a.dO + (int64_t)b * a.T * a.H * kDv + (int64_t)head * kDv;
+  const int64_t sdo = (int64_t)a.H * kDv;
+
+  f32x16 dv[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  StagedDT sd;
+  auto stage_issue = [&](int qt, char* st) {
+    dma_qk(qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, st, tid);
+    load_doT(sd, dob, sdo, 32 * qt, a.T, tid);
+  };
+  auto stage_store = [&](int qt, char* st) {
+    store_doT(sd, st + 2 * kQKTile, tid);
+    if (tid < 32) {
+      const int q = 32 * qt + tid;
+      f32x2 l = {__builtin_inff(), __builtin_inff()};
+      if (q < a.T) l = *reinterpret_cast<const f32x2*>(a.lse + (((int64_t)b * a.T + q) * a.H + head) * 2);
+      float* s = reinterpret_cast<float*>(st + 2 * kQKTile + kDT);
+      s[tid] = l.x;
+      s[32 + tid] = l.y;
+    }
+  };
+  if (qt0 < nqt) {
+    stage_issue(qt0, smem);
+    stage_store(qt0, smem);
+  }
+  wait_dma();
+  __syncthreads();
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int it = qt - qt0;
+    char* cur = smem + (it & 1) * kDvStage;
+    char* nxt = smem + ((it + 1) & 1) * kDvStage;
+    const bool more = qt + 1 < nqt;
+    if (more) stage_issue(qt + 1, nxt);
+    if (wave_live && qt >= diag) {
+      f32x16 s1 = scores_qk(cur, k1t, lk, hf);
+      f32x16 s2 = scores_qk(cur + kQKTile, k2t, lk, hf);
+      const float* stats = reinterpret_cast<const float*>(cur + 2 * kQKTile + kDT);
+      const bool dg = qt == diag;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = 8 * g + 4 * hf;
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(stats + r0);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 32 + r0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * g + r;
+          const bool vis = !dg || lk <= r0 + r;
+          const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r])) : 0.f;
+          const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r])) : 0.f;
+          s1[i] = p1 - lam * p2;
+        }
+      }
+      f16x8 p0, p1;
+      pack16(s1, p0, p1);
+      // dV^T += dO^T (P_1 - lambda P_2)
+      const char* dT = cur + 2 * kQKTile;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) dv[blk] = mfma_T(dT, blk, lk, hf, p0, p1, dv[blk]);
+    }
+    if (more) stage_store(qt + 1, nxt);
+    wait_dma();
+    __syncthreads();
+  }
+  if (!ok) return;
+  const int64_t rk = ((int64_t)b * a.T + key) * a.H + head;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) store_col(a.dv + rk * kDv, dv[blk], blk, hf, 1.0f);
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)a.nchunks, (unsigned)a.H), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)a.H), dim3(192), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t blocks = (int64_t)((a.T + kRows - 1) / kRows) * a.B * a.H;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dk_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace diffattn

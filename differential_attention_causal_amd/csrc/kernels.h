@@ -40,6 +40,12 @@ struct PrefillArgs {
   void* out;              // [B, T, H, kDv] bf16 or fp32
   int out_f32;
   float* o_pre;           // [B, T, H, kDv] fp32 or null
+  // Training outputs (all or none): each map's normalised output O_m / l_m,
+  // fp32 [B, T, H, kDv], and its base-2 log-sum-exp m_m + log2 l_m of the
+  // scores in base-2 units, fp32 [B, T, H, 2].
+  float* o1n;
+  float* o2n;
+  float* lse;
 };
 
 struct DecodeArgs {
@@ -84,11 +90,49 @@ struct RopeApplyArgs {
   RopeArgs rope;
 };
 
+// Backward pass of the causal prefill (no window, no rotary embedding).
+struct BackwardArgs {
+  const uint16_t* q1;
+  const uint16_t* q2;
+  const uint16_t* k1;
+  const uint16_t* k2;
+  const uint16_t* v;
+  Strides sq1, sq2, sk1, sk2, sv;
+  int B, T, H;
+  float c;                // scale * log2(e)
+  float scale;            // score factor
+  float lambda;
+  const float* lambda_h;  // [H] or null
+  const float* gain;      // [H, kDv]
+  float eps;
+  const float* o1n;       // forward training outputs (see PrefillArgs)
+  const float* o2n;
+  const float* lse;
+  const void* dy;         // [B, T, H, kDv] bf16 or fp32
+  int dy_f32;
+  float* dq1;             // [B, T, H, kDqk] fp32, contiguous
+  float* dq2;
+  float* dk1;
+  float* dk2;
+  float* dv;              // [B, T, H, kDv] fp32
+  float* dlam;            // [H]
+  float* dgain;           // [H, kDv]
+  // workspace
+  uint16_t* dO;           // [B, T, H, kDv] fp16: gradient of the pre-norm output
+  float* dstat;           // [B, T, H, 2]: D_m = rowsum(dO_m * O_m) per map
+  float* partial;         // [H, nchunks, kDv + 1]: gain and lambda gradient partials
+  int nchunks;
+};
+
+// Rows (b, t) of one head per workgroup of the backward's first kernel.
+constexpr int kBwdRowsPerChunk = 64;
+
 // Fills rope.phase for base theta (host).
 void rope_phases(float theta, RopeArgs& r);
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t stream);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace diffattn

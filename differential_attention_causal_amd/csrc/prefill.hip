@@ -27,7 +27,7 @@
 // the two lanes (l, l ^ 32) that share a query.  P^T feeds the second product
 // straight from registers: the score accumulator already holds, per lane, the
 // key indices the f16 operand needs, provided V^T's keys are stored in LDS in
-// the matching order (see kVPos below).
+// the matching order (see kVPos in tile.h).
 //
 // Precision.  Scores: bf16 inputs, fp32 accumulation.  Softmax in fp32 base-2
 // units (c = scale * log2 e).  P is rounded to fp16 and V is converted
@@ -37,18 +37,10 @@
 // the O rescale is rare after the first tiles.
 #include "kernels.h"
 #include "rope.h"
+#include "tile.h"
 
 namespace diffattn {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGroupWaves = 4;              // waves per group, 32 queries each
 constexpr int kBM = 32 * kGroupWaves;       // queries per workgroup
@@ -66,21 +58,6 @@ constexpr int kMergeML = kGroupWaves * 64 * 2 * 4;
 static_assert(kMergeO + kMergeML <= 2 * 2 * kTile, "merge buffer must fit in the stage memory");
 constexpr float kSlack = 8.0f;
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Position (in units of 4 keys) of key group kg inside a V^T row.  Key
-// k = 16s + 8m + 4h + r of a tile must sit at 16s + 8h + 4m + r, so that lane
-// half h reads the 8 keys {16s + 8m + 4h + r} of product step s as one
-// contiguous 16-byte word: the same keys, in the same slot order, that half h
-// holds in its score accumulator.  That is a swap of bits 0 and 1 of kg.
-__device__ __forceinline__ int kVPos(int kg) { return (kg & 4) | ((kg & 1) << 1) | ((kg >> 1) & 1); }
-
-// 16-byte chunk swizzle of K rows: row r's chunk c sits at c ^ kSwz(r).  Any 8
-// consecutive rows, and the 8 even or the 8 odd rows of any 16, read the same
-// logical chunk from 8 distinct chunk slots, so a 16-byte read by 8 or 16
-// lanes (one key row each) is free of bank conflicts on 32 or 64 banks.
-__device__ __forceinline__ int kSwz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 load8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
@@ -90,16 +67,6 @@ struct Staged {
   u32x2 v[4];
   uint32_t kpos;  // position of this thread's key row (rotary embedding)
 };
-
-// Buffer resource over key rows k0 .. kend-1 of one (b, h) (row stride
-// `stride` elements, rows of `row` elements): loads past the last valid row
-// return zero in hardware, so tile loads need no per-row branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t stride, int k0, int kend,
-                                                             int row) {
-  const uint16_t* p = base + (int64_t)k0 * stride;
-  const int nrec = kend > k0 ? (int)(((int64_t)(kend - k0 - 1) * stride + row) * 2) : 0;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, nrec, 0x00020000);
-}
 
 // Per-thread byte offsets of the staging loads inside a tile (see stage_load).
 struct StageOffsets {
@@ -125,8 +92,6 @@ __device__ __forceinline__ StageOffsets stage_offsets(const PrefillArgs& a, int 
   o.v = (uint32_t)((4 * kg * a.sv.t + 4 * cg) * 2);
   return o;
 }
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Memory -> LDS for the key tiles of one step (no registers involved): each
 // wave moves 64 chunks of K1 and of K2 into its quarter of its group's tile.
@@ -171,10 +136,6 @@ __device__ __forceinline__ void stage_load(Staged& st, const PrefillArgs& a, con
 #pragma unroll
   for (int r = 0; r < 4; ++r) st.v[r] = __builtin_amdgcn_raw_buffer_load_b64(rv, off.v, r * vrow, 0);
 }
-
-// Waits for this wave's outstanding memory loads, the LDS-destination ones
-// included (vmcnt 0; export and LDS counters left alone).
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Split-half rotation of a staged key row piece: words 0-1 hold dims
 // 4j .. 4j+3 of K1 (K2), words 2-3 the pair partners 32 + 4j .., so pairs
@@ -549,6 +510,29 @@ prefill_kernel(PrefillArgs a) {
   // (lane ^ 32) holds the other 64.
   l1 += __shfl_xor(l1, 32);
   l2 += __shfl_xor(l2, 32);
+  if (a.o1n != nullptr && q < a.T) {
+    // Training outputs for the backward pass.
+    const int64_t rq = ((int64_t)b * a.T + q) * a.H + head;
+    const float i1 = 1.0f / l1, i2 = 1.0f / l2;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ch = 32 * cb + 8 * r4 + 4 * hf;
+        f32x4 v1, v2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v1[r] = O1[cb][4 * r4 + r] * i1;
+          v2[r] = O2[cb][4 * r4 + r] * i2;
+        }
+        *reinterpret_cast<f32x4*>(a.o1n + rq * kDv + ch) = v1;
+        *reinterpret_cast<f32x4*>(a.o2n + rq * kDv + ch) = v2;
+      }
+    if (hf == 0) {
+      a.lse[rq * 2] = m1 + __builtin_log2f(l1);
+      a.lse[rq * 2 + 1] = m2 + __builtin_log2f(l2);
+    }
+  }
   const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
   const float r1 = 1.0f / l1;
   const float r2 = lam / l2;

@@ -215,11 +215,59 @@ DIFFATTN_API int diffattn_rope_apply(const void* x, const diffattn_strides* x_st
                                      const diffattn_strides* out_strides, int B, int T, int H, int d, int mode,
                                      float theta, int pos0, const int32_t* pos_start, void* stream);
 
+/*
+ * Training forward: diffattn_fwd_prefill (plain causal: no window, no RoPE)
+ * that also saves what the backward pass needs.
+ *   o1, o2 : fp32 [B, T, H, d_v], each map's normalised output
+ *            softmax(Q_m K_m^T * scale) V (so o = o1 - lambda o2)
+ *   lse    : fp32 [B, T, H, 2], each map's log-sum-exp of its scaled scores
+ *            in base 2: log2 sum_j 2^(scale * log2(e) * q_i . k_j)
+ * All three are required, C-contiguous and 16-byte aligned; other arguments
+ * and errors as for diffattn_fwd_prefill.
+ */
+DIFFATTN_API int diffattn_fwd_prefill_train(const void* q1, const void* q2, const void* k1, const void* k2,
+                                            const void* v, const diffattn_strides* strides, int B, int T, int H,
+                                            int d_qk, int d_v, float lambda, const float* lambda_per_head,
+                                            const float* gain, float gn_eps, float scale, void* out, int out_dtype,
+                                            float* o_pre, float* o1, float* o2, float* lse, void* stream);
+
+/*
+ * Bytes of device workspace diffattn_bwd_prefill needs (256-byte aligned
+ * buffer): the pre-norm output gradient in fp16, two row statistics and the
+ * gain/lambda partial sums.  Returns 0 for invalid sizes.
+ */
+DIFFATTN_API size_t diffattn_bwd_workspace_bytes(int B, int T, int H, int d_v);
+
+/*
+ * Backward pass of the causal prefill: the gradients of sum(y * dy) for the
+ * operation above (the calculus of the definition on the Motif 2.6B
+ * explainer, section "Differential attention"; plain causal only).
+ *   q1 .. v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head, gain,
+ *   gn_eps, scale : the forward's arguments
+ *   o1, o2, lse   : the forward's training outputs (diffattn_fwd_prefill_train)
+ *   dy            : [B, T, H, d_v] bf16 or fp32 per dy_dtype, C-contiguous
+ *   dq1, dq2, dk1, dk2 : fp32 [B, T, H, d_qk] out, C-contiguous
+ *   dv            : fp32 [B, T, H, d_v] out
+ *   dlambda       : fp32 [H] out, per head (for one shared lambda, sum it)
+ *   dgain         : fp32 [H, d_v] out
+ *   workspace     : >= diffattn_bwd_workspace_bytes() bytes, 256-byte aligned
+ * Every output is written (not accumulated).  Errors as for the forward,
+ * plus DIFFATTN_ERR_WORKSPACE.  Deterministic (no atomics).
+ */
+DIFFATTN_API int diffattn_bwd_prefill(const void* q1, const void* q2, const void* k1, const void* k2,
+                                      const void* v, const diffattn_strides* strides, int B, int T, int H,
+                                      int d_qk, int d_v, float lambda, const float* lambda_per_head,
+                                      const float* gain, float gn_eps, float scale, const float* o1,
+                                      const float* o2, const float* lse, const void* dy, int dy_dtype, float* dq1,
+                                      float* dq2, float* dk1, float* dk2, float* dv, float* dlambda,
+                                      float* dgain, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 DIFFATTN_API const char* diffattn_status_string(int status);
 
 /* Library ABI version (major * 100 + minor): 101 adds the *_ex entry points,
- * 102 the rotary embedding (diffattn_options.rope, diffattn_rope_apply). */
+ * 102 the rotary embedding (diffattn_options.rope, diffattn_rope_apply), 103
+ * the training forward and the backward pass. */
 DIFFATTN_API int diffattn_abi_version(void);
 
 #ifdef __cplusplus

@@ -25,11 +25,12 @@ def test_header_symbols_exported():
     names = _declared()
     assert set(names) == {"diffattn_fwd_prefill", "diffattn_fwd_decode", "diffattn_decode_workspace_bytes",
                           "diffattn_fwd_prefill_ex", "diffattn_fwd_decode_ex", "diffattn_rope_apply",
+                          "diffattn_fwd_prefill_train", "diffattn_bwd_workspace_bytes", "diffattn_bwd_prefill",
                           "diffattn_status_string", "diffattn_abi_version"}
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 102
+    assert da.diffattn_abi_version() == 103
 
 
 def test_status_strings():
@@ -159,3 +160,44 @@ def test_rope_apply_rejects(kw, rc):
 def test_rope_apply_rejects_bad_strides():
     assert _rope_apply(sx=ctypes.byref(da._Strides(960, 192, 60))) == ELAYOUT
     assert _rope_apply(so=ctypes.byref(da._Strides(960, -64, 64))) == ELAYOUT
+
+
+def _train(**kw):
+    args = dict(q1=A, q2=A, k1=A, k2=A, v=A, st=None, B=1, T=128, H=2, dqk=64, dv=128, lam=0.5, lamh=None,
+                gain=A, eps=1e-5, scale=0.0, out=A, odt=0, opre=None, o1=A, o2=A, lse=A, stream=None)
+    args.update(kw)
+    return da._lib.diffattn_fwd_prefill_train(*args.values())
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(o1=None), ENULL), (dict(lse=None), ENULL), (dict(o2=A + 4), ELAYOUT), (dict(T=0), ESHAPE),
+    (dict(dqk=32), EUNSUP), (dict(lam=float("nan")), EVALUE),
+])
+def test_train_forward_rejects(kw, rc):
+    assert _train(**kw) == rc
+
+
+def _bwd(**kw):
+    need = da.diffattn_bwd_workspace_bytes(1, 128, 2, 128)
+    args = dict(q1=A, q2=A, k1=A, k2=A, v=A, st=None, B=1, T=128, H=2, dqk=64, dv=128, lam=0.5, lamh=None,
+                gain=A, eps=1e-5, scale=0.0, o1=A, o2=A, lse=A, dy=A, dyt=0, dq1=A, dq2=A, dk1=A, dk2=A, dvv=A,
+                dlam=A, dgain=A, ws=A, wsb=need, stream=None)
+    args.update(kw)
+    return da._lib.diffattn_bwd_prefill(*args.values())
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(dy=None), ENULL), (dict(dlam=None), ENULL), (dict(o1=None), ENULL), (dict(B=0), ESHAPE),
+    (dict(T=(1 << 22) + 1), ESHAPE), (dict(dv=64), EUNSUP), (dict(dk2=A + 4), ELAYOUT), (dict(dyt=3), EVALUE),
+    (dict(eps=-1.0), EVALUE), (dict(ws=None), EWS), (dict(ws=A + 16), EWS), (dict(wsb=64), EWS),
+])
+def test_bwd_rejects(kw, rc):
+    assert _bwd(**kw) == rc
+
+
+def test_bwd_workspace_bytes():
+    n = da.diffattn_bwd_workspace_bytes(2, 100, 3, 128)
+    rows = 2 * 100 * 3
+    assert n >= rows * 128 * 2 + rows * 2 * 4 + 3 * ((200 + 63) // 64) * 129 * 4 and n % 256 == 0
+    assert da.diffattn_bwd_workspace_bytes(0, 100, 3, 128) == 0
+    assert da.diffattn_bwd_workspace_bytes(1, 100, 3, 64) == 0
