@@ -66,35 +66,48 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BackwardArgs a) {
   const float lam = a.lambda_h ? a.lambda_h[h] : a.lambda;
   const f32x2 g = *reinterpret_cast<const f32x2*>(a.gain + (int64_t)h * kDv + 2 * lane);
   float dg0 = 0.f, dg1 = 0.f, dl = 0.f;
-  for (int k = wave; k < kBwdRowsPerChunk; k += kWaves) {
-    const int rbt = chunk * kBwdRowsPerChunk + k;
-    if (rbt >= BT) break;
-    const int64_t row = (int64_t)rbt * a.H + h;
-    const int64_t off = row * kDv + 2 * lane;
-    const f32x2 o1 = *reinterpret_cast<const f32x2*>(a.o1n + off);
-    const f32x2 o2 = *reinterpret_cast<const f32x2*>(a.o2n + off);
-    const f32x2 dy = load_dy(a, off);
-    const float x0 = o1.x - lam * o2.x, x1 = o1.y - lam * o2.y;
-    const float mu = wave_sum(x0 + x1) * (1.0f / kDv);
-    const float d0 = x0 - mu, d1 = x1 - mu;
-    const float var = wave_sum(d0 * d0 + d1 * d1) * (1.0f / kDv);
-    const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
-    const float xh0 = d0 * rs, xh1 = d1 * rs;
-    dg0 += dy.x * xh0;
-    dg1 += dy.y * xh1;
-    const float g0 = dy.x * g.x, g1 = dy.y * g.y;
-    const float mg = wave_sum(g0 + g1) * (1.0f / kDv);
-    const float mgx = wave_sum(g0 * xh0 + g1 * xh1) * (1.0f / kDv);
-    const float do0 = rs * (g0 - mg - xh0 * mgx), do1 = rs * (g1 - mg - xh1 * mgx);
-    dl -= wave_sum(do0 * o2.x + do1 * o2.y);
-    // D_m from the fp16 dO the products use, so that sum_j P_ij dP_ij = D_i
-    // holds up to fp32 rounding (at T = 1, dS is then 0 as it must be).
-    const f16x2 hv = {(_Float16)do0, (_Float16)do1};
-    const float h0 = (float)hv[0], h1 = (float)hv[1];
-    const float dd1 = wave_sum(h0 * o1.x + h1 * o1.y);
-    const float s2 = wave_sum(h0 * o2.x + h1 * o2.y);
-    *reinterpret_cast<f16x2*>(a.dO + off) = hv;
-    if (lane == 0) *reinterpret_cast<f32x2*>(a.dstat + row * 2) = f32x2{dd1, -lam * s2};
+  // Two rows per pass (rows k and k + kWaves) so their reductions overlap.
+  for (int k = wave; k < kBwdRowsPerChunk; k += 2 * kWaves) {
+    const int rbt0 = chunk * kBwdRowsPerChunk + k;
+    if (rbt0 >= BT) break;
+    const bool two = rbt0 + kWaves < BT && k + kWaves < kBwdRowsPerChunk;
+    int64_t off[2];
+    f32x2 o1[2], o2[2], dy[2];
+    float x[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t row = (int64_t)(u && two ? rbt0 + kWaves : rbt0) * a.H + h;
+      off[u] = row * kDv + 2 * lane;
+      o1[u] = *reinterpret_cast<const f32x2*>(a.o1n + off[u]);
+      o2[u] = *reinterpret_cast<const f32x2*>(a.o2n + off[u]);
+      dy[u] = load_dy(a, off[u]);
+      x[u][0] = o1[u].x - lam * o2[u].x;
+      x[u][1] = o1[u].y - lam * o2[u].y;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !two) break;
+      const float mu = wave_sum(x[u][0] + x[u][1]) * (1.0f / kDv);
+      const float d0 = x[u][0] - mu, d1 = x[u][1] - mu;
+      const float var = wave_sum(d0 * d0 + d1 * d1) * (1.0f / kDv);
+      const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
+      const float xh0 = d0 * rs, xh1 = d1 * rs;
+      dg0 += dy[u].x * xh0;
+      dg1 += dy[u].y * xh1;
+      const float g0 = dy[u].x * g.x, g1 = dy[u].y * g.y;
+      const float mg = wave_sum(g0 + g1) * (1.0f / kDv);
+      const float mgx = wave_sum(g0 * xh0 + g1 * xh1) * (1.0f / kDv);
+      const float do0 = rs * (g0 - mg - xh0 * mgx), do1 = rs * (g1 - mg - xh1 * mgx);
+      dl -= wave_sum(do0 * o2[u].x + do1 * o2[u].y);
+      // D_m from the fp16 dO the products use, so that sum_j P_ij dP_ij = D_i
+      // holds up to fp32 rounding (at T = 1, dS is then 0 as it must be).
+      const f16x2 hv = {(_Float16)do0, (_Float16)do1};
+      const float h0 = (float)hv[0], h1 = (float)hv[1];
+      const float dd1 = wave_sum(h0 * o1[u].x + h1 * o1[u].y);
+      const float s2 = wave_sum(h0 * o2[u].x + h1 * o2[u].y);
+      *reinterpret_cast<f16x2*>(a.dO + off[u]) = hv;
+      if (lane == 0) *reinterpret_cast<f32x2*>(a.dstat + (off[u] / kDv) * 2) = f32x2{dd1, -lam * s2};
+    }
   }
   red[wave][2 * lane] = dg0;
   red[wave][2 * lane + 1] = dg1;
@@ -112,8 +125,14 @@ __global__ void __launch_bounds__(192) bwd_reduce_kernel(BackwardArgs a) {
   const int h = blockIdx.x, t = threadIdx.x;
   if (t > kDv) return;
   const float* p = a.partial + (int64_t)h * a.nchunks * (kDv + 1) + t;
-  float s = 0.f;
-  for (int c = 0; c < a.nchunks; ++c) s += p[(int64_t)c * (kDv + 1)];
+  // Eight running sums in a fixed order: eight independent loads in flight.
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int c = 0;
+  for (; c + 8 <= a.nchunks; c += 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += p[(int64_t)(c + u) * (kDv + 1)];
+  for (; c < a.nchunks; ++c) acc[0] += p[(int64_t)c * (kDv + 1)];
+  const float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   if (t < kDv)
     a.dgain[(int64_t)h * kDv + t] = s;
   else
