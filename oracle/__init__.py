@@ -47,6 +47,8 @@ def _bind(path):
                                    I64, P, P, I]
     lib.oracle_decode.restype = I
     lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, D, D, I, I, I, D, I64, P, P, I]
+    lib.oracle_grouped.restype = I
+    lib.oracle_grouped.argtypes = [P, P, P, I, I, I, I, I, I, P, P, D, P, I64, P, I]
     lib.oracle_rope.restype = I
     lib.oracle_rope.argtypes = [P, P, I, I, I, I, I, D, I64, P]
     return lib
@@ -194,3 +196,37 @@ def decode(q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens=None, nthreads=0, l
     if rc != 0:
         raise RuntimeError("oracle_decode failed")
     return o, y
+
+
+def grouped(q, k, v, group, lam, gate=None, scale=None, rows=None, nthreads=0, lib=None):
+    """Grouped differential attention with token-wise lambda and output gate,
+    in fp64 (see oracle_grouped in diffattn_oracle.c for the definition and
+    the readings).  q, k: bf16 bits [B, T, n_H, d_qk]; v: [B, T, n_H, d_v];
+    group: g (n_N = n_H / (g + 1) noise heads, n_S = g n_N signal heads);
+    lam: [B, T, n_S]; gate: optional [B, T, n_S, d_v] logits (fp32 values);
+    rows: optional (b, i, s) triples.  Returns [B, T, n_S, d_v] or
+    [n_rows, d_v]."""
+    q, k, v = (_u16(a) for a in (q, k, v))
+    B, T, n_H, d_qk = q.shape
+    d_v = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != (B, T, n_H):
+        raise ValueError("grouped shapes disagree")
+    if group < 1 or n_H % (group + 1):
+        raise ValueError("n_H must be a multiple of group + 1")
+    n_S = group * (n_H // (group + 1))
+    lam = np.ascontiguousarray(lam, dtype=np.float32).reshape(B, T, n_S)
+    g = None if gate is None else np.ascontiguousarray(gate, dtype=np.float32).reshape(B, T, n_S, d_v)
+    scale = 1.0 / np.sqrt(d_qk) if scale is None else float(scale)
+    if rows is None:
+        flat, n = None, B * T * n_S
+    else:
+        r = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+        flat = np.ascontiguousarray((r[:, 0] * T + r[:, 1]) * n_S + r[:, 2])
+        n = flat.shape[0]
+    out = np.empty((n, d_v), dtype=np.float64)
+    rc = (lib or _load()).oracle_grouped(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, T, n_H, int(group), d_qk,
+                                         d_v, lam.ctypes.data, None if g is None else g.ctypes.data, scale,
+                                         None if flat is None else flat.ctypes.data, n, out.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_grouped failed")
+    return out.reshape(B, T, n_S, d_v) if rows is None else out

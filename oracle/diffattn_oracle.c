@@ -322,3 +322,84 @@ int oracle_decode(const uint16_t* q1, const uint16_t* q2, const uint16_t* k1,
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Grouped differential attention with token-wise lambda and an output gate
+ * (picx.dev summary of the Motif 3 report, section 2.2, "Grouped Differential
+ * Attention" and "Output Gating"): n_H heads split into n_S = g n_N signal
+ * heads and n_N = n_H / (g + 1) noise heads.  Each head is ordinary causal
+ * softmax attention with its own query, key and value, H = softmax(Q K^T
+ * scale) V.  Signal head s is paired with noise head Repeat_g(s):
+ *     D_s = H_S,s - lambda_t[s] * H_N,(s / g)
+ *     out_s = sigmoid(G_s) * D_s          (elementwise over d_v; no gate: D_s)
+ * Readings (the pages fix none of these): heads 0 .. n_S-1 are the signal
+ * heads and n_S .. n_H-1 the noise heads; Repeat_g repeats each noise head g
+ * times in place (signal head s uses noise head s / g); no GroupNorm follows
+ * (the GDLA formula applies only the gate).
+ * q, k: bf16 [B, T, n_H, d_qk]; v: bf16 [B, T, n_H, d_v]; lam: fp32 [B, T, n_S];
+ * gate: fp32 [B, T, n_S, d_v] or NULL; rows: flat ((b * T + i) * n_S + s) or NULL
+ * for all; out: fp64 [n_rows, d_v].
+ */
+static void head_row(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kstride, int64_t vstride,
+                     int64_t n_keys, int d_qk, int d_v, double scale, double* p, double* o) {
+    for (int64_t j = 0; j < n_keys; ++j) {
+        double a = 0.0;
+        for (int c = 0; c < d_qk; ++c) a += bf16_to_f64(q[c]) * bf16_to_f64(k[j * kstride + c]);
+        p[j] = scale * a;
+    }
+    softmax_inplace(p, n_keys);
+    for (int c = 0; c < d_v; ++c) o[c] = 0.0;
+    for (int64_t j = 0; j < n_keys; ++j)
+        for (int c = 0; c < d_v; ++c) o[c] += p[j] * bf16_to_f64(v[j * vstride + c]);
+}
+
+int oracle_grouped(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int T, int n_H, int g,
+                   int d_qk, int d_v, const float* lam, const float* gate, double scale, const int64_t* rows,
+                   int64_t n_rows, double* out, int nthreads) {
+    if (B <= 0 || T <= 0 || n_H <= 0 || g <= 0 || n_H % (g + 1) || d_qk <= 0 || d_v <= 0) return -1;
+    const int n_N = n_H / (g + 1), n_S = g * n_N;
+    if (!rows && n_rows != (int64_t)B * T * n_S) return -1;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)T);
+        double* hs = (double*)malloc(sizeof(double) * (size_t)d_v);
+        double* hn = (double*)malloc(sizeof(double) * (size_t)d_v);
+        if (!p || !hs || !hn) {
+            bad = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 16)
+#endif
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t flat = rows ? rows[r] : r;
+                if (flat < 0 || flat >= (int64_t)B * T * n_S) { bad = 1; continue; }
+                int s = (int)(flat % n_S);
+                int64_t i = (flat / n_S) % T;
+                int64_t b = flat / ((int64_t)n_S * T);
+                int hn_head = n_S + s / g;
+                int64_t ks = (int64_t)n_H * d_qk, vs = (int64_t)n_H * d_v;
+                head_row(q + ((b * T + i) * n_H + s) * d_qk, k + (b * T * n_H + s) * (int64_t)d_qk,
+                         v + (b * T * n_H + s) * (int64_t)d_v, ks, vs, i + 1, d_qk, d_v, scale, p, hs);
+                head_row(q + ((b * T + i) * n_H + hn_head) * d_qk, k + (b * T * n_H + hn_head) * (int64_t)d_qk,
+                         v + (b * T * n_H + hn_head) * (int64_t)d_v, ks, vs, i + 1, d_qk, d_v, scale, p, hn);
+                double l = (double)lam[(b * T + i) * n_S + s];
+                for (int c = 0; c < d_v; ++c) {
+                    double d = hs[c] - l * hn[c];
+                    if (gate) {
+                        double gv = (double)gate[((b * T + i) * n_S + s) * (int64_t)d_v + c];
+                        d *= 1.0 / (1.0 + exp(-gv));
+                    }
+                    out[r * d_v + c] = d;
+                }
+            }
+        }
+        free(p);
+        free(hs);
+        free(hn);
+    }
+    return bad ? -1 : 0;
+}

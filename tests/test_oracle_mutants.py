@@ -48,6 +48,10 @@ MUTANTS = {
                                          "int i1 = mode == 1 ? 2 * c + 1 : 2 * c + 1;"),
     "rope query one position late": ("load_rotated(q1 + qoff, qa, d_qk, rope, theta, (double)(pos0 + i));",
                                      "load_rotated(q1 + qoff, qa, d_qk, rope, theta, (double)(pos0 + i + 1));"),
+    "grouped repeat tiled": ("int hn_head = n_S + s / g;", "int hn_head = n_S + s % n_N;"),
+    "grouped gate sign": ("d *= 1.0 / (1.0 + exp(-gv));", "d *= 1.0 / (1.0 + exp(gv));"),
+    "grouped lambda of token 0": ("double l = (double)lam[(b * T + i) * n_S + s];",
+                                  "double l = (double)lam[(b * T) * n_S + s];"),
     "rope decode query at n": ("load_rotated(q1 + qoff, qa, d_qk, rope, theta, (double)(pos0 + n - 1));",
                                "load_rotated(q1 + qoff, qa, d_qk, rope, theta, (double)(pos0 + n));"),
 }
@@ -128,6 +132,42 @@ def _pins(lib):
     if not all(np.array_equal(o[:, :, h], (1.0 - lam[h]) * _f64(x["v"])[:, :, h]) for h in range(2)):
         failed.append("window 1")
     failed += _rope_pins(lib)
+    failed += _grouped_pins(lib)
+    return failed
+
+
+def _grouped_pins(lib):
+    """The grouped-attention pins of tests/test_oracle_grouped.py, compactly."""
+    failed = []
+    q = synth.normal_bf16(84, 1, (1, 9, 8, 8))
+    k = synth.normal_bf16(84, 3, (1, 9, 8, 8))
+    v = synth.normal_bf16(84, 5, (1, 9, 8, 16))
+    lam = synth.uniform_f32(84, 7, (1, 9, 6), 0.0, 1.0)
+    # lambda 0: SDPA on the signal heads
+    out = oracle.grouped(q, k, v, 3, np.zeros_like(lam), lib=lib)
+    qt, kt, vt = (torch.from_numpy(_f64(a)[:, :, :6]).permute(0, 2, 1, 3) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=8 ** -0.5)
+    if not np.allclose(out, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12):
+        failed.append("grouped lambda0")
+    # pairing: noise head 7 feeds signal heads 3-5 only
+    a = oracle.grouped(q, k, v, 3, lam, lib=lib)
+    v2 = v.copy()
+    v2[:, :, 7] = synth.normal_bf16(999, 5, v2[:, :, 7].shape)
+    b = oracle.grouped(q, k, v2, 3, lam, lib=lib)
+    if not (np.array_equal(a[:, :, :3], b[:, :, :3]) and np.all(np.abs(a[:, :, 3:] - b[:, :, 3:]).max(axis=(0, 1, 3)) > 1e-6)):
+        failed.append("grouped pairing")
+    # the gate against torch.sigmoid
+    g = synth.normal_f32(84, 8, (1, 9, 6, 16), std=3.0)
+    gated = oracle.grouped(q, k, v, 3, lam, gate=g, lib=lib)
+    if not np.allclose(gated, a * torch.sigmoid(torch.from_numpy(g.astype(np.float64))).numpy(), rtol=1e-13, atol=1e-15):
+        failed.append("grouped gate")
+    # token-wise lambda: the difference from lambda 0 scales with each row's own lambda
+    lam2 = lam.copy()
+    lam2[0, 5, 1] += 0.25
+    c = oracle.grouped(q, k, v, 3, lam2, lib=lib)
+    d = np.abs(a - c).max(axis=3)
+    if not (d[0, 5, 1] > 0 and np.count_nonzero(d) == 1):
+        failed.append("grouped token lambda")
     return failed
 
 
