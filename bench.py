@@ -37,6 +37,9 @@ FLOP_PER_PAIR = 768
 # Backward: recomputed scores (2 x 128) + dP (256, shared by the maps since
 # dO_2 = -lambda dO_1) + dV (256) + dQ (2 x 128) + dK (2 x 128) per pair.
 BWD_FLOP_PER_PAIR = 1280
+# Grouped attention: every head is one softmax map with its own values:
+# 2 x 64 (scores) + 2 x 128 (P V) per pair and head.
+GROUPED_FLOP_PER_PAIR_HEAD = 384
 PREFILL_WL = "prefill_b1_t4096_h16"
 DECODE_WL = "decode_b64_l4096_h16"
 SWA_PREFILL_WL = "swa_b1_t16384_h16_w128"
@@ -134,7 +137,8 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     """The variant rows, timed after, and outside, the step's timed region:
     Motif 3's sliding-window layer type (128-token windows) as the windowed
     prefill at T=16384 and the windowed decode over the 4096-long caches, the
-    T=4096 prefill with the fused RoPE prologue, and the T=4096 backward."""
+    T=4096 prefill with the fused RoPE prologue, the T=4096 backward, and
+    the grouped form (Motif 3) on the same 16-head T=4096 shape."""
     import synth
 
     pw = synth.WORKLOADS[SWA_PREFILL_WL]
@@ -185,10 +189,24 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
         da.diffattn_bwd_prefill(B_["q1"], B_["q2"], B_["k1"], B_["k2"], B_["v"], rw.lam, bgain, bo1, bo2, blse, bdy,
                                 eps=rw.eps, scale=rw.scale, workspace=bws, grads=bgr)
 
+    # grouped attention (Motif 3 form): 16 heads, g = 3, token-wise lambda, gate
+    gq, gk = to_dev(bx["q1"], dev), to_dev(bx["k1"], dev)
+    gv = B_["v"]
+    glam = torch.from_numpy(synth.uniform_f32(rw.seed, 7, (rw.B, rw.T, 12), 0.0, 1.0)).to(dev)
+    ggate = to_dev(synth.f32_to_bf16_bits(synth.normal_f32(rw.seed, 8, (rw.B, rw.T, 12, rw.d_v), std=2.0)), dev)
+    gws = torch.empty(da.diffattn_grouped_workspace_bytes(rw.B, rw.T, rw.H, 3, rw.d_v), dtype=torch.uint8, device=dev)
+    gout = torch.empty((rw.B, rw.T, 12, rw.d_v), dtype=torch.bfloat16, device=dev)
+
+    def grouped():
+        da.diffattn_fwd_grouped(gq, gk, gv, 3, glam, gate=ggate, out=gout, workspace=gws)
+
     p_us, p_min = _time_calls(torch, np, prefill, warmup, iters)
     d_us, d_min = _time_calls(torch, np, decode, warmup, iters)
     r_us, r_min = _time_calls(torch, np, prefill_rope, warmup, iters)
     bw_us, bw_min = _time_calls(torch, np, backward, warmup // 3, iters)
+    g_us, g_min = _time_calls(torch, np, grouped, warmup, iters)
+    assert bool(torch.isfinite(gout.float()).all())
+    g_flop = rw.causal_pairs * GROUPED_FLOP_PER_PAIR_HEAD  # causal_pairs already counts the 16 heads
     assert all(bool(torch.isfinite(t).all()) for t in bgr.values())
     bw_flop = rw.causal_pairs * BWD_FLOP_PER_PAIR
     assert bool(torch.isfinite(r_out.float()).all())
@@ -197,6 +215,10 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     p_flop = pw.causal_pairs * FLOP_PER_PAIR
     d_bytes = decode_bytes(dw)
     return {
+        "grouped": {"workload": "B=1 T=4096 16 heads (12 signal, 4 noise, g=3), token-wise lambda, gate",
+                    "us_mean": round(g_us, 2), "us_min": round(g_min, 2),
+                    "tflops": round(g_flop / g_us / 1e6, 2),
+                    "frac_mfma_peak": round(g_flop / g_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},
         "backward": {"workload": PREFILL_WL, "us_mean": round(bw_us, 2), "us_min": round(bw_min, 2),
                      "flop_per_pair": BWD_FLOP_PER_PAIR, "tflops": round(bw_flop / bw_us / 1e6, 2),
                      "frac_mfma_peak": round(bw_flop / bw_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},

@@ -26,6 +26,8 @@ __all__ = [
     "diffattn_fwd_prefill_train",
     "diffattn_bwd_workspace_bytes",
     "diffattn_bwd_prefill",
+    "diffattn_grouped_workspace_bytes",
+    "diffattn_fwd_grouped",
     "diffattn_decode_workspace_bytes",
     "diffattn_status_string",
     "diffattn_abi_version",
@@ -42,7 +44,7 @@ OUT_F32 = 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdiffattn.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libdiffattn.so is not built; run `python -m differential_attention_causal_amd.build` "
+        "libdiffattn.so is not built; run `python differential_attention_causal_amd/build.py` "
         "(or __graft_entry__.build()) first"
     )
 
@@ -86,6 +88,11 @@ _lib.diffattn_bwd_prefill.restype = _I
 _lib.diffattn_bwd_prefill.argtypes = ([_P, _P, _P, _P, _P, ctypes.POINTER(_Strides), _I, _I, _I, _I, _I, ctypes.c_float,
                                       _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P, _I]
                                      + [_P] * 7 + [_P, ctypes.c_size_t, _P])
+_lib.diffattn_grouped_workspace_bytes.restype = ctypes.c_size_t
+_lib.diffattn_grouped_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+_lib.diffattn_fwd_grouped.restype = _I
+_lib.diffattn_fwd_grouped.argtypes = [_P, _P, _P, ctypes.POINTER(_Strides), _I, _I, _I, _I, _I, _I, _P, _P,
+                                      ctypes.c_float, _P, _I, _P, ctypes.c_size_t, _P]
 _lib.diffattn_status_string.restype = ctypes.c_char_p
 _lib.diffattn_status_string.argtypes = [_I]
 _lib.diffattn_abi_version.restype = _I
@@ -340,6 +347,42 @@ def diffattn_bwd_prefill(q1, q2, k1, k2, v, lam, gain, o1, o2, lse, dy, eps=1e-5
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc)
     return grads
+
+
+def diffattn_grouped_workspace_bytes(B: int, T: int, n_heads: int, group: int, d_v: int = D_V) -> int:
+    return int(_lib.diffattn_grouped_workspace_bytes(B, T, n_heads, group, d_v))
+
+
+def diffattn_fwd_grouped(q, k, v, group, lambda_t, gate=None, scale=0.0, out=None, out_dtype=torch.bfloat16,
+                         workspace=None, stream=None):
+    """Grouped differential attention (signal heads first, signal head s paired
+    with noise head n_S + s // group), token-wise lambda_t (fp32 [B, T, n_S]),
+    optional bf16 gate logits [B, T, n_S, 128].  q, k: bf16 [B, T, n_heads, 64];
+    v: bf16 [B, T, n_heads, 128].  Returns out [B, T, n_S, 128]."""
+    B, T, n_heads, d_qk = q.shape
+    d_v = v.shape[3]
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError("q, k, v must be bf16 device tensors")
+    if group < 1 or n_heads % (group + 1):
+        raise ValueError("n_heads must be a multiple of group + 1")
+    n_S = group * (n_heads // (group + 1))
+    if (lambda_t.dtype != torch.float32 or tuple(lambda_t.shape) != (B, T, n_S) or not lambda_t.is_contiguous()):
+        raise ValueError("lambda_t must be a contiguous fp32 [B, T, n_S] tensor")
+    if gate is not None and (gate.dtype != torch.bfloat16 or tuple(gate.shape) != (B, T, n_S, d_v)
+                             or not gate.is_contiguous()):
+        raise ValueError("gate must be a contiguous bf16 [B, T, n_S, d_v] tensor")
+    if out is None:
+        out = torch.empty((B, T, n_S, d_v), dtype=out_dtype, device=q.device)
+    need = diffattn_grouped_workspace_bytes(B, T, n_heads, group, d_v)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = (_Strides * 3)(*[_strides4(t) for t in (q, k, v)])
+    rc = _lib.diffattn_fwd_grouped(_ptr(q), _ptr(k), _ptr(v), st, B, T, n_heads, int(group), d_qk, d_v,
+                                   _ptr(lambda_t), _ptr(gate), float(scale), _ptr(out), _out_code(out.dtype),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+    return out
 
 
 def default_scale(d_qk: int = D_QK) -> float:

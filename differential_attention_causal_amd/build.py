@@ -1,6 +1,8 @@
 """Builds libdiffattn.so in place: hipcc for gfx950, one object per source.
 
-    python -m differential_attention_causal_amd.build
+    python differential_attention_causal_amd/build.py
+
+(run as a script: importing the package would load the library it builds).
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ COMMON = [
     # with VALU ops, and AGPR accumulators cost a copy each way per key tile
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
-SOURCES = ["prefill.hip", "decode.hip", "rope.hip", "backward.hip", "api.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "rope.hip", "backward.hip", "grouped.hip", "api.cpp"]
 
 
 def _compile(src: str) -> str:

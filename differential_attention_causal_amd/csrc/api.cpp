@@ -74,7 +74,7 @@ float score_factor(float scale) {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 103; }
+int diffattn_abi_version(void) { return 104; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -381,6 +381,57 @@ int diffattn_rope_apply(const void* x, const diffattn_strides* x_strides, void* 
   a.rope.pos0 = (uint32_t)pos0;
   diffattn::rope_phases(theta, a.rope);
   if (diffattn::launch_rope_apply(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
+  return DIFFATTN_OK;
+}
+
+size_t diffattn_grouped_workspace_bytes(int B, int T, int n_heads, int group, int d_v) {
+  if (B <= 0 || T <= 0 || n_heads <= 0 || group <= 0 || n_heads % (group + 1) != 0 || d_v != kDv) return 0;
+  return (size_t)B * T * n_heads * kDv * sizeof(float);
+}
+
+int diffattn_fwd_grouped(const void* q, const void* k, const void* v, const diffattn_strides* strides, int B, int T,
+                         int n_heads, int group, int d_qk, int d_v, const float* lambda_t, const void* gate,
+                         float scale, void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!q || !k || !v || !lambda_t || !out) return DIFFATTN_ERR_NULL;
+  if (B <= 0 || T <= 0 || T > (1 << 22) || n_heads <= 0 || group <= 0) return DIFFATTN_ERR_SHAPE;
+  if (n_heads % (group + 1) != 0) return DIFFATTN_ERR_SHAPE;
+  if ((int64_t)B * n_heads > (int64_t(1) << 24)) return DIFFATTN_ERR_SHAPE;
+  if ((int64_t)((T + 127) / 128) * B * n_heads > kMaxWorkgroups) return DIFFATTN_ERR_SHAPE;
+  if (d_qk != kDqk || d_v != kDv) return DIFFATTN_ERR_UNSUPPORTED;
+  if (std::isnan(scale) || std::isinf(scale)) return DIFFATTN_ERR_VALUE;
+  if (out_dtype != DIFFATTN_OUT_BF16 && out_dtype != DIFFATTN_OUT_F32) return DIFFATTN_ERR_VALUE;
+  const void* ptrs[] = {q, k, v, lambda_t, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return DIFFATTN_ERR_LAYOUT;
+  if (gate && (reinterpret_cast<uintptr_t>(gate) & 7u) != 0) return DIFFATTN_ERR_LAYOUT;
+  diffattn_strides st[3];
+  for (int i = 0; i < 3; ++i) {
+    st[i] = strides ? strides[i] : contiguous(T, n_heads, i == 2 ? d_v : d_qk);
+    if (!strides_ok(st[i])) return DIFFATTN_ERR_LAYOUT;
+  }
+  if (!workspace || !aligned16(workspace)) return DIFFATTN_ERR_WORKSPACE;
+  if (workspace_bytes < diffattn_grouped_workspace_bytes(B, T, n_heads, group, d_v)) return DIFFATTN_ERR_WORKSPACE;
+  diffattn::GroupedArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sq = to_internal(st[0]);
+  a.sk = to_internal(st[1]);
+  a.sv = to_internal(st[2]);
+  a.B = B;
+  a.T = T;
+  a.nH = n_heads;
+  a.g = group;
+  a.nN = n_heads / (group + 1);
+  a.nS = group * a.nN;
+  a.c = score_factor(scale);
+  a.lam = lambda_t;
+  a.gate = static_cast<const uint16_t*>(gate);
+  a.out = out;
+  a.out_f32 = out_dtype == DIFFATTN_OUT_F32;
+  a.hw = static_cast<float*>(workspace);
+  if (diffattn::launch_grouped(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
   return DIFFATTN_OK;
 }
 

@@ -124,6 +124,25 @@ struct BackwardArgs {
   int nchunks;
 };
 
+// Grouped differential attention with token-wise lambda and output gate:
+// n_H = nS + nN heads, signal heads 0 .. nS-1, noise heads nS .. n_H-1,
+// signal head s paired with noise head nS + s / g.
+struct GroupedArgs {
+  const uint16_t* q;  // [B, T, n_H, kDqk] with strides
+  const uint16_t* k;
+  const uint16_t* v;  // [B, T, n_H, kDv] with strides
+  Strides sq, sk, sv;
+  int B, T, nH, g, nN, nS;
+  float c;               // scale * log2(e)
+  const float* lam;      // [B, T, nS] fp32
+  const uint16_t* gate;  // [B, T, nS, kDv] bf16 logits, or null
+  void* out;             // [B, T, nS, kDv] bf16 or fp32
+  int out_f32;
+  float* hw;             // workspace [B, T, nH, kDv] fp32: every head's normalised output
+};
+
+hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream);
+
 // Rows (b, t) of one head per workgroup of the backward's first kernel.
 constexpr int kBwdRowsPerChunk = 64;
 

@@ -51,12 +51,7 @@ constexpr int kVRow = (kBN + 8) * 2;        // 80 bytes per V^T channel row (16-
 constexpr int kVBytes = kDv * kVRow;        // 10 KiB per V^T tile
 constexpr int kTile = 2 * kKBytes + kVBytes;
 constexpr int kTileThreads = 256;           // threads that stage one tile
-// End-of-loop merge buffer (reuses the stage memory): one map's O^T of the four
-// group-1 waves stored [wave][register][lane], then their (max, sum) pairs.
-constexpr int kMergeO = kGroupWaves * 64 * 64 * 4;
-constexpr int kMergeML = kGroupWaves * 64 * 2 * 4;
-static_assert(kMergeO + kMergeML <= 2 * 2 * kTile, "merge buffer must fit in the stage memory");
-constexpr float kSlack = 8.0f;
+static_assert(kMergeBytes <= 2 * 2 * kTile, "merge buffer must fit in the stage memory");
 
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -258,81 +253,6 @@ __device__ __forceinline__ void rope_query(bf16x8 (&q1)[4], bf16x8 (&q2)[4], int
     q1[s] = __builtin_bit_cast(bf16x8, rope_pack<true>(x1[s]));
     q2[s] = __builtin_bit_cast(bf16x8, rope_pack<true>(x2[s]));
   }
-}
-
-// One map's online-softmax step on a 32x32 score tile held as S^T (lane: one
-// query, 16 keys).  Keeps the running reference max m (base-2 units) unless
-// a score lies more than kSlack above it: only when some lane of the wave sees
-// one are the two lanes of each query pair reconciled, and the queries over
-// the bound raise m to their tile max and rescale that map's O^T and partial
-// sum l.  Returns the tile's probabilities
-// 2^(c s - m) <= 2^kSlack as the two f16 operands of the P^T V^T product.
-__device__ __forceinline__ void softmax_step(f32x16& s, float c, float& m, float& l, f32x16 (&O)[4],
-                                             f16x8& p0, f16x8& p1) {
-  float mx = s[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-  if (__any(mx * c > m + kSlack)) {
-    // Each query decides from its own scores only (its two lanes agree after
-    // the exchange), so a row's result never depends on other rows' data.
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mc = mx * c;
-    const float mn = mc > m + kSlack ? mc : m;
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    l *= alpha;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) O[cb] *= alpha;
-    m = mn;
-  }
-  float p[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m));
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    p0[j] = (_Float16)p[j];
-    p1[j] = (_Float16)p[8 + j];
-  }
-  // The sum runs over the rounded f16 values the product uses, two per
-  // instruction (dot product with (1, 1), fp32 accumulation).
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-  float sum = l;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sum = __builtin_amdgcn_fdot2(f16x2{p0[2 * j], p0[2 * j + 1]}, one, sum, false);
-    sum = __builtin_amdgcn_fdot2(f16x2{p1[2 * j], p1[2 * j + 1]}, one, sum, false);
-  }
-  l = sum;
-}
-
-// Merge one map's (m, l, O^T) of a group-1 wave into the matching group-0 wave
-// through LDS.  Every thread of the workgroup calls it (it holds two barriers).
-__device__ __forceinline__ void merge_map(char* smem, int grp, int wq, int lane, bool live, float& m, float& l,
-                                          f32x16 (&O)[4]) {
-  float* mo = reinterpret_cast<float*>(smem);
-  float* ml = reinterpret_cast<float*>(smem + kMergeO);
-  if (grp == 1 && live) {
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mo[((wq * 64) + cb * 16 + i) * 64 + lane] = O[cb][i];
-    ml[(wq * 64 + lane) * 2 + 0] = m;
-    ml[(wq * 64 + lane) * 2 + 1] = l;
-  }
-  __syncthreads();
-  if (grp == 0 && live) {
-    const float mb = ml[(wq * 64 + lane) * 2 + 0];
-    const float lb = ml[(wq * 64 + lane) * 2 + 1];
-    const float mn = fmaxf(m, mb);  // every query sees at least itself
-    const float aa = __builtin_amdgcn_exp2f(m - mn);
-    const float ab = __builtin_amdgcn_exp2f(mb - mn);
-    l = l * aa + lb * ab;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) O[cb][i] = O[cb][i] * aa + mo[((wq * 64) + cb * 16 + i) * 64 + lane] * ab;
-    m = mn;
-  }
-  __syncthreads();
 }
 
 // kGroups wave groups of four waves share a workgroup's 128 queries and split

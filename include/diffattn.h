@@ -262,12 +262,44 @@ DIFFATTN_API int diffattn_bwd_prefill(const void* q1, const void* q2, const void
                                       float* dq2, float* dk1, float* dk2, float* dv, float* dlambda,
                                       float* dgain, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Grouped differential attention with a token-wise lambda and an output gate
+ * (picx.dev summary of the Motif 3 report, section 2.2, "Grouped
+ * Differential Attention" and "Output Gating"), causal prefill:
+ *   n_heads = n_S + n_N heads with n_N = n_heads / (group + 1) noise heads
+ *   and n_S = group * n_N signal heads; heads 0 .. n_S-1 are the signal heads,
+ *   n_S .. n_heads-1 the noise heads, and signal head s is paired with noise
+ *   head n_S + s / group (each noise head repeated group times in place).
+ *   Every head is ordinary causal softmax attention with its own values,
+ *   H_h = softmax(Q_h K_h^T * scale) V_h, and
+ *     out_s = sigmoid(G_s) * (H_s - lambda_t[s] * H_(n_S + s / group))
+ *   with no GroupNorm (the formula applies only the gate).
+ *   q, k        : bf16 [B, T, n_heads, d_qk];  v : bf16 [B, T, n_heads, d_v]
+ *   strides     : 3 entries for q, k, v, or NULL (C-contiguous)
+ *   lambda_t    : device fp32 [B, T, n_S], C-contiguous (any finite values;
+ *                 the model's sigmoid output lies in (0, 1))
+ *   gate        : device bf16 [B, T, n_S, d_v] gate logits G, C-contiguous
+ *                 and 8-byte aligned, or NULL for no gate
+ *   scale       : score factor; <= 0 selects 1/sqrt(d_qk)
+ *   out         : [B, T, n_S, d_v] bf16 or fp32 per out_dtype
+ *   workspace   : >= diffattn_grouped_workspace_bytes() bytes, 16-byte
+ *                 aligned: every head's normalised output (fp32), each noise
+ *                 head's computed once
+ * Errors: DIFFATTN_ERR_SHAPE also when n_heads is not a multiple of group + 1.
+ */
+DIFFATTN_API size_t diffattn_grouped_workspace_bytes(int B, int T, int n_heads, int group, int d_v);
+DIFFATTN_API int diffattn_fwd_grouped(const void* q, const void* k, const void* v,
+                                      const diffattn_strides* strides, int B, int T, int n_heads, int group,
+                                      int d_qk, int d_v, const float* lambda_t, const void* gate, float scale,
+                                      void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
 /* Static text for a status code (never NULL). */
 DIFFATTN_API const char* diffattn_status_string(int status);
 
 /* Library ABI version (major * 100 + minor): 101 adds the *_ex entry points,
  * 102 the rotary embedding (diffattn_options.rope, diffattn_rope_apply), 103
- * the training forward and the backward pass. */
+ * the training forward and the backward pass, 104 grouped attention. */
 DIFFATTN_API int diffattn_abi_version(void);
 
 #ifdef __cplusplus

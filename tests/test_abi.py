@@ -26,11 +26,12 @@ def test_header_symbols_exported():
     assert set(names) == {"diffattn_fwd_prefill", "diffattn_fwd_decode", "diffattn_decode_workspace_bytes",
                           "diffattn_fwd_prefill_ex", "diffattn_fwd_decode_ex", "diffattn_rope_apply",
                           "diffattn_fwd_prefill_train", "diffattn_bwd_workspace_bytes", "diffattn_bwd_prefill",
+                          "diffattn_grouped_workspace_bytes", "diffattn_fwd_grouped",
                           "diffattn_status_string", "diffattn_abi_version"}
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 103
+    assert da.diffattn_abi_version() == 104
 
 
 def test_status_strings():
@@ -201,3 +202,30 @@ def test_bwd_workspace_bytes():
     assert n >= rows * 128 * 2 + rows * 2 * 4 + 3 * ((200 + 63) // 64) * 129 * 4 and n % 256 == 0
     assert da.diffattn_bwd_workspace_bytes(0, 100, 3, 128) == 0
     assert da.diffattn_bwd_workspace_bytes(1, 100, 3, 64) == 0
+
+
+def _grouped(**kw):
+    need = da.diffattn_grouped_workspace_bytes(1, 128, 8, 3, 128)
+    args = dict(q=A, k=A, v=A, st=None, B=1, T=128, nh=8, g=3, dqk=64, dv=128, lam=A, gate=None, scale=0.0, out=A,
+                odt=0, ws=A, wsb=need, stream=None)
+    args.update(kw)
+    return da._lib.diffattn_fwd_grouped(*args.values())
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(q=None), ENULL), (dict(lam=None), ENULL), (dict(out=None), ENULL), (dict(B=0), ESHAPE),
+    (dict(T=0), ESHAPE), (dict(nh=6), ESHAPE), (dict(g=0), ESHAPE), (dict(nh=9, g=2), OK - 99),
+    (dict(dqk=128), EUNSUP), (dict(scale=float("nan")), EVALUE), (dict(odt=5), EVALUE), (dict(k=A + 2), ELAYOUT),
+    (dict(gate=A + 4), ELAYOUT), (dict(ws=None), EWS), (dict(wsb=16), EWS),
+])
+def test_grouped_rejects(kw, rc):
+    if rc == OK - 99:  # valid shape (9 heads, g = 2): stops at the workspace size instead
+        assert _grouped(**kw) == EWS
+    else:
+        assert _grouped(**kw) == rc
+
+
+def test_grouped_workspace_bytes():
+    assert da.diffattn_grouped_workspace_bytes(2, 100, 8, 3, 128) == 2 * 100 * 8 * 128 * 4
+    assert da.diffattn_grouped_workspace_bytes(2, 100, 8, 2, 128) == 0
+    assert da.diffattn_grouped_workspace_bytes(2, 100, 8, 3, 64) == 0
