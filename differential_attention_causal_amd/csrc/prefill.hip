@@ -9,14 +9,21 @@
 // Work split.  A workgroup owns 128 consecutive queries of one (b, h); within
 // a group of four wave64s, wave w takes queries 32w .. 32w+31.  Keys stream
 // through LDS in 32-key tiles; tiles past the causal diagonal are never
-// loaded, and a wave skips tiles past its own diagonal.  Two launch shapes:
-//   - one group (4 waves): the default; two workgroups share a CU, and a grid
-//     larger than the chip balances itself in longest-first order;
-//   - two groups (8 waves) that take alternate tiles of the causal range
-//     (group 0 the even ones, group 1 the odd ones), each with its own softmax
-//     states and accumulators, merged through LDS at the end.  For a grid that
-//     fits on the chip in one round, this halves the run time of the longest
-//     query blocks, which would otherwise finish alone.
+// loaded, and a wave skips tiles past its own diagonal.  Launch shapes:
+//   - ping-pong (prefill_pp_kernel, 8 waves): two groups take alternate tiles
+//     of the causal range (group 0 the even ones, group 1 the odd ones), each
+//     with its own softmax states and accumulators, merged through LDS at the
+//     end; group 1 runs half a step behind group 0, so that on every SIMD one
+//     wave's matrix products run while the other wave does its softmax.  Used
+//     for grids that fit on the chip in one round (two workgroups per CU in
+//     longest-first order then sum to the same work on every CU), without the
+//     rotary embedding;
+//   - one group (4 waves, prefill_kernel<1, .>): two workgroups share a CU,
+//     and a grid larger than the chip balances itself in longest-first order;
+//   - two groups in lock step (prefill_kernel<2, .>): the split of the
+//     ping-pong kernel without its phase offset, for small grids with the
+//     rotary embedding (keys rotated while staged) or key spans past 2^31
+//     bytes.
 //
 // Transposed products.  Each wave computes S^T = K Q^T (32 keys x 32 queries)
 // on v_mfma_f32_32x32x16_bf16 with K from LDS and Q^T held in registers for the
@@ -35,6 +42,8 @@
 // accumulation.  The running max is only raised when a tile's max exceeds it
 // by more than kSlack (base 2), so P <= 2^kSlack stays far inside fp16 range and
 // the O rescale is rare after the first tiles.
+#include <algorithm>
+
 #include "kernels.h"
 #include "rope.h"
 #include "tile.h"
@@ -55,7 +64,6 @@ static_assert(kMergeBytes <= 2 * 2 * kTile, "merge buffer must fit in the stage 
 
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 load8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 struct Staged {
   u32x4 k1, k2;
@@ -255,6 +263,453 @@ __device__ __forceinline__ void rope_query(bf16x8 (&q1)[4], bf16x8 (&q2)[4], int
   }
 }
 
+// GroupNorm over the 128 channels of the query (o in O, lane (hf, lq)
+// holding channels 32cb + 8(i/4) + 4hf + i%4, its partner lane the other 64),
+// then the stores.  g: the head's gain (global or shared memory).
+__device__ __forceinline__ void norm_store(const PrefillArgs& a, int b, int head, int q, int hf, f32x16 (&O)[4],
+                                           const float* g) {
+  float sum = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += O[cb][i];
+  sum += __shfl_xor(sum, 32);
+  const float mu = sum * (1.0f / kDv);
+  float ss = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float d = O[cb][i] - mu;
+      ss += d * d;
+    }
+  }
+  ss += __shfl_xor(ss, 32);
+  const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / kDv) + a.eps);
+
+  if (q >= a.T) return;
+  const int64_t row = (((int64_t)b * a.T + q) * a.H + head) * kDv;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int ch = 32 * cb + 8 * r4 + 4 * hf;
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(g + ch);
+      f32x4 o, y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        o[r] = O[cb][4 * r4 + r];
+        y[r] = (o[r] - mu) * inv * gv[r];
+      }
+      if (a.o_pre) *reinterpret_cast<f32x4*>(a.o_pre + row + ch) = o;
+      if (a.out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row + ch) = y;
+      } else {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 yb = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+        *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(a.out) + row + ch) = yb;
+      }
+    }
+  }
+}
+
+// Fold the two wave groups' softmax states of each query and form the
+// differential output o = O1 / l1 - lambda O2 / l2 in group 0's O1: both
+// groups exchange (m, l) per map, weight their own accumulators, and group
+// 1's part of o crosses LDS once.  Both groups compute the merged sums with
+// the same operations (sums of two terms, commutative), so their weights
+// agree bit for bit.  kTrain adds the training outputs (each map's O_m / l_m
+// and log-sum-exp) through two more exchanges; o is computed the same way
+// either way, so the training forward's y equals the plain forward's.  Every
+// thread calls it (the barriers are unconditional).
+template <bool kTrain>
+__device__ __forceinline__ void merge_out(const PrefillArgs& a, char* smem, int grp, int wq, int lane, bool live,
+                                          float lam, int b, int head, int q, int hf, float m1, float l1, float m2,
+                                          float l2, f32x16 (&O1)[4], f32x16 (&O2)[4]) {
+  float* mo = reinterpret_cast<float*>(smem);
+  f32x4* ml = reinterpret_cast<f32x4*>(smem + kMergeO);  // [group][wave][lane]: m1, l1, m2, l2
+  auto slot = [&](int cb, int i) { return ((wq * 64) + cb * 16 + i) * 64 + lane; };
+  if (live) ml[(grp * 4 + wq) * 64 + lane] = f32x4{m1, l1, m2, l2};
+  __syncthreads();
+  float M1 = 0.f, M2 = 0.f, a1 = 0.f, a2 = 0.f, L1 = 1.f, L2 = 1.f;
+  if (live) {
+    const f32x4 ot = ml[((grp ^ 1) * 4 + wq) * 64 + lane];
+    M1 = fmaxf(m1, ot[0]);
+    M2 = fmaxf(m2, ot[2]);
+    a1 = __builtin_amdgcn_exp2f(m1 - M1);
+    a2 = __builtin_amdgcn_exp2f(m2 - M2);
+    L1 = l1 * a1 + ot[1] * __builtin_amdgcn_exp2f(ot[0] - M1);
+    L2 = l2 * a2 + ot[3] * __builtin_amdgcn_exp2f(ot[2] - M2);
+  }
+  L1 += __shfl_xor(L1, 32);
+  L2 += __shfl_xor(L2, 32);
+  if constexpr (kTrain) {
+    // O_m / l_m of each map, summed over the two groups.
+    const int64_t rq = ((int64_t)b * a.T + q) * a.H + head;
+#pragma unroll
+    for (int map = 0; map < 2; ++map) {
+      f32x16 (&O)[4] = map == 0 ? O1 : O2;
+      float* dst = map == 0 ? a.o1n : a.o2n;
+      const float w = map == 0 ? a1 / L1 : a2 / L2;
+      if (grp == 1 && live) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mo[slot(cb, i)] = O[cb][i] * w;
+      }
+      __syncthreads();
+      if (grp == 0 && live && q < a.T) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = O[cb][4 * r4 + r] * w + mo[slot(cb, 4 * r4 + r)];
+            *reinterpret_cast<f32x4*>(dst + rq * kDv + 32 * cb + 8 * r4 + 4 * hf) = v;
+          }
+      }
+      __syncthreads();
+    }
+    if (grp == 0 && live && q < a.T && hf == 0) {
+      a.lse[rq * 2] = M1 + __builtin_log2f(L1);
+      a.lse[rq * 2 + 1] = M2 + __builtin_log2f(L2);
+    }
+  }
+  if (live) {
+    const float w1 = a1 / L1, w2 = lam * a2 / L2;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        // both products rounded before the subtraction (no FMA contraction):
+        // two identical maps at lambda = 1 cancel to exactly zero
+#pragma clang fp contract(off)
+        O1[cb][i] = O1[cb][i] * w1 - O2[cb][i] * w2;
+      }
+    if (grp == 1) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mo[slot(cb, i)] = O1[cb][i];
+    }
+  }
+  __syncthreads();
+  if (grp == 0 && live) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O1[cb][i] += mo[slot(cb, i)];
+  }
+}
+
+// Combine the two maps of one query row (lane pair) from their final softmax
+// states, write the training outputs if asked, then GroupNorm and store.
+__device__ __forceinline__ void finish_rows(const PrefillArgs& a, int b, int head, int q, int hf, float m1, float m2,
+                                            float l1, float l2, f32x16 (&O1)[4], f32x16 (&O2)[4]) {
+  l1 += __shfl_xor(l1, 32);
+  l2 += __shfl_xor(l2, 32);
+  if (a.o1n != nullptr && q < a.T) {
+    // Training outputs for the backward pass.
+    const int64_t rq = ((int64_t)b * a.T + q) * a.H + head;
+    const float i1 = 1.0f / l1, i2 = 1.0f / l2;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ch = 32 * cb + 8 * r4 + 4 * hf;
+        f32x4 v1, v2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v1[r] = O1[cb][4 * r4 + r] * i1;
+          v2[r] = O2[cb][4 * r4 + r] * i2;
+        }
+        *reinterpret_cast<f32x4*>(a.o1n + rq * kDv + ch) = v1;
+        *reinterpret_cast<f32x4*>(a.o2n + rq * kDv + ch) = v2;
+      }
+    if (hf == 0) {
+      a.lse[rq * 2] = m1 + __builtin_log2f(l1);
+      a.lse[rq * 2 + 1] = m2 + __builtin_log2f(l2);
+    }
+  }
+  const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
+  const float r1 = 1.0f / l1;
+  const float r2 = lam / l2;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // Both products rounded before the subtraction (no FMA contraction), so
+      // two identical maps at lambda = 1 cancel to exactly zero.
+#pragma clang fp contract(off)
+      O1[cb][i] = O1[cb][i] * r1 - O2[cb][i] * r2;
+    }
+  }
+  norm_store(a, b, head, q, hf, O1, a.gain + (int64_t)head * kDv);
+}
+
+// Waits: vmcnt(n) alone, lgkmcnt(0) alone (gfx9 s_waitcnt encoding).
+template <int n>
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70); }
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier with no memory wait of its own; the asm memory clobber
+// keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// S^T = K Q^T of one tile for both maps (bf16 operands, K from LDS).
+__device__ __forceinline__ void scores_tile(const char* kt, int lq, int hf, int ksw, const bf16x8 (&qa)[4],
+                                            const bf16x8 (&qb2)[4], f32x16& s1, f32x16& s2) {
+  s1 = f32x16{};
+  s2 = f32x16{};
+  const int krow = lq * kKRow;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int off = krow + (((2 * s + hf) ^ ksw) << 4);
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + off);
+    const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kt + kKBytes + off);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qa[s], s1, 0, 0, 0);
+    s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qb2[s], s2, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void mask_tile(const PrefillArgs& a, f32x16& s1, f32x16& s2, int j, int wave_last_tile,
+                                          int q_first, int q, int hf) {
+  // Key row kr = 8(i/4) + 4hf + i%4 of tile j is key 32j + kr: visible to
+  // query q iff it is <= q (and > q - window).  The bounds depend on j, so the
+  // compiler keeps the compares inside the loop instead of holding sixteen
+  // lane masks.
+  if (j == wave_last_tile) {
+    const int hi = q - j * kBN - 4 * hf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (8 * (i >> 2) + (i & 3) > hi) {
+        s1[i] = -__builtin_inff();
+        s2[i] = -__builtin_inff();
+      }
+    }
+  }
+  if (a.window > 0 && j * kBN < q_first + 32 - a.window) {
+    const int lo = q - a.window - j * kBN - 4 * hf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (8 * (i >> 2) + (i & 3) <= lo) {
+        s1[i] = -__builtin_inff();
+        s2[i] = -__builtin_inff();
+      }
+    }
+  }
+}
+
+// Two 32-channel blocks of O += V P for both maps, ordered so that
+// consecutive products never share an accumulator.
+__device__ __forceinline__ void pv_pair(const char* kt, int lq, int hf, int cb, const f16x8& p1a, const f16x8& p1b,
+                                        const f16x8& p2a, const f16x8& p2b, f32x16 (&O1)[4], f32x16 (&O2)[4]) {
+  const char* vt = kt + 2 * kKBytes + lq * kVRow + hf * 16 + cb * 32 * kVRow;
+  const f16x8 a0 = *reinterpret_cast<const f16x8*>(vt);
+  const f16x8 b0 = *reinterpret_cast<const f16x8*>(vt + 32 * kVRow);
+  O1[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, p1a, O1[cb], 0, 0, 0);
+  O2[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, p2a, O2[cb], 0, 0, 0);
+  O1[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, p1a, O1[cb + 1], 0, 0, 0);
+  O2[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, p2a, O2[cb + 1], 0, 0, 0);
+  const f16x8 a1 = *reinterpret_cast<const f16x8*>(vt + 32);
+  const f16x8 b1 = *reinterpret_cast<const f16x8*>(vt + 32 * kVRow + 32);
+  O1[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, p1b, O1[cb], 0, 0, 0);
+  O2[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, p2b, O2[cb], 0, 0, 0);
+  O1[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, p1b, O1[cb + 1], 0, 0, 0);
+  O2[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, p2b, O2[cb + 1], 0, 0, 0);
+}
+
+// Buffer resources over one (b, h)'s key rows 0 .. kend-1, fixed for the whole
+// kernel (rows past kend read as zero); a tile is addressed by adding its first
+// key's byte offset to the per-lane offset, so the host keeps a (b, h)'s key
+// span under 2^31 bytes for this kernel.
+struct KeyRes {
+  __amdgpu_buffer_rsrc_t k1, k2, v;
+  uint32_t ks1, ks2, vs;  // bytes per key row
+};
+
+// DMA of one group's key tile (first key kbase) into the group's slot.
+__device__ __forceinline__ void pp_dma_k(const KeyRes& r, const StageOffsets& off, char* slot, int kbase, int part) {
+  char* dst = slot + part * 1024;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.k1, (lds_ptr_t)dst, 16, off.k1 + (uint32_t)kbase * r.ks1, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.k2, (lds_ptr_t)(dst + kKBytes), 16, off.k2 + (uint32_t)kbase * r.ks2, 0,
+                                           0, 0);
+}
+
+// Global -> registers: the thread's 4-key x 4-channel block of one group's
+// value tile (first key kbase).
+__device__ __forceinline__ void pp_load_v(Staged& st, const KeyRes& r, const StageOffsets& off, int kbase) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    st.v[i] = __builtin_amdgcn_raw_buffer_load_b64(r.v, off.v + (uint32_t)(kbase + i) * r.vs, 0, 0);
+}
+
+// Ping-pong split-key kernel (two groups of four waves, one wave of each group
+// per SIMD).  Each group runs a two-phase step: a matrix phase (O += V P for
+// its current tile, then S = K Q^T for its next tile) and a vector phase
+// (softmax of that S into P, V staging).  Group 1 runs one phase behind group
+// 0, so on every SIMD one wave's matrix products overlap the other's vector
+// work; every phase ends in a workgroup barrier that keeps the two in step.
+// Each group stages its own tiles in two slots: tile x's keys and values sit
+// in slot x % 2.  In the matrix phase of step x the group reads V(x) and
+// K(x + 1) while the DMA of K(x + 2) fills slot x % 2; V(x + 1) is stored in
+// the vector phase of step x from registers loaded a step earlier.
+template <bool kTrain>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_pp_kernel(PrefillArgs a) {
+  constexpr int kStage = 2 * kTile;
+  // One LDS object (the stages, then the epilogue's gain and lambda): the
+  // compiler then has no per-object alias scopes to go on and adds no waits
+  // of its own for the key DMA before LDS reads; the explicit waits order them.
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage + kDv * 4 + 16];
+  f32x4* const gain_s = reinterpret_cast<f32x4*>(smem + 2 * kStage);
+  float* const lam_s = reinterpret_cast<float*>(smem + 2 * kStage + kDv * 4);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / kGroupWaves;
+  const int wq = wave % kGroupWaves;
+  const int lane = tid & 63;
+  const int hf = lane >> 5;
+  const int lq = lane & 31;
+
+  const int nqb = (a.T + kBM - 1) / kBM;
+  const int BH = a.B * a.H;
+  const int qb = nqb - 1 - (int)(blockIdx.x / BH);
+  const int bh = (int)(blockIdx.x % BH);
+  const int head = bh % a.H;
+  const int b = bh / a.H;
+
+  const int q_first = qb * kBM + 32 * wq;
+  const int q = q_first + lq;
+  const bool wave_live = q_first < a.T;
+  const int ntiles = min(qb * (kBM / kBN) + (kBM / kBN), (a.T + kBN - 1) / kBN);
+  const int kend = min(a.T, ntiles * kBN);
+  const int tile0 = a.window > 0 ? max(0, qb * kBM - a.window + 1) / kBN : 0;
+  const int nsteps = (ntiles - tile0 + 1) / 2;
+  const int wave_last_tile = q_first / kBN;
+  const int wave_first_tile = a.window > 0 ? max(0, q_first - a.window + 1) / kBN : 0;
+
+  bf16x8 qa[4], qb2[4];
+  {
+    const bool ok = q < a.T;
+    const uint16_t* p1 = a.q1 + (int64_t)b * a.sq1.b + (int64_t)q * a.sq1.t + (int64_t)head * a.sq1.h + 8 * hf;
+    const uint16_t* p2 = a.q2 + (int64_t)b * a.sq2.b + (int64_t)q * a.sq2.t + (int64_t)head * a.sq2.h + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 x1 = ok ? load16(p1 + 16 * s) : u32x4{0, 0, 0, 0};
+      u32x4 x2 = ok ? load16(p2 + 16 * s) : u32x4{0, 0, 0, 0};
+      qa[s] = __builtin_bit_cast(bf16x8, x1);
+      qb2[s] = __builtin_bit_cast(bf16x8, x2);
+    }
+  }
+
+  f32x16 O1[4], O2[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    O1[cb] = f32x16{};
+    O2[cb] = f32x16{};
+  }
+  float m1 = kNoMax, m2 = kNoMax, l1 = 0.f, l2 = 0.f;
+  const float c = a.c;
+  const int ksw = kSwz(lq);
+
+  const uint16_t* kb1 = a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h;
+  const uint16_t* kb2 = a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h;
+  const uint16_t* vbase = a.v + (int64_t)b * a.sv.b + (int64_t)head * a.sv.h;
+  const StageOffsets soff = stage_offsets<0>(a, tid);
+  KeyRes res;
+  res.k1 = rows_rsrc(kb1, a.sk1.t, 0, kend, kDqk);
+  res.k2 = rows_rsrc(kb2, a.sk2.t, 0, kend, kDqk);
+  res.v = rows_rsrc(vbase, a.sv.t, 0, kend, kDv);
+  res.ks1 = (uint32_t)(a.sk1.t * 2);
+  res.ks2 = (uint32_t)(a.sk2.t * 2);
+  res.vs = (uint32_t)(a.sv.t * 2);
+  auto key0 = [&](int x) { return (tile0 + 2 * x + grp) * kBN; };  // first key of the group's tile of step x
+  char* const slot0 = smem + grp * kTile;                          // the group's tile in stage 0
+  auto live = [&](int j) { return wave_live && j >= wave_first_tile && j <= wave_last_tile; };
+
+  // The epilogue's gain and lambda, fetched while the first tiles load.
+  f32x4 gpre = f32x4{};
+  float lpre = 0.f;
+  if (tid < kDv / 4) gpre = *reinterpret_cast<const f32x4*>(a.gain + (int64_t)head * kDv + 4 * tid);
+  if (tid == kDv / 4) lpre = a.lambda_h ? a.lambda_h[head] : a.lambda;
+
+  // Prologue: tile 0 complete in slot 0, K(1) in slot 1, V(1) in registers
+  // (wait: everything but the four V(1) loads).
+  Staged st;
+  pp_dma_k(res, soff, slot0, key0(0), wq);
+  pp_load_v(st, res, soff, key0(0));
+  pp_dma_k(res, soff, slot0 + kStage, key0(1), wq);
+  stage_store<0>(st, smem, tid, nullptr);
+  pp_load_v(st, res, soff, key0(1));
+  if (tid < kDv / 4) gain_s[tid] = gpre;
+  if (tid == kDv / 4) *lam_s = lpre;
+  wait_vm<4>();
+  wait_lds();
+  phase_barrier();
+
+  f16x8 p1a, p1b, p2a, p2b;
+  {
+    const int j = tile0 + grp;
+    if (live(j)) {
+      f32x16 s1, s2;
+      scores_tile(smem + grp * kTile, lq, hf, ksw, qa, qb2, s1, s2);
+      mask_tile(a, s1, s2, j, wave_last_tile, q_first, q, hf);
+      softmax_step(s1, c, m1, l1, O1, p1a, p1b);
+      softmax_step(s2, c, m2, l2, O2, p2a, p2b);
+    }
+  }
+  if (grp == 1) phase_barrier();  // group 1 starts one phase late
+
+  for (int it = 0; it < nsteps; ++it) {
+    char* cur = smem + (it & 1) * kStage + grp * kTile;
+    char* nxt = smem + ((it + 1) & 1) * kStage + grp * kTile;
+    const int j = tile0 + 2 * it + grp;
+    const bool next = it + 1 < nsteps && live(j + 2);
+    // Matrix phase (raised issue priority: its products go first whenever
+    // both waves of a SIMD are ready).
+    __builtin_amdgcn_s_setprio(1);
+    f32x16 s1, s2;
+    const bool lj = live(j);
+    if (lj) pv_pair(cur, lq, hf, 0, p1a, p1b, p2a, p2b, O1, O2);
+    // K(it + 2) into slot it % 2, issued once the first products are queued.
+    // Unconditional: past the last tile the loads read zeros (rows past kend)
+    // into a slot nobody reads again, and the wait counts stay the same on
+    // every iteration.
+    __builtin_amdgcn_sched_barrier(0);
+    pp_dma_k(res, soff, slot0 + (it & 1) * kStage, key0(it + 2), wq);
+    __builtin_amdgcn_sched_barrier(0);
+    if (lj) pv_pair(cur, lq, hf, 2, p1a, p1b, p2a, p2b, O1, O2);
+    if (next) scores_tile(nxt, lq, hf, ksw, qa, qb2, s1, s2);
+    __builtin_amdgcn_s_setprio(0);
+    phase_barrier();
+    // Vector phase.
+    if (it + 1 < nsteps) stage_store<0>(st, smem + ((it + 1) & 1) * kStage, tid, nullptr);
+    pp_load_v(st, res, soff, key0(it + 2));
+    if (next) {
+      mask_tile(a, s1, s2, j + 2, wave_last_tile, q_first, q, hf);
+      softmax_step(s1, c, m1, l1, O1, p1a, p1b);
+      softmax_step(s2, c, m2, l2, O2, p2a, p2b);
+    }
+    wait_vm<4>();  // K(it + 2) has landed; only the four V(it + 2) loads may be in flight
+    wait_lds();    // V(it + 1) stored
+    phase_barrier();
+  }
+  if (grp == 0) phase_barrier();
+  wait_vm<0>();  // the zero-filling DMAs past the last tile, before the merge reuses the stages
+  __syncthreads();
+
+  merge_out<kTrain>(a, smem, grp, wq, lane, wave_live, *lam_s, b, head, q, hf, m1, l1, m2, l2, O1, O2);
+  if (grp != 0 || !wave_live) return;
+  norm_store(a, b, head, q, hf, O1, reinterpret_cast<const float*>(gain_s));
+}
+
 // kGroups wave groups of four waves share a workgroup's 128 queries and split
 // its key tiles.  Two waves per SIMD (<= 256 VGPRs each): one wave's softmax
 // VALU work overlaps the other's matrix products.
@@ -425,89 +880,7 @@ prefill_kernel(PrefillArgs a) {
   }
   if (grp != 0 || !wave_live) return;
 
-  // Combine the two maps, then GroupNorm over the 128 channels of the query.
-  // Lane (hf, lq) holds channels 32cb + 8(i/4) + 4hf + i%4; its partner lane
-  // (lane ^ 32) holds the other 64.
-  l1 += __shfl_xor(l1, 32);
-  l2 += __shfl_xor(l2, 32);
-  if (a.o1n != nullptr && q < a.T) {
-    // Training outputs for the backward pass.
-    const int64_t rq = ((int64_t)b * a.T + q) * a.H + head;
-    const float i1 = 1.0f / l1, i2 = 1.0f / l2;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int ch = 32 * cb + 8 * r4 + 4 * hf;
-        f32x4 v1, v2;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v1[r] = O1[cb][4 * r4 + r] * i1;
-          v2[r] = O2[cb][4 * r4 + r] * i2;
-        }
-        *reinterpret_cast<f32x4*>(a.o1n + rq * kDv + ch) = v1;
-        *reinterpret_cast<f32x4*>(a.o2n + rq * kDv + ch) = v2;
-      }
-    if (hf == 0) {
-      a.lse[rq * 2] = m1 + __builtin_log2f(l1);
-      a.lse[rq * 2 + 1] = m2 + __builtin_log2f(l2);
-    }
-  }
-  const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
-  const float r1 = 1.0f / l1;
-  const float r2 = lam / l2;
-  float sum = 0.f;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      // Both products rounded before the subtraction (no FMA contraction), so
-      // two identical maps at lambda = 1 cancel to exactly zero.
-#pragma clang fp contract(off)
-      const float o = O1[cb][i] * r1 - O2[cb][i] * r2;
-      O1[cb][i] = o;
-      sum += o;
-    }
-  }
-  sum += __shfl_xor(sum, 32);
-  const float mu = sum * (1.0f / kDv);
-  float ss = 0.f;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float d = O1[cb][i] - mu;
-      ss += d * d;
-    }
-  }
-  ss += __shfl_xor(ss, 32);
-  const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / kDv) + a.eps);
-
-  if (q >= a.T) return;
-  const int64_t row = (((int64_t)b * a.T + q) * a.H + head) * kDv;
-  const float* g = a.gain + (int64_t)head * kDv;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int ch = 32 * cb + 8 * r4 + 4 * hf;
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(g + ch);
-      f32x4 o, y;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        o[r] = O1[cb][4 * r4 + r];
-        y[r] = (o[r] - mu) * inv * gv[r];
-      }
-      if (a.o_pre) *reinterpret_cast<f32x4*>(a.o_pre + row + ch) = o;
-      if (a.out_f32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row + ch) = y;
-      } else {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 yb = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
-        *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(a.out) + row + ch) = yb;
-      }
-    }
-  }
+  finish_rows(a, b, head, q, hf, m1, m2, l1, l2, O1, O2);
 }
 
 }  // namespace
@@ -525,6 +898,17 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   const bool split = grid <= 2 * (int64_t)cus;
+  const int64_t row_max = std::max(std::max(a.sk1.t, a.sk2.t), a.sv.t);
+  // The ping-pong kernel addresses a (b, h)'s key rows from one buffer base
+  // with 32-bit offsets (up to about T + 192 rows).
+  const bool pingpong = split && a.rope.mode == 0 && (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31);
+  if (pingpong) {
+    if (a.o1n != nullptr)
+      hipLaunchKernelGGL(prefill_pp_kernel<true>, dim3((unsigned)grid), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL(prefill_pp_kernel<false>, dim3((unsigned)grid), dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 g((unsigned)grid), b1(64 * kGroupWaves), b2(64 * kGroupWaves * 2);
   switch (a.rope.mode * 2 + (split ? 1 : 0)) {
     case 0: hipLaunchKernelGGL((prefill_kernel<1, 0>), g, b1, 0, stream, a); break;
