@@ -47,7 +47,7 @@ SWA_DECODE_WL = "swa_decode_b64_l4096_h16_w128"
 ROPE_THETA = 500000.0        # Motif 2.6B's RoPE base
 CSRC = os.path.join(ROOT, "differential_attention_causal_amd", "csrc")
 PREFILL_PMC = os.path.join(ROOT, "profiles", "prefill_kernel_b1_t4096_h16_hbm_counters.txt")
-PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("prefill.hip", "kernels.h", "rope.h")]
+PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("prefill.hip", "kernels.h", "rope.h", "tile.h")]
 DECODE_PMC = os.path.join(ROOT, "profiles", "decode_split_kernel_b64_l4096_h16_hbm_counters.txt")
 DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode.hip", "kernels.h", "rope.h")]
 
@@ -339,7 +339,7 @@ def main() -> int:
                    "lambda": pw.lam, "causal": True, "step_also_runs": DECODE_WL},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "prefill_kernel", "algorithmic_flop_per_launch": p_flop},
+                     "kernel": "prefill_pp_kernel", "algorithmic_flop_per_launch": p_flop},
         "prefill": {"us_mean": round(p_s * 1e6, 2), "us_min": round(float(p_ms.min()) * 1e3, 2),
                     "tflops": round(tflops, 2), "tflops_512_per_pair": round(pw.causal_pairs * 512 / p_s / 1e12, 2),
                     "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4)},
