@@ -15,9 +15,10 @@
 //     with its own softmax states and accumulators, merged through LDS at the
 //     end; group 1 runs half a step behind group 0, so that on every SIMD one
 //     wave's matrix products run while the other wave does its softmax.  Used
-//     for grids that fit on the chip in one round (two workgroups per CU in
-//     longest-first order then sum to the same work on every CU), without the
-//     rotary embedding;
+//     for grids that fit on the chip in one round, without the rotary
+//     embedding; each workgroup runs two query blocks of one (b, h) back to
+//     back (the longest with the shortest), so one workgroup per CU carries
+//     the same work everywhere;
 //   - one group (4 waves, prefill_kernel<1, .>): two workgroups share a CU,
 //     and a grid larger than the chip balances itself in longest-first order;
 //   - two groups in lock step (prefill_kernel<2, .>): the split of the
@@ -559,14 +560,12 @@ __device__ __forceinline__ void pp_load_v(Staged& st, const KeyRes& r, const Sta
 // in slot x % 2.  In the matrix phase of step x the group reads V(x) and
 // K(x + 1) while the DMA of K(x + 2) fills slot x % 2; V(x + 1) is stored in
 // the vector phase of step x from registers loaded a step earlier.
+constexpr int kPPStage = 2 * kTile;
+constexpr int kPPSmem = 2 * kPPStage + kDv * 4 + 16;
+
 template <bool kTrain>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-prefill_pp_kernel(PrefillArgs a) {
-  constexpr int kStage = 2 * kTile;
-  // One LDS object (the stages, then the epilogue's gain and lambda): the
-  // compiler then has no per-object alias scopes to go on and adds no waits
-  // of its own for the key DMA before LDS reads; the explicit waits order them.
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage + kDv * 4 + 16];
+__device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int item) {
+  constexpr int kStage = kPPStage;
   f32x4* const gain_s = reinterpret_cast<f32x4*>(smem + 2 * kStage);
   float* const lam_s = reinterpret_cast<float*>(smem + 2 * kStage + kDv * 4);
 
@@ -580,8 +579,8 @@ prefill_pp_kernel(PrefillArgs a) {
 
   const int nqb = (a.T + kBM - 1) / kBM;
   const int BH = a.B * a.H;
-  const int qb = nqb - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
+  const int qb = nqb - 1 - item / BH;
+  const int bh = item % BH;
   const int head = bh % a.H;
   const int b = bh / a.H;
 
@@ -710,7 +709,27 @@ prefill_pp_kernel(PrefillArgs a) {
   norm_store(a, b, head, q, hf, O1, reinterpret_cast<const float*>(gain_s));
 }
 
-// kGroups wave groups of four waves share a workgroup's 128 queries and split
+// Persistent form: workgroup w = r * B*H + bh runs the query blocks of row r
+// and of row nqb - 1 - r of the longest-first order, both of (b, h) = bh,
+// back to back: the longest block with the shortest, so one workgroup per CU
+// carries the same work everywhere, and a head's blocks stay on the XCD that
+// holds its keys in L2 (B*H a multiple of 8).  An odd middle row runs alone.
+template <bool kTrain>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_pp_kernel(PrefillArgs a) {
+  // One LDS object (the stages, then the epilogue's gain and lambda): the
+  // compiler then has no per-object alias scopes to go on and adds no waits
+  // of its own for the key DMA before LDS reads; the explicit waits order them.
+  __shared__ __attribute__((aligned(16))) char smem[kPPSmem];
+  const int BH = a.B * a.H;
+  const int nqb = (a.T + kBM - 1) / kBM;
+  const int r = (int)blockIdx.x / BH, bh = (int)blockIdx.x % BH;
+  pp_item<kTrain>(a, smem, (int)blockIdx.x);
+  if (nqb - 1 - r > r) {
+    __syncthreads();  // the first block's epilogue is done with LDS
+    pp_item<kTrain>(a, smem, (nqb - 1 - r) * BH + bh);
+  }
+}// kGroups wave groups of four waves share a workgroup's 128 queries and split
 // its key tiles.  Two waves per SIMD (<= 256 VGPRs each): one wave's softmax
 // VALU work overlaps the other's matrix products.
 // kRope: the rotary embedding mode (0 none, 1 split-half, 2 interleaved),
@@ -903,10 +922,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   // with 32-bit offsets (up to about T + 192 rows).
   const bool pingpong = split && a.rope.mode == 0 && (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31);
   if (pingpong) {
+    const dim3 gp((unsigned)((int64_t)((nqb + 1) / 2) * a.B * a.H));
     if (a.o1n != nullptr)
-      hipLaunchKernelGGL(prefill_pp_kernel<true>, dim3((unsigned)grid), dim3(512), 0, stream, a);
+      hipLaunchKernelGGL(prefill_pp_kernel<true>, gp, dim3(512), 0, stream, a);
     else
-      hipLaunchKernelGGL(prefill_pp_kernel<false>, dim3((unsigned)grid), dim3(512), 0, stream, a);
+      hipLaunchKernelGGL(prefill_pp_kernel<false>, gp, dim3(512), 0, stream, a);
     return hipGetLastError();
   }
   const dim3 g((unsigned)grid), b1(64 * kGroupWaves), b2(64 * kGroupWaves * 2);
