@@ -19,9 +19,10 @@
 //   bwd_dq_kernel      queries own lanes (the forward's orientation): recompute
 //                      S^T, P^T from the saved log-sum-exp, dP^T = V dO^T,
 //                      dQ^T += K^T dS^T
-//   bwd_dk_kernel      keys own lanes: S = Q K^T, dP = dO V^T, dK^T += Q^T dS
-//   bwd_dv_kernel      keys own lanes: S = Q K^T, dV^T += dO^T (P_1 - lambda P_2)
-// The last three use v_mfma_f32_32x32x16 like the prefill: a 32x32 accumulator
+//   bwd_dkv_kernel     keys own lanes, two kinds of waves on the same keys and
+//                      query tiles: S = Q K^T, dP = dO V^T, dK^T += Q^T dS;
+//                      and S = Q K^T, dV^T += dO^T (P_1 - lambda P_2)
+// The last two use v_mfma_f32_32x32x16 like the prefill: a 32x32 accumulator
 // held by a wave is used directly as the next product's operand, with the
 // transposed LDS tiles stored in the matching (kVPos) order.  Scores are bf16
 // products of the exact inputs; dO, P, dS, V^T, K^T and Q^T enter the other
@@ -459,24 +460,34 @@ __device__ __forceinline__ void load_krow(bf16x8 (&kt)[4], const uint16_t* base,
   for (int s = 0; s < 4; ++s) kt[s] = ok ? *reinterpret_cast<const bf16x8*>(p + 16 * s) : bf16x8{};
 }
 
-constexpr int kDkStage = 2 * kQKTile + kD16Tile + 2 * kQKT + 4 * 32 * 4;
+// dK and dV in one launch: a workgroup of 8 waves owns 128 keys of one (b, h).
+// Waves 0-3 compute dK_1, dK_2 and waves 4-7 dV for the same keys, so each SIMD holds one wave of each kind and every
+// query tile is staged once for both: Q_1, Q_2 row-major bf16 and dO
+// row-major fp16 by DMA plus Q^T by registers (staged by the dK waves), dO^T
+// and the per-query statistics (staged by the dV waves).  Each role runs its
+// own copy of the loop (same trip count, one barrier per query tile), so its
+// registers are allocated for that role alone.
+constexpr int kDkvStage = 2 * kQKTile + kD16Tile + 2 * kQKT + kDT + 4 * 32 * 4;
+constexpr int kOffDo = 2 * kQKTile, kOffQT = kOffDo + kD16Tile, kOffDT = kOffQT + 2 * kQKT, kOffSt = kOffDT + kDT;
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dk_kernel(BackwardArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kDkStage];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, lk = lane & 31;
+template <bool kDV>
+__device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int tid) {
+  const int rt = tid & 255;                                   // thread within its role
+  const int rw = __builtin_amdgcn_readfirstlane(rt >> 6);     // wave within its role
+  const int lane = tid & 63, hf = lane >> 5, lk = lane & 31;
   const int BH = a.B * a.H;
   const int kb = (int)(blockIdx.x / BH);  // longest column blocks first
   const int bh = (int)(blockIdx.x % BH), head = bh % a.H, b = bh / a.H;
-  const int k_first = kb * kRows + 32 * wave, key = k_first + lk;
+  const int k_first = kb * kRows + 32 * rw, key = k_first + lk;
   const bool wave_live = k_first < a.T, ok = key < a.T;
   const int nqt = (a.T + 31) / 32, qt0 = kb * (kRows / 32);
   const int diag = k_first / 32;  // this wave's first (diagonal) query tile
 
   bf16x8 k1t[4], k2t[4];
-  f16x8 vt[8];
   load_krow(k1t, a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h, a.sk1.t, key, ok, hf);
   load_krow(k2t, a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h, a.sk2.t, key, ok, hf);
-  {
+  f16x8 vt[kDV ? 1 : 8];
+  if constexpr (!kDV) {
     const uint16_t* p = a.v + (int64_t)b * a.sv.b + (int64_t)key * a.sv.t + (int64_t)head * a.sv.h + 8 * hf;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -495,16 +506,25 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const uint16_t* dob = a.dO + (int64_t)b * a.T * a.H * kDv + (int64_t)head * kDv;
   const int64_t sdo = (int64_t)a.H * kDv;
 
-  f32x16 dk1[2] = {f32x16{}, f32x16{}}, dk2[2] = {f32x16{}, f32x16{}};
+  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};  // dK_1 (0, 1), dK_2 (2, 3) or dV^T (0 .. 3)
   StagedT sq;
+  StagedDT sd;
   auto stage_issue = [&](int qt, char* st) {
-    dma_qk(qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, st, tid);
-    dma_do(dob, sdo, 32 * qt, a.T, st + 2 * kQKTile, tid);
-    load_qkT(sq, qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, tid);
+    if constexpr (!kDV) {
+      dma_qk(qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, st, rt);
+      dma_do(dob, sdo, 32 * qt, a.T, st + kOffDo, rt);
+      load_qkT(sq, qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, rt);
+    } else {
+      load_doT(sd, dob, sdo, 32 * qt, a.T, rt);
+    }
   };
   auto stage_store = [&](int qt, char* st) {
-    store_qkT(sq, st + 2 * kQKTile + kD16Tile, tid);
-    stage_stats(a, b, head, 32 * qt, reinterpret_cast<float*>(st + 2 * kQKTile + kD16Tile + 2 * kQKT), tid);
+    if constexpr (!kDV) {
+      store_qkT(sq, st + kOffQT, rt);
+    } else {
+      store_doT(sd, st + kOffDT, rt);
+      stage_stats(a, b, head, 32 * qt, reinterpret_cast<float*>(st + kOffSt), rt);
+    }
   };
   if (qt0 < nqt) {
     stage_issue(qt0, smem);
@@ -515,49 +535,71 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   for (int qt = qt0; qt < nqt; ++qt) {
     const int it = qt - qt0;
-    char* cur = smem + (it & 1) * kDkStage;
-    char* nxt = smem + ((it + 1) & 1) * kDkStage;
+    char* cur = smem + (it & 1) * kDkvStage;
+    char* nxt = smem + ((it + 1) & 1) * kDkvStage;
     const bool more = qt + 1 < nqt;
     if (more) stage_issue(qt + 1, nxt);
     if (wave_live && qt >= diag) {
       f32x16 s1 = scores_qk(cur, k1t, lk, hf);
       f32x16 s2 = scores_qk(cur + kQKTile, k2t, lk, hf);
-      // dP = dO V^T (32 queries x 32 keys)
-      f32x16 dp = f32x16{};
-      const char* dt = cur + 2 * kQKTile + lk * kD16Row;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            *reinterpret_cast<const f16x8*>(dt + (((2 * s + hf) ^ swz16(lk)) << 4)), vt[s], dp, 0, 0, 0);
-      const float* stats = reinterpret_cast<const float*>(cur + 2 * kQKTile + kD16Tile + 2 * kQKT);
+      const float* stats = reinterpret_cast<const float*>(cur + kOffSt);
       const bool dg = qt == diag;  // rows are queries 8(i/4) + 4hf + i%4 of the tile, the column key lk
+      if constexpr (!kDV) {
+        // dP = dO V^T (32 queries x 32 keys)
+        f32x16 dp = f32x16{};
+        const char* dt = cur + kOffDo + lk * kD16Row;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // statistics of rows 8g + 4hf .. +3, four registers at a time
-        const int r0 = 8 * g + 4 * hf;
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(stats + r0);
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 32 + r0);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(stats + 64 + r0);
-        const f32x4 d2 = *reinterpret_cast<const f32x4*>(stats + 96 + r0);
+        for (int s = 0; s < 8; ++s)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              *reinterpret_cast<const f16x8*>(dt + (((2 * s + hf) ^ swz16(lk)) << 4)), vt[s], dp, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * g + r;
-          const bool vis = !dg || lk <= r0 + r;
-          const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r])) : 0.f;
-          const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r])) : 0.f;
-          s1[i] = p1 * (dp[i] - d1[r]);
-          s2[i] = p2 * (-lam * dp[i] - d2[r]);
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = 8 * g + 4 * hf;
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(stats + r0);
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 32 + r0);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(stats + 64 + r0);
+          const f32x4 d2 = *reinterpret_cast<const f32x4*>(stats + 96 + r0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g + r;
+            const bool vis = !dg || lk <= r0 + r;
+            const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r])) : 0.f;
+            const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r])) : 0.f;
+            s1[i] = p1 * (dp[i] - d1[r]);
+            s2[i] = p2 * (-lam * dp[i] - d2[r]);
+          }
         }
-      }
-      f16x8 a0, a1, b0, b1;
-      pack16(s1, a0, a1);
-      pack16(s2, b0, b1);
-      // dK_m^T += Q_m^T dS_m
-      const char* qtT = cur + 2 * kQKTile + kD16Tile;
+        f16x8 a0, a1, b0, b1;
+        pack16(s1, a0, a1);
+        pack16(s2, b0, b1);
+        // dK_m^T += Q_m^T dS_m
+        const char* qtT = cur + kOffQT;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        dk1[blk] = mfma_T(qtT, blk, lk, hf, a0, a1, dk1[blk]);
-        dk2[blk] = mfma_T(qtT + kQKT, blk, lk, hf, b0, b1, dk2[blk]);
+        for (int blk = 0; blk < 2; ++blk) {
+          acc[blk] = mfma_T(qtT, blk, lk, hf, a0, a1, acc[blk]);
+          acc[2 + blk] = mfma_T(qtT + kQKT, blk, lk, hf, b0, b1, acc[2 + blk]);
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = 8 * g + 4 * hf;
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(stats + r0);
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 32 + r0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g + r;
+            const bool vis = !dg || lk <= r0 + r;
+            const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r])) : 0.f;
+            const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r])) : 0.f;
+            s1[i] = p1 - lam * p2;
+          }
+        }
+        f16x8 p0, p1;
+        pack16(s1, p0, p1);
+        // dV^T += dO^T (P_1 - lambda P_2)
+        const char* dT = cur + kOffDT;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) acc[blk] = mfma_T(dT, blk, lk, hf, p0, p1, acc[blk]);
       }
     }
     if (more) stage_store(qt + 1, nxt);
@@ -566,100 +608,25 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   if (!ok) return;
   const int64_t rk = ((int64_t)b * a.T + key) * a.H + head;
+  if constexpr (!kDV) {
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    store_col(a.dk1 + rk * kDqk, dk1[blk], blk, hf, a.scale);
-    store_col(a.dk2 + rk * kDqk, dk2[blk], blk, hf, a.scale);
+    for (int blk = 0; blk < 2; ++blk) {
+      store_col(a.dk1 + rk * kDqk, acc[blk], blk, hf, a.scale);
+      store_col(a.dk2 + rk * kDqk, acc[2 + blk], blk, hf, a.scale);
+    }
+  } else {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) store_col(a.dv + rk * kDv, acc[blk], blk, hf, 1.0f);
   }
 }
 
-constexpr int kDvStage = 2 * kQKTile + kDT + 2 * 32 * 4;
-
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dv_kernel(BackwardArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kDvStage];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, lk = lane & 31;
-  const int BH = a.B * a.H;
-  const int kb = (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH), head = bh % a.H, b = bh / a.H;
-  const int k_first = kb * kRows + 32 * wave, key = k_first + lk;
-  const bool wave_live = k_first < a.T, ok = key < a.T;
-  const int nqt = (a.T + 31) / 32, qt0 = kb * (kRows / 32);
-  const int diag = k_first / 32;
-
-  bf16x8 k1t[4], k2t[4];
-  load_krow(k1t, a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h, a.sk1.t, key, ok, hf);
-  load_krow(k2t, a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h, a.sk2.t, key, ok, hf);
-  const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
-  const float c = a.c;
-  const uint16_t* qb1 = a.q1 + (int64_t)b * a.sq1.b + (int64_t)head * a.sq1.h;
-  const uint16_t* qb2 = a.q2 + (int64_t)b * a.sq2.b + (int64_t)head * a.sq2.h;
-  const uint16_t* dob = a.dO + (int64_t)b * a.T * a.H * kDv + (int64_t)head * kDv;
-  const int64_t sdo = (int64_t)a.H * kDv;
-
-  f32x16 dv[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-  StagedDT sd;
-  auto stage_issue = [&](int qt, char* st) {
-    dma_qk(qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, st, tid);
-    load_doT(sd, dob, sdo, 32 * qt, a.T, tid);
-  };
-  auto stage_store = [&](int qt, char* st) {
-    store_doT(sd, st + 2 * kQKTile, tid);
-    if (tid < 32) {
-      const int q = 32 * qt + tid;
-      f32x2 l = {__builtin_inff(), __builtin_inff()};
-      if (q < a.T) l = *reinterpret_cast<const f32x2*>(a.lse + (((int64_t)b * a.T + q) * a.H + head) * 2);
-      float* s = reinterpret_cast<float*>(st + 2 * kQKTile + kDT);
-      s[tid] = l.x;
-      s[32 + tid] = l.y;
-    }
-  };
-  if (qt0 < nqt) {
-    stage_issue(qt0, smem);
-    stage_store(qt0, smem);
-  }
-  wait_dma();
-  __syncthreads();
-
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int it = qt - qt0;
-    char* cur = smem + (it & 1) * kDvStage;
-    char* nxt = smem + ((it + 1) & 1) * kDvStage;
-    const bool more = qt + 1 < nqt;
-    if (more) stage_issue(qt + 1, nxt);
-    if (wave_live && qt >= diag) {
-      f32x16 s1 = scores_qk(cur, k1t, lk, hf);
-      f32x16 s2 = scores_qk(cur + kQKTile, k2t, lk, hf);
-      const float* stats = reinterpret_cast<const float*>(cur + 2 * kQKTile + kDT);
-      const bool dg = qt == diag;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = 8 * g + 4 * hf;
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(stats + r0);
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 32 + r0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * g + r;
-          const bool vis = !dg || lk <= r0 + r;
-          const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r])) : 0.f;
-          const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r])) : 0.f;
-          s1[i] = p1 - lam * p2;
-        }
-      }
-      f16x8 p0, p1;
-      pack16(s1, p0, p1);
-      // dV^T += dO^T (P_1 - lambda P_2)
-      const char* dT = cur + 2 * kQKTile;
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) dv[blk] = mfma_T(dT, blk, lk, hf, p0, p1, dv[blk]);
-    }
-    if (more) stage_store(qt + 1, nxt);
-    wait_dma();
-    __syncthreads();
-  }
-  if (!ok) return;
-  const int64_t rk = ((int64_t)b * a.T + key) * a.H + head;
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) store_col(a.dv + rk * kDv, dv[blk], blk, hf, 1.0f);
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dkv_kernel(BackwardArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kDkvStage];
+  const int tid = threadIdx.x;
+  if (__builtin_amdgcn_readfirstlane(tid >> 6) >= kWaves)
+    dkv_role<true>(a, smem, tid);
+  else
+    dkv_role<false>(a, smem, tid);
 }
 
 }  // namespace
@@ -673,9 +640,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)((a.T + kRows - 1) / kRows) * a.B * a.H;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dk_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)blocks), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
