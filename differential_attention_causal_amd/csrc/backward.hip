@@ -48,75 +48,132 @@ constexpr int kDT = kDv * kTRow;        // 10 KiB: transposed 128 x 32 tile
 // conflicted.
 __device__ __forceinline__ int swz16(int r) { return r & 15; }
 
-__device__ __forceinline__ f32x2 load_dy(const BackwardArgs& a, int64_t off) {
-  if (a.dy_f32) return *reinterpret_cast<const f32x2*>(static_cast<const float*>(a.dy) + off);
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.dy) + off);
-  return f32x2{bf16_lo(w), bf16_hi(w)};
-}
-
 // ---------------------------------------------------------------------------
 // Per row: the GroupNorm backward, do, D_1 = rowsum(do O_1),
 // D_2 = rowsum(-lambda do O_2), and partial sums of dgain and dlambda over a
-// chunk of kBwdRowsPerChunk rows of one head.  One wave per row, two channels
-// per lane.
+// chunk of kBwdRowsPerChunk rows of one head.  Sixteen lanes per row (eight
+// channels each), four rows per wave at a time; row sums are reduced within
+// the 16-lane DPP row in four steps.
+
+// Sum over the 16 lanes of a DPP row, the same value in every lane: xor 1 and
+// xor 2 within quads, then the mirrored halves of 8, then of 16.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror
+  x += dpp_f32<0x140>(x);  // row_mirror
+  return x;
+}
+
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BackwardArgs a) {
-  __shared__ float red[kWaves][kDv + 1];
+  constexpr int kRowsPerPass = 4 * kWaves;  // 16: four per wave
+  __shared__ float red[kRowsPerPass][kDv + 1];
   const int chunk = blockIdx.x, h = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane >> 4, li = lane & 15;  // row within the wave's four, lane within the row
   const int BT = a.B * a.T;
   const float lam = a.lambda_h ? a.lambda_h[h] : a.lambda;
-  const f32x2 g = *reinterpret_cast<const f32x2*>(a.gain + (int64_t)h * kDv + 2 * lane);
-  float dg0 = 0.f, dg1 = 0.f, dl = 0.f;
-  // Two rows per pass (rows k and k + kWaves) so their reductions overlap.
-  for (int k = wave; k < kBwdRowsPerChunk; k += 2 * kWaves) {
-    const int rbt0 = chunk * kBwdRowsPerChunk + k;
-    if (rbt0 >= BT) break;
-    const bool two = rbt0 + kWaves < BT && k + kWaves < kBwdRowsPerChunk;
-    int64_t off[2];
-    f32x2 o1[2], o2[2], dy[2];
-    float x[2][2];
+  const float* gp = a.gain + (int64_t)h * kDv + 8 * li;
+  float g[8];
+  {
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp), g1 = *reinterpret_cast<const f32x4*>(gp + 4);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t row = (int64_t)(u && two ? rbt0 + kWaves : rbt0) * a.H + h;
-      off[u] = row * kDv + 2 * lane;
-      o1[u] = *reinterpret_cast<const f32x2*>(a.o1n + off[u]);
-      o2[u] = *reinterpret_cast<const f32x2*>(a.o2n + off[u]);
-      dy[u] = load_dy(a, off[u]);
-      x[u][0] = o1[u].x - lam * o2[u].x;
-      x[u][1] = o1[u].y - lam * o2[u].y;
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (u == 1 && !two) break;
-      const float mu = wave_sum(x[u][0] + x[u][1]) * (1.0f / kDv);
-      const float d0 = x[u][0] - mu, d1 = x[u][1] - mu;
-      const float var = wave_sum(d0 * d0 + d1 * d1) * (1.0f / kDv);
-      const float rs = 1.0f / __builtin_sqrtf(var + a.eps);
-      const float xh0 = d0 * rs, xh1 = d1 * rs;
-      dg0 += dy[u].x * xh0;
-      dg1 += dy[u].y * xh1;
-      const float g0 = dy[u].x * g.x, g1 = dy[u].y * g.y;
-      const float mg = wave_sum(g0 + g1) * (1.0f / kDv);
-      const float mgx = wave_sum(g0 * xh0 + g1 * xh1) * (1.0f / kDv);
-      const float do0 = rs * (g0 - mg - xh0 * mgx), do1 = rs * (g1 - mg - xh1 * mgx);
-      dl -= wave_sum(do0 * o2[u].x + do1 * o2[u].y);
-      // D_m from the fp16 dO the products use, so that sum_j P_ij dP_ij = D_i
-      // holds up to fp32 rounding (at T = 1, dS is then 0 as it must be).
-      const f16x2 hv = {(_Float16)do0, (_Float16)do1};
-      const float h0 = (float)hv[0], h1 = (float)hv[1];
-      const float dd1 = wave_sum(h0 * o1[u].x + h1 * o1[u].y);
-      const float s2 = wave_sum(h0 * o2[u].x + h1 * o2[u].y);
-      *reinterpret_cast<f16x2*>(a.dO + off[u]) = hv;
-      if (lane == 0) *reinterpret_cast<f32x2*>(a.dstat + (off[u] / kDv) * 2) = f32x2{dd1, -lam * s2};
+    for (int e = 0; e < 4; ++e) {
+      g[e] = g0[e];
+      g[4 + e] = g1[e];
     }
   }
-  red[wave][2 * lane] = dg0;
-  red[wave][2 * lane + 1] = dg1;
-  if (lane == 0) red[wave][kDv] = dl;
+  float dg[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float dl = 0.f;
+#pragma unroll 1
+  for (int pass = 0; pass < kBwdRowsPerChunk / kRowsPerPass; ++pass) {
+    const int rbt = chunk * kBwdRowsPerChunk + pass * kRowsPerPass + wave * 4 + grp;
+    if (rbt >= BT) continue;  // per-lane; the DPP rows of a wave are independent
+    const int64_t off = ((int64_t)rbt * a.H + h) * kDv + 8 * li;
+    float o1[8], o2[8], dy[8], x[8];
+    {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(a.o1n + off), a1 = *reinterpret_cast<const f32x4*>(a.o1n + off + 4);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(a.o2n + off), b1 = *reinterpret_cast<const f32x4*>(a.o2n + off + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o1[e] = a0[e];
+        o1[4 + e] = a1[e];
+        o2[e] = b0[e];
+        o2[4 + e] = b1[e];
+      }
+      if (a.dy_f32) {
+        const float* d = static_cast<const float*>(a.dy) + off;
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(d), d1 = *reinterpret_cast<const f32x4*>(d + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dy[e] = d0[e];
+          dy[4 + e] = d1[e];
+        }
+      } else {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dy) + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dy[2 * e] = bf16_lo(w[e]);
+          dy[2 * e + 1] = bf16_hi(w[e]);
+        }
+      }
+    }
+    float sx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = o1[e] - lam * o2[e];
+      sx += x[e];
+    }
+    const float mu = sum16(sx) * (1.0f / kDv);
+    float sd = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] -= mu;
+      sd += x[e] * x[e];
+    }
+    const float rs = 1.0f / __builtin_sqrtf(sum16(sd) * (1.0f / kDv) + a.eps);
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] *= rs;  // x-hat
+      dg[e] += dy[e] * x[e];
+      dy[e] *= g[e];  // g = dy * gain
+      sg += dy[e];
+      sgx += dy[e] * x[e];
+    }
+    const float mg = sum16(sg) * (1.0f / kDv), mgx = sum16(sgx) * (1.0f / kDv);
+    float sdl = 0.f, sd1 = 0.f, sd2 = 0.f;
+    f16x8 hv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = rs * (dy[e] - mg - x[e] * mgx);
+      sdl += d * o2[e];
+      // D_m from the fp16 dO the products use, so that sum_j P_ij dP_ij = D_i
+      // holds up to fp32 rounding (at T = 1, dS is then 0 as it must be).
+      hv[e] = (_Float16)d;
+      sd1 += (float)hv[e] * o1[e];
+      sd2 += (float)hv[e] * o2[e];
+    }
+    dl -= sum16(sdl);
+    const float dd1 = sum16(sd1), s2 = sum16(sd2);
+    *reinterpret_cast<f16x8*>(a.dO + off) = hv;
+    if (li == 0) *reinterpret_cast<f32x2*>(a.dstat + (off / kDv) * 2) = f32x2{dd1, -lam * s2};
+  }
+  const int rr = wave * 4 + grp;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rr][8 * li + e] = dg[e];
+  if (li == 0) red[rr][kDv] = dl;
   __syncthreads();
   const int t = threadIdx.x;
   if (t <= kDv) {
-    const float s = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < kRowsPerPass; ++r) s += red[r][t];
     a.partial[((int64_t)h * a.nchunks + chunk) * (kDv + 1) + t] = s;
   }
 }
