@@ -90,19 +90,47 @@ def decode_bytes(wl) -> int:
     return cache + q + out + gain
 
 
-def cpu_baseline(x, wl):
-    """Time the fp64 oracle on all rows of the prefill workload on this host."""
+def cpu_baseline(x, wl, gpu=None):
+    """Time the fp64 oracle on all rows of the prefill workload on this host.
+    gpu: the benchmarked kernel's outputs on the same inputs (bf16 y, fp32 y,
+    fp32 pre-norm o, as numpy arrays); the oracle's rows are then also the
+    parity check of the measured launch configuration."""
+    import numpy as np
     import oracle
 
     cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"],
-                   nthreads=cores)
+    o_ref, y_ref = oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"],
+                                  x["scale"], nthreads=cores)
     dt = time.perf_counter() - t0
     flop = wl.causal_pairs * FLOP_PER_PAIR
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "all %d rows of %s (B=1,T=4096,H=16), fp64, %.2f s wall; FLOP counted at %d per "
-                      "causal pair like the GPU value" % (wl.B * wl.T * wl.H, wl.name, dt, FLOP_PER_PAIR)}
+    rec = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": "all %d rows of %s (B=1,T=4096,H=16), fp64, %.2f s wall; FLOP counted at %d per "
+                     "causal pair like the GPU value" % (wl.B * wl.T * wl.H, wl.name, dt, FLOP_PER_PAIR)}
+    if gpu is not None:
+        def ymet(y):
+            d = np.abs(y.astype(np.float64) - y_ref)
+            return {"y_max_abs": float(d.max()), "y_mean_abs": float(d.mean())}
+        o = gpu["o_pre"].astype(np.float64)
+        rec["parity"] = {"bound": {"y_max_abs": 2e-2, "y_mean_abs": 2e-3, "o_rel_f": 5e-3},
+                         "bf16_out": ymet(gpu["y_bf16"]), "fp32_out": ymet(gpu["y_f32"]),
+                         "o_rel_f": float(np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref))}
+    return rec
+
+
+def gpu_env(torch) -> dict:
+    """Device, software versions and current clocks (rocm-smi, when it answers)."""
+    import subprocess
+
+    env = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+        env["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() or "sclk" in k or "mclk" in k}
+    except Exception as e:  # no rocm-smi, no permission, unexpected output: report without clocks
+        env["clocks"] = None
+        env["clocks_error"] = type(e).__name__
+    return env
 
 
 def copy_calibration(steps: int) -> None:
@@ -349,9 +377,19 @@ def main() -> int:
         "variants": var,
         "wall_s_timed": round(wall, 3),
         "kernel_source_sha256_16": kernel_source_digest(),
+        "env": gpu_env(torch),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(xp, pw)
+        # the benchmarked prefill once more (outside the timed region) with
+        # fp32 and pre-norm outputs, for the parity record
+        y32 = torch.empty((pw.B, pw.T, pw.H, pw.d_v), dtype=torch.float32, device=dev)
+        o_pre = torch.empty_like(y32)
+        da.diffattn_fwd_prefill(P["q1"], P["q2"], P["k1"], P["k2"], P["v"], pw.lam, P["gain"], eps=pw.eps,
+                                scale=pw.scale, out=y32, o_pre=o_pre)
+        prefill()
+        torch.cuda.synchronize()
+        gpu = {"y_bf16": p_out.float().cpu().numpy(), "y_f32": y32.cpu().numpy(), "o_pre": o_pre.cpu().numpy()}
+        rec["cpu_baseline"] = cpu_baseline(xp, pw, gpu)
     print(json.dumps(rec), flush=True)
     return 0
 
