@@ -20,6 +20,8 @@ import torch  # first: the HIP runtime torch loads is the one the library binds 
 __all__ = [
     "diffattn_fwd_prefill",
     "diffattn_fwd_prefill_ex",
+    "diffattn_fwd_prefill_ws",
+    "diffattn_prefill_workspace_bytes",
     "diffattn_fwd_decode",
     "diffattn_fwd_decode_ex",
     "diffattn_rope_apply",
@@ -75,6 +77,11 @@ _lib.diffattn_fwd_decode.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(_Strides
                                      _F, _P, _P, _F, _F, _I, _P, ctypes.c_size_t, _P, _I, _P, _P]
 _lib.diffattn_fwd_prefill_ex.restype = _I
 _lib.diffattn_fwd_prefill_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffattn_fwd_prefill.argtypes
+_lib.diffattn_prefill_workspace_bytes.restype = ctypes.c_size_t
+_lib.diffattn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(_Options), _I, _I, _I]
+_lib.diffattn_fwd_prefill_ws.restype = _I
+_lib.diffattn_fwd_prefill_ws.argtypes = ([ctypes.POINTER(_Options)] + _lib.diffattn_fwd_prefill.argtypes[:-1]
+                                         + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
 _lib.diffattn_fwd_decode_ex.restype = _I
 _lib.diffattn_fwd_decode_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffattn_fwd_decode.argtypes
 _lib.diffattn_rope_apply.restype = _I
@@ -156,14 +163,44 @@ def diffattn_fwd_prefill(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, out=
 
 def diffattn_fwd_prefill_ex(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, out=None,
                             out_dtype=torch.bfloat16, o_pre=None, stream=None, window=0, rope=ROPE_NONE,
-                            rope_theta=0.0, rope_pos0=0):
+                            rope_theta=0.0, rope_pos0=0, workspace=True):
     """diffattn_fwd_prefill with variants: window > 0 is a sliding window
-    (query i attends keys i-window+1 .. i); rope selects the rotary prologue."""
+    (query i attends keys i-window+1 .. i); rope selects the rotary prologue.
+    workspace: with rope on, True (default) runs diffattn_fwd_prefill_ws with a
+    workspace from torch's allocator (keys rotated once), a uint8 device tensor
+    runs it with that buffer, and False runs diffattn_fwd_prefill_ex (the keys
+    rotated inside the kernels)."""
     opt = _Options(window=int(window), rope=int(rope), rope_pos0=int(rope_pos0), rope_theta=float(rope_theta))
-    return _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream)
+    ws = None
+    if int(rope) != ROPE_NONE and workspace is not False:
+        B, T, H, _ = q1.shape
+        need = diffattn_prefill_workspace_bytes(B, T, H, rope=rope)
+        if isinstance(workspace, torch.Tensor):
+            if workspace.dtype != torch.uint8 or not workspace.is_cuda or workspace.numel() < need:
+                raise ValueError("workspace must be a uint8 device tensor of at least %d bytes" % need)
+            ws = workspace
+        else:
+            ws = torch.empty(need, dtype=torch.uint8, device=q1.device)
+    return _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream, ws=ws)
 
 
-def _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream, train=None):
+def diffattn_fwd_prefill_ws(q1, q2, k1, k2, v, lam, gain, workspace, eps=1e-5, scale=0.0, out=None,
+                            out_dtype=torch.bfloat16, o_pre=None, stream=None, window=0, rope=ROPE_NONE,
+                            rope_theta=0.0, rope_pos0=0):
+    """diffattn_fwd_prefill_ex with a caller's workspace (uint8 device tensor of
+    diffattn_prefill_workspace_bytes(...) bytes; may be None without rope)."""
+    opt = _Options(window=int(window), rope=int(rope), rope_pos0=int(rope_pos0), rope_theta=float(rope_theta))
+    return _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream,
+                    ws=workspace if workspace is not None else False)
+
+
+def diffattn_prefill_workspace_bytes(B, T, H, rope=ROPE_NONE):
+    """Workspace bytes diffattn_fwd_prefill_ws needs (0 without rope)."""
+    opt = _Options(rope=int(rope), rope_theta=1.0)
+    return int(_lib.diffattn_prefill_workspace_bytes(ctypes.byref(opt), int(B), int(T), int(H)))
+
+
+def _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream, train=None, ws=None):
     """Causal differential-attention prefill.
 
     q1, q2, k1, k2: bf16 [B, T, H, 64]; v: bf16 [B, T, H, 128] (any strides with
@@ -199,6 +236,10 @@ def _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pr
         rc = _lib.diffattn_fwd_prefill_train(*args[:-1], *(_ptr(t) for t in train), args[-1])
     elif opt is None:
         rc = _lib.diffattn_fwd_prefill(*args)
+    elif ws is not None:
+        # ws False: the _ws entry point with no workspace (the library's checks apply)
+        wsp, wsn = (None, 0) if ws is False else (_ptr(ws), ws.numel())
+        rc = _lib.diffattn_fwd_prefill_ws(ctypes.byref(opt), *args[:-1], wsp, wsn, args[-1])
     else:
         rc = _lib.diffattn_fwd_prefill_ex(ctypes.byref(opt), *args)
     _check(rc)

@@ -74,7 +74,7 @@ float score_factor(float scale) {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 104; }
+int diffattn_abi_version(void) { return 105; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -83,7 +83,7 @@ const char* diffattn_status_string(int status) {
     case DIFFATTN_ERR_SHAPE: return "diffattn: a size is non-positive or beyond the supported range";
     case DIFFATTN_ERR_UNSUPPORTED: return "diffattn: unsupported head size (needs d_qk=64, d_v=128)";
     case DIFFATTN_ERR_LAYOUT: return "diffattn: pointer not 16-byte aligned or stride not a multiple of 8 elements";
-    case DIFFATTN_ERR_WORKSPACE: return "diffattn: decode workspace missing, misaligned or too small";
+    case DIFFATTN_ERR_WORKSPACE: return "diffattn: workspace missing, misaligned or too small";
     case DIFFATTN_ERR_HIP: return "diffattn: the HIP runtime refused the kernel launch";
     case DIFFATTN_ERR_VALUE:
       return "diffattn: invalid scalar argument (lambda, eps, scale, dtype, split count or option)";
@@ -93,12 +93,20 @@ const char* diffattn_status_string(int status) {
 
 namespace {
 
-// Shared by diffattn_fwd_prefill_ex and diffattn_fwd_prefill_train; `train`
-// holds the three training outputs or nulls.
+// Bytes of one fp16 copy of a [B, T, H, 64] key tensor in the prefill
+// workspace (256-byte aligned slices).
+size_t rope_keys_bytes(int B, int T, int H) {
+  return ((size_t)B * T * H * diffattn::kDqk * 2 + 255) & ~size_t(255);
+}
+
+// Shared by diffattn_fwd_prefill_ex, _ws and _train; `train` holds the three
+// training outputs or nulls; `ws`: the prefill workspace (rotated keys) or
+// null for the rotation inside the kernels.
 int prefill_impl(const diffattn_options* opt, const void* q1, const void* q2, const void* k1, const void* k2,
                  const void* v, const diffattn_strides* strides, int B, int T, int H, int d_qk, int d_v,
                  float lambda, const float* lambda_per_head, const float* gain, float gn_eps, float scale, void* out,
-                 int out_dtype, float* o_pre, float* const train[3], void* stream) {
+                 int out_dtype, float* o_pre, float* const train[3], void* stream, void* ws = nullptr,
+                 size_t ws_bytes = 0) {
   if (!q1 || !q2 || !k1 || !k2 || !v || !gain || !out) return DIFFATTN_ERR_NULL;
   int rc = check_common(B, H, d_qk, d_v, lambda, gn_eps, scale, out_dtype);
   if (rc != DIFFATTN_OK) return rc;
@@ -148,7 +156,32 @@ int prefill_impl(const diffattn_options* opt, const void* q1, const void* q2, co
     a.o2n = train[1];
     a.lse = train[2];
   }
-  if (diffattn::launch_prefill(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (ws != nullptr && a.rope.mode != 0) {
+    // Rotate both key tensors once into the workspace (fp16, C-contiguous);
+    // the prefill then stages them like plain keys.
+    const size_t one = rope_keys_bytes(B, T, H);
+    if (ws_bytes < 2 * one || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return DIFFATTN_ERR_WORKSPACE;
+    diffattn::RopeKeysArgs r{};
+    r.k1 = a.k1;
+    r.k2 = a.k2;
+    r.s1 = a.sk1;
+    r.s2 = a.sk2;
+    r.out1 = static_cast<uint16_t*>(ws);
+    r.out2 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + one);
+    r.B = B;
+    r.T = T;
+    r.H = H;
+    r.rope = a.rope;
+    if (diffattn::launch_rope_keys(r, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
+    const diffattn::Strides kc = to_internal(contiguous(T, H, d_qk));
+    a.k1 = r.out1;
+    a.k2 = r.out2;
+    a.sk1 = kc;
+    a.sk2 = kc;
+    a.keys_rotated = 1;
+  }
+  if (diffattn::launch_prefill(a, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
   return DIFFATTN_OK;
 }
 
@@ -160,6 +193,22 @@ int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void* q1, const v
                             float gn_eps, float scale, void* out, int out_dtype, float* o_pre, void* stream) {
   return prefill_impl(opt, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head, gain, gn_eps,
                       scale, out, out_dtype, o_pre, nullptr, stream);
+}
+
+size_t diffattn_prefill_workspace_bytes(const diffattn_options* opt, int B, int T, int H) {
+  if (B <= 0 || T <= 0 || H <= 0 || (int64_t)B * H > (1 << 24) || T > (1 << 22)) return 0;
+  if (!opt || opt->rope == DIFFATTN_ROPE_NONE) return 0;
+  return 2 * rope_keys_bytes(B, T, H);
+}
+
+int diffattn_fwd_prefill_ws(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,
+                            const void* k2, const void* v, const diffattn_strides* strides, int B, int T, int H,
+                            int d_qk, int d_v, float lambda, const float* lambda_per_head, const float* gain,
+                            float gn_eps, float scale, void* out, int out_dtype, float* o_pre, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (opt && opt->rope != DIFFATTN_ROPE_NONE && workspace == nullptr) return DIFFATTN_ERR_WORKSPACE;
+  return prefill_impl(opt, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head, gain, gn_eps,
+                      scale, out, out_dtype, o_pre, nullptr, stream, workspace, workspace_bytes);
 }
 
 int diffattn_fwd_prefill_train(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,

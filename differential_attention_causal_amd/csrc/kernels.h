@@ -32,6 +32,7 @@ struct PrefillArgs {
   int B, T, H;
   int window;             // > 0: query i sees keys i-window+1 .. i; 0: every key <= i
   RopeArgs rope;          // token t at position rope.pos0 + t
+  int keys_rotated;       // rope on: k1, k2 hold the keys already rotated, as fp16
   float c;                // scale * log2(e): scores are kept in base-2 units
   float lambda;           // used when lambda_h is null
   const float* lambda_h;  // [H] or null
@@ -86,6 +87,18 @@ struct RopeApplyArgs {
   uint16_t* out;
   Strides sx, so;
   const int32_t* pos_start;  // [B] or null
+  int B, T, H;
+  RopeArgs rope;
+};
+
+// Both key tensors of a prefill rotated once (rope.h) into fp16 copies,
+// C-contiguous [B, T, H, 64].
+struct RopeKeysArgs {
+  const uint16_t* k1;
+  const uint16_t* k2;
+  Strides s1, s2;
+  uint16_t* out1;
+  uint16_t* out2;
   int B, T, H;
   RopeArgs rope;
 };
@@ -152,6 +165,7 @@ void rope_phases(float theta, RopeArgs& r);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t stream);
+hipError_t launch_rope_keys(const RopeKeysArgs& a, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace diffattn

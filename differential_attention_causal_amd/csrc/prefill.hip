@@ -130,7 +130,7 @@ __device__ __forceinline__ void stage_load(Staged& st, const PrefillArgs& a, con
                                            int k0, int kend, int tid) {
   const int tile = __builtin_amdgcn_readfirstlane(tid / kTileThreads);
   const int kbase = k0 + tile * kBN;
-  if constexpr (kRope != 0) {
+  if constexpr (kRope == 1 || kRope == 2) {
     st.kpos = a.rope.pos0 + (uint32_t)(kbase + ((tid % kTileThreads) >> 3));
     st.k1 = load_krow(rows_rsrc(kb1, a.sk1.t, kbase, kend, kDqk), off.k1, kRope == 1);
     st.k2 = load_krow(rows_rsrc(kb2, a.sk2.t, kbase, kend, kDqk), off.k2, kRope == 1);
@@ -462,7 +462,9 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// S^T = K Q^T of one tile for both maps (bf16 operands, K from LDS).
+// S^T = K Q^T of one tile for both maps, K from LDS: bf16 operands, or fp16
+// (kF16: rotated keys and queries, see rope_query).
+template <bool kF16>
 __device__ __forceinline__ void scores_tile(const char* kt, int lq, int hf, int ksw, const bf16x8 (&qa)[4],
                                             const bf16x8 (&qb2)[4], f32x16& s1, f32x16& s2) {
   s1 = f32x16{};
@@ -473,8 +475,15 @@ __device__ __forceinline__ void scores_tile(const char* kt, int lq, int hf, int 
     const int off = krow + (((2 * s + hf) ^ ksw) << 4);
     const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + off);
     const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kt + kKBytes + off);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qa[s], s1, 0, 0, 0);
-    s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qb2[s], s2, 0, 0, 0);
+    if constexpr (kF16) {
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, ka), __builtin_bit_cast(f16x8, qa[s]), s1,
+                                                  0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kb), __builtin_bit_cast(f16x8, qb2[s]),
+                                                  s2, 0, 0, 0);
+    } else {
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qa[s], s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qb2[s], s2, 0, 0, 0);
+    }
   }
 }
 
@@ -563,7 +572,7 @@ __device__ __forceinline__ void pp_load_v(Staged& st, const KeyRes& r, const Sta
 constexpr int kPPStage = 2 * kTile;
 constexpr int kPPSmem = 2 * kPPStage + kDv * 4 + 16;
 
-template <bool kTrain>
+template <bool kTrain, bool kRopeQ>
 __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int item) {
   constexpr int kStage = kPPStage;
   f32x4* const gain_s = reinterpret_cast<f32x4*>(smem + 2 * kStage);
@@ -607,6 +616,8 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
       qb2[s] = __builtin_bit_cast(bf16x8, x2);
     }
   }
+  // With pre-rotated keys, the query is rotated here (fp16 operands).
+  if constexpr (kRopeQ) rope_query(qa, qb2, hf, a.rope.pos0 + (uint32_t)q, a.rope.mode, a.rope);
 
   f32x16 O1[4], O2[4];
 #pragma unroll
@@ -658,7 +669,7 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
     const int j = tile0 + grp;
     if (live(j)) {
       f32x16 s1, s2;
-      scores_tile(smem + grp * kTile, lq, hf, ksw, qa, qb2, s1, s2);
+      scores_tile<kRopeQ>(smem + grp * kTile, lq, hf, ksw, qa, qb2, s1, s2);
       mask_tile(a, s1, s2, j, wave_last_tile, q_first, q, hf);
       softmax_step(s1, c, m1, l1, O1, p1a, p1b);
       softmax_step(s2, c, m2, l2, O2, p2a, p2b);
@@ -685,7 +696,7 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
     pp_dma_k(res, soff, slot0 + (it & 1) * kStage, key0(it + 2), wq);
     __builtin_amdgcn_sched_barrier(0);
     if (lj) pv_pair(cur, lq, hf, 2, p1a, p1b, p2a, p2b, O1, O2);
-    if (next) scores_tile(nxt, lq, hf, ksw, qa, qb2, s1, s2);
+    if (next) scores_tile<kRopeQ>(nxt, lq, hf, ksw, qa, qb2, s1, s2);
     __builtin_amdgcn_s_setprio(0);
     phase_barrier();
     // Vector phase.
@@ -714,7 +725,7 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
 // back to back: the longest block with the shortest, so one workgroup per CU
 // carries the same work everywhere, and a head's blocks stay on the XCD that
 // holds its keys in L2 (B*H a multiple of 8).  An odd middle row runs alone.
-template <bool kTrain>
+template <bool kTrain, bool kRopeQ>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_pp_kernel(PrefillArgs a) {
   // One LDS object (the stages, then the epilogue's gain and lambda): the
@@ -724,16 +735,20 @@ prefill_pp_kernel(PrefillArgs a) {
   const int BH = a.B * a.H;
   const int nqb = (a.T + kBM - 1) / kBM;
   const int r = (int)blockIdx.x / BH, bh = (int)blockIdx.x % BH;
-  pp_item<kTrain>(a, smem, (int)blockIdx.x);
+  pp_item<kTrain, kRopeQ>(a, smem, (int)blockIdx.x);
   if (nqb - 1 - r > r) {
     __syncthreads();  // the first block's epilogue is done with LDS
-    pp_item<kTrain>(a, smem, (nqb - 1 - r) * BH + bh);
+    pp_item<kTrain, kRopeQ>(a, smem, (nqb - 1 - r) * BH + bh);
   }
-}// kGroups wave groups of four waves share a workgroup's 128 queries and split
+}
+
+// kGroups wave groups of four waves share a workgroup's 128 queries and split
 // its key tiles.  Two waves per SIMD (<= 256 VGPRs each): one wave's softmax
 // VALU work overlaps the other's matrix products.
-// kRope: the rotary embedding mode (0 none, 1 split-half, 2 interleaved),
-// fixed at compile time so the plain kernel carries none of its registers.
+// kRope: the rotary embedding, fixed at compile time so the plain kernel
+// carries none of its registers: 0 none; 1 split-half and 2 interleaved, with
+// the key tiles rotated while staged; 3 keys rotated beforehand (fp16 copies
+// moved by DMA like plain keys), the query rotated here in mode a.rope.mode.
 template <int kGroups, int kRope>
 __global__ void __launch_bounds__(64 * kGroupWaves * kGroups) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillArgs a) {
@@ -784,7 +799,9 @@ prefill_kernel(PrefillArgs a) {
       qb2[s] = __builtin_bit_cast(bf16x8, x2);
     }
   }
-  if constexpr (kRope != 0) {
+  if constexpr (kRope == 3) {
+    rope_query(qa, qb2, hf, a.rope.pos0 + (uint32_t)q, a.rope.mode, a.rope);
+  } else if constexpr (kRope != 0) {
     // Phase table for the key tiles, then the lane's own query in registers.
     if (tid < 32) {
 #pragma unroll
@@ -811,10 +828,10 @@ prefill_kernel(PrefillArgs a) {
   const StageOffsets soff = stage_offsets<kRope>(a, tid);
 
   Staged st;
-  if constexpr (kRope == 0) stage_dma_k(a, kb1, kb2, soff, smem, tile0 * kBN, kend, tid);
+  if constexpr (kRope == 0 || kRope == 3) stage_dma_k(a, kb1, kb2, soff, smem, tile0 * kBN, kend, tid);
   stage_load<kRope>(st, a, kb1, kb2, vbase, soff, tile0 * kBN, kend, tid);
   stage_store<kRope>(st, smem, tid, rope_tab);
-  if constexpr (kRope == 0) wait_dma();
+  if constexpr (kRope == 0 || kRope == 3) wait_dma();
   __syncthreads();
 
   for (int it = 0; it < nsteps; ++it) {
@@ -822,7 +839,8 @@ prefill_kernel(PrefillArgs a) {
     char* nxt = smem + ((it + 1) & 1) * kStage;
     const bool more = it + 1 < nsteps;
     if (more) {
-      if constexpr (kRope == 0) stage_dma_k(a, kb1, kb2, soff, nxt, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
+      if constexpr (kRope == 0 || kRope == 3)
+        stage_dma_k(a, kb1, kb2, soff, nxt, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
       stage_load<kRope>(st, a, kb1, kb2, vbase, soff, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
     }
 
@@ -887,7 +905,7 @@ prefill_kernel(PrefillArgs a) {
     }
 
     if (more) stage_store<kRope>(st, nxt, tid, rope_tab);
-    if constexpr (kRope == 0) wait_dma();
+    if constexpr (kRope == 0 || kRope == 3) wait_dma();
     __syncthreads();
   }
 
@@ -918,18 +936,31 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     cus = 256;
   const bool split = grid <= 2 * (int64_t)cus;
   const int64_t row_max = std::max(std::max(a.sk1.t, a.sk2.t), a.sv.t);
+  // Keys already rotated (fp16 copies): they are staged like plain keys, and
+  // only the queries turn inside the kernels.
+  const bool prerot = a.rope.mode != 0 && a.keys_rotated;
   // The ping-pong kernel addresses a (b, h)'s key rows from one buffer base
   // with 32-bit offsets (up to about T + 192 rows).
-  const bool pingpong = split && a.rope.mode == 0 && (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31);
+  const bool pingpong = split && (a.rope.mode == 0 || prerot) && !(prerot && a.o1n != nullptr) &&
+                        (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31);
   if (pingpong) {
     const dim3 gp((unsigned)((int64_t)((nqb + 1) / 2) * a.B * a.H));
-    if (a.o1n != nullptr)
-      hipLaunchKernelGGL(prefill_pp_kernel<true>, gp, dim3(512), 0, stream, a);
+    if (prerot)
+      hipLaunchKernelGGL((prefill_pp_kernel<false, true>), gp, dim3(512), 0, stream, a);
+    else if (a.o1n != nullptr)
+      hipLaunchKernelGGL((prefill_pp_kernel<true, false>), gp, dim3(512), 0, stream, a);
     else
-      hipLaunchKernelGGL(prefill_pp_kernel<false>, gp, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((prefill_pp_kernel<false, false>), gp, dim3(512), 0, stream, a);
     return hipGetLastError();
   }
   const dim3 g((unsigned)grid), b1(64 * kGroupWaves), b2(64 * kGroupWaves * 2);
+  if (prerot) {
+    if (split)
+      hipLaunchKernelGGL((prefill_kernel<2, 3>), g, b2, 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<1, 3>), g, b1, 0, stream, a);
+    return hipGetLastError();
+  }
   switch (a.rope.mode * 2 + (split ? 1 : 0)) {
     case 0: hipLaunchKernelGGL((prefill_kernel<1, 0>), g, b1, 0, stream, a); break;
     case 1: hipLaunchKernelGGL((prefill_kernel<2, 0>), g, b2, 0, stream, a); break;

@@ -1,6 +1,7 @@
 // Standalone rotary embedding of a [B, T, H, 64] bf16 tensor (results rounded
-// to bf16), and the host computation of the per-pair phases that every RoPE
-// kernel here uses.  The angle convention is the one in rope.h.
+// to bf16), the prefill's key pre-pass (both key tensors rotated once into
+// fp16 copies), and the host computation of the per-pair phases that every
+// RoPE kernel here uses.  The angle convention is the one in rope.h.
 #include <cmath>
 
 #include "rope.h"
@@ -46,7 +47,44 @@ __global__ void __launch_bounds__(kThreads) rope_apply_kernel(RopeApplyArgs a) {
   if (live) *reinterpret_cast<rope_u32x4*>(a.out + b * a.so.b + t * a.so.t + h * a.so.h + 8 * ch) = v[0];
 }
 
+// The prefill's keys, rotated once per token instead of once per query block
+// that reads them: K1 and K2 of one token in the same lanes (they share the
+// angles), results rounded to fp16 as the prefill's score products take them.
+__global__ void __launch_bounds__(kThreads) rope_keys_kernel(RopeKeysArgs a) {
+  __shared__ uint64_t tab[32];
+  if (threadIdx.x < 32) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      if (c == (int)threadIdx.x) tab[c] = a.rope.phase[c];
+  }
+  __syncthreads();
+  const int64_t vec = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
+  const int ch = threadIdx.x & 7;
+  const int64_t nvec = (int64_t)a.B * a.T * a.H;
+  const bool live = vec < nvec;
+  const int h = live ? (int)(vec % a.H) : 0;
+  const int64_t t = live ? (vec / a.H) % a.T : 0;
+  const int b = live ? (int)(vec / ((int64_t)a.H * a.T)) : 0;
+  rope_u32x4 v[2] = {rope_u32x4{0, 0, 0, 0}, rope_u32x4{0, 0, 0, 0}};
+  if (live) {
+    v[0] = *reinterpret_cast<const rope_u32x4*>(a.k1 + b * a.s1.b + t * a.s1.t + h * a.s1.h + 8 * ch);
+    v[1] = *reinterpret_cast<const rope_u32x4*>(a.k2 + b * a.s2.b + t * a.s2.t + h * a.s2.h + 8 * ch);
+  }
+  rope_chunks<2, true>(v, ch, a.rope.pos0 + (uint32_t)t, a.rope.mode, tab);
+  if (live) {
+    *reinterpret_cast<rope_u32x4*>(a.out1 + vec * 64 + 8 * ch) = v[0];
+    *reinterpret_cast<rope_u32x4*>(a.out2 + vec * 64 + 8 * ch) = v[1];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rope_keys(const RopeKeysArgs& a, hipStream_t stream) {
+  const int64_t nvec = (int64_t)a.B * a.T * a.H;
+  const int64_t blocks = (nvec + kThreads / 8 - 1) / (kThreads / 8);
+  hipLaunchKernelGGL(rope_keys_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t stream) {
   const int64_t nvec = (int64_t)a.B * a.T * a.H;

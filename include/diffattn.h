@@ -64,7 +64,7 @@ enum diffattn_status {
     DIFFATTN_ERR_SHAPE = 2,       /* a size is non-positive or too large */
     DIFFATTN_ERR_UNSUPPORTED = 3, /* head sizes other than d_qk=64, d_v=128 */
     DIFFATTN_ERR_LAYOUT = 4,      /* misaligned pointer or stride */
-    DIFFATTN_ERR_WORKSPACE = 5,   /* decode workspace missing or too small */
+    DIFFATTN_ERR_WORKSPACE = 5,   /* workspace missing, misaligned or too small */
     DIFFATTN_ERR_HIP = 6,         /* the HIP runtime refused a launch */
     DIFFATTN_ERR_VALUE = 7        /* non-finite lambda/eps/scale, eps < 0, bad dtype, split count or option */
 };
@@ -187,6 +187,35 @@ DIFFATTN_API int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void
                                          const float* gain, float gn_eps, float scale, void* out,
                                          int out_dtype, float* o_pre, void* stream);
 
+/*
+ * Bytes of device workspace diffattn_fwd_prefill_ws needs for these options
+ * and sizes: with rope on, one fp16 copy of each of K1 and K2, rotated once
+ * (2 * B * T * H * 64 * 2 bytes, rounded up to 256-byte slices); 0 without
+ * rope (and for invalid sizes).
+ */
+DIFFATTN_API size_t diffattn_prefill_workspace_bytes(const diffattn_options* opt, int B, int T, int H);
+
+/*
+ * diffattn_fwd_prefill_ex with a workspace.  With rope on, K1 and K2 are first
+ * rotated into the workspace, each key once (the same fp32 rotation and fp16
+ * rounding the kernels of diffattn_fwd_prefill_ex apply to every key tile they
+ * stage), and the prefill then reads those copies: the query blocks no longer
+ * repeat the rotation of the keys they share.  Without rope the workspace is
+ * not used (may be NULL).
+ *   workspace : >= diffattn_prefill_workspace_bytes(opt, B, T, H) bytes,
+ *               256-byte aligned; contents need no initialisation
+ * Errors as for diffattn_fwd_prefill_ex, plus DIFFATTN_ERR_WORKSPACE (rope on
+ * with a missing, misaligned or too small workspace).  The workspace is
+ * overwritten on the stream: calls that share one must not overlap.
+ */
+DIFFATTN_API int diffattn_fwd_prefill_ws(const diffattn_options* opt, const void* q1, const void* q2,
+                                         const void* k1, const void* k2, const void* v,
+                                         const diffattn_strides* strides, int B, int T, int H, int d_qk,
+                                         int d_v, float lambda, const float* lambda_per_head,
+                                         const float* gain, float gn_eps, float scale, void* out,
+                                         int out_dtype, float* o_pre, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
 /* diffattn_fwd_decode with variants (opt may be NULL: every cached position).
  * Errors as for diffattn_fwd_prefill_ex, and DIFFATTN_ERR_VALUE for a ring
  * cache with window > L.  With a ring cache, seqlens may exceed L (up to
@@ -299,7 +328,8 @@ DIFFATTN_API const char* diffattn_status_string(int status);
 
 /* Library ABI version (major * 100 + minor): 101 adds the *_ex entry points,
  * 102 the rotary embedding (diffattn_options.rope, diffattn_rope_apply), 103
- * the training forward and the backward pass, 104 grouped attention. */
+ * the training forward and the backward pass, 104 grouped attention, 105 the
+ * prefill workspace entry points (keys rotated once). */
 DIFFATTN_API int diffattn_abi_version(void);
 
 #ifdef __cplusplus

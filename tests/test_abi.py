@@ -27,11 +27,12 @@ def test_header_symbols_exported():
                           "diffattn_fwd_prefill_ex", "diffattn_fwd_decode_ex", "diffattn_rope_apply",
                           "diffattn_fwd_prefill_train", "diffattn_bwd_workspace_bytes", "diffattn_bwd_prefill",
                           "diffattn_grouped_workspace_bytes", "diffattn_fwd_grouped",
+                          "diffattn_prefill_workspace_bytes", "diffattn_fwd_prefill_ws",
                           "diffattn_status_string", "diffattn_abi_version"}
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 104
+    assert da.diffattn_abi_version() == 105
 
 
 def test_status_strings():
@@ -129,6 +130,37 @@ def test_prefill_ex_options(opt, rc):
 ])
 def test_decode_ex_options(opt, rc):
     assert (_decode(opt=opt, L=0) if rc == ESHAPE else _decode(opt=opt)) == rc
+
+
+def _prefill_ws(opt, ws=A, wsb=1 << 30, **kw):
+    args = dict(q1=A, q2=A, k1=A, k2=A, v=A, st=None, B=1, T=128, H=2, dqk=64, dv=128, lam=0.5, lamh=None,
+                gain=A, eps=1e-5, scale=0.0, out=A, odt=0, opre=None)
+    args.update(kw)
+    o = da._Options(**opt)
+    return da._lib.diffattn_fwd_prefill_ws(ctypes.byref(o), *args.values(), ws, wsb, None)
+
+
+def test_prefill_workspace_bytes():
+    one = -(-1 * 4096 * 16 * 64 * 2 // 256) * 256
+    assert da.diffattn_prefill_workspace_bytes(1, 4096, 16, rope=1) == 2 * one
+    assert da.diffattn_prefill_workspace_bytes(2, 77, 3, rope=2) == 2 * (-(-2 * 77 * 3 * 128 // 256) * 256)
+    assert da.diffattn_prefill_workspace_bytes(1, 4096, 16) == 0  # no rope: nothing to rotate
+    assert da.diffattn_prefill_workspace_bytes(0, 4096, 16, rope=1) == 0
+    assert da.diffattn_prefill_workspace_bytes(1, (1 << 22) + 1, 16, rope=1) == 0
+    assert da._lib.diffattn_prefill_workspace_bytes(None, 1, 128, 2) == 0
+
+
+@pytest.mark.parametrize("opt,kw,rc", [
+    (dict(rope=1, rope_theta=5e5), dict(ws=None), EWS),         # rope needs the workspace
+    (dict(rope=2, rope_theta=5e5), dict(ws=A + 16), EWS),       # 256-byte alignment
+    (dict(rope=1, rope_theta=5e5), dict(wsb=2 * 128 * 2 * 64 * 2 - 1), EWS),
+    (dict(rope=1, rope_theta=5e5), dict(T=0), ESHAPE),          # arguments checked before the workspace
+    (dict(rope=1, rope_theta=-1.0), dict(), EVALUE),
+    (dict(rope=1, rope_theta=5e5), dict(k1=A + 2), ELAYOUT),
+    (dict(), dict(ws=None, T=0), ESHAPE),                        # no rope: the workspace is not needed
+])
+def test_prefill_ws_rejects(opt, kw, rc):
+    assert _prefill_ws(opt, **kw) == rc
 
 
 def test_options_layout():

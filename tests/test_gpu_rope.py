@@ -1,9 +1,11 @@
 """GPU parity of the rotary position embedding (Motif 2.6B explainer, section
 "The block": RoPE with base 500,000) through the C ABI against the fp64
-oracle: the standalone rotation, the prefill with its fused rotation of Q1,
-Q2, K1, K2 (alone and with a sliding window), and the decode, which rotates
-its query against a cache of already rotated keys.  Every case prints its
-name first so a failure is attributable."""
+oracle: the standalone rotation, the prefill with its rotation of Q1, Q2, K1,
+K2 (alone and with a sliding window) in both forms (keys rotated once into the
+workspace by diffattn_fwd_prefill_ws, or inside the kernels by
+diffattn_fwd_prefill_ex), and the decode, which rotates its query against a
+cache of already rotated keys.  Every case prints its name first so a failure
+is attributable."""
 import numpy as np
 import pytest
 
@@ -75,32 +77,66 @@ def _inputs(B, T, H, seed, lam=0.8, lam_range=None):
     return synth.make_prefill_inputs(wl)
 
 
-def _prefill(x, mode, pos0=0, window=0, per_head=False):
+def _prefill(x, mode, pos0=0, window=0, per_head=False, ws=True):
     q1, q2, k1, k2, v = (to_dev(x[n]) for n in ("q1", "q2", "k1", "k2", "v"))
     gain = f32_dev(x["gain"])
     lam = f32_dev(x["lam"]) if per_head else float(x["lam"][0])
     B, T, H, _ = x["q1"].shape
     o_pre = torch.empty((B, T, H, 128), dtype=torch.float32, device="cuda")
     out = da.diffattn_fwd_prefill_ex(q1, q2, k1, k2, v, lam, gain, eps=x["eps"], scale=x["scale"], o_pre=o_pre,
-                                     window=window, rope=mode, rope_theta=THETA, rope_pos0=pos0)
+                                     window=window, rope=mode, rope_theta=THETA, rope_pos0=pos0, workspace=ws)
     torch.cuda.synchronize()
     return out, o_pre
 
 
-# Small grids take the split-key workgroup, the (1, 8192, 16) grid the
-# four-wave one.
+# Small grids take the split-key workgroups (ping-pong with pre-rotated keys,
+# lock-step with the rotation inside), the (1, 8192, 16) grid the four-wave
+# one.
+@pytest.mark.parametrize("ws", [True, False], ids=["keys-rotated-once", "rotated-in-kernel"])
 @pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("B,T,H,pos0,window", [(1, 1, 1, 0, 0), (1, 77, 2, 0, 0), (2, 300, 3, 5, 0),
                                                (1, 515, 2, 100000, 0), (1, 700, 2, 3, 128)])
-def test_prefill_rope_all_rows(mode, B, T, H, pos0, window):
-    _say("prefill rope all rows", mode, B, T, H, pos0, window)
+def test_prefill_rope_all_rows(mode, B, T, H, pos0, window, ws):
+    _say("prefill rope all rows", mode, B, T, H, pos0, window, "workspace" if ws else "in-kernel")
     x = _inputs(B, T, H, seed=400 + T)
     o_ref, y_ref = oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"],
                                   x["scale"], window=window, rope=mode, rope_theta=THETA, rope_pos0=pos0)
-    out, o_pre = _prefill(x, mode, pos0=pos0, window=window)
+    out, o_pre = _prefill(x, mode, pos0=pos0, window=window, ws=ws)
     m = metrics(out.float().cpu().numpy(), y_ref, o_pre.cpu().numpy(), o_ref)
     _say("metrics", m)
-    assert_parity(m, (mode, B, T, H, pos0, window))
+    assert_parity(m, (mode, B, T, H, pos0, window, ws))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_prefill_rope_two_forms_agree(mode):
+    # Both forms rotate the keys in fp32 and round them to fp16; the two code
+    # paths may contract the rotation's products differently (a last-bit
+    # difference in some rotated keys), and their kernels sum in different
+    # orders: far below the 5e-3 parity bound, well above fp32 rounding.
+    _say("prefill rope: workspace form vs in-kernel form", mode)
+    x = _inputs(2, 333, 3, seed=77 + mode)
+    _, a = _prefill(x, mode, pos0=11, ws=True)
+    _, b = _prefill(x, mode, pos0=11, ws=False)
+    rel = float((a - b).norm() / b.norm())
+    _say("rel", rel)
+    assert rel < 1e-4
+    # a caller's workspace, reused by a second call of another size
+    q = {n: to_dev(x[n]) for n in ("q1", "q2", "k1", "k2", "v")}
+    need = da.diffattn_prefill_workspace_bytes(2, 333, 3, rope=mode)
+    wsbuf = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o1 = torch.empty((2, 333, 3, 128), dtype=torch.float32, device="cuda")
+    da.diffattn_fwd_prefill_ws(q["q1"], q["q2"], q["k1"], q["k2"], q["v"], float(x["lam"][0]), f32_dev(x["gain"]),
+                               wsbuf, eps=x["eps"], scale=x["scale"], o_pre=o1, rope=mode, rope_theta=THETA,
+                               rope_pos0=11)
+    y = _inputs(1, 100, 3, seed=5)
+    _, c = _prefill(y, mode, pos0=11, ws=wsbuf)
+    _, d = _prefill(y, mode, pos0=11, ws=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, a) and torch.equal(c, d)
+    # rope on without a workspace is an error of the _ws entry point
+    with pytest.raises(RuntimeError, match="workspace"):
+        da.diffattn_fwd_prefill_ws(q["q1"], q["q2"], q["k1"], q["k2"], q["v"], 0.5, f32_dev(x["gain"]), None,
+                                   rope=mode, rope_theta=THETA)
 
 
 def _rows(B, T, H, rng, n_random=40):
@@ -110,11 +146,12 @@ def _rows(B, T, H, rng, n_random=40):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("mode,B,T,H", [(1, 1, 4096, 16), (2, 1, 4096, 16), (1, 1, 8192, 16)])
-def test_prefill_rope_large_sampled(mode, B, T, H):
-    _say("prefill rope sampled rows", mode, B, T, H)
+@pytest.mark.parametrize("mode,B,T,H,ws", [(1, 1, 4096, 16, True), (2, 1, 4096, 16, True), (1, 1, 8192, 16, True),
+                                         (2, 1, 8192, 16, False)])
+def test_prefill_rope_large_sampled(mode, B, T, H, ws):
+    _say("prefill rope sampled rows", mode, B, T, H, ws)
     x = _inputs(B, T, H, seed=T + mode)
-    out, o_pre = _prefill(x, mode)
+    out, o_pre = _prefill(x, mode, ws=ws)
     assert bool(torch.isfinite(out.float()).all())
     rows = _rows(B, T, H, np.random.default_rng(T))
     o_ref, y_ref = oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"],
