@@ -191,8 +191,9 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
                                   window=dw.window)
 
     def prefill_rope():
-        # the Motif 2.6B layer itself: RoPE with base 500,000 fused in front
-        da.diffattn_fwd_prefill_ex(R["q1"], R["q2"], R["k1"], R["k2"], R["v"], rw.lam, rg, eps=rw.eps,
+        # the Motif 2.6B layer itself: RoPE with base 500,000 in front (keys
+        # rotated once into the workspace, queries in the prefill's prologue)
+        da.diffattn_fwd_prefill_ws(R["q1"], R["q2"], R["k1"], R["k2"], R["v"], rw.lam, rg, r_ws, eps=rw.eps,
                                    scale=rw.scale, out=r_out, rope=da.ROPE_HALF, rope_theta=ROPE_THETA)
 
     rw = synth.WORKLOADS[PREFILL_WL]
@@ -200,6 +201,8 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     R = {n: to_dev(xr[n], dev) for n in ("q1", "q2", "k1", "k2", "v")}
     rg = f32_dev(xr["gain"], dev)
     r_out = torch.empty((rw.B, rw.T, rw.H, rw.d_v), dtype=torch.bfloat16, device=dev)
+    r_ws = torch.empty(da.diffattn_prefill_workspace_bytes(rw.B, rw.T, rw.H, rope=da.ROPE_HALF),
+                       dtype=torch.uint8, device=dev)
 
     # backward of the T=4096 layer: training forward once, then the timed
     # backward (dy ~ N(0,1) bf16, seeded like the inputs)
