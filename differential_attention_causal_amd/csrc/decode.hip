@@ -8,6 +8,7 @@
 // A merge kernel per (b, h) rescales the splits to a common max per map, keeps
 // the maps apart until o = O1/L1 - lambda O2/L2, then applies the per-head
 // GroupNorm (Motif 2.6B explainer, "Differential attention", figure 1 caption).
+// With one split the split kernel does that epilogue itself.
 //
 // Inside a split, keys go in blocks of kKB: scores (8 lanes per key, exact
 // bf16 products, fp32 accumulation) -> LDS; block max and exp2 in fp32 (P stays
@@ -235,18 +236,53 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  {
-    const int map = tid >> 7, ch = tid & 127;
-    float s = 0.f;
+  const int map = tid >> 7, ch = tid & 127;
+  float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += acc[w][map][ch];
+  for (int w = 0; w < kWaves; ++w) sum += acc[w][map][ch];
+  if (a.splits > 1) {
     float* r = rec + map * kPartialStride;
-    r[2 + ch] = s;
+    r[2 + ch] = sum;
     if (ch == 0) {
       r[0] = map ? m2 : m1;
       r[1] = map ? l2 : l1;
     }
+    return;
   }
+  // One split: the merge of a single record is the record itself (weight
+  // 2^0 = 1), so the epilogue runs here with the merge kernel's arithmetic,
+  // threads 0 .. 127 one channel each (the other two waves only pass the
+  // barriers).
+  __syncthreads();  // every wave has read acc
+  acc[0][map][ch] = sum;
+  __syncthreads();
+  const bool chan = tid < kDv;
+  const bool empty = m1 == -__builtin_inff();  // no cached position (uniform)
+  float o = 0.f, y = 0.f;
+  if (!empty) {
+    const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
+    if (chan) {
+#pragma clang fp contract(off)
+      o = acc[0][0][ch] / l1 - lam * (acc[0][1][ch] / l2);
+    }
+    const float s = wave_sum(o);
+    if (lane == 0 && chan) red[0][wave][0] = s;
+    __syncthreads();
+    const float mu = (red[0][0][0] + red[0][1][0]) * (1.0f / kDv);
+    const float d = chan ? o - mu : 0.f;
+    const float v = wave_sum(d * d);
+    if (lane == 0 && chan) red[1][wave][0] = v;
+    __syncthreads();
+    const float var = (red[1][0][0] + red[1][1][0]) * (1.0f / kDv);
+    if (chan) y = d * (1.0f / __builtin_sqrtf(var + a.eps)) * a.gain[(int64_t)head * kDv + ch];
+  }
+  if (!chan) return;
+  const int64_t row = (int64_t)bh * kDv + ch;
+  if (a.o_pre) a.o_pre[row] = o;
+  if (a.out_f32)
+    static_cast<float*>(a.out)[row] = y;
+  else
+    static_cast<__bf16*>(a.out)[row] = (__bf16)y;
 }
 
 // Merge the splits of one (b, h): one thread per channel.  Every split
@@ -329,7 +365,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int64_t bh = (int64_t)a.B * a.H;
   hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)(bh * a.splits)), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.splits == 1) return e;  // one split finishes in the split kernel
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)bh), dim3(kDv), 0, stream, a);
   return hipGetLastError();
 }
