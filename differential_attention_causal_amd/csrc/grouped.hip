@@ -15,7 +15,8 @@
 // (softmax_step), O^T = V^T P^T on v_mfma_f32_32x32x16_f16 with P in fp16 and
 // V converted to fp16 on staging.  Key tiles reach LDS by buffer-load DMA.  A
 // grid that fits on the chip in one round uses two groups of four waves that
-// take alternate key tiles and merge at the end (as the prefill does).
+// take alternate key tiles and merge at the end, in the prefill's ping-pong
+// form (grouped_pp_kernel); larger grids use four-wave workgroups.
 #include "kernels.h"
 #include "tile.h"
 
@@ -154,6 +155,182 @@ grouped_attn_kernel(GroupedArgs a) {
     }
 }
 
+// Ping-pong split-key form of the single-map kernel (the prefill's ping-pong
+// kernel with one map and per-head values): two groups of four waves on the
+// same 128 queries take alternate key tiles, group 1 one phase behind group
+// 0, so on every SIMD one wave's matrix phase (O += V P of its tile, then
+// S = K Q^T of its next) runs beside the other wave's vector phase (softmax,
+// V staging).  Keys come by DMA two steps ahead from buffer resources fixed
+// for the kernel (the host keeps a head's key span under 2^31 bytes), values
+// one step ahead through registers.  Workgroup r * B*nH + bh runs query-block
+// rows r and nqb - 1 - r of (b, head) = bh back to back.
+constexpr int kGStage = 2 * kStage;  // one step: a tile for each group
+constexpr int kGSmem = 2 * kGStage > kMergeBytes ? 2 * kGStage : kMergeBytes;
+
+__device__ __forceinline__ void gpp_block(const GroupedArgs& a, char* smem, int item) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / 4, wq = wave % 4;
+  const int lane = tid & 63, hf = lane >> 5, lq = lane & 31, rt = tid & 255;
+  const int nqb = (a.T + kBM - 1) / kBM, BH = a.B * a.nH;
+  const int qb = nqb - 1 - item / BH;
+  const int bh = item % BH, head = bh % a.nH, b = bh / a.nH;
+  const int q_first = qb * kBM + 32 * wq, q = q_first + lq;
+  const bool wave_live = q_first < a.T, ok = q < a.T;
+  const int ntiles = min(qb * (kBM / kBN) + kBM / kBN, (a.T + kBN - 1) / kBN);
+  const int nsteps = (ntiles + 1) / 2;
+  const int kend = min(a.T, ntiles * kBN);
+  const int last_tile = q_first / kBN;
+  auto live = [&](int j) { return wave_live && j <= last_tile; };
+
+  bf16x8 qa[4];
+  {
+    const uint16_t* p = a.q + (int64_t)b * a.sq.b + (int64_t)q * a.sq.t + (int64_t)head * a.sq.h + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = ok ? *reinterpret_cast<const bf16x8*>(p + 16 * s) : bf16x8{};
+  }
+  const uint16_t* kb = a.k + (int64_t)b * a.sk.b + (int64_t)head * a.sk.h;
+  const uint16_t* vb = a.v + (int64_t)b * a.sv.b + (int64_t)head * a.sv.h;
+  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kb, a.sk.t, 0, kend, kDqk);
+  const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vb, a.sv.t, 0, kend, kDv);
+  const uint32_t ks = (uint32_t)(a.sk.t * 2), vs = (uint32_t)(a.sv.t * 2);
+  // DMA: thread rt of the group fetches key row rt / 8, logical chunk
+  // (rt % 8) ^ kSwz(row), landing at chunk position rt of the group's tile.
+  const int kr = rt >> 3;
+  const uint32_t koff = (uint32_t)((kr * a.sk.t + 8 * ((rt & 7) ^ kSwz(kr))) * 2);
+  // V loads: keys 4(rt % 8) .. +3, channels 4(rt / 8) .. +3 (see load_vt).
+  const uint32_t voff = (uint32_t)((4 * (rt & 7) * a.sv.t + 4 * (rt >> 3)) * 2);
+  auto key0 = [&](int x) { return (2 * x + grp) * kBN; };
+  char* const slot0 = smem + grp * kStage;
+  auto dma_k = [&](char* slot, int k0) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(slot + wq * 1024), 16, koff + (uint32_t)k0 * ks, 0, 0,
+                                             0);
+  };
+  u32x2 vw[4];
+  auto load_v = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vw[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, voff + (uint32_t)(k0 + i) * vs, 0, 0);
+  };
+
+  f32x16 O[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  float m = kNoMax, l = 0.f;
+  const float c = a.c;
+  const int ksw = kSwz(lq);
+  auto scores = [&](const char* kt) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(kt + lq * kKRow + (((2 * k + hf) ^ ksw) << 4)), qa[k], s, 0, 0, 0);
+    return s;
+  };
+  auto mask = [&](f32x16& s, int j) {
+    if (j == last_tile) {
+      // key row 8(i/4) + 4hf + i%4 of tile j is key 32j + row: visible iff <= q
+      const int hi = q - j * kBN - 4 * hf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) > hi) s[i] = -__builtin_inff();
+    }
+  };
+  // O += V^T P for channel blocks cb, cb + 1 (consecutive products on
+  // different accumulators).
+  auto pv_pair = [&](const char* kt, int cb, const f16x8& pa, const f16x8& pb) {
+    const char* vt = kt + kKBytes + lq * kVRow + hf * 16 + cb * 32 * kVRow;
+    const f16x8 a0 = *reinterpret_cast<const f16x8*>(vt), b0 = *reinterpret_cast<const f16x8*>(vt + 32 * kVRow);
+    O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, pa, O[cb], 0, 0, 0);
+    O[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, pa, O[cb + 1], 0, 0, 0);
+    const f16x8 a1 = *reinterpret_cast<const f16x8*>(vt + 32),
+                b1 = *reinterpret_cast<const f16x8*>(vt + 32 * kVRow + 32);
+    O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, pb, O[cb], 0, 0, 0);
+    O[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, pb, O[cb + 1], 0, 0, 0);
+  };
+
+  // Prologue: tile 0 complete in slot 0, K(1) in slot 1, V(1) in registers.
+  dma_k(slot0, key0(0));
+  load_v(key0(0));
+  dma_k(slot0 + kGStage, key0(1));
+  store_vt(vw, slot0 + kKBytes, rt);
+  load_v(key0(1));
+  wait_vm<4>();
+  wait_lds();
+  phase_barrier();
+  f16x8 pa, pb;
+  if (live(grp)) {
+    f32x16 s = scores(slot0);
+    mask(s, grp);
+    softmax_step(s, c, m, l, O, pa, pb);
+  }
+  // Every wave is done reading slot 0's keys before step 0 refills them.
+  phase_barrier();
+  if (grp == 1) phase_barrier();  // group 1 starts one phase late
+
+  for (int it = 0; it < nsteps; ++it) {
+    char* cur = smem + (it & 1) * kGStage + grp * kStage;
+    char* nxt = smem + ((it + 1) & 1) * kGStage + grp * kStage;
+    const int j = 2 * it + grp;
+    const bool next = it + 1 < nsteps && live(j + 2);
+    // Matrix phase.
+    __builtin_amdgcn_s_setprio(1);
+    f32x16 s;
+    const bool lj = live(j);
+    if (lj) pv_pair(cur, 0, pa, pb);
+    // K(it + 2) into slot it % 2 (unconditional: past the last tile the
+    // loads read zeros into a slot nobody reads again).
+    __builtin_amdgcn_sched_barrier(0);
+    dma_k(slot0 + (it & 1) * kGStage, key0(it + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    if (lj) pv_pair(cur, 2, pa, pb);
+    if (next) s = scores(nxt);
+    __builtin_amdgcn_s_setprio(0);
+    phase_barrier();
+    // Vector phase.
+    if (it + 1 < nsteps) store_vt(vw, nxt + kKBytes, rt);
+    load_v(key0(it + 2));
+    if (next) {
+      mask(s, j + 2);
+      softmax_step(s, c, m, l, O, pa, pb);
+    }
+    wait_vm<4>();  // K(it + 2) has landed; only the four V(it + 2) loads may be in flight
+    wait_lds();    // V(it + 1) stored
+    phase_barrier();
+  }
+  if (grp == 0) phase_barrier();
+  wait_vm<0>();  // the zero-filling loads past the last tile, before the merge reuses LDS
+  __syncthreads();
+
+  merge_map(smem, grp, wq, lane, wave_live, m, l, O);
+  if (grp != 0) return;
+  l += __shfl_xor(l, 32);
+  if (!ok) return;
+  const float r = 1.0f / l;
+  float* dst = a.hw + (((int64_t)b * a.T + q) * a.nH + head) * kDv;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = O[cb][4 * r4 + i] * r;
+      *reinterpret_cast<f32x4*>(dst + 32 * cb + 8 * r4 + 4 * hf) = o;
+    }
+}
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+grouped_pp_kernel(GroupedArgs a) {
+  // One LDS object: no per-object alias scopes, so the compiler adds no waits
+  // of its own for the key DMA before LDS reads (the explicit ones order them).
+  __shared__ __attribute__((aligned(16))) char smem[kGSmem];
+  const int BH = a.B * a.nH;
+  const int nqb = (a.T + kBM - 1) / kBM;
+  const int r = (int)blockIdx.x / BH, bh = (int)blockIdx.x % BH;
+  gpp_block(a, smem, (int)blockIdx.x);
+  if (nqb - 1 - r > r) {
+    __syncthreads();  // the first block's epilogue is done with LDS
+    gpp_block(a, smem, (nqb - 1 - r) * BH + bh);
+  }
+}
+
 // out_s = sigmoid(G_s) * (H_s - lambda_t,s * H_(nS + s / g)): 32 threads per
 // (b, t, s) row, four channels each.
 __global__ void __launch_bounds__(256) grouped_combine_kernel(GroupedArgs a) {
@@ -191,10 +368,18 @@ hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (grid <= 2 * (int64_t)cus)
+  const bool split = grid <= 2 * (int64_t)cus;
+  // The ping-pong form addresses a head's key rows from one buffer base with
+  // 32-bit offsets (up to about T + 192 rows).
+  const int64_t row_max = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
+  if (split && (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31)) {
+    const int64_t nqb = (a.T + kBM - 1) / kBM;
+    hipLaunchKernelGGL(grouped_pp_kernel, dim3((unsigned)((nqb + 1) / 2 * a.B * a.nH)), dim3(512), 0, stream, a);
+  } else if (split) {
     hipLaunchKernelGGL(grouped_attn_kernel<2>, dim3((unsigned)grid), dim3(512), 0, stream, a);
-  else
+  } else {
     hipLaunchKernelGGL(grouped_attn_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.B * a.T * a.nS;

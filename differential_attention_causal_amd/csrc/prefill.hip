@@ -449,19 +449,6 @@ __device__ __forceinline__ void finish_rows(const PrefillArgs& a, int b, int hea
   norm_store(a, b, head, q, hf, O1, a.gain + (int64_t)head * kDv);
 }
 
-// Waits: vmcnt(n) alone, lgkmcnt(0) alone (gfx9 s_waitcnt encoding).
-template <int n>
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70); }
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// Workgroup barrier with no memory wait of its own; the asm memory clobber
-// keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // S^T = K Q^T of one tile for both maps, K from LDS: bf16 operands, or fp16
 // (kF16: rotated keys and queries, see rope_query).
 template <bool kF16>
@@ -675,6 +662,8 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
       softmax_step(s2, c, m2, l2, O2, p2a, p2b);
     }
   }
+  // Every wave is done reading slot 0's keys before step 0 refills them.
+  phase_barrier();
   if (grp == 1) phase_barrier();  // group 1 starts one phase late
 
   for (int it = 0; it < nsteps; ++it) {

@@ -50,6 +50,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
 // included (vmcnt 0; export and LDS counters left alone).
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Waits: vmcnt(n) alone, lgkmcnt(0) alone (gfx9 s_waitcnt encoding).
+template <int n>
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70); }
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier with no memory wait of its own; the asm memory clobber
+// keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
