@@ -74,6 +74,36 @@ __device__ __forceinline__ float wave_sum(float x) {
 // probabilities 2^(c s - m) stay <= 2^kSlack, far inside fp16 range.
 constexpr float kSlack = 8.0f;
 
+// Probabilities 2^(c s - m) of a tile as the two f16 operands of the P^T V^T
+// product, and the running sum l += their sum, taken over the rounded f16
+// values the product uses, two per instruction (dot product with (1, 1), fp32
+// accumulation).
+__device__ __forceinline__ void softmax_probs(const f32x16& s, float c, float m, float& l, f16x8& p0, f16x8& p1) {
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p0[j] = (_Float16)p[j];
+    p1[j] = (_Float16)p[8 + j];
+  }
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  float sum = l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sum = __builtin_amdgcn_fdot2(f16x2{p0[2 * j], p0[2 * j + 1]}, one, sum, false);
+    sum = __builtin_amdgcn_fdot2(f16x2{p1[2 * j], p1[2 * j + 1]}, one, sum, false);
+  }
+  l = sum;
+}
+
+__device__ __forceinline__ float tile_max(const f32x16& s) {
+  float mx = s[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+  return mx;
+}
+
 // One map's online-softmax step on a 32x32 score tile held as S^T (lane: one
 // query, 16 keys).  Keeps the running reference max m (base-2 units) unless
 // a score lies more than kSlack above it: only when some lane of the wave sees
@@ -81,11 +111,8 @@ constexpr float kSlack = 8.0f;
 // the bound raise m to their tile max and rescale that map's O^T and partial
 // sum l.  Returns the tile's probabilities
 // 2^(c s - m) <= 2^kSlack as the two f16 operands of the P^T V^T product.
-__device__ __forceinline__ void softmax_step(f32x16& s, float c, float& m, float& l, f32x16 (&O)[4],
-                                             f16x8& p0, f16x8& p1) {
-  float mx = s[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+__device__ __forceinline__ void softmax_rebase(const f32x16& s, float c, float& m, float& l, f32x16 (&O)[4]) {
+  float mx = tile_max(s);
   if (__any(mx * c > m + kSlack)) {
     // Each query decides from its own scores only (its two lanes agree after
     // the exchange), so a row's result never depends on other rows' data.
@@ -98,24 +125,12 @@ __device__ __forceinline__ void softmax_step(f32x16& s, float c, float& m, float
     for (int cb = 0; cb < 4; ++cb) O[cb] *= alpha;
     m = mn;
   }
-  float p[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m));
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    p0[j] = (_Float16)p[j];
-    p1[j] = (_Float16)p[8 + j];
-  }
-  // The sum runs over the rounded f16 values the product uses, two per
-  // instruction (dot product with (1, 1), fp32 accumulation).
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-  float sum = l;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sum = __builtin_amdgcn_fdot2(f16x2{p0[2 * j], p0[2 * j + 1]}, one, sum, false);
-    sum = __builtin_amdgcn_fdot2(f16x2{p1[2 * j], p1[2 * j + 1]}, one, sum, false);
-  }
-  l = sum;
+}
+
+__device__ __forceinline__ void softmax_step(f32x16& s, float c, float& m, float& l, f32x16 (&O)[4],
+                                             f16x8& p0, f16x8& p1) {
+  softmax_rebase(s, c, m, l, O);
+  softmax_probs(s, c, m, l, p0, p1);
 }
 
 // End-of-loop merge buffer of a split-key workgroup (two groups of four

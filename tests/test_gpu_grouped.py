@@ -87,6 +87,23 @@ def test_grouped_motif3_shape_sampled():
     assert rel <= REL
 
 
+def test_grouped_large_grid_sampled():
+    # B=4, T=1100, 16 heads: 9 query blocks x 64 (b, head) = 576 workgroups, more
+    # than two per CU, so the four-wave kernel runs instead of the ping-pong one
+    _say("grouped B=4 T=1100 n_H=16 g=3 (four-wave grid)")
+    x = _inputs(4, 1100, 16, 3, seed=33)
+    out = _gpu(x, 3)
+    rng = np.random.default_rng(4)
+    rows = sorted({(int(b), int(i), int(s)) for b, i, s in zip(rng.integers(0, 4, 60), rng.integers(0, 1100, 60),
+                                                                rng.integers(0, 12, 60))}
+                  | {(0, 0, 0), (3, 1099, 11), (1, 1023, 5), (2, 1024, 6)})
+    ref = _ref(x, 3, rows=rows)
+    got = np.stack([out[b, i, s] for b, i, s in rows])
+    rel = _rel(got, ref)
+    _say("rel", rel)
+    assert rel <= REL
+
+
 def test_grouped_structure():
     _say("grouped: noise head feeds its g signal heads only; deterministic")
     x = _inputs(1, 200, 8, 3, seed=32)
