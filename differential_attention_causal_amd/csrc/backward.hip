@@ -41,7 +41,6 @@ constexpr int kD16Row = kDv * 2;        // 256-byte fp16 rows of dO or V
 constexpr int kD16Tile = 32 * kD16Row;  // 8 KiB
 constexpr int kTRow = (32 + 8) * 2;     // 80-byte transposed fp16 rows (16-byte pad)
 constexpr int kQKT = kDqk * kTRow;      // 5 KiB: one map's transposed 64 x 32 tile
-constexpr int kDT = kDv * kTRow;        // 10 KiB: transposed 128 x 32 tile
 
 // 16-byte chunk swizzle of 256-byte rows (16 chunks): rows r and r ^ 16 share
 // it, so a 16-byte read by 32 lanes of consecutive rows is at most 2-way
@@ -262,37 +261,6 @@ __device__ __forceinline__ void store_qkT(const StagedT& s, char* dst, int tid) 
   }
 }
 
-// Transposed fp16 dO tile: [128 channels][80 B], channel row holding rows
-// r0..r0+31 in kVPos order.  Thread t loads rows 4(t%8) .. +3, channels
-// 4(t/8) .. +3 (8-byte loads of fp16).
-struct StagedDT {
-  u32x2 w[4];
-};
-
-__device__ __forceinline__ void load_doT(StagedDT& s, const uint16_t* base, int64_t stride, int r0, int end,
-                                         int tid) {
-  const int kg = tid & 7, cg = tid >> 3;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(base, stride, r0, end, kDv);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    s.w[r] = __builtin_amdgcn_raw_buffer_load_b64(rs, (uint32_t)(((4 * kg + r) * stride + 4 * cg) * 2), 0, 0);
-}
-
-__device__ __forceinline__ void store_doT(const StagedDT& s, char* dst, int tid) {
-  const int kg = tid & 7, cg = tid >> 3;
-  char* d = dst + kVPos(kg) * 8;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    // channel 4cg + c of rows 4kg .. 4kg+3
-    const int word = c >> 1, shift = (c & 1) * 16;
-    uint32_t e[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) e[r] = (s.w[r][word] >> shift) & 0xffffu;
-    const u32x2 pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-    *reinterpret_cast<u32x2*>(d + (4 * cg + c) * kTRow) = pk;
-  }
-}
-
 // Row-major fp16 V tile (keys x 128 channels) through registers: thread t
 // takes row t/8, channels 16(t%8) .. +15 (two 16-byte loads), stores them
 // converted at logical chunks 2(t%8), 2(t%8)+1 with the swz16 swizzle.
@@ -352,6 +320,30 @@ __device__ __forceinline__ void store_col(float* dst, const f32x16& acc, int blk
     for (int r = 0; r < 4; ++r) v[r] = acc[4 * r4 + r] * f;
     *reinterpret_cast<f32x4*>(dst + 32 * blk + 8 * r4 + 4 * hf) = v;
   }
+}
+
+// The transposed operand of a row-major fp16 tile (32 rows x 128 columns,
+// swz16-swizzled 256-byte rows) by ds_read_b64_tr_b16, which hands lane i of
+// each 16-lane group element i % 4 of the 8-byte reads of lanes 4k + i / 4,
+// k = 0..3.  For column block blk and k-half kh, lane (hf, g, L) (g: 16-lane
+// group within the half, L: lane within it) reads 4 columns 32blk + 16g +
+// 4(L % 4) .. +3 of row 16kh + 8h + 4hf + L / 4 for h = 0, 1, so it receives
+// column 32blk + 16g + L of rows 16kh + 8(j / 4) + 4hf + j % 4, j = 0..7:
+// the A operand of a product whose B operand is a 32x32 accumulator packed by
+// pack16 (rows in the accumulator's order).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ f16x8 tr_operand(const char* tile, int blk, int kh, int lane) {
+  const int hf = lane >> 5, g = (lane >> 4) & 1, L = lane & 15;
+  const int col = 32 * blk + 16 * g + 4 * (L & 3);
+  auto rd = [&](int h) {
+    const int row = 16 * kh + 8 * h + 4 * hf + (L >> 2);
+    const char* p = tile + row * kD16Row + (((col >> 3) ^ swz16(row)) << 4) + (col & 7) * 2;
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+  };
+  const f16x4 lo = rd(0), hi = rd(1);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -442,12 +434,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
             *reinterpret_cast<const f16x8*>(vt + (((2 * s + hf) ^ swz16(lq)) << 4)), dot[s], dp, 0, 0, 0);
       // P_m^T from the saved log-sum-exp, then dS_m^T; the diagonal tile
       // keeps keys <= query only (register i is key 8(i/4) + 4hf + i%4).
-      const bool diag = j == last_tile;
+      if (j == last_tile) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + 4 * hf + (i & 3) > lq) s1[i] = s2[i] = -__builtin_inff();  // P = 0, dS = 0
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const bool vis = !diag || 8 * (i >> 2) + 4 * hf + (i & 3) <= lq;
-        const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lse1)) : 0.f;
-        const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -lse2)) : 0.f;
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lse1));
+        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -lse2));
         s1[i] = p1 * (dp[i] - D1);
         s2[i] = p2 * (-lam * dp[i] - D2);
       }
@@ -520,12 +515,13 @@ __device__ __forceinline__ void load_krow(bf16x8 (&kt)[4], const uint16_t* base,
 // dK and dV in one launch: a workgroup of 8 waves owns 128 keys of one (b, h).
 // Waves 0-3 compute dK_1, dK_2 and waves 4-7 dV for the same keys, so each SIMD holds one wave of each kind and every
 // query tile is staged once for both: Q_1, Q_2 row-major bf16 and dO
-// row-major fp16 by DMA plus Q^T by registers (staged by the dK waves), dO^T
-// and the per-query statistics (staged by the dV waves).  Each role runs its
-// own copy of the loop (same trip count, one barrier per query tile), so its
-// registers are allocated for that role alone.
-constexpr int kDkvStage = 2 * kQKTile + kD16Tile + 2 * kQKT + kDT + 4 * 32 * 4;
-constexpr int kOffDo = 2 * kQKTile, kOffQT = kOffDo + kD16Tile, kOffDT = kOffQT + 2 * kQKT, kOffSt = kOffDT + kDT;
+// row-major fp16 by DMA plus Q^T by registers (staged by the dK waves), and
+// the per-query statistics (staged by the dV waves, which read dO^T from the
+// row-major dO tile by transposed reads).  Each role runs its own copy of the
+// loop (same trip count, one barrier per query tile), so its registers are
+// allocated for that role alone.
+constexpr int kDkvStage = 2 * kQKTile + kD16Tile + 2 * kQKT + 4 * 32 * 4;
+constexpr int kOffDo = 2 * kQKTile, kOffQT = kOffDo + kD16Tile, kOffSt = kOffQT + 2 * kQKT;
 
 template <bool kDV>
 __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int tid) {
@@ -565,23 +561,18 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
 
   f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};  // dK_1 (0, 1), dK_2 (2, 3) or dV^T (0 .. 3)
   StagedT sq;
-  StagedDT sd;
   auto stage_issue = [&](int qt, char* st) {
     if constexpr (!kDV) {
       dma_qk(qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, st, rt);
       dma_do(dob, sdo, 32 * qt, a.T, st + kOffDo, rt);
       load_qkT(sq, qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, rt);
-    } else {
-      load_doT(sd, dob, sdo, 32 * qt, a.T, rt);
     }
   };
   auto stage_store = [&](int qt, char* st) {
-    if constexpr (!kDV) {
+    if constexpr (!kDV)
       store_qkT(sq, st + kOffQT, rt);
-    } else {
-      store_doT(sd, st + kOffDT, rt);
+    else
       stage_stats(a, b, head, 32 * qt, reinterpret_cast<float*>(st + kOffSt), rt);
-    }
   };
   if (qt0 < nqt) {
     stage_issue(qt0, smem);
@@ -600,7 +591,11 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
       f32x16 s1 = scores_qk(cur, k1t, lk, hf);
       f32x16 s2 = scores_qk(cur + kQKTile, k2t, lk, hf);
       const float* stats = reinterpret_cast<const float*>(cur + kOffSt);
-      const bool dg = qt == diag;  // rows are queries 8(i/4) + 4hf + i%4 of the tile, the column key lk
+      if (qt == diag) {  // rows are queries 8(i/4) + 4hf + i%4 of the tile, the column key lk
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (lk > 8 * (i >> 2) + 4 * hf + (i & 3)) s1[i] = s2[i] = -__builtin_inff();  // P = 0
+      }
       if constexpr (!kDV) {
         // dP = dO V^T (32 queries x 32 keys)
         f32x16 dp = f32x16{};
@@ -619,9 +614,8 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * g + r;
-            const bool vis = !dg || lk <= r0 + r;
-            const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r])) : 0.f;
-            const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r])) : 0.f;
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r]));
+            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r]));
             s1[i] = p1 * (dp[i] - d1[r]);
             s2[i] = p2 * (-lam * dp[i] - d2[r]);
           }
@@ -645,18 +639,20 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * g + r;
-            const bool vis = !dg || lk <= r0 + r;
-            const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r])) : 0.f;
-            const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r])) : 0.f;
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r]));
+            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r]));
             s1[i] = p1 - lam * p2;
           }
         }
         f16x8 p0, p1;
         pack16(s1, p0, p1);
-        // dV^T += dO^T (P_1 - lambda P_2)
-        const char* dT = cur + kOffDT;
+        // dV^T += dO^T (P_1 - lambda P_2), dO^T read transposed from the dO tile
+        const char* dt = cur + kOffDo;
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) acc[blk] = mfma_T(dT, blk, lk, hf, p0, p1, acc[blk]);
+        for (int blk = 0; blk < 4; ++blk) {
+          acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tr_operand(dt, blk, 0, lane), p0, acc[blk], 0, 0, 0);
+          acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tr_operand(dt, blk, 1, lane), p1, acc[blk], 0, 0, 0);
+        }
       }
     }
     if (more) stage_store(qt + 1, nxt);
