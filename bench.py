@@ -118,11 +118,16 @@ def cpu_baseline(x, wl, gpu=None):
     return rec
 
 
-def gpu_env(torch) -> dict:
-    """Device, software versions and current clocks (rocm-smi, when it answers)."""
+def gpu_env(torch, clocks: bool = True) -> dict:
+    """Device, software versions and current clocks (rocm-smi, when it answers;
+    skipped under a profiler, which has the GPU open before the program starts,
+    so that no child process is started from a process holding the GPU)."""
     import subprocess
 
     env = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__}
+    if not clocks:
+        env["clocks"] = None
+        return env
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
         card = next(iter(json.loads(r.stdout).values()))
@@ -275,6 +280,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the sliding-window and RoPE timings")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the rocm-smi clock query (for profiler runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -380,7 +386,7 @@ def main() -> int:
         "variants": var,
         "wall_s_timed": round(wall, 3),
         "kernel_source_sha256_16": kernel_source_digest(),
-        "env": gpu_env(torch),
+        "env": gpu_env(torch, clocks=not args.no_clocks),
     }
     if not args.no_cpu_baseline:
         # the benchmarked prefill once more (outside the timed region) with
