@@ -74,7 +74,7 @@ float score_factor(float scale) {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 105; }
+int diffattn_abi_version(void) { return 106; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -228,18 +228,24 @@ namespace {
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 struct BwdLayout {
-  size_t dO, dstat, partial, total;
+  size_t q1h, q2h, k1h, k2h, vh, dO, dstat, partial, total;
   int nchunks;
 };
 
-// Workspace of the backward pass: dO fp16 [B,T,H,d_v], D fp32 [B,T,H,2],
+// Workspace of the backward pass: fp16 copies of Q_1, Q_2, K_1, K_2
+// [B,T,H,d_qk] and V [B,T,H,d_v], dO fp16 [B,T,H,d_v], D fp32 [B,T,H,2],
 // gain/lambda partials fp32 [H, nchunks, d_v + 1].
 BwdLayout bwd_layout(int B, int T, int H) {
   BwdLayout l;
   const size_t rows = (size_t)B * T * H;
   l.nchunks = (int)(((int64_t)B * T + diffattn::kBwdRowsPerChunk - 1) / diffattn::kBwdRowsPerChunk);
-  l.dO = 0;
-  l.dstat = align256(rows * kDv * 2);
+  l.q1h = 0;
+  l.q2h = l.q1h + align256(rows * kDqk * 2);
+  l.k1h = l.q2h + align256(rows * kDqk * 2);
+  l.k2h = l.k1h + align256(rows * kDqk * 2);
+  l.vh = l.k2h + align256(rows * kDqk * 2);
+  l.dO = l.vh + align256(rows * kDv * 2);
+  l.dstat = l.dO + align256(rows * kDv * 2);
   l.partial = l.dstat + align256(rows * 2 * sizeof(float));
   l.total = l.partial + align256((size_t)H * l.nchunks * (kDv + 1) * sizeof(float));
   return l;
@@ -311,6 +317,11 @@ int diffattn_bwd_prefill(const void* q1, const void* q2, const void* k1, const v
   a.dlam = dlambda;
   a.dgain = dgain;
   char* ws = static_cast<char*>(workspace);
+  a.q1h = reinterpret_cast<uint16_t*>(ws + lay.q1h);
+  a.q2h = reinterpret_cast<uint16_t*>(ws + lay.q2h);
+  a.k1h = reinterpret_cast<uint16_t*>(ws + lay.k1h);
+  a.k2h = reinterpret_cast<uint16_t*>(ws + lay.k2h);
+  a.vh = reinterpret_cast<uint16_t*>(ws + lay.vh);
   a.dO = reinterpret_cast<uint16_t*>(ws + lay.dO);
   a.dstat = reinterpret_cast<float*>(ws + lay.dstat);
   a.partial = reinterpret_cast<float*>(ws + lay.partial);

@@ -16,17 +16,21 @@
 // Kernels (all deterministic, no atomics):
 //   bwd_pre_kernel     per row: do (fp16), D_1, D_2; gain/lambda partials
 //   bwd_reduce_kernel  per head: sum of the partials
+//   bwd_cast_kernel    fp16 copies of Q_1, Q_2, K_1, K_2, V in the workspace
 //   bwd_dq_kernel      queries own lanes (the forward's orientation): recompute
 //                      S^T, P^T from the saved log-sum-exp, dP^T = V dO^T,
 //                      dQ^T += K^T dS^T
 //   bwd_dkv_kernel     keys own lanes, two kinds of waves on the same keys and
 //                      query tiles: S = Q K^T, dP = dO V^T, dK^T += Q^T dS;
 //                      and S = Q K^T, dV^T += dO^T (P_1 - lambda P_2)
-// The last two use v_mfma_f32_32x32x16 like the prefill: a 32x32 accumulator
-// held by a wave is used directly as the next product's operand, with the
-// transposed LDS tiles stored in the matching (kVPos) order.  Scores are bf16
-// products of the exact inputs; dO, P, dS, V^T, K^T and Q^T enter the other
-// products as fp16 (inputs converted exactly, |x| in [2^-14, 65504)).
+// The last two use v_mfma_f32_32x32x16_f16 like the prefill: a 32x32
+// accumulator held by a wave is used directly as the next product's operand.
+// Every tile is a row-major fp16 tile moved by DMA; the transposed operands
+// (K^T, Q^T, dO^T) come from the same tiles by ds_read_b64_tr_b16, with
+// addresses chosen so that their k order matches the accumulator's rows.  All
+// inputs enter the products as fp16 (bf16 converted exactly for |x| in
+// [2^-14, 65504)), so the scores are the same products of the inputs as the
+// forward's bf16 ones; P, dS and dO are rounded to fp16; fp32 accumulation.
 #include "kernels.h"
 #include "tile.h"
 
@@ -35,12 +39,10 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kRows = 32 * kWaves;      // queries (dQ) or keys (dK, dV) per workgroup
-constexpr int kKRow = kDqk * 2;         // 128-byte bf16 rows of Q or K
-constexpr int kQKTile = 32 * kKRow;     // 4 KiB: one map's 32-row bf16 tile
+constexpr int kKRow = kDqk * 2;         // 128-byte fp16 rows of Q or K
+constexpr int kQKTile = 32 * kKRow;     // 4 KiB: one map's 32-row fp16 tile
 constexpr int kD16Row = kDv * 2;        // 256-byte fp16 rows of dO or V
 constexpr int kD16Tile = 32 * kD16Row;  // 8 KiB
-constexpr int kTRow = (32 + 8) * 2;     // 80-byte transposed fp16 rows (16-byte pad)
-constexpr int kQKT = kDqk * kTRow;      // 5 KiB: one map's transposed 64 x 32 tile
 
 // 16-byte chunk swizzle of 256-byte rows (16 chunks): rows r and r ^ 16 share
 // it, so a 16-byte read by 32 lanes of consecutive rows is at most 2-way
@@ -196,12 +198,49 @@ __global__ void __launch_bounds__(192) bwd_reduce_kernel(BackwardArgs a) {
     a.dlam[h] = s;
 }
 
+// fp16 copies of Q_1, Q_2, K_1, K_2 and V, contiguous [B, T, H, d] (exact for
+// |x| in [2^-14, 65504), like every fp16 operand of the products).  One thread
+// converts 8 elements: 48 chunks per (b, t, h) row, 8 from each 64-dim input
+// and 16 from V, so consecutive threads read consecutive 16-byte chunks.
+__global__ void __launch_bounds__(256) bwd_cast_kernel(BackwardArgs a) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)a.B * a.T * a.H;
+  if (g >= rows * 48) return;
+  const int64_t row = g / 48;
+  const int c = (int)(g % 48);
+  const int h = (int)(row % a.H);
+  const int64_t bt = row / a.H;
+  const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+  const uint16_t* src;
+  uint16_t* dst;
+  if (c < 32) {
+    const int m = c >> 3, ch = c & 7;
+    const uint16_t* base = m == 0 ? a.q1 : m == 1 ? a.q2 : m == 2 ? a.k1 : a.k2;
+    const Strides& st = m == 0 ? a.sq1 : m == 1 ? a.sq2 : m == 2 ? a.sk1 : a.sk2;
+    uint16_t* out = m == 0 ? a.q1h : m == 1 ? a.q2h : m == 2 ? a.k1h : a.k2h;
+    src = base + (int64_t)b * st.b + (int64_t)t * st.t + (int64_t)h * st.h + 8 * ch;
+    dst = out + row * kDqk + 8 * ch;
+  } else {
+    const int ch = c - 32;
+    src = a.v + (int64_t)b * a.sv.b + (int64_t)t * a.sv.t + (int64_t)h * a.sv.h + 8 * ch;
+    dst = a.vh + row * kDv + 8 * ch;
+  }
+  const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+  f16x8 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = (_Float16)bf16_lo(w[i]);
+    o[2 * i + 1] = (_Float16)bf16_hi(w[i]);
+  }
+  *reinterpret_cast<f16x8*>(dst) = o;
+}
+
 // ---------------------------------------------------------------------------
 // Tile staging shared by the three product kernels.  A tile is 32 rows
 // (keys or queries) of one (b, h), rows r0 .. r0+31, rows at or past `end`
 // reading as zero.  Threads 0..255 of the workgroup take part.
 
-// Row-major bf16 tiles of both maps (Q or K) by DMA into [map][32][128 B]
+// Row-major fp16 tiles of both maps (Q or K) by DMA into [map][32][128 B]
 // with the kSwz chunk swizzle: thread t fetches row t/8, logical chunk
 // (t % 8) ^ kSwz(t / 8), landing at chunk position t.
 __device__ __forceinline__ void dma_qk(const uint16_t* b1, const uint16_t* b2, int64_t st1, int64_t st2, int r0,
@@ -227,68 +266,6 @@ __device__ __forceinline__ void dma_do(const uint16_t* base, int64_t stride, int
   }
 }
 
-// Transposed fp16 tiles of both maps (Q^T or K^T): [map][64 dims][80 B], row
-// d holding rows r0..r0+31 of dim d in kVPos order.  Thread t loads rows
-// 4(t%8) .. +3, dims 2(t/8), 2(t/8)+1 of each map (4-byte loads) ...
-struct StagedT {
-  uint32_t w[2][4];
-};
-
-__device__ __forceinline__ void load_qkT(StagedT& s, const uint16_t* b1, const uint16_t* b2, int64_t st1,
-                                         int64_t st2, int r0, int end, int tid) {
-  const int kg = tid & 7, dg = tid >> 3;
-  const __amdgpu_buffer_rsrc_t x1 = rows_rsrc(b1, st1, r0, end, kDqk);
-  const __amdgpu_buffer_rsrc_t x2 = rows_rsrc(b2, st2, r0, end, kDqk);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    s.w[0][r] = __builtin_amdgcn_raw_buffer_load_b32(x1, (uint32_t)(((4 * kg + r) * st1 + 2 * dg) * 2), 0, 0);
-    s.w[1][r] = __builtin_amdgcn_raw_buffer_load_b32(x2, (uint32_t)(((4 * kg + r) * st2 + 2 * dg) * 2), 0, 0);
-  }
-}
-
-// ... and writes them converted to fp16.
-__device__ __forceinline__ void store_qkT(const StagedT& s, char* dst, int tid) {
-  const int kg = tid & 7, dg = tid >> 3;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const f16x4 lo = {(_Float16)bf16_lo(s.w[m][0]), (_Float16)bf16_lo(s.w[m][1]), (_Float16)bf16_lo(s.w[m][2]),
-                      (_Float16)bf16_lo(s.w[m][3])};
-    const f16x4 hi = {(_Float16)bf16_hi(s.w[m][0]), (_Float16)bf16_hi(s.w[m][1]), (_Float16)bf16_hi(s.w[m][2]),
-                      (_Float16)bf16_hi(s.w[m][3])};
-    char* d = dst + m * kQKT + kVPos(kg) * 8;
-    *reinterpret_cast<f16x4*>(d + (2 * dg) * kTRow) = lo;
-    *reinterpret_cast<f16x4*>(d + (2 * dg + 1) * kTRow) = hi;
-  }
-}
-
-// Row-major fp16 V tile (keys x 128 channels) through registers: thread t
-// takes row t/8, channels 16(t%8) .. +15 (two 16-byte loads), stores them
-// converted at logical chunks 2(t%8), 2(t%8)+1 with the swz16 swizzle.
-struct StagedV {
-  u32x4 w[2];
-};
-
-__device__ __forceinline__ void load_v(StagedV& s, const uint16_t* base, int64_t stride, int r0, int end, int tid) {
-  const int r = tid >> 3, p = tid & 7;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(base, stride, r0, end, kDv);
-  s.w[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((r * stride + 16 * p) * 2), 0, 0);
-  s.w[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((r * stride + 16 * p + 8) * 2), 0, 0);
-}
-
-__device__ __forceinline__ void store_v(const StagedV& s, char* dst, int tid) {
-  const int r = tid >> 3, p = tid & 7;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    f16x8 h;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[2 * i] = (_Float16)bf16_lo(s.w[k][i]);
-      h[2 * i + 1] = (_Float16)bf16_hi(s.w[k][i]);
-    }
-    *reinterpret_cast<f16x8*>(dst + r * kD16Row + (((2 * p + k) ^ swz16(r)) << 4)) = h;
-  }
-}
-
 // Packs a 32x32 accumulator (16 values per lane) as the two fp16 operands of
 // the next product's k-steps: registers 0..7, then 8..15.
 __device__ __forceinline__ void pack16(const f32x16& v, f16x8& p0, f16x8& p1) {
@@ -297,17 +274,6 @@ __device__ __forceinline__ void pack16(const f32x16& v, f16x8& p0, f16x8& p1) {
     p0[j] = (_Float16)v[j];
     p1[j] = (_Float16)v[8 + j];
   }
-}
-
-// acc (32 rows x 32 lanes' columns) += T^T(rows 32blk.., kVPos-ordered 32)
-// * B for one 32-row block of a transposed fp16 tile.
-__device__ __forceinline__ f32x16 mfma_T(const char* tT, int blk, int lq, int hf, const f16x8& b0, const f16x8& b1,
-                                         f32x16 acc) {
-  const char* t = tT + (32 * blk + lq) * kTRow + hf * 16;
-  const f16x8 a0 = *reinterpret_cast<const f16x8*>(t);
-  const f16x8 a1 = *reinterpret_cast<const f16x8*>(t + 32);
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc, 0, 0, 0);
 }
 
 // Stores a lane's column of a 32-row accumulator block (rows 32blk + 8(i/4) +
@@ -322,36 +288,48 @@ __device__ __forceinline__ void store_col(float* dst, const f32x16& acc, int blk
   }
 }
 
-// The transposed operand of a row-major fp16 tile (32 rows x 128 columns,
-// swz16-swizzled 256-byte rows) by ds_read_b64_tr_b16, which hands lane i of
-// each 16-lane group element i % 4 of the 8-byte reads of lanes 4k + i / 4,
-// k = 0..3.  For column block blk and k-half kh, lane (hf, g, L) (g: 16-lane
-// group within the half, L: lane within it) reads 4 columns 32blk + 16g +
-// 4(L % 4) .. +3 of row 16kh + 8h + 4hf + L / 4 for h = 0, 1, so it receives
-// column 32blk + 16g + L of rows 16kh + 8(j / 4) + 4hf + j % 4, j = 0..7:
-// the A operand of a product whose B operand is a 32x32 accumulator packed by
-// pack16 (rows in the accumulator's order).
+// The transposed operand of a row-major fp16 tile of 32 rows (kRowBytes-byte
+// rows: 256 with the swz16 chunk swizzle, 128 with kSwz) by
+// ds_read_b64_tr_b16, which hands lane i of each 16-lane group element i % 4
+// of the 8-byte reads of lanes 4k + i / 4, k = 0..3.  For column block blk
+// and k-half kh, lane (hf, g, L) (g: 16-lane group within the half, L: lane
+// within it) reads 4 columns 32blk + 16g + 4(L % 4) .. +3 of row 16kh + 8h +
+// 4hf + L / 4 for h = 0, 1, so it receives column 32blk + 16g + L of rows
+// 16kh + 8(j / 4) + 4hf + j % 4, j = 0..7: the A operand of a product whose B
+// operand is a 32x32 accumulator packed by pack16 (rows in the accumulator's
+// order).
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+template <int kRowBytes>
 __device__ __forceinline__ f16x8 tr_operand(const char* tile, int blk, int kh, int lane) {
   const int hf = lane >> 5, g = (lane >> 4) & 1, L = lane & 15;
   const int col = 32 * blk + 16 * g + 4 * (L & 3);
   auto rd = [&](int h) {
     const int row = 16 * kh + 8 * h + 4 * hf + (L >> 2);
-    const char* p = tile + row * kD16Row + (((col >> 3) ^ swz16(row)) << 4) + (col & 7) * 2;
+    const int sw = kRowBytes == 256 ? swz16(row) : kSwz(row);
+    const char* p = tile + row * kRowBytes + (((col >> 3) ^ sw) << 4) + (col & 7) * 2;
     return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
   };
   const f16x4 lo = rd(0), hi = rd(1);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// acc += T^T P for column block blk of a row-major tile T (32 rows): the two
+// k-halves of the product, P packed by pack16.
+template <int kRowBytes>
+__device__ __forceinline__ f32x16 mfma_tr(const char* tile, int blk, int lane, const f16x8& p0, const f16x8& p1,
+                                          f32x16 acc) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(tr_operand<kRowBytes>(tile, blk, 0, lane), p0, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(tr_operand<kRowBytes>(tile, blk, 1, lane), p1, acc, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // dQ_1, dQ_2: a workgroup owns 128 queries of one (b, h); wave w queries
-// 32w .. 32w+31, lane (hf, lq) query lq.  Key tiles stream through LDS:
-// K_1, K_2 row-major bf16 (score operands), V row-major fp16 (dP^T operand),
-// K_1^T, K_2^T fp16 (dQ^T operands).
-constexpr int kDqStage = 2 * kQKTile + kD16Tile + 2 * kQKT;
+// 32w .. 32w+31, lane (hf, lq) query lq.  Key tiles of the fp16 copies stream
+// through LDS by DMA alone: K_1, K_2 (score operands, and K^T by transposed
+// reads for dQ^T) and V (dP^T operand), all row-major.
+constexpr int kDqStage = 2 * kQKTile + kD16Tile;
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BackwardArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kDqStage];
@@ -365,19 +343,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int kend = min(a.T, ntiles * 32);
   const int last_tile = q_first / 32;
 
-  // Operands held for the whole kernel: Q_m^T (score B operands, bf16) and
-  // dO^T (dP^T B operand, fp16), both for this lane's query.
-  bf16x8 qa[4], qb2[4];
+  // Operands held for the whole kernel: Q_m^T (score B operands) and dO^T
+  // (dP^T B operand), fp16, both for this lane's query.
+  f16x8 qa[4], qb2[4];
   f16x8 dot[8];
   const int64_t rq = ((int64_t)b * a.T + q) * a.H + head;
   {
-    const uint16_t* p1 = a.q1 + (int64_t)b * a.sq1.b + (int64_t)q * a.sq1.t + (int64_t)head * a.sq1.h + 8 * hf;
-    const uint16_t* p2 = a.q2 + (int64_t)b * a.sq2.b + (int64_t)q * a.sq2.t + (int64_t)head * a.sq2.h + 8 * hf;
+    const uint16_t* p1 = a.q1h + rq * kDqk + 8 * hf;
+    const uint16_t* p2 = a.q2h + rq * kDqk + 8 * hf;
     const uint16_t* pd = a.dO + rq * kDv + 8 * hf;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      qa[s] = ok ? *reinterpret_cast<const bf16x8*>(p1 + 16 * s) : bf16x8{};
-      qb2[s] = ok ? *reinterpret_cast<const bf16x8*>(p2 + 16 * s) : bf16x8{};
+      qa[s] = ok ? *reinterpret_cast<const f16x8*>(p1 + 16 * s) : f16x8{};
+      qb2[s] = ok ? *reinterpret_cast<const f16x8*>(p2 + 16 * s) : f16x8{};
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) dot[s] = ok ? *reinterpret_cast<const f16x8*>(pd + 16 * s) : f16x8{};
@@ -387,43 +365,36 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
   const float c = a.c;
 
-  const uint16_t* kb1 = a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h;
-  const uint16_t* kb2 = a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h;
-  const uint16_t* vb = a.v + (int64_t)b * a.sv.b + (int64_t)head * a.sv.h;
+  const int64_t row0 = (int64_t)b * a.T * a.H + head;  // (b, t = 0, head)
+  const uint16_t* kb1 = a.k1h + row0 * kDqk;
+  const uint16_t* kb2 = a.k2h + row0 * kDqk;
+  const uint16_t* vb = a.vh + row0 * kDv;
+  const int64_t sk = (int64_t)a.H * kDqk, sv = (int64_t)a.H * kDv;
 
   f32x16 dq1[2] = {f32x16{}, f32x16{}}, dq2[2] = {f32x16{}, f32x16{}};
   const int ksw = kSwz(lq);
 
-  StagedV sv;
-  StagedT sk;
   auto stage_issue = [&](int j, char* st) {
-    dma_qk(kb1, kb2, a.sk1.t, a.sk2.t, 32 * j, kend, st, tid);
-    load_v(sv, vb, a.sv.t, 32 * j, kend, tid);
-    load_qkT(sk, kb1, kb2, a.sk1.t, a.sk2.t, 32 * j, kend, tid);
-  };
-  auto stage_store = [&](char* st) {
-    store_v(sv, st + 2 * kQKTile, tid);
-    store_qkT(sk, st + 2 * kQKTile + kD16Tile, tid);
+    dma_qk(kb1, kb2, sk, sk, 32 * j, kend, st, tid);
+    dma_do(vb, sv, 32 * j, kend, st + 2 * kQKTile, tid);
   };
   stage_issue(0, smem);
-  stage_store(smem);
   wait_dma();
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
     char* cur = smem + (j & 1) * kDqStage;
     char* nxt = smem + ((j + 1) & 1) * kDqStage;
-    const bool more = j + 1 < ntiles;
-    if (more) stage_issue(j + 1, nxt);
+    if (j + 1 < ntiles) stage_issue(j + 1, nxt);
     if (wave_live && j <= last_tile) {
       // S_m^T = K_m Q_m^T (32 keys x 32 queries)
       f32x16 s1 = f32x16{}, s2 = f32x16{};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int off = lq * kKRow + (((2 * s + hf) ^ ksw) << 4);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(cur + off), qa[s], s1, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(cur + kQKTile + off), qb2[s],
-                                                     s2, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8*>(cur + off), qa[s], s1, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8*>(cur + kQKTile + off), qb2[s], s2,
+                                                    0, 0, 0);
       }
       // dP^T = V dO^T
       f32x16 dp = f32x16{};
@@ -432,8 +403,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int s = 0; s < 8; ++s)
         dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
             *reinterpret_cast<const f16x8*>(vt + (((2 * s + hf) ^ swz16(lq)) << 4)), dot[s], dp, 0, 0, 0);
-      // P_m^T from the saved log-sum-exp, then dS_m^T; the diagonal tile
-      // keeps keys <= query only (register i is key 8(i/4) + 4hf + i%4).
+      // P_m^T from the saved log-sum-exp, then dS_m^T; on the diagonal tile the
+      // keys past the query (register i is key 8(i/4) + 4hf + i%4) get P = 0.
       if (j == last_tile) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -449,15 +420,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       f16x8 a0, a1, b0, b1;
       pack16(s1, a0, a1);
       pack16(s2, b0, b1);
-      // dQ_m^T += K_m^T dS_m^T
-      const char* kt = cur + 2 * kQKTile + kD16Tile;
+      // dQ_m^T += K_m^T dS_m^T, K_m^T read transposed from the key tiles
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        dq1[blk] = mfma_T(kt, blk, lq, hf, a0, a1, dq1[blk]);
-        dq2[blk] = mfma_T(kt + kQKT, blk, lq, hf, b0, b1, dq2[blk]);
+        dq1[blk] = mfma_tr<kKRow>(cur, blk, lane, a0, a1, dq1[blk]);
+        dq2[blk] = mfma_tr<kKRow>(cur + kQKTile, blk, lane, b0, b1, dq2[blk]);
       }
     }
-    if (more) stage_store(nxt);
     wait_dma();
     __syncthreads();
   }
@@ -493,35 +462,36 @@ __device__ __forceinline__ void stage_stats(const BackwardArgs& a, int b, int he
   }
 }
 
-// S_m = Q_m K_m^T for one map from a row-major bf16 Q tile.
-__device__ __forceinline__ f32x16 scores_qk(const char* qt, const bf16x8 (&kt)[4], int lq, int hf) {
+// S_m = Q_m K_m^T for one map from a row-major fp16 Q tile.
+__device__ __forceinline__ f32x16 scores_qk(const char* qt, const f16x8 (&kt)[4], int lq, int hf) {
   f32x16 acc = f32x16{};
   const int sw = kSwz(lq);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        *reinterpret_cast<const bf16x8*>(qt + lq * kKRow + (((2 * s + hf) ^ sw) << 4)), kt[s], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+        *reinterpret_cast<const f16x8*>(qt + lq * kKRow + (((2 * s + hf) ^ sw) << 4)), kt[s], acc, 0, 0, 0);
   return acc;
 }
 
-// Loads this lane's key row as the score B operand (K_m^T: dims 16s + 8hf ..).
-__device__ __forceinline__ void load_krow(bf16x8 (&kt)[4], const uint16_t* base, int64_t stride, int key, bool ok,
-                                          int hf) {
-  const uint16_t* p = base + (int64_t)key * stride + 8 * hf;
+// Loads 16-dim chunks 16s + 8hf .. of a row of an fp16 copy (row `row` of
+// the [B, T, H, d] layout) as operands.
+template <int kN>
+__device__ __forceinline__ void load_row16(f16x8 (&r)[kN], const uint16_t* base, int64_t row, bool ok, int hf) {
+  const uint16_t* p = base + row * (16 * kN) + 8 * hf;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) kt[s] = ok ? *reinterpret_cast<const bf16x8*>(p + 16 * s) : bf16x8{};
+  for (int s = 0; s < kN; ++s) r[s] = ok ? *reinterpret_cast<const f16x8*>(p + 16 * s) : f16x8{};
 }
 
 // dK and dV in one launch: a workgroup of 8 waves owns 128 keys of one (b, h).
-// Waves 0-3 compute dK_1, dK_2 and waves 4-7 dV for the same keys, so each SIMD holds one wave of each kind and every
-// query tile is staged once for both: Q_1, Q_2 row-major bf16 and dO
-// row-major fp16 by DMA plus Q^T by registers (staged by the dK waves), and
-// the per-query statistics (staged by the dV waves, which read dO^T from the
-// row-major dO tile by transposed reads).  Each role runs its own copy of the
+// Waves 0-3 compute dK_1, dK_2 and waves 4-7 dV for the same keys, so each
+// SIMD holds one wave of each kind and every query tile is staged once for
+// both: Q_1, Q_2 and dO row-major fp16 by DMA (issued by the dK waves; Q^T and
+// dO^T come from the same tiles by transposed reads) and the per-query
+// statistics (stored by the dV waves).  Each role runs its own copy of the
 // loop (same trip count, one barrier per query tile), so its registers are
 // allocated for that role alone.
-constexpr int kDkvStage = 2 * kQKTile + kD16Tile + 2 * kQKT + 4 * 32 * 4;
-constexpr int kOffDo = 2 * kQKTile, kOffQT = kOffDo + kD16Tile, kOffSt = kOffQT + 2 * kQKT;
+constexpr int kDkvStage = 2 * kQKTile + kD16Tile + 4 * 32 * 4;
+constexpr int kOffDo = 2 * kQKTile, kOffSt = kOffDo + kD16Tile;
 
 template <bool kDV>
 __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int tid) {
@@ -536,43 +506,29 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
   const int nqt = (a.T + 31) / 32, qt0 = kb * (kRows / 32);
   const int diag = k_first / 32;  // this wave's first (diagonal) query tile
 
-  bf16x8 k1t[4], k2t[4];
-  load_krow(k1t, a.k1 + (int64_t)b * a.sk1.b + (int64_t)head * a.sk1.h, a.sk1.t, key, ok, hf);
-  load_krow(k2t, a.k2 + (int64_t)b * a.sk2.b + (int64_t)head * a.sk2.h, a.sk2.t, key, ok, hf);
+  const int64_t rk = ((int64_t)b * a.T + key) * a.H + head;
+  f16x8 k1t[4], k2t[4];
+  load_row16(k1t, a.k1h, rk, ok, hf);
+  load_row16(k2t, a.k2h, rk, ok, hf);
   f16x8 vt[kDV ? 1 : 8];
-  if constexpr (!kDV) {
-    const uint16_t* p = a.v + (int64_t)b * a.sv.b + (int64_t)key * a.sv.t + (int64_t)head * a.sv.h + 8 * hf;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const u32x4 w = ok ? *reinterpret_cast<const u32x4*>(p + 16 * s) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vt[s][2 * i] = (_Float16)bf16_lo(w[i]);
-        vt[s][2 * i + 1] = (_Float16)bf16_hi(w[i]);
-      }
-    }
-  }
+  if constexpr (!kDV) load_row16(vt, a.vh, rk, ok, hf);
   const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
   const float c = a.c;
-  const uint16_t* qb1 = a.q1 + (int64_t)b * a.sq1.b + (int64_t)head * a.sq1.h;
-  const uint16_t* qb2 = a.q2 + (int64_t)b * a.sq2.b + (int64_t)head * a.sq2.h;
-  const uint16_t* dob = a.dO + (int64_t)b * a.T * a.H * kDv + (int64_t)head * kDv;
-  const int64_t sdo = (int64_t)a.H * kDv;
+  const int64_t row0 = (int64_t)b * a.T * a.H + head;  // (b, t = 0, head)
+  const uint16_t* qb1 = a.q1h + row0 * kDqk;
+  const uint16_t* qb2 = a.q2h + row0 * kDqk;
+  const uint16_t* dob = a.dO + row0 * kDv;
+  const int64_t sq = (int64_t)a.H * kDqk, sdo = (int64_t)a.H * kDv;
 
   f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};  // dK_1 (0, 1), dK_2 (2, 3) or dV^T (0 .. 3)
-  StagedT sq;
   auto stage_issue = [&](int qt, char* st) {
     if constexpr (!kDV) {
-      dma_qk(qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, st, rt);
+      dma_qk(qb1, qb2, sq, sq, 32 * qt, a.T, st, rt);
       dma_do(dob, sdo, 32 * qt, a.T, st + kOffDo, rt);
-      load_qkT(sq, qb1, qb2, a.sq1.t, a.sq2.t, 32 * qt, a.T, rt);
     }
   };
   auto stage_store = [&](int qt, char* st) {
-    if constexpr (!kDV)
-      store_qkT(sq, st + kOffQT, rt);
-    else
-      stage_stats(a, b, head, 32 * qt, reinterpret_cast<float*>(st + kOffSt), rt);
+    if constexpr (kDV) stage_stats(a, b, head, 32 * qt, reinterpret_cast<float*>(st + kOffSt), rt);
   };
   if (qt0 < nqt) {
     stage_issue(qt0, smem);
@@ -623,12 +579,11 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
         f16x8 a0, a1, b0, b1;
         pack16(s1, a0, a1);
         pack16(s2, b0, b1);
-        // dK_m^T += Q_m^T dS_m
-        const char* qtT = cur + kOffQT;
+        // dK_m^T += Q_m^T dS_m, Q_m^T read transposed from the query tiles
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-          acc[blk] = mfma_T(qtT, blk, lk, hf, a0, a1, acc[blk]);
-          acc[2 + blk] = mfma_T(qtT + kQKT, blk, lk, hf, b0, b1, acc[2 + blk]);
+          acc[blk] = mfma_tr<kKRow>(cur, blk, lane, a0, a1, acc[blk]);
+          acc[2 + blk] = mfma_tr<kKRow>(cur + kQKTile, blk, lane, b0, b1, acc[2 + blk]);
         }
       } else {
 #pragma unroll
@@ -647,12 +602,8 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
         f16x8 p0, p1;
         pack16(s1, p0, p1);
         // dV^T += dO^T (P_1 - lambda P_2), dO^T read transposed from the dO tile
-        const char* dt = cur + kOffDo;
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tr_operand(dt, blk, 0, lane), p0, acc[blk], 0, 0, 0);
-          acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tr_operand(dt, blk, 1, lane), p1, acc[blk], 0, 0, 0);
-        }
+        for (int blk = 0; blk < 4; ++blk) acc[blk] = mfma_tr<kD16Row>(cur + kOffDo, blk, lane, p0, p1, acc[blk]);
       }
     }
     if (more) stage_store(qt + 1, nxt);
@@ -660,7 +611,6 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
     __syncthreads();
   }
   if (!ok) return;
-  const int64_t rk = ((int64_t)b * a.T + key) * a.H + head;
   if constexpr (!kDV) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -689,6 +639,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)a.H), dim3(192), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t chunks = (int64_t)a.B * a.T * a.H * 48;
+  hipLaunchKernelGGL(bwd_cast_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t blocks = (int64_t)((a.T + kRows - 1) / kRows) * a.B * a.H;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);

@@ -131,6 +131,11 @@ struct BackwardArgs {
   float* dlam;            // [H]
   float* dgain;           // [H, kDv]
   // workspace
+  uint16_t* q1h;          // fp16 copies of the inputs, contiguous [B, T, H, d] (the
+  uint16_t* q2h;          // product kernels take every tile by DMA and every
+  uint16_t* k1h;          // transposed operand by transposed LDS reads)
+  uint16_t* k2h;
+  uint16_t* vh;
   uint16_t* dO;           // [B, T, H, kDv] fp16: gradient of the pre-norm output
   float* dstat;           // [B, T, H, 2]: D_m = rowsum(dO_m * O_m) per map
   float* partial;         // [H, nchunks, kDv + 1]: gain and lambda gradient partials

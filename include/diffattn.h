@@ -262,8 +262,9 @@ DIFFATTN_API int diffattn_fwd_prefill_train(const void* q1, const void* q2, cons
 
 /*
  * Bytes of device workspace diffattn_bwd_prefill needs (256-byte aligned
- * buffer): the pre-norm output gradient in fp16, two row statistics and the
- * gain/lambda partial sums.  Returns 0 for invalid sizes.
+ * buffer): fp16 copies of q1, q2, k1, k2 and v, the pre-norm output gradient
+ * in fp16, two row statistics and the gain/lambda partial sums (about
+ * B * T * H * (4 d_qk + 2 d_v) * 2 bytes).  Returns 0 for invalid sizes.
  */
 DIFFATTN_API size_t diffattn_bwd_workspace_bytes(int B, int T, int H, int d_v);
 
@@ -329,7 +330,8 @@ DIFFATTN_API const char* diffattn_status_string(int status);
 /* Library ABI version (major * 100 + minor): 101 adds the *_ex entry points,
  * 102 the rotary embedding (diffattn_options.rope, diffattn_rope_apply), 103
  * the training forward and the backward pass, 104 grouped attention, 105 the
- * prefill workspace entry points (keys rotated once). */
+ * prefill workspace entry points (keys rotated once), 106 a larger backward
+ * workspace (fp16 input copies; query diffattn_bwd_workspace_bytes again). */
 DIFFATTN_API int diffattn_abi_version(void);
 
 #ifdef __cplusplus

@@ -32,7 +32,7 @@ def test_header_symbols_exported():
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 105
+    assert da.diffattn_abi_version() == 106
 
 
 def test_status_strings():
