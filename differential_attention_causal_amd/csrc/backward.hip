@@ -325,25 +325,33 @@ __device__ __forceinline__ f32x16 mfma_tr(const char* tile, int blk, int lane, c
 }
 
 // ---------------------------------------------------------------------------
-// dQ_1, dQ_2: a workgroup owns 128 queries of one (b, h); wave w queries
-// 32w .. 32w+31, lane (hf, lq) query lq.  Key tiles of the fp16 copies stream
-// through LDS by DMA alone: K_1, K_2 (score operands, and K^T by transposed
-// reads for dQ^T) and V (dP^T operand), all row-major.
-constexpr int kDqStage = 2 * kQKTile + kD16Tile;
+// dQ_1, dQ_2: 128 queries of one (b, h) per work item; wave w of a group
+// queries 32w .. 32w+31, lane (hf, lq) query lq.  Two groups of four waves
+// take alternate key tiles of the same queries and add their dQ at the end.
+// Key tiles of the fp16 copies stream through LDS by DMA alone: K_1, K_2
+// (score operands, and K^T by transposed reads for dQ^T) and V (dP^T
+// operand), all row-major.  Workgroup r * B*H + bh runs the items of rows r
+// and nqb - 1 - r (longest-first order) of (b, h) = bh back to back, so every
+// workgroup carries the same number of key tiles.
+constexpr int kDqTile = 2 * kQKTile + kD16Tile;  // one group's key tile
+constexpr int kDqStage = 2 * kDqTile;             // one step: a tile for each group
+static_assert(4 * 64 * 64 * 4 <= 2 * kDqStage, "the dQ merge must fit in the stages");
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BackwardArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kDqStage];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, lq = lane & 31;
+__device__ __forceinline__ void dq_item(const BackwardArgs& a, char* smem, int item) {
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, lq = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wq = wave & 3, rt = tid & 255;
   const int nqb = (a.T + kRows - 1) / kRows, BH = a.B * a.H;
-  const int qb = nqb - 1 - (int)(blockIdx.x / BH);  // longest rows first
-  const int bh = (int)(blockIdx.x % BH), head = bh % a.H, b = bh / a.H;
-  const int q_first = qb * kRows + 32 * wave, q = q_first + lq;
+  const int qb = nqb - 1 - item / BH;
+  const int bh = item % BH, head = bh % a.H, b = bh / a.H;
+  const int q_first = qb * kRows + 32 * wq, q = q_first + lq;
   const bool wave_live = q_first < a.T, ok = q < a.T;
   const int ntiles = min(qb * (kRows / 32) + kRows / 32, (a.T + 31) / 32);
+  const int nsteps = (ntiles + 1) / 2;
   const int kend = min(a.T, ntiles * 32);
   const int last_tile = q_first / 32;
 
-  // Operands held for the whole kernel: Q_m^T (score B operands) and dO^T
+  // Operands held for the whole item: Q_m^T (score B operands) and dO^T
   // (dP^T B operand), fp16, both for this lane's query.
   f16x8 qa[4], qb2[4];
   f16x8 dot[8];
@@ -374,18 +382,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   f32x16 dq1[2] = {f32x16{}, f32x16{}}, dq2[2] = {f32x16{}, f32x16{}};
   const int ksw = kSwz(lq);
 
-  auto stage_issue = [&](int j, char* st) {
-    dma_qk(kb1, kb2, sk, sk, 32 * j, kend, st, tid);
-    dma_do(vb, sv, 32 * j, kend, st + 2 * kQKTile, tid);
+  // Each group stages its own tile of the step (tile 2 it + grp; past the
+  // last tile the rows read as zero).
+  auto stage_issue = [&](int it, char* st) {
+    const int j = 2 * it + grp;
+    char* t = st + grp * kDqTile;
+    dma_qk(kb1, kb2, sk, sk, 32 * j, kend, t, rt);
+    dma_do(vb, sv, 32 * j, kend, t + 2 * kQKTile, rt);
   };
   stage_issue(0, smem);
   wait_dma();
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    char* cur = smem + (j & 1) * kDqStage;
-    char* nxt = smem + ((j + 1) & 1) * kDqStage;
-    if (j + 1 < ntiles) stage_issue(j + 1, nxt);
+  for (int it = 0; it < nsteps; ++it) {
+    char* cur = smem + (it & 1) * kDqStage + grp * kDqTile;
+    if (it + 1 < nsteps) stage_issue(it + 1, smem + ((it + 1) & 1) * kDqStage);
+    const int j = 2 * it + grp;
     if (wave_live && j <= last_tile) {
       // S_m^T = K_m Q_m^T (32 keys x 32 queries)
       f32x16 s1 = f32x16{}, s2 = f32x16{};
@@ -430,11 +442,45 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     wait_dma();
     __syncthreads();
   }
-  if (!ok) return;
+  // Group 1's sums through LDS (the stages are free after the last barrier),
+  // added to group 0's in a fixed order: group 0's partial + group 1's.
+  float* mo = reinterpret_cast<float*>(smem);
+  auto slot = [&](int k, int i) { return ((wq * 64) + k * 16 + i) * 64 + lane; };
+  if (grp == 1) {
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    store_col(a.dq1 + rq * kDqk, dq1[blk], blk, hf, a.scale);
-    store_col(a.dq2 + rq * kDqk, dq2[blk], blk, hf, a.scale);
+    for (int i = 0; i < 16; ++i) {
+      mo[slot(0, i)] = dq1[0][i];
+      mo[slot(1, i)] = dq1[1][i];
+      mo[slot(2, i)] = dq2[0][i];
+      mo[slot(3, i)] = dq2[1][i];
+    }
+  }
+  __syncthreads();
+  if (grp == 0 && ok) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dq1[0][i] += mo[slot(0, i)];
+      dq1[1][i] += mo[slot(1, i)];
+      dq2[0][i] += mo[slot(2, i)];
+      dq2[1][i] += mo[slot(3, i)];
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      store_col(a.dq1 + rq * kDqk, dq1[blk], blk, hf, a.scale);
+      store_col(a.dq2 + rq * kDqk, dq2[blk], blk, hf, a.scale);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BackwardArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kDqStage];
+  const int BH = a.B * a.H;
+  const int nqb = (a.T + kRows - 1) / kRows;
+  const int r = (int)blockIdx.x / BH, bh = (int)blockIdx.x % BH;
+  dq_item(a, smem, (int)blockIdx.x);
+  if (nqb - 1 - r > r) {
+    __syncthreads();  // the first item's merge is done with LDS
+    dq_item(a, smem, (nqb - 1 - r) * BH + bh);
   }
 }
 
@@ -643,8 +689,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   const int64_t chunks = (int64_t)a.B * a.T * a.H * 48;
   hipLaunchKernelGGL(bwd_cast_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t blocks = (int64_t)((a.T + kRows - 1) / kRows) * a.B * a.H;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  const int64_t nqb = (a.T + kRows - 1) / kRows;
+  const int64_t blocks = nqb * a.B * a.H;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((nqb + 1) / 2 * a.B * a.H)), dim3(512), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)blocks), dim3(512), 0, stream, a);
   return hipGetLastError();
