@@ -44,10 +44,19 @@ constexpr int kQKTile = 32 * kKRow;     // 4 KiB: one map's 32-row fp16 tile
 constexpr int kD16Row = kDv * 2;        // 256-byte fp16 rows of dO or V
 constexpr int kD16Tile = 32 * kD16Row;  // 8 KiB
 
-// 16-byte chunk swizzle of 256-byte rows (16 chunks): rows r and r ^ 16 share
-// it, so a 16-byte read by 32 lanes of consecutive rows is at most 2-way
-// conflicted.
-__device__ __forceinline__ int swz16(int r) { return r & 15; }
+// 16-byte chunk swizzles of the tiles' rows, logical chunk c of row r stored
+// at chunk c ^ swz(r).  Two kinds of reads must be conflict-free on 64 banks:
+// a 16-byte read by lanes of consecutive rows at one logical chunk (row-major
+// operands), and a transposed 8-byte read (ds_read_b64_tr_b16) whose 32
+// lanes of a pass cover four consecutive rows 4m .. 4m+3 and four chunks of
+// one aligned group.  256-byte rows (16 chunks; every row spans all banks):
+// swz16 is a bijection on r % 16 for the first, and gives rows 4m .. 4m+3
+// different chunk groups for the second.  128-byte rows (8 chunks; rows r and
+// r + 1 share the banks' halves): swz8 takes 8 distinct values over the even
+// rows and over the odd rows of 16 consecutive ones, and rows 4m and 4m + 2
+// differ in its group bit.
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz8(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 // ---------------------------------------------------------------------------
 // Per row: the GroupNorm backward, do, D_1 = rowsum(do O_1),
@@ -241,11 +250,11 @@ __global__ void __launch_bounds__(256) bwd_cast_kernel(BackwardArgs a) {
 // reading as zero.  Threads 0..255 of the workgroup take part.
 
 // Row-major fp16 tiles of both maps (Q or K) by DMA into [map][32][128 B]
-// with the kSwz chunk swizzle: thread t fetches row t/8, logical chunk
-// (t % 8) ^ kSwz(t / 8), landing at chunk position t.
+// with the swz8 chunk swizzle: thread t fetches row t/8, logical chunk
+// (t % 8) ^ swz8(t / 8), landing at chunk position t.
 __device__ __forceinline__ void dma_qk(const uint16_t* b1, const uint16_t* b2, int64_t st1, int64_t st2, int r0,
                                        int end, char* dst, int tid) {
-  const int r = tid >> 3, c = (tid & 7) ^ kSwz(r);
+  const int r = tid >> 3, c = (tid & 7) ^ swz8(r);
   char* d = dst + (tid >> 6) * 1024;  // each wave fills 1 KiB of each map's tile
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(b1, st1, r0, end, kDqk), (lds_ptr_t)d, 16,
                                            (uint32_t)((r * st1 + 8 * c) * 2), 0, 0, 0);
@@ -289,7 +298,7 @@ __device__ __forceinline__ void store_col(float* dst, const f32x16& acc, int blk
 }
 
 // The transposed operand of a row-major fp16 tile of 32 rows (kRowBytes-byte
-// rows: 256 with the swz16 chunk swizzle, 128 with kSwz) by
+// rows: 256 with the swz16 chunk swizzle, 128 with swz8) by
 // ds_read_b64_tr_b16, which hands lane i of each 16-lane group element i % 4
 // of the 8-byte reads of lanes 4k + i / 4, k = 0..3.  For column block blk
 // and k-half kh, lane (hf, g, L) (g: 16-lane group within the half, L: lane
@@ -307,7 +316,7 @@ __device__ __forceinline__ f16x8 tr_operand(const char* tile, int blk, int kh, i
   const int col = 32 * blk + 16 * g + 4 * (L & 3);
   auto rd = [&](int h) {
     const int row = 16 * kh + 8 * h + 4 * hf + (L >> 2);
-    const int sw = kRowBytes == 256 ? swz16(row) : kSwz(row);
+    const int sw = kRowBytes == 256 ? swz16(row) : swz8(row);
     const char* p = tile + row * kRowBytes + (((col >> 3) ^ sw) << 4) + (col & 7) * 2;
     return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
   };
@@ -380,7 +389,7 @@ __device__ __forceinline__ void dq_item(const BackwardArgs& a, char* smem, int i
   const int64_t sk = (int64_t)a.H * kDqk, sv = (int64_t)a.H * kDv;
 
   f32x16 dq1[2] = {f32x16{}, f32x16{}}, dq2[2] = {f32x16{}, f32x16{}};
-  const int ksw = kSwz(lq);
+  const int ksw = swz8(lq);
 
   // Each group stages its own tile of the step (tile 2 it + grp; past the
   // last tile the rows read as zero).
@@ -511,7 +520,7 @@ __device__ __forceinline__ void stage_stats(const BackwardArgs& a, int b, int he
 // S_m = Q_m K_m^T for one map from a row-major fp16 Q tile.
 __device__ __forceinline__ f32x16 scores_qk(const char* qt, const f16x8 (&kt)[4], int lq, int hf) {
   f32x16 acc = f32x16{};
-  const int sw = kSwz(lq);
+  const int sw = swz8(lq);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(
