@@ -50,11 +50,15 @@ def _oracle_prefill(x, window, rows=None):
                           x["scale"], rows=rows, window=window)
 
 
-# Small grids run the split-key workgroup (two wave groups), the larger ones
-# below the four-wave one; both skip the tiles before each wave's window.
+# Windows of at most four key tiles before the diagonal one (w <= 129) run the
+# streaming kernel (four query blocks per workgroup, key tiles through a ring);
+# deeper windows the split-key or four-wave kernels, which skip the tiles
+# before each wave's window.  The cases span every depth 0..4 of the
+# streaming kernel (w = 1, 7, 31, 32, 33; 64, 65; 96; 100, 128, 129), ragged
+# ends, several blocks per workgroup and several workgroups per head.
 SMALL = [
     (1, 64, 1, 31), (1, 129, 2, 33), (1, 333, 2, 1), (1, 333, 2, 7), (2, 200, 3, 32), (1, 515, 2, 100),
-    (1, 1000, 2, 128), (1, 1000, 2, 129), (2, 700, 2, 1000), (1, 257, 2, 96),
+    (1, 1000, 2, 128), (1, 1000, 2, 129), (2, 700, 2, 1000), (1, 257, 2, 96), (1, 700, 2, 64), (2, 600, 3, 65),
 ]
 
 
