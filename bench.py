@@ -47,7 +47,7 @@ SWA_DECODE_WL = "swa_decode_b64_l4096_h16_w128"
 ROPE_THETA = 500000.0        # Motif 2.6B's RoPE base
 CSRC = os.path.join(ROOT, "differential_attention_causal_amd", "csrc")
 PREFILL_PMC = os.path.join(ROOT, "profiles", "prefill_kernel_b1_t4096_h16_hbm_counters.txt")
-PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("prefill.hip", "kernels.h", "rope.h", "tile.h")]
+PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("prefill.hip", "prefill_tiles.h", "kernels.h", "rope.h", "tile.h")]
 DECODE_PMC = os.path.join(ROOT, "profiles", "decode_split_kernel_b64_l4096_h16_hbm_counters.txt")
 DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode.hip", "kernels.h", "rope.h")]
 

@@ -28,7 +28,7 @@ COMMON = [
     # with VALU ops, and AGPR accumulators cost a copy each way per key tile
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
-SOURCES = ["prefill.hip", "decode.hip", "rope.hip", "backward.hip", "grouped.hip", "api.cpp"]
+SOURCES = ["prefill.hip", "window.hip", "decode.hip", "rope.hip", "backward.hip", "grouped.hip", "api.cpp"]
 
 
 def _compile(src: str) -> str:

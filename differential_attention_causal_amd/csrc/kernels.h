@@ -168,6 +168,11 @@ constexpr int kBwdRowsPerChunk = 64;
 void rope_phases(float theta, RopeArgs& r);
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// The sliding-window streaming kernel (window.hip): whether it takes a's
+// configuration (window of at most 129 keys, no rotary embedding, no training
+// outputs), and its launch.
+bool prefill_window_kernel_fits(const PrefillArgs& a);
+hipError_t launch_prefill_window(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t stream);
 hipError_t launch_rope_keys(const RopeKeysArgs& a, hipStream_t stream);
