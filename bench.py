@@ -90,6 +90,18 @@ def decode_bytes(wl) -> int:
     return cache + q + out + gain
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "" where unavailable."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(x, wl, gpu=None):
     """Time the fp64 oracle on all rows of the prefill workload on this host.
     gpu: the benchmarked kernel's outputs on the same inputs (bf16 y, fp32 y,
@@ -106,7 +118,8 @@ def cpu_baseline(x, wl, gpu=None):
     flop = wl.causal_pairs * FLOP_PER_PAIR
     rec = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
            "sample": "all %d rows of %s (B=1,T=4096,H=16), fp64, %.2f s wall; FLOP counted at %d per "
-                     "causal pair like the GPU value" % (wl.B * wl.T * wl.H, wl.name, dt, FLOP_PER_PAIR)}
+                     "causal pair like the GPU value" % (wl.B * wl.T * wl.H, wl.name, dt, FLOP_PER_PAIR),
+           "seconds": dt, "cpu_model": cpu_model()}
     if gpu is not None:
         def ymet(y):
             d = np.abs(y.astype(np.float64) - y_ref)
