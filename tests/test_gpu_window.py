@@ -73,6 +73,29 @@ def test_prefill_window_all_rows(B, T, H, W):
     assert_parity(m, (B, T, H, W))
 
 
+@pytest.mark.parametrize("W", [100, 128])
+def test_prefill_window_options(W):
+    """The streaming kernel with per-head lambda, fp32 output, no pre-norm
+    output, and Q1, Q2, K1, K2, V as slices of one fused [B, T, H, 384]
+    projection output (row strides of 384 elements)."""
+    _say("prefill window options", W)
+    B, T, H = 2, 450, 3
+    x = _inputs(B, T, H, seed=500 + W, lam_range=(0.2, 0.9))
+    o_ref, y_ref = _oracle_prefill(x, W)
+    out, o_pre = _prefill(x, W, per_head=True)
+    assert_parity(metrics(out.float().cpu().numpy(), y_ref, o_pre.cpu().numpy(), o_ref), ("per-head", W))
+    out32, _ = _prefill(x, W, per_head=True, out_dtype=torch.float32)
+    assert_parity(metrics(out32.cpu().numpy(), y_ref, o_pre.cpu().numpy(), o_ref), ("fp32 out", W))
+    fused = to_dev(np.concatenate([x["q1"], x["q2"], x["k1"], x["k2"], x["v"]], axis=3))
+    q1, q2, k1, k2, v = (fused[..., 0:64], fused[..., 64:128], fused[..., 128:192], fused[..., 192:256],
+                         fused[..., 256:384])
+    out_s = da.diffattn_fwd_prefill_ex(q1, q2, k1, k2, v, f32_dev(x["lam"]), f32_dev(x["gain"]), eps=x["eps"],
+                                       scale=x["scale"], window=W)
+    torch.cuda.synchronize()
+    # Same kernel, same arithmetic: the layout and the missing o_pre change nothing.
+    assert torch.equal(out_s, out)
+
+
 def _window_rows(B, T, H, W, rng, n_random=40):
     rows = set()
     for b in {0, B - 1}:
