@@ -231,9 +231,11 @@ __device__ __forceinline__ void rope_query(bf16x8 (&q1)[4], bf16x8 (&q2)[4], int
 
 // GroupNorm over the 128 channels of the query (o in O, lane (hf, lq)
 // holding channels 32cb + 8(i/4) + 4hf + i%4, its partner lane the other 64),
-// then the stores.  g: the head's gain (global or shared memory).
-__device__ __forceinline__ void norm_store(const PrefillArgs& a, int b, int head, int q, int hf, f32x16 (&O)[4],
-                                           const float* g) {
+// then the stores.  gain(cb, r4): the head's gain of channels 32cb + 8r4 + 4hf
+// .. +3.
+template <class GainFn>
+__device__ __forceinline__ void norm_store_g(const PrefillArgs& a, int b, int head, int q, int hf, f32x16 (&O)[4],
+                                             GainFn gain) {
   float sum = 0.f;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
@@ -260,7 +262,7 @@ __device__ __forceinline__ void norm_store(const PrefillArgs& a, int b, int head
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int ch = 32 * cb + 8 * r4 + 4 * hf;
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(g + ch);
+      const f32x4 gv = gain(cb, r4);
       f32x4 o, y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -277,6 +279,49 @@ __device__ __forceinline__ void norm_store(const PrefillArgs& a, int b, int head
       }
     }
   }
+}
+
+// norm_store_g with the gain read from g (shared memory) at each store.
+__device__ __forceinline__ void norm_store(const PrefillArgs& a, int b, int head, int q, int hf, f32x16 (&O)[4],
+                                           const float* g) {
+  norm_store_g(a, b, head, q, hf, O,
+               [&](int cb, int r4) { return *reinterpret_cast<const f32x4*>(g + 32 * cb + 8 * r4 + 4 * hf); });
+}
+
+// A lane's 64 gains of the head (the channels norm_store_g stores) from global
+// memory.  Loaded before any store of the epilogue: the memory counter also
+// counts stores, so a load issued after a store waits for that store too.
+__device__ __forceinline__ void load_gain(const PrefillArgs& a, int head, int hf, f32x4 (&gv)[4][4]) {
+  const float* g = a.gain + (int64_t)head * kDv + 4 * hf;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) gv[cb][r4] = *reinterpret_cast<const f32x4*>(g + 32 * cb + 8 * r4);
+}
+
+// The same gains through the scalar cache: the head's 128 gains sit at a
+// uniform address, read through the constant address space (the gain is not
+// written while a kernel runs), so they come in by scalar loads.  These take
+// no vector registers and are not ordered behind the vector memory counter,
+// whose in-order waits would also wait for stores already issued.  Both
+// halves of a lane pair's four channels are read; the lane picks its own.
+struct ScalarGain {
+  const __attribute__((address_space(4))) f32x4* g;  // the head's gains, 32 float4s
+  int hf;
+  __device__ __forceinline__ f32x4 operator()(int cb, int r4) const {
+    const f32x4 lo = g[8 * cb + 2 * r4], hi = g[8 * cb + 2 * r4 + 1];
+    return hf ? hi : lo;
+  }
+};
+
+__device__ __forceinline__ ScalarGain scalar_gain(const PrefillArgs& a, int head, int hf) {
+  // Global and constant addresses coincide: the conversion goes through the
+  // integer address.
+  return ScalarGain{(const __attribute__((address_space(4))) f32x4*)(uintptr_t)(a.gain + (int64_t)head * kDv), hf};
+}
+
+__device__ __forceinline__ float head_lambda(const PrefillArgs& a, int head) {
+  return a.lambda_h ? a.lambda_h[head] : a.lambda;
 }
 
 // Fold the two wave groups' softmax states of each query and form the
@@ -369,10 +414,29 @@ __device__ __forceinline__ void merge_out(const PrefillArgs& a, char* smem, int 
   }
 }
 
+// o = O1 / l1 - lam O2 / l2 into O1 (l1, l2: the row's full sums).
+__device__ __forceinline__ void combine_maps(float lam, float l1, float l2, f32x16 (&O1)[4], const f32x16 (&O2)[4]) {
+  const float r1 = 1.0f / l1;
+  const float r2 = lam / l2;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // Both products rounded before the subtraction (no FMA contraction), so
+      // two identical maps at lambda = 1 cancel to exactly zero.
+#pragma clang fp contract(off)
+      O1[cb][i] = O1[cb][i] * r1 - O2[cb][i] * r2;
+    }
+  }
+}
+
 // Combine the two maps of one query row (lane pair) from their final softmax
-// states, write the training outputs if asked, then GroupNorm and store.
+// states, write the training outputs if asked, then GroupNorm and store; lam
+// is the head's lambda and gv its gains (load_gain), both read before any
+// store.
 __device__ __forceinline__ void finish_rows(const PrefillArgs& a, int b, int head, int q, int hf, float m1, float m2,
-                                            float l1, float l2, f32x16 (&O1)[4], f32x16 (&O2)[4]) {
+                                            float l1, float l2, f32x16 (&O1)[4], f32x16 (&O2)[4], float lam,
+                                            const f32x4 (&gv)[4][4]) {
   l1 += __shfl_xor(l1, 32);
   l2 += __shfl_xor(l2, 32);
   if (a.o1n != nullptr && q < a.T) {
@@ -398,20 +462,20 @@ __device__ __forceinline__ void finish_rows(const PrefillArgs& a, int b, int hea
       a.lse[rq * 2 + 1] = m2 + __builtin_log2f(l2);
     }
   }
-  const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
-  const float r1 = 1.0f / l1;
-  const float r2 = lam / l2;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      // Both products rounded before the subtraction (no FMA contraction), so
-      // two identical maps at lambda = 1 cancel to exactly zero.
-#pragma clang fp contract(off)
-      O1[cb][i] = O1[cb][i] * r1 - O2[cb][i] * r2;
-    }
-  }
-  norm_store(a, b, head, q, hf, O1, a.gain + (int64_t)head * kDv);
+  combine_maps(lam, l1, l2, O1, O2);
+  // The gains have landed before the first store (left to itself the
+  // compiler waits for each gain after the stores issued before its use).
+  wait_vm<0>();
+  norm_store_g(a, b, head, q, hf, O1, [&](int cb, int r4) { return gv[cb][r4]; });
+}
+
+// finish_rows with lambda and the gains loaded first.
+__device__ __forceinline__ void finish_rows(const PrefillArgs& a, int b, int head, int q, int hf, float m1, float m2,
+                                            float l1, float l2, f32x16 (&O1)[4], f32x16 (&O2)[4]) {
+  const float lam = head_lambda(a, head);
+  f32x4 gv[4][4];
+  load_gain(a, head, hf, gv);
+  finish_rows(a, b, head, q, hf, m1, m2, l1, l2, O1, O2, lam, gv);
 }
 
 // S^T = K Q^T of one tile for both maps, K from LDS: bf16 operands, or fp16

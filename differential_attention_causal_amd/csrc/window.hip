@@ -94,12 +94,24 @@ prefill_swa_kernel(PrefillArgs a) {
     }
   };
 
-  // Prologue: the first block's queries and the four tiles of its first step.
+  // Prologue: lambda, the first block's queries and the four tiles of its
+  // first step, all loads issued before the first V store (one round trip).
+  const float lam = head_lambda(a, head);
   load_q(qb0);
-  for (int k = 4 * qb0 - d; k < 4 * qb0 - d + 4; ++k) {
-    if (k < 0) continue;
-    load_kv(k);
-    store_v(k);
+  {
+    Staged st4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = 4 * qb0 - d + i;
+      if (k < 0) continue;
+      stage_dma_k(a, kb1, kb2, soff, slot(k), k * kBN, a.T, tid);
+      stage_load<0>(st4[i], a, kb1, kb2, vbase, soff, k * kBN, a.T, tid);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = 4 * qb0 - d + i;
+      if (k >= 0) sw_store_v(st4[i], slot(k), tid);
+    }
   }
   wait_dma();
   __syncthreads();
@@ -123,12 +135,11 @@ prefill_swa_kernel(PrefillArgs a) {
       // unless the window is exactly four tiles deep (nothing new then).
       const bool next_block = last && qb + 1 < qb1;
       const int pf = (!last || (next_block && d < 4)) ? t0 + 4 : -1;
-      if (pf >= 0) load_kv(pf);
-
       const int j = t0 + wave;
-      if (wave_live && j >= 0) {
-        const char* kt = slot(j);
-        f32x16 s1 = f32x16{}, s2 = f32x16{};
+      const bool act = wave_live && j >= 0;
+      const char* kt = slot(j < 0 ? 0 : j);
+      f32x16 s1 = f32x16{}, s2 = f32x16{};
+      if (act) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int off = lq * kKRow + (((2 * k + hf) ^ ksw) << 4);
@@ -136,6 +147,14 @@ prefill_swa_kernel(PrefillArgs a) {
           s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kt + kKBytes + off), qb2[k],
                                                        s2, 0, 0, 0);
         }
+      }
+      // The next tile's loads go out after the score products: a wait for the
+      // query registers before the first product (which the compiler places
+      // conservatively) then has nothing newer in flight to wait for.
+      __builtin_amdgcn_sched_barrier(0);
+      if (pf >= 0) load_kv(pf);
+      __builtin_amdgcn_sched_barrier(0);
+      if (act) {
         mask_tile(a, s1, s2, j, wave_last_tile, q_first, q, hf);
         f16x8 p1a, p1b, p2a, p2b;
         softmax_step(s1, c, m1, l1, O1, p1a, p1b);
@@ -156,9 +175,18 @@ prefill_swa_kernel(PrefillArgs a) {
       wait_dma();
       __syncthreads();
     }
-    if (wave_live) finish_rows(a, b, head, q, hf, m1, m2, l1, l2, O1, O2);
-    if (qb + 1 < qb1) {
-      load_q(qb + 1);
+    // Epilogue.  The next block's queries are fetched first (unconditionally:
+    // rows at or past T read as zero, and no second set of query registers
+    // is needed) and waited for once the two maps are combined, before any
+    // store: left to the compiler, that wait would sit before the next
+    // block's first product, where it would also cover each step's tile
+    // prefetch.  The gains come by scalar loads (no wait behind the stores).
+    const bool more = qb + 1 < qb1;
+    load_q(qb + 1);
+    if (wave_live) combine_maps(lam, l1 + __shfl_xor(l1, 32), l2 + __shfl_xor(l2, 32), O1, O2);
+    wait_vm<0>();
+    if (wave_live) norm_store_g(a, b, head, q, hf, O1, scalar_gain(a, head, hf));
+    if (more) {
       if (d < 3) {
         // A window under three tiles deep moves the next block's first step
         // past the prefetched tile: load the rest (their slots held tiles
