@@ -405,9 +405,24 @@ __device__ __forceinline__ void dq_item(const BackwardArgs& a, char* smem, int i
 
   for (int it = 0; it < nsteps; ++it) {
     char* cur = smem + (it & 1) * kDqStage + grp * kDqTile;
-    if (it + 1 < nsteps) stage_issue(it + 1, smem + ((it + 1) & 1) * kDqStage);
     const int j = 2 * it + grp;
-    if (wave_live && j <= last_tile) {
+    const bool act = wave_live && j <= last_tile;
+    // K_m^T operands of the dQ products, read transposed before the next
+    // tile's DMA goes out: the compiler orders transposed LDS reads behind
+    // every LDS DMA in flight, which would make these products wait for the
+    // prefetch.
+    f16x8 kt1[2][2], kt2[2][2];
+    if (act) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          kt1[blk][kh] = tr_operand<kKRow>(cur, blk, kh, lane);
+          kt2[blk][kh] = tr_operand<kKRow>(cur + kQKTile, blk, kh, lane);
+        }
+    }
+    if (it + 1 < nsteps) stage_issue(it + 1, smem + ((it + 1) & 1) * kDqStage);
+    if (act) {
       // S_m^T = K_m Q_m^T (32 keys x 32 queries)
       f32x16 s1 = f32x16{}, s2 = f32x16{};
 #pragma unroll
@@ -441,11 +456,13 @@ __device__ __forceinline__ void dq_item(const BackwardArgs& a, char* smem, int i
       f16x8 a0, a1, b0, b1;
       pack16(s1, a0, a1);
       pack16(s2, b0, b1);
-      // dQ_m^T += K_m^T dS_m^T, K_m^T read transposed from the key tiles
+      // dQ_m^T += K_m^T dS_m^T
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        dq1[blk] = mfma_tr<kKRow>(cur, blk, lane, a0, a1, dq1[blk]);
-        dq2[blk] = mfma_tr<kKRow>(cur + kQKTile, blk, lane, b0, b1, dq2[blk]);
+        dq1[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kt1[blk][0], a0, dq1[blk], 0, 0, 0);
+        dq1[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kt1[blk][1], a1, dq1[blk], 0, 0, 0);
+        dq2[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kt2[blk][0], b0, dq2[blk], 0, 0, 0);
+        dq2[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kt2[blk][1], b1, dq2[blk], 0, 0, 0);
       }
     }
     wait_dma();
