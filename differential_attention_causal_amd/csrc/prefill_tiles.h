@@ -299,25 +299,31 @@ __device__ __forceinline__ void load_gain(const PrefillArgs& a, int head, int hf
     for (int r4 = 0; r4 < 4; ++r4) gv[cb][r4] = *reinterpret_cast<const f32x4*>(g + 32 * cb + 8 * r4);
 }
 
-// The same gains through the scalar cache: the head's 128 gains sit at a
-// uniform address, read through the constant address space (the gain is not
-// written while a kernel runs), so they come in by scalar loads.  These take
-// no vector registers and are not ordered behind the vector memory counter,
-// whose in-order waits would also wait for stores already issued.  Both
-// halves of a lane pair's four channels are read; the lane picks its own.
-struct ScalarGain {
-  const __attribute__((address_space(4))) f32x4* g;  // the head's gains, 32 float4s
+// The same gains spread over the wave: lane L holds the head's gains 2L and
+// 2L + 1 (one coalesced 8-byte load, two registers), and each store's four
+// gains are broadcast from their lanes by v_readlane (the lane index is a
+// constant once unrolled).  Used where 64 registers of gains do not fit.
+struct LaneGain {
+  float g0, g1;
   int hf;
   __device__ __forceinline__ f32x4 operator()(int cb, int r4) const {
-    const f32x4 lo = g[8 * cb + 2 * r4], hi = g[8 * cb + 2 * r4 + 1];
-    return hf ? hi : lo;
+    f32x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c0 = 32 * cb + 8 * r4 + r, c1 = c0 + 4;  // the channel of a lane with hf = 0, hf = 1
+      const float a = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, (c0 & 1) ? g1 : g0), c0 >> 1));
+      const float b = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, (c1 & 1) ? g1 : g0), c1 >> 1));
+      v[r] = hf ? b : a;
+    }
+    return v;
   }
 };
 
-__device__ __forceinline__ ScalarGain scalar_gain(const PrefillArgs& a, int head, int hf) {
-  // Global and constant addresses coincide: the conversion goes through the
-  // integer address.
-  return ScalarGain{(const __attribute__((address_space(4))) f32x4*)(uintptr_t)(a.gain + (int64_t)head * kDv), hf};
+// The lane's two gains (lane = 0 .. 63).
+__device__ __forceinline__ f32x2 load_lane_gain(const PrefillArgs& a, int head, int lane) {
+  return *reinterpret_cast<const f32x2*>(a.gain + (int64_t)head * kDv + 2 * lane);
 }
 
 __device__ __forceinline__ float head_lambda(const PrefillArgs& a, int head) {

@@ -175,17 +175,19 @@ prefill_swa_kernel(PrefillArgs a) {
       wait_dma();
       __syncthreads();
     }
-    // Epilogue.  The next block's queries are fetched first (unconditionally:
-    // rows at or past T read as zero, and no second set of query registers
-    // is needed) and waited for once the two maps are combined, before any
-    // store: left to the compiler, that wait would sit before the next
-    // block's first product, where it would also cover each step's tile
-    // prefetch.  The gains come by scalar loads (no wait behind the stores).
+    // Epilogue.  The next block's queries (unconditionally: rows at or past
+    // T read as zero, and no second set of query registers is needed) and
+    // the lane's two gains go out first and are waited for once the two maps
+    // are combined, before any store.  Left to the compiler, the wait for the
+    // queries would sit before the next block's first product, where it
+    // would also cover each step's tile prefetch; a gain load after a store
+    // would wait for that store.
     const bool more = qb + 1 < qb1;
     load_q(qb + 1);
+    const f32x2 gl = load_lane_gain(a, head, lane);
     if (wave_live) combine_maps(lam, l1 + __shfl_xor(l1, 32), l2 + __shfl_xor(l2, 32), O1, O2);
     wait_vm<0>();
-    if (wave_live) norm_store_g(a, b, head, q, hf, O1, scalar_gain(a, head, hf));
+    if (wave_live) norm_store_g(a, b, head, q, hf, O1, LaneGain{gl.x, gl.y, hf});
     if (more) {
       if (d < 3) {
         // A window under three tiles deep moves the next block's first step
