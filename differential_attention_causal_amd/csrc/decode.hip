@@ -95,11 +95,7 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a) {
     // The query is the sequence's last token, rotated in fp32 (no rounding);
     // cached keys are already rotated.
     __shared__ uint64_t rope_tab[32];
-    if (tid < 32) {
-#pragma unroll
-      for (int c = 0; c < 32; ++c)
-        if (c == tid) rope_tab[c] = a.rope.phase[c];
-    }
+    if (tid < 32) rope_tab[tid] = rope_phase_at(a.rope, tid);
     __syncthreads();
     rope_floats<2>(q, e, a.rope.pos0 + (uint32_t)(n - 1), a.rope.mode, rope_tab);
   }

@@ -319,11 +319,7 @@ prefill_kernel(PrefillArgs a) {
     rope_query(qa, qb2, hf, a.rope.pos0 + (uint32_t)q, a.rope.mode, a.rope);
   } else if constexpr (kRope != 0) {
     // Phase table for the key tiles, then the lane's own query in registers.
-    if (tid < 32) {
-#pragma unroll
-      for (int c = 0; c < 32; ++c)
-        if (c == tid) rope_tab[c] = a.rope.phase[c];
-    }
+    if (tid < 32) rope_tab[tid] = rope_phase_at(a.rope, tid);
     rope_query(qa, qb2, hf, a.rope.pos0 + (uint32_t)q, kRope, a.rope);
     __syncthreads();
   }

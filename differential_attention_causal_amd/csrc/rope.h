@@ -20,6 +20,17 @@ namespace diffattn {
 
 typedef uint32_t rope_u32x4 __attribute__((ext_vector_type(4)));
 
+// phase[c] of the rotary arguments for a lane-dependent c (0 .. 31) without
+// indexing the kernel argument dynamically: a chain of selects over the 32
+// values, which arrive by scalar loads issued together (a branch per value
+// would wait for each load in turn).
+__device__ __forceinline__ uint64_t rope_phase_at(const RopeArgs& r, int c) {
+  uint64_t v = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v = i == c ? r.phase[i] : v;
+  return v;
+}
+
 __device__ __forceinline__ void rope_cos_sin(uint32_t pos, uint64_t phase, float& c, float& s) {
   const uint32_t lo = (uint32_t)phase, hi = (uint32_t)(phase >> 32);
   const uint32_t top = __umulhi(pos, lo) + pos * hi;  // bits 32..63 of pos * phase

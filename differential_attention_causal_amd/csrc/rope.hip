@@ -26,11 +26,7 @@ constexpr int kThreads = 256;  // 32 vectors of 8 chunks per workgroup
 // partner exchange, with zeros, and store nothing.
 __global__ void __launch_bounds__(kThreads) rope_apply_kernel(RopeApplyArgs a) {
   __shared__ uint64_t tab[32];
-  if (threadIdx.x < 32) {
-#pragma unroll
-    for (int c = 0; c < 32; ++c)
-      if (c == (int)threadIdx.x) tab[c] = a.rope.phase[c];
-  }
+  if (threadIdx.x < 32) tab[threadIdx.x] = rope_phase_at(a.rope, (int)threadIdx.x);
   __syncthreads();
   const int64_t vec = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
   const int ch = threadIdx.x & 7;
@@ -52,11 +48,7 @@ __global__ void __launch_bounds__(kThreads) rope_apply_kernel(RopeApplyArgs a) {
 // angles), results rounded to fp16 as the prefill's score products take them.
 __global__ void __launch_bounds__(kThreads) rope_keys_kernel(RopeKeysArgs a) {
   __shared__ uint64_t tab[32];
-  if (threadIdx.x < 32) {
-#pragma unroll
-    for (int c = 0; c < 32; ++c)
-      if (c == (int)threadIdx.x) tab[c] = a.rope.phase[c];
-  }
+  if (threadIdx.x < 32) tab[threadIdx.x] = rope_phase_at(a.rope, (int)threadIdx.x);
   __syncthreads();
   const int64_t vec = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
   const int ch = threadIdx.x & 7;
