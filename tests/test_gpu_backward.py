@@ -111,3 +111,29 @@ def test_backward_deterministic_and_training_outputs():
     assert _rel((o1 - lam * o2).cpu().numpy(), ref["o"]) < 5e-3
     # lse: log2 sum_j 2^(c s_ij); the row max bounds it below, + log2(i+1) above
     assert bool(torch.isfinite(lse).all())
+
+
+def test_training_forward_large_grid():
+    """The training forward on a grid larger than two workgroups per CU (the
+    four-wave kernel, whose epilogue writes the training outputs): y equals the
+    plain forward bitwise, o1 - lambda o2 matches the oracle's pre-norm output
+    on sampled rows, and every log-sum-exp is finite."""
+    import oracle
+
+    _say("training forward, large grid (B=1, T=2048, H=40)")
+    x = _inputs(1, 2048, 40, seed=24)
+    q1, q2, k1, k2, v = (to_dev(x[n]) for n in ("q1", "q2", "k1", "k2", "v"))
+    lam, gain = f32_dev(x["lam"]), f32_dev(x["gain"])
+    out, o1, o2, lse = da.diffattn_fwd_prefill_train(q1, q2, k1, k2, v, lam, gain, eps=x["eps"], scale=x["scale"])
+    plain = da.diffattn_fwd_prefill(q1, q2, k1, k2, v, lam, gain, eps=x["eps"], scale=x["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)
+    rng = np.random.default_rng(24)
+    rows = sorted({(0, i, h) for i in (0, 1, 127, 128, 1023, 2046, 2047) for h in (0, 39)}
+                  | {(0, int(rng.integers(2048)), int(rng.integers(40))) for _ in range(24)})
+    o_ref, _ = oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"],
+                              rows=rows)
+    idx = torch.tensor(rows, dtype=torch.long, device="cuda")
+    o = (o1 - lam[None, None, :, None] * o2)[idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy()
+    assert _rel(o, o_ref) < 5e-3
+    assert bool(torch.isfinite(lse).all())
