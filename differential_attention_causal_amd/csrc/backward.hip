@@ -208,32 +208,26 @@ __global__ void __launch_bounds__(192) bwd_reduce_kernel(BackwardArgs a) {
 }
 
 // fp16 copies of Q_1, Q_2, K_1, K_2 and V, contiguous [B, T, H, d] (exact for
-// |x| in [2^-14, 65504), like every fp16 operand of the products).  One thread
-// converts 8 elements: 48 chunks per (b, t, h) row, 8 from each 64-dim input
-// and 16 from V, so consecutive threads read consecutive 16-byte chunks.
+// |x| in [2^-14, 65504), like every fp16 operand of the products).  blockIdx.y
+// picks the tensor (0 .. 3 the 64-dim inputs, 4 V), so a wave streams
+// consecutive 16-byte chunks of one tensor: 8 chunks per (b, t, h) row of a
+// 64-dim input, 16 of V; one thread converts 8 elements.
 __global__ void __launch_bounds__(256) bwd_cast_kernel(BackwardArgs a) {
+  const int m = (int)blockIdx.y;
+  const int per_row = m < 4 ? 8 : 16;  // chunks per row
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t rows = (int64_t)a.B * a.T * a.H;
-  if (g >= rows * 48) return;
-  const int64_t row = g / 48;
-  const int c = (int)(g % 48);
+  if (g >= rows * per_row) return;
+  const int64_t row = g / per_row;
+  const int ch = (int)(g - row * per_row);
   const int h = (int)(row % a.H);
   const int64_t bt = row / a.H;
   const int t = (int)(bt % a.T), b = (int)(bt / a.T);
-  const uint16_t* src;
-  uint16_t* dst;
-  if (c < 32) {
-    const int m = c >> 3, ch = c & 7;
-    const uint16_t* base = m == 0 ? a.q1 : m == 1 ? a.q2 : m == 2 ? a.k1 : a.k2;
-    const Strides& st = m == 0 ? a.sq1 : m == 1 ? a.sq2 : m == 2 ? a.sk1 : a.sk2;
-    uint16_t* out = m == 0 ? a.q1h : m == 1 ? a.q2h : m == 2 ? a.k1h : a.k2h;
-    src = base + (int64_t)b * st.b + (int64_t)t * st.t + (int64_t)h * st.h + 8 * ch;
-    dst = out + row * kDqk + 8 * ch;
-  } else {
-    const int ch = c - 32;
-    src = a.v + (int64_t)b * a.sv.b + (int64_t)t * a.sv.t + (int64_t)h * a.sv.h + 8 * ch;
-    dst = a.vh + row * kDv + 8 * ch;
-  }
+  const uint16_t* base = m == 0 ? a.q1 : m == 1 ? a.q2 : m == 2 ? a.k1 : m == 3 ? a.k2 : a.v;
+  const Strides& st = m == 0 ? a.sq1 : m == 1 ? a.sq2 : m == 2 ? a.sk1 : m == 3 ? a.sk2 : a.sv;
+  uint16_t* out = m == 0 ? a.q1h : m == 1 ? a.q2h : m == 2 ? a.k1h : m == 3 ? a.k2h : a.vh;
+  const uint16_t* src = base + (int64_t)b * st.b + (int64_t)t * st.t + (int64_t)h * st.h + 8 * ch;
+  uint16_t* dst = out + row * (8 * per_row) + 8 * ch;
   const u32x4 w = *reinterpret_cast<const u32x4*>(src);
   f16x8 o;
 #pragma unroll
@@ -712,8 +706,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)a.H), dim3(192), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t chunks = (int64_t)a.B * a.T * a.H * 48;
-  hipLaunchKernelGGL(bwd_cast_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, a);
+  const int64_t chunks = (int64_t)a.B * a.T * a.H * 16;  // the most of any tensor (V)
+  hipLaunchKernelGGL(bwd_cast_kernel, dim3((unsigned)((chunks + 255) / 256), 5), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t nqb = (a.T + kRows - 1) / kRows;
   const int64_t blocks = nqb * a.B * a.H;
