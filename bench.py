@@ -15,8 +15,11 @@ cpu_baseline object times the fp64 oracle on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 
-The default warm-up (2000 steps, about a second of GPU work) lets the GPU reach
-its steady clocks before the timed region; the timed region is 200 steps.
+Before any counted warm-up step, a time-based settle phase runs whole steps for
+--settle seconds of wall clock (default 2 s, whatever --warmup says), so the GPU
+reaches its steady clocks before the timed region; the shader clock is read
+from sysfs right before and right after the timed region.  Then --warmup
+counted steps, then --steps timed steps.
     python bench.py --copy-calibration     # plain device copy, for HBM counter scaling
 """
 from __future__ import annotations
@@ -44,6 +47,8 @@ PREFILL_WL = "prefill_b1_t4096_h16"
 DECODE_WL = "decode_b64_l4096_h16"
 SWA_PREFILL_WL = "swa_b1_t16384_h16_w128"
 SWA_DECODE_WL = "swa_decode_b64_l4096_h16_w128"
+BATCH_WL = "batch_b8_t4096_h16"
+LONGCTX_WL = "longctx_b1_t16384_h16"
 ROPE_THETA = 500000.0        # Motif 2.6B's RoPE base
 CSRC = os.path.join(ROOT, "differential_attention_causal_amd", "csrc")
 PREFILL_PMC = os.path.join(ROOT, "profiles", "prefill_kernel_b1_t4096_h16_hbm_counters.txt")
@@ -90,6 +95,13 @@ def decode_bytes(wl) -> int:
     return cache + q + out + gain
 
 
+def swa_prefill_bytes(wl) -> int:
+    """Bytes a prefill must move: Q1, Q2, K1, K2, V read once, the bf16 output
+    written once, and the gain."""
+    rows = wl.B * wl.T * wl.H
+    return rows * (4 * wl.d_qk + wl.d_v) * 2 + rows * wl.d_v * 2 + wl.H * wl.d_v * 4
+
+
 def cpu_model() -> str:
     """The host CPU's model name (/proc/cpuinfo), or "" where unavailable."""
     try:
@@ -131,24 +143,47 @@ def cpu_baseline(x, wl, gpu=None):
     return rec
 
 
-def gpu_env(torch, clocks: bool = True) -> dict:
-    """Device, software versions and current clocks (rocm-smi, when it answers;
-    skipped under a profiler, which has the GPU open before the program starts,
-    so that no child process is started from a process holding the GPU)."""
-    import subprocess
+def gpu_env(torch) -> dict:
+    """Device and software versions (the clocks come from read_sclk_mhz)."""
+    return {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__}
 
-    env = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__}
-    if not clocks:
-        env["clocks"] = None
-        return env
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        card = next(iter(json.loads(r.stdout).values()))
-        env["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() or "sclk" in k or "mclk" in k}
-    except Exception as e:  # no rocm-smi, no permission, unexpected output: report without clocks
-        env["clocks"] = None
-        env["clocks_error"] = type(e).__name__
-    return env
+
+def read_sclk_mhz():
+    """Current shader clock in MHz from sysfs (hwmon freq1_input, else the
+    starred pp_dpm_sclk level), or None where neither is readable.  A file
+    read: no child process, no idle gap on the GPU."""
+    import glob
+
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/freq1_input")):
+        try:
+            with open(path) as f:
+                return round(int(f.read().strip()) / 1e6, 1)
+        except (OSError, ValueError):
+            continue
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def settle(torch, step, seconds: float):
+    """Run step() back to back until `seconds` of wall clock have passed
+    (synchronising every 20 steps); returns (seconds, steps)."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        n += 20
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            return dt, n
 
 
 def copy_calibration(steps: int) -> None:
@@ -181,6 +216,7 @@ def _time_calls(torch, np, fn, warmup: int, iters: int):
 
 def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     """The variant rows, timed after, and outside, the step's timed region:
+    the batch (B=8, lambda per head) and long-context (T=16384) prefills,
     Motif 3's sliding-window layer type (128-token windows) as the windowed
     prefill at T=16384 and the windowed decode over the 4096-long caches, the
     T=4096 prefill with the fused RoPE prologue, the T=4096 backward, and
@@ -249,6 +285,30 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     def grouped():
         da.diffattn_fwd_grouped(gq, gk, gv, 3, glam, gate=ggate, out=gout, workspace=gws)
 
+    # the two other full-attention workloads: the training-shaped batch
+    # (B=8, lambda per head) and the long-context layer (T=16384)
+    big = {}
+    for key, name in (("batch_prefill", BATCH_WL), ("longctx_prefill", LONGCTX_WL)):
+        w = synth.WORKLOADS[name]
+        xw = synth.make_prefill_inputs(w)
+        W = {n: to_dev(xw[n], dev) for n in ("q1", "q2", "k1", "k2", "v")}
+        wg = f32_dev(xw["gain"], dev)
+        wl_lam = f32_dev(xw["lam"], dev) if w.lam_range is not None else w.lam
+        w_out = torch.empty((w.B, w.T, w.H, w.d_v), dtype=torch.bfloat16, device=dev)
+
+        def run(W=W, wg=wg, wl_lam=wl_lam, w_out=w_out, w=w):
+            da.diffattn_fwd_prefill(W["q1"], W["q2"], W["k1"], W["k2"], W["v"], wl_lam, wg, eps=w.eps,
+                                    scale=w.scale, out=w_out)
+
+        us, us_min = _time_calls(torch, np, run, 60, 40)
+        assert bool(torch.isfinite(w_out.float()).all())
+        flop = w.causal_pairs * FLOP_PER_PAIR
+        big[key] = {"workload": name, "B": w.B, "T": w.T, "H": w.H, "us_mean": round(us, 2),
+                    "us_min": round(us_min, 2), "tflops": round(flop / us / 1e6, 2),
+                    "frac_mfma_peak": round(flop / us / 1e6 / MFMA_PEAK_TFLOPS, 4),
+                    "kernel": "prefill_kernel<1,0>"}
+        del W, w_out
+
     p_us, p_min = _time_calls(torch, np, prefill, warmup, iters)
     d_us, d_min = _time_calls(torch, np, decode, warmup, iters)
     r_us, r_min = _time_calls(torch, np, prefill_rope, warmup, iters)
@@ -262,8 +322,10 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     r_flop = rw.causal_pairs * FLOP_PER_PAIR
     assert bool(torch.isfinite(p_out.float()).all()) and bool(torch.isfinite(d_out.float()).all())
     p_flop = pw.causal_pairs * FLOP_PER_PAIR
+    p_bytes = swa_prefill_bytes(pw)
     d_bytes = decode_bytes(dw)
-    return {
+    rec = dict(big)
+    rec.update({
         "grouped": {"workload": "B=1 T=4096 16 heads (12 signal, 4 noise, g=3), token-wise lambda, gate",
                     "us_mean": round(g_us, 2), "us_min": round(g_min, 2),
                     "tflops": round(g_flop / g_us / 1e6, 2),
@@ -275,25 +337,30 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
                          "us_mean": round(r_us, 2), "us_min": round(r_min, 2),
                          "tflops": round(r_flop / r_us / 1e6, 2),
                          "frac_mfma_peak": round(r_flop / r_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},
-        "prefill": {"workload": SWA_PREFILL_WL, "window": pw.window, "us_mean": round(p_us, 2),
-                    "us_min": round(p_min, 2), "visible_pairs": pw.causal_pairs,
-                    "tflops": round(p_flop / p_us / 1e6, 2),
-                    "frac_mfma_peak": round(p_flop / p_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},
-        "decode": {"workload": SWA_DECODE_WL, "window": dw.window, "us_mean": round(d_us, 2),
-                   "us_min": round(d_min, 2), "bytes": d_bytes, "gbs": round(d_bytes / d_us / 1e3, 1),
-                   "frac_hbm_peak": round(d_bytes / d_us / 1e3 / HBM_PEAK_GBS, 4), "splits": dw.num_splits},
-    }
+        # 128-key windows: 96 FLOP per algorithmic byte, below the chip's
+        # ridge (about 315), so the bound is HBM
+        "swa_prefill": {"workload": SWA_PREFILL_WL, "window": pw.window, "bound": "hbm",
+                        "us_mean": round(p_us, 2), "us_min": round(p_min, 2), "visible_pairs": pw.causal_pairs,
+                        "bytes": p_bytes, "gbs": round(p_bytes / p_us / 1e3, 1),
+                        "frac_hbm_peak": round(p_bytes / p_us / 1e3 / HBM_PEAK_GBS, 4),
+                        "tflops": round(p_flop / p_us / 1e6, 2)},
+        "swa_decode": {"workload": SWA_DECODE_WL, "window": dw.window, "bound": "hbm", "us_mean": round(d_us, 2),
+                       "us_min": round(d_min, 2), "bytes": d_bytes, "gbs": round(d_bytes / d_us / 1e3, 1),
+                       "frac_hbm_peak": round(d_bytes / d_us / 1e3 / HBM_PEAK_GBS, 4), "splits": dw.num_splits},
+    })
+    return rec
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle", type=float, default=2.0,
+                    help="seconds of back-to-back steps before the counted warm-up (clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--no-variants", action="store_true", help="skip the sliding-window and RoPE timings")
-    ap.add_argument("--no-clocks", action="store_true", help="skip the rocm-smi clock query (for profiler runs)")
+    ap.add_argument("--no-variants", action="store_true", help="skip the variant timings")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -340,10 +407,15 @@ def main() -> int:
         da.diffattn_fwd_decode(D["q1"], D["q2"], D["k1"], D["k2"], D["v"], dw.lam, D["gain"], eps=dw.eps,
                                scale=dw.scale, num_splits=dw.num_splits, workspace=ws, out=d_out)
 
-    for _ in range(args.warmup):
+    def step():
         prefill()
         decode()
+
+    settle_s, settle_steps = settle(torch, step, args.settle)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
+    sclk_before = read_sclk_mhz()
 
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -357,6 +429,7 @@ def main() -> int:
         ev[k][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk_after = read_sclk_mhz()
     p_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)])
     d_ms = np.array([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)])
     step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
@@ -397,9 +470,12 @@ def main() -> int:
                    "bytes": d_bytes, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                    "splits": dw.num_splits, "traffic": read_traffic(DECODE_PMC, DECODE_SOURCES)},
         "variants": var,
+        "settle_s": round(settle_s, 3),
+        "settle_steps": settle_steps,
+        "sclk_mhz": {"before_timed": sclk_before, "after_timed": sclk_after},
         "wall_s_timed": round(wall, 3),
         "kernel_source_sha256_16": kernel_source_digest(),
-        "env": gpu_env(torch, clocks=not args.no_clocks),
+        "env": gpu_env(torch),
     }
     if not args.no_cpu_baseline:
         # the benchmarked prefill once more (outside the timed region) with

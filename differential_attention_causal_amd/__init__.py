@@ -11,6 +11,7 @@ this package raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -133,6 +134,14 @@ def _strides4(t: torch.Tensor) -> _Strides:
     return _Strides(t.stride(0), t.stride(1), t.stride(2))
 
 
+def _alloc_on(stream):
+    """Context in which torch allocations belong to `stream` (when given): the
+    caching allocator then reuses a temporary workspace, freed when the call
+    returns, only for later work on that same stream, which the kernels
+    enqueued on it precede."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -180,7 +189,8 @@ def diffattn_fwd_prefill_ex(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, o
                 raise ValueError("workspace must be a uint8 device tensor of at least %d bytes" % need)
             ws = workspace
         else:
-            ws = torch.empty(need, dtype=torch.uint8, device=q1.device)
+            with _alloc_on(stream):
+                ws = torch.empty(need, dtype=torch.uint8, device=q1.device)
     return _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream, ws=ws)
 
 
@@ -222,7 +232,8 @@ def _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pr
     if gain.dtype != torch.float32 or tuple(gain.shape) != (H, d_v) or not gain.is_contiguous():
         raise ValueError("gain must be a contiguous fp32 [H, d_v] tensor")
     if out is None:
-        out = torch.empty((B, T, H, d_v), dtype=out_dtype, device=q1.device)
+        with _alloc_on(stream):
+            out = torch.empty((B, T, H, d_v), dtype=out_dtype, device=q1.device)
     if tuple(out.shape) != (B, T, H, d_v) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B, T, H, d_v] tensor")
     if o_pre is not None and (o_pre.dtype != torch.float32 or tuple(o_pre.shape) != (B, T, H, d_v)
@@ -291,9 +302,11 @@ def _decode(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens, num_splits, 
         raise ValueError("seqlens must be an int32 [B] device tensor")
     need = diffattn_decode_workspace_bytes(B, H, d_v, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+        with _alloc_on(stream):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
     if out is None:
-        out = torch.empty((B, H, d_v), dtype=out_dtype, device=q1.device)
+        with _alloc_on(stream):
+            out = torch.empty((B, H, d_v), dtype=out_dtype, device=q1.device)
     if tuple(out.shape) != (B, H, d_v) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B, H, d_v] tensor")
     if o_pre is not None and (o_pre.dtype != torch.float32 or tuple(o_pre.shape) != (B, H, d_v)
@@ -319,7 +332,8 @@ def diffattn_rope_apply(x, mode, theta, pos0=0, pos_start=None, out=None, stream
         raise ValueError("x must be a bf16 [B, T, H, d] device tensor")
     B, T, H, d = x.shape
     if out is None:
-        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+        with _alloc_on(stream):
+            out = torch.empty_like(x, memory_format=torch.contiguous_format)
     if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, T, H, d):
         raise ValueError("out must be a bf16 tensor shaped like x")
     if pos_start is not None and (pos_start.dtype != torch.int32 or tuple(pos_start.shape) != (B,)
@@ -338,9 +352,10 @@ def diffattn_fwd_prefill_train(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0
     (out, o1, o2, lse) with o1, o2 fp32 [B, T, H, 128] (each map's normalised
     output) and lse fp32 [B, T, H, 2] (base-2 log-sum-exp per map)."""
     B, T, H, _ = q1.shape
-    o1 = torch.empty((B, T, H, D_V), dtype=torch.float32, device=q1.device)
-    o2 = torch.empty_like(o1)
-    lse = torch.empty((B, T, H, 2), dtype=torch.float32, device=q1.device)
+    with _alloc_on(stream):
+        o1 = torch.empty((B, T, H, D_V), dtype=torch.float32, device=q1.device)
+        o2 = torch.empty_like(o1)
+        lse = torch.empty((B, T, H, 2), dtype=torch.float32, device=q1.device)
     out = _prefill(None, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream,
                    train=(o1, o2, lse))
     return out, o1, o2, lse
@@ -371,13 +386,15 @@ def diffattn_bwd_prefill(q1, q2, k1, k2, v, lam, gain, o1, o2, lse, dy, eps=1e-5
         raise ValueError("gain must be a contiguous fp32 [H, d_v] tensor")
     if grads is None:
         f = dict(dtype=torch.float32, device=q1.device)
-        grads = {"dq1": torch.empty((B, T, H, d_qk), **f), "dq2": torch.empty((B, T, H, d_qk), **f),
-                 "dk1": torch.empty((B, T, H, d_qk), **f), "dk2": torch.empty((B, T, H, d_qk), **f),
-                 "dv": torch.empty((B, T, H, d_v), **f), "dlam": torch.empty((H,), **f),
-                 "dgain": torch.empty((H, d_v), **f)}
+        with _alloc_on(stream):
+            grads = {"dq1": torch.empty((B, T, H, d_qk), **f), "dq2": torch.empty((B, T, H, d_qk), **f),
+                     "dk1": torch.empty((B, T, H, d_qk), **f), "dk2": torch.empty((B, T, H, d_qk), **f),
+                     "dv": torch.empty((B, T, H, d_v), **f), "dlam": torch.empty((H,), **f),
+                     "dgain": torch.empty((H, d_v), **f)}
     need = diffattn_bwd_workspace_bytes(B, T, H, d_v)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q1.device)
+        with _alloc_on(stream):
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q1.device)
     lam_v, lam_t = _lambda_args(lam, H, q1.device)
     st = (_Strides * 5)(*[_strides4(t) for t in (q1, q2, k1, k2, v)])
     g = grads
@@ -414,10 +431,12 @@ def diffattn_fwd_grouped(q, k, v, group, lambda_t, gate=None, scale=0.0, out=Non
                              or not gate.is_contiguous()):
         raise ValueError("gate must be a contiguous bf16 [B, T, n_S, d_v] tensor")
     if out is None:
-        out = torch.empty((B, T, n_S, d_v), dtype=out_dtype, device=q.device)
+        with _alloc_on(stream):
+            out = torch.empty((B, T, n_S, d_v), dtype=out_dtype, device=q.device)
     need = diffattn_grouped_workspace_bytes(B, T, n_heads, group, d_v)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        with _alloc_on(stream):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     st = (_Strides * 3)(*[_strides4(t) for t in (q, k, v)])
     rc = _lib.diffattn_fwd_grouped(_ptr(q), _ptr(k), _ptr(v), st, B, T, n_heads, int(group), d_qk, d_v,
                                    _ptr(lambda_t), _ptr(gate), float(scale), _ptr(out), _out_code(out.dtype),

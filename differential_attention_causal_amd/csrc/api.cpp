@@ -3,6 +3,7 @@
 // are documented in include/diffattn.h.
 #include "diffattn.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -21,8 +22,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Strides: non-negative multiples of 8 elements (16-byte rows), and a token
+// stride below kMaxTokenStride elements, so that the per-lane byte offsets of a
+// 32-row tile fit the 32-bit offsets of buffer loads.
+constexpr int64_t kMaxTokenStride = int64_t(1) << 25;
+
 bool strides_ok(const diffattn_strides& s) {
-  return s.b >= 0 && s.t >= 0 && s.h >= 0 && s.b % 8 == 0 && s.t % 8 == 0 && s.h % 8 == 0;
+  return s.b >= 0 && s.t >= 0 && s.h >= 0 && s.b % 8 == 0 && s.t % 8 == 0 && s.h % 8 == 0 &&
+         s.t < kMaxTokenStride;
 }
 
 Strides to_internal(const diffattn_strides& s) { return Strides{s.b, s.t, s.h}; }
@@ -71,6 +78,26 @@ float score_factor(float scale) {
 }
 
 }  // namespace
+
+namespace diffattn {
+
+int device_cu_count() {
+  // One slot per device ordinal; a racing first query stores the same value.
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace diffattn
 
 extern "C" {
 

@@ -701,20 +701,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 }  // namespace
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)a.nchunks, (unsigned)a.H), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_kernel(bwd_pre_kernel, dim3((unsigned)a.nchunks, (unsigned)a.H), dim3(256), stream, a);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)a.H), dim3(192), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_kernel(bwd_reduce_kernel, dim3((unsigned)a.H), dim3(192), stream, a)) != hipSuccess) return e;
   const int64_t chunks = (int64_t)a.B * a.T * a.H * 16;  // the most of any tensor (V)
-  hipLaunchKernelGGL(bwd_cast_kernel, dim3((unsigned)((chunks + 255) / 256), 5), dim3(256), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = launch_kernel(bwd_cast_kernel, dim3((unsigned)((chunks + 255) / 256), 5), dim3(256), stream, a);
+  if (e != hipSuccess) return e;
   const int64_t nqb = (a.T + kRows - 1) / kRows;
   const int64_t blocks = nqb * a.B * a.H;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((nqb + 1) / 2 * a.B * a.H)), dim3(512), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)blocks), dim3(512), 0, stream, a);
-  return hipGetLastError();
+  e = launch_kernel(bwd_dq_kernel, dim3((unsigned)((nqb + 1) / 2 * a.B * a.H)), dim3(512), stream, a);
+  if (e != hipSuccess) return e;
+  return launch_kernel(bwd_dkv_kernel, dim3((unsigned)blocks), dim3(512), stream, a);
 }
 
 }  // namespace diffattn

@@ -359,11 +359,9 @@ __global__ void __launch_bounds__(kDv) decode_merge_kernel(DecodeArgs a) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int64_t bh = (int64_t)a.B * a.H;
-  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)(bh * a.splits)), dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_kernel(decode_split_kernel, dim3((unsigned)(bh * a.splits)), dim3(kThreads), stream, a);
   if (e != hipSuccess || a.splits == 1) return e;  // one split finishes in the split kernel
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)bh), dim3(kDv), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(decode_merge_kernel, dim3((unsigned)bh), dim3(kDv), stream, a);
 }
 
 }  // namespace diffattn

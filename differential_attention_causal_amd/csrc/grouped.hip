@@ -364,27 +364,23 @@ __global__ void __launch_bounds__(256) grouped_combine_kernel(GroupedArgs a) {
 
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)((a.T + kBM - 1) / kBM) * a.B * a.nH;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int cus = device_cu_count();
   const bool split = grid <= 2 * (int64_t)cus;
   // The ping-pong form addresses a head's key rows from one buffer base with
   // 32-bit offsets (up to about T + 192 rows).
   const int64_t row_max = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
+  hipError_t e;
   if (split && (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31)) {
     const int64_t nqb = (a.T + kBM - 1) / kBM;
-    hipLaunchKernelGGL(grouped_pp_kernel, dim3((unsigned)((nqb + 1) / 2 * a.B * a.nH)), dim3(512), 0, stream, a);
+    e = launch_kernel(grouped_pp_kernel, dim3((unsigned)((nqb + 1) / 2 * a.B * a.nH)), dim3(512), stream, a);
   } else if (split) {
-    hipLaunchKernelGGL(grouped_attn_kernel<2>, dim3((unsigned)grid), dim3(512), 0, stream, a);
+    e = launch_kernel(grouped_attn_kernel<2>, dim3((unsigned)grid), dim3(512), stream, a);
   } else {
-    hipLaunchKernelGGL(grouped_attn_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    e = launch_kernel(grouped_attn_kernel<1>, dim3((unsigned)grid), dim3(256), stream, a);
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.B * a.T * a.nS;
-  hipLaunchKernelGGL(grouped_combine_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(grouped_combine_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), stream, a);
 }
 
 }  // namespace diffattn

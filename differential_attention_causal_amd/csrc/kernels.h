@@ -168,6 +168,24 @@ constexpr int kBwdRowsPerChunk = 64;
 void rope_phases(float theta, RopeArgs& r);
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Compute units of the current device, queried once per device and cached.
+int device_cu_count();
+
+template <class T>
+struct NoDeduce {
+  using type = T;
+};
+
+// Enqueues kernel f on `stream` with one argument struct and returns the
+// status of this launch alone (hipLaunchKernel reports its own result, so a
+// sticky error left by an earlier, unrelated call is not taken for this one).
+template <class A>
+inline hipError_t launch_kernel(void (*f)(A), dim3 grid, dim3 block, hipStream_t stream,
+                                typename NoDeduce<A>::type arg) {
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(f), grid, block, args, 0, stream);
+}
 // The sliding-window streaming kernel (window.hip): whether it takes a's
 // configuration (window of at most 129 keys, no rotary embedding, no training
 // outputs), and its launch.

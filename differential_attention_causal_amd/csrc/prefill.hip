@@ -442,10 +442,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   // splitting each workgroup's key range over two wave groups halves that
   // tail.  Larger grids balance by themselves in longest-first order and run
   // better as independent 4-wave workgroups.
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int cus = device_cu_count();
   const bool split = grid <= 2 * (int64_t)cus;
   const int64_t row_max = std::max(std::max(a.sk1.t, a.sk2.t), a.sv.t);
   // Keys already rotated (fp16 copies): they are staged like plain keys, and
@@ -460,32 +457,23 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (prefill_window_kernel_fits(a)) return launch_prefill_window(a, stream);
   if (pingpong) {
     const dim3 gp((unsigned)((int64_t)((nqb + 1) / 2) * a.B * a.H));
-    if (prerot)
-      hipLaunchKernelGGL((prefill_pp_kernel<false, true>), gp, dim3(512), 0, stream, a);
-    else if (a.o1n != nullptr)
-      hipLaunchKernelGGL((prefill_pp_kernel<true, false>), gp, dim3(512), 0, stream, a);
-    else
-      hipLaunchKernelGGL((prefill_pp_kernel<false, false>), gp, dim3(512), 0, stream, a);
-    return hipGetLastError();
+    if (prerot) return launch_kernel(prefill_pp_kernel<false, true>, gp, dim3(512), stream, a);
+    if (a.o1n != nullptr) return launch_kernel(prefill_pp_kernel<true, false>, gp, dim3(512), stream, a);
+    return launch_kernel(prefill_pp_kernel<false, false>, gp, dim3(512), stream, a);
   }
   const dim3 g((unsigned)grid), b1(64 * kGroupWaves), b2(64 * kGroupWaves * 2);
-  if (prerot) {
-    if (split)
-      hipLaunchKernelGGL((prefill_kernel<2, 3>), g, b2, 0, stream, a);
-    else
-      hipLaunchKernelGGL((prefill_kernel<1, 3>), g, b1, 0, stream, a);
-    return hipGetLastError();
-  }
+  if (prerot)
+    return split ? launch_kernel(prefill_kernel<2, 3>, g, b2, stream, a)
+                 : launch_kernel(prefill_kernel<1, 3>, g, b1, stream, a);
   switch (a.rope.mode * 2 + (split ? 1 : 0)) {
-    case 0: hipLaunchKernelGGL((prefill_kernel<1, 0>), g, b1, 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((prefill_kernel<2, 0>), g, b2, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<1, 1>), g, b1, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((prefill_kernel<2, 1>), g, b2, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<1, 2>), g, b1, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL((prefill_kernel<2, 2>), g, b2, 0, stream, a); break;
+    case 0: return launch_kernel(prefill_kernel<1, 0>, g, b1, stream, a);
+    case 1: return launch_kernel(prefill_kernel<2, 0>, g, b2, stream, a);
+    case 2: return launch_kernel(prefill_kernel<1, 1>, g, b1, stream, a);
+    case 3: return launch_kernel(prefill_kernel<2, 1>, g, b2, stream, a);
+    case 4: return launch_kernel(prefill_kernel<1, 2>, g, b1, stream, a);
+    case 5: return launch_kernel(prefill_kernel<2, 2>, g, b2, stream, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace diffattn

@@ -74,15 +74,13 @@ __global__ void __launch_bounds__(kThreads) rope_keys_kernel(RopeKeysArgs a) {
 hipError_t launch_rope_keys(const RopeKeysArgs& a, hipStream_t stream) {
   const int64_t nvec = (int64_t)a.B * a.T * a.H;
   const int64_t blocks = (nvec + kThreads / 8 - 1) / (kThreads / 8);
-  hipLaunchKernelGGL(rope_keys_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(rope_keys_kernel, dim3((unsigned)blocks), dim3(kThreads), stream, a);
 }
 
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t stream) {
   const int64_t nvec = (int64_t)a.B * a.T * a.H;
   const int64_t blocks = (nvec + kThreads / 8 - 1) / (kThreads / 8);
-  hipLaunchKernelGGL(rope_apply_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(rope_apply_kernel, dim3((unsigned)blocks), dim3(kThreads), stream, a);
 }
 
 }  // namespace diffattn

@@ -3,6 +3,7 @@
 // bounded buffer resources over the rows of one (b, h).
 #pragma once
 
+#include "extent.h"
 #include "kernels.h"
 
 namespace diffattn {
@@ -42,7 +43,7 @@ __device__ __forceinline__ int kSwz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t stride, int k0, int kend,
                                                              int row) {
   const uint16_t* p = base + (int64_t)k0 * stride;
-  const int nrec = kend > k0 ? (int)(((int64_t)(kend - k0 - 1) * stride + row) * 2) : 0;
+  const int nrec = (int)rows_extent_bytes(stride, k0, kend, row);
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, nrec, 0x00020000);
 }
 

@@ -214,8 +214,7 @@ hipError_t launch_prefill_window(const PrefillArgs& a, hipStream_t stream) {
   if (!prefill_window_kernel_fits(a)) return hipErrorInvalidValue;
   const int nqb = (a.T + kBM - 1) / kBM;
   const int64_t chunks = (nqb + kSwBlocks - 1) / kSwBlocks;
-  hipLaunchKernelGGL(prefill_swa_kernel, dim3((unsigned)(chunks * a.B * a.H)), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(prefill_swa_kernel, dim3((unsigned)(chunks * a.B * a.H)), dim3(256), stream, a);
 }
 
 }  // namespace diffattn

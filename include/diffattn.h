@@ -29,7 +29,9 @@
  *   - Layout [B, T, H, D] with element strides given per tensor by
  *     diffattn_strides {b, t, h}; the innermost dimension D is contiguous.  A
  *     NULL strides pointer means C-contiguous [B, T, H, D].  Base pointers
- *     must be 16-byte aligned and every stride a multiple of 8 elements.
+ *     must be 16-byte aligned, every stride a non-negative multiple of 8
+ *     elements, and the t stride below 2^25 elements (DIFFATTN_ERR_LAYOUT
+ *     otherwise).
  *   - Outputs are C-contiguous.  out: bf16 (round to nearest even) or fp32,
  *     chosen by out_dtype.  o_pre: optional fp32 copy of o before the norm
  *     (NULL to skip).
@@ -38,8 +40,10 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
  *     returns immediately.  Arguments are validated on the host before any
  *     HIP call: on an invalid argument the call returns a nonzero status and
- *     touches no memory.  A failed launch returns DIFFATTN_ERR_HIP.  Faults
- *     inside kernels surface at the caller's next synchronisation.
+ *     touches no memory.  DIFFATTN_ERR_HIP reports the failure of one of this
+ *     call's own launches (an error left by an earlier, unrelated HIP call is
+ *     neither reported nor cleared).  Faults inside kernels surface at the
+ *     caller's next synchronisation.
  *   - Results are bitwise reproducible run to run (no atomics).
  */
 #ifndef DIFFATTN_H

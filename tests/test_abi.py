@@ -261,3 +261,48 @@ def test_grouped_workspace_bytes():
     assert da.diffattn_grouped_workspace_bytes(2, 100, 8, 3, 128) == 2 * 100 * 8 * 128 * 4
     assert da.diffattn_grouped_workspace_bytes(2, 100, 8, 2, 128) == 0
     assert da.diffattn_grouped_workspace_bytes(2, 100, 8, 3, 64) == 0
+
+
+def test_prefill_rejects_token_stride_at_limit():
+    # a token stride of 2^25 elements would overflow the 32-bit per-lane
+    # offsets of a 32-row tile; one step below is accepted by validation
+    # (the call then stops at the invalid shape B=0 before any HIP call)
+    big = 1 << 25
+    st = (da._Strides * 5)(*[da._Strides(128 * big, big, 64) for _ in range(5)])
+    assert _prefill(st=st) == ELAYOUT
+    st = (da._Strides * 5)(*[da._Strides(128 * (big - 8), big - 8, 64) for _ in range(5)])
+    assert _prefill(st=st, B=0) == ESHAPE
+
+
+HARNESS = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include "extent.h"
+int main(int argc, char** argv) {
+  for (int i = 1; i + 3 < argc; i += 4) {
+    long long stride = atoll(argv[i]);
+    int k0 = atoi(argv[i + 1]), kend = atoi(argv[i + 2]), row = atoi(argv[i + 3]);
+    printf("%u\n", diffattn::rows_extent_bytes(stride, k0, kend, row));
+  }
+  return 0;
+}
+"""
+
+
+def test_rows_extent_bytes_host(tmp_path):
+    """The num_records of a buffer resource over rows k0 .. kend-1: exact below
+    2^32 bytes, clamped above (a fused 12288-byte-row layout at 400K tokens
+    spans 4.9 GB from the first row)."""
+    import subprocess
+
+    src = tmp_path / "h.cpp"
+    src.write_text(HARNESS)
+    exe = tmp_path / "h"
+    subprocess.check_call(["g++", "-O1", "-std=c++17", "-I",
+                           os.path.join(ROOT, "differential_attention_causal_amd", "csrc"), str(src), "-o", str(exe)])
+    cases = [(64, 0, 0, 64), (64, 5, 5, 64), (64, 0, 1, 64), (1024, 0, 128, 64), (6144, 0, 400000, 128),
+             (6144, 399968, 400000, 128), (6144, 0, 349000, 64), (1 << 20, 0, 4096, 128), (8, 3, 10, 8)]
+    out = subprocess.check_output([str(exe)] + [str(x) for c in cases for x in c], text=True).split()
+    for (stride, k0, kend, row), got in zip(cases, out):
+        exact = 0 if kend <= k0 else ((kend - k0 - 1) * stride + row) * 2
+        assert int(got) == min(exact, 0xFFFFFFFF), (stride, k0, kend, row, got)

@@ -2,11 +2,19 @@
 diffattn_bwd_prefill, through the C ABI) against the fp64 autograd oracle
 (oracle/backward.py).
 
-Bound: every gradient tensor within 5e-3 relative Frobenius error of the
-oracle's.  The kernels see exact bf16 inputs; the rounding they add is fp16
-(2^-11 relative) on dO, P, dS and the transposed operands, plus fp32
-accumulation, so the expected error is a few 1e-4; 5e-3 is the forward's
-pre-norm bound, kept for the gradients.  Every case prints its name first."""
+Bounds, for every gradient tensor g against the oracle's r:
+  - relative Frobenius error |g - r| / |r| <= 5e-3 (the forward's pre-norm
+    bound, kept for the gradients);
+  - element-wise max |g - r| <= 2e-2 * RMS(r).
+The kernels see exact bf16 inputs; the rounding they add is fp16 (2^-11
+relative) on dO, P, dS and the transposed operands, plus fp32 accumulation, so
+the per-element error is a few 1e-4 of RMS(r) (measured relative Frobenius
+errors are about 3e-4), and the largest of up to 4M such errors stays within
+about six of their standard deviations: 2e-2 leaves a margin of about ten.  A
+key or query tile whose contribution is lost or misplaced changes the elements
+it touches by at least about 1/sqrt(128) (one of at most 128 query tiles) of
+their size, which the element-wise bound catches where the norm would not.
+Every case prints its name first."""
 import numpy as np
 import pytest
 
@@ -24,6 +32,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import differential_attention_causal_amd as da  # noqa: E402
 
 REL = 5e-3
+ELEM = 2e-2
 NAMES = ("dq1", "dq2", "dk1", "dk2", "dv", "dlam", "dgain")
 
 
@@ -57,9 +66,15 @@ def _rel(a, b):
 def _check(x, g, what):
     ref = bwd.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"],
                        synth.bf16_bits_to_f32(x["dy"]).astype(np.float64))
-    rel = {n: _rel(g[n], ref[n]) for n in NAMES}
+    _compare(g, ref, what)
+
+
+def _compare(g, ref, what, names=NAMES):
+    rel = {n: _rel(g[n], ref[n]) for n in names}
+    elem = {n: float(np.abs(g[n] - ref[n]).max() / max(np.sqrt(np.mean(ref[n] ** 2)), 1e-30)) for n in names}
     _say("rel", {n: float("%.3g" % r) for n, r in rel.items()})
-    for n in NAMES:
+    _say("max/rms", {n: float("%.3g" % r) for n, r in elem.items()})
+    for n in names:
         assert np.isfinite(g[n]).all(), (what, n)
         if np.linalg.norm(ref[n]) <= 1e-9 * np.sqrt(ref[n].size):
             # the gradient vanishes (a softmax over one key has none): only
@@ -67,6 +82,7 @@ def _check(x, g, what):
             assert np.abs(g[n]).max() <= 1e-4, (what, n, np.abs(g[n]).max())
             continue
         assert rel[n] <= REL, (what, n, rel[n])
+        assert elem[n] <= ELEM, (what, n, elem[n])
 
 
 # ragged sizes over several 32-row tiles and 128-row workgroups
@@ -137,3 +153,39 @@ def test_training_forward_large_grid():
     o = (o1 - lam[None, None, :, None] * o2)[idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy()
     assert _rel(o, o_ref) < 5e-3
     assert bool(torch.isfinite(lse).all())
+
+
+def _heads_subset(x, bs, hs):
+    """The inputs of batch rows bs and heads hs alone (heads and batch rows are
+    independent, so the oracle on the subset gives those rows' gradients)."""
+    sub = {}
+    for n in ("q1", "q2", "k1", "k2", "v", "dy"):
+        sub[n] = np.ascontiguousarray(x[n][bs][:, :, hs])
+    sub["lam"] = np.ascontiguousarray(np.asarray(x["lam"])[hs])
+    sub["gain"] = np.ascontiguousarray(np.asarray(x["gain"])[hs])
+    sub["eps"], sub["scale"] = x["eps"], x["scale"]
+    return sub
+
+
+@pytest.mark.parametrize("B,seed", [(1, 41), (8, 42)])
+def test_backward_full_layer_h16(B, seed):
+    """The whole 16-head T=4096 layer (the benchmark's backward shape), and the
+    training-shaped batch B=8 with lambda per head, run at full size on the
+    GPU; the oracle checks batch rows {0, B-1} x heads {0, 15}.  dlam and dgain
+    sum over every batch row, so they are compared at B=1 only; at B=8 the
+    five attention gradients are."""
+    _say("backward full layer", B, 4096, 16)
+    x = _inputs(B, 4096, 16, seed=seed)
+    g, _ = _gpu(x)
+    bs = [0] if B == 1 else [0, B - 1]
+    hs = [0, 15]
+    sub = _heads_subset(x, bs, hs)
+    ref = bwd.backward(sub["q1"], sub["q2"], sub["k1"], sub["k2"], sub["v"], sub["lam"], sub["gain"], sub["eps"],
+                       sub["scale"], synth.bf16_bits_to_f32(sub["dy"]).astype(np.float64))
+    gs = {n: np.ascontiguousarray(g[n][bs][:, :, hs]) for n in ("dq1", "dq2", "dk1", "dk2", "dv")}
+    names = NAMES
+    if B == 1:
+        gs["dlam"], gs["dgain"] = g["dlam"][hs], g["dgain"][hs]
+    else:
+        names = ("dq1", "dq2", "dk1", "dk2", "dv")
+    _compare(gs, ref, ("full layer", B), names)

@@ -2,10 +2,18 @@
 output gate (picx.dev summary of the Motif 3 report, section 2.2) through the
 C ABI against the fp64 oracle.
 
-Bound: relative Frobenius error <= 5e-3 over the output (there is no
+Bounds: relative Frobenius error <= 5e-3 over the output (there is no
 GroupNorm, so the output plays the role of the forward's pre-norm output and
-takes its bound); the fp32-output mode is also held to 5e-3 element-wise
-relative to the output's RMS.  Every case prints its name first."""
+takes its bound), and element by element
+    |out - ref| <= 2e-2 * RMS_c(ref row)  [+ 2^-8 |ref| for bf16 output].
+Rows differ in scale by orders of magnitude (an early row averages few values,
+a late one thousands), so the element bound is relative to the row: the
+computation's error is a few 1e-4 of the row's RMS (fp16 P and V, fp32
+accumulation), and a lost or misplaced key tile moves the rows it touches by
+far more.  The bf16 output mode adds its own rounding, at most 2^-9 of the
+element (the gate makes a row's elements range widely, so this allowance is
+per element, with a factor of 2 for the error the value had before rounding).
+Every case prints its name first."""
 import numpy as np
 import pytest
 
@@ -22,6 +30,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import differential_attention_causal_amd as da  # noqa: E402
 
 REL = 5e-3
+ELEM = 2e-2
 
 
 def _say(*a):
@@ -56,35 +65,39 @@ def _rel(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
+def _elem(a, b, bf16):
+    """Largest over elements of |a - b| / allowance, with the allowance
+    ELEM * RMS of b's row (the last axis) [+ 2^-8 |b| for bf16 output]."""
+    rms = np.sqrt(np.mean(b ** 2, axis=-1, keepdims=True))
+    allow = ELEM * rms + (2.0 ** -8 * np.abs(b) if bf16 else 0.0)
+    return float((np.abs(a - b) / np.maximum(allow, 1e-30)).max())
+
+
+def _assert_close(got, ref, what, bf16=False):
+    rel, elem = _rel(got, ref), _elem(got, ref, bf16)
+    _say(what, "rel", rel, "err/allowance", elem)
+    assert rel <= REL, (what, rel)
+    assert elem <= 1.0, (what, elem)
+
+
 @pytest.mark.parametrize("B,T,n_H,g,gate", [(1, 1, 2, 1, True), (1, 77, 2, 1, False), (2, 130, 4, 1, True),
                                             (1, 300, 4, 3, True), (2, 515, 8, 3, True), (1, 257, 6, 2, False)])
 def test_grouped_all_rows(B, T, n_H, g, gate):
     _say("grouped", B, T, n_H, g, gate)
     x = _inputs(B, T, n_H, g, seed=600 + T + g, gate=gate)
     ref = _ref(x, g)
-    out = _gpu(x, g)
-    rel = _rel(out, ref)
-    _say("rel fp32 out", rel)
-    assert rel <= REL
-    outb = _gpu(x, g, torch.bfloat16)
-    relb = _rel(outb, ref)
-    _say("rel bf16 out", relb)
-    assert relb <= REL
+    _assert_close(_gpu(x, g), ref, "fp32 out")
+    _assert_close(_gpu(x, g, torch.bfloat16), ref, "bf16 out", bf16=True)
 
 
-def test_grouped_motif3_shape_sampled():
-    # 16 heads, g = 3 (4 noise, 12 signal heads), T = 4096
-    _say("grouped B=1 T=4096 n_H=16 g=3")
+def test_grouped_motif3_shape_every_row():
+    # 16 heads, g = 3 (4 noise, 12 signal heads), T = 4096: the benchmark's
+    # grouped shape, every output row
+    _say("grouped B=1 T=4096 n_H=16 g=3, every row")
     x = _inputs(1, 4096, 16, 3, seed=31)
-    out = _gpu(x, 3)
-    rng = np.random.default_rng(3)
-    rows = sorted({(0, int(i), int(s)) for i, s in zip(rng.integers(0, 4096, 60), rng.integers(0, 12, 60))}
-                  | {(0, 0, 0), (0, 4095, 11), (0, 127, 3), (0, 128, 4)})
-    ref = _ref(x, 3, rows=rows)
-    got = np.stack([out[b, i, s] for b, i, s in rows])
-    rel = _rel(got, ref)
-    _say("rel", rel)
-    assert rel <= REL
+    ref = _ref(x, 3)
+    _assert_close(_gpu(x, 3), ref, "fp32 out")
+    _assert_close(_gpu(x, 3, torch.bfloat16), ref, "bf16 out", bf16=True)
 
 
 def test_grouped_large_grid_sampled():
@@ -99,9 +112,7 @@ def test_grouped_large_grid_sampled():
                   | {(0, 0, 0), (3, 1099, 11), (1, 1023, 5), (2, 1024, 6)})
     ref = _ref(x, 3, rows=rows)
     got = np.stack([out[b, i, s] for b, i, s in rows])
-    rel = _rel(got, ref)
-    _say("rel", rel)
-    assert rel <= REL
+    _assert_close(got, ref, "sampled")
 
 
 def test_grouped_structure():
