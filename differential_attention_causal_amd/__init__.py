@@ -25,6 +25,7 @@ __all__ = [
     "diffattn_prefill_workspace_bytes",
     "diffattn_fwd_decode",
     "diffattn_fwd_decode_ex",
+    "diffattn_fwd_decode_noalloc",
     "diffattn_rope_apply",
     "diffattn_fwd_prefill_train",
     "diffattn_bwd_workspace_bytes",
@@ -85,6 +86,10 @@ _lib.diffattn_fwd_prefill_ws.argtypes = ([ctypes.POINTER(_Options)] + _lib.diffa
                                          + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
 _lib.diffattn_fwd_decode_ex.restype = _I
 _lib.diffattn_fwd_decode_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffattn_fwd_decode.argtypes
+_lib.diffattn_fwd_decode_noalloc.restype = _I
+_lib.diffattn_fwd_decode_noalloc.argtypes = ([ctypes.POINTER(_Options)] + _lib.diffattn_fwd_decode.argtypes[:18]
+                                             + _lib.diffattn_fwd_decode.argtypes[20:])
+DECODE_SCRATCH_BYTES = 16 << 20
 _lib.diffattn_rope_apply.restype = _I
 _lib.diffattn_rope_apply.argtypes = [_P, ctypes.POINTER(_Strides), _P, ctypes.POINTER(_Strides), _I, _I, _I, _I,
                                      _I, ctypes.c_float, _I, _P, _P]
@@ -275,8 +280,23 @@ def diffattn_fwd_decode_ex(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, se
                    out_dtype, o_pre, stream)
 
 
+def diffattn_fwd_decode_noalloc(q1, q2, k1, k2, v, lam, gain, out, eps=1e-5, scale=0.0, seqlens=None,
+                                num_splits=0, o_pre=None, stream=None, window=0, kv_ring=False, rope=ROPE_NONE,
+                                rope_theta=0.0, rope_pos0=0):
+    """diffattn_fwd_decode_ex with no workspace and no allocation (for callers
+    that cannot allocate): the split partials live in the library's per-device
+    buffer of DECODE_SCRATCH_BYTES; `out` (and `o_pre`) must be given.  Calls
+    that overlap on one device race on that buffer."""
+    if out is None:
+        raise ValueError("out must be given: this entry point allocates nothing")
+    opt = _Options(window=int(window), kv_ring=int(bool(kv_ring)), rope=int(rope), rope_pos0=int(rope_pos0),
+                   rope_theta=float(rope_theta))
+    return _decode(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens, num_splits, None, out, out.dtype,
+                   o_pre, stream, noalloc=True)
+
+
 def _decode(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens, num_splits, workspace, out, out_dtype,
-            o_pre, stream):
+            o_pre, stream, noalloc=False):
     """Single-query decode against a KV cache, split over cache positions.
 
     q1, q2: bf16 [B, H, 64] contiguous; k1, k2: bf16 cache [B, L, H, 64];
@@ -301,7 +321,7 @@ def _decode(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens, num_splits, 
                                 or not seqlens.is_cuda):
         raise ValueError("seqlens must be an int32 [B] device tensor")
     need = diffattn_decode_workspace_bytes(B, H, d_v, num_splits)
-    if workspace is None:
+    if workspace is None and not noalloc:
         with _alloc_on(stream):
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
     if out is None:
@@ -314,10 +334,14 @@ def _decode(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, seqlens, num_splits, 
         raise ValueError("o_pre must be a contiguous fp32 [B, H, d_v] tensor")
     lam_v, lam_t = _lambda_args(lam, H, q1.device)
     st = (_Strides * 3)(*[_strides4(t) for t in (k1, k2, v)])
-    args = (_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, _ptr(seqlens), B, L, H, d_qk, d_v, lam_v,
-            _ptr(lam_t), _ptr(gain), float(eps), float(scale), int(num_splits), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), _ptr(out), _out_code(out.dtype), _ptr(o_pre),
-            _stream(stream))
+    head = (_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, _ptr(seqlens), B, L, H, d_qk, d_v, lam_v,
+            _ptr(lam_t), _ptr(gain), float(eps), float(scale), int(num_splits))
+    tail = (_ptr(out), _out_code(out.dtype), _ptr(o_pre), _stream(stream))
+    if noalloc:
+        rc = _lib.diffattn_fwd_decode_noalloc(ctypes.byref(opt), *head, *tail)
+        _check(rc)
+        return out
+    args = head + (_ptr(workspace), workspace.numel() * workspace.element_size()) + tail
     rc = _lib.diffattn_fwd_decode(*args) if opt is None else _lib.diffattn_fwd_decode_ex(ctypes.byref(opt), *args)
     _check(rc)
     return out

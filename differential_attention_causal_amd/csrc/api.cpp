@@ -101,7 +101,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 106; }
+int diffattn_abi_version(void) { return 107; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -372,12 +372,18 @@ size_t diffattn_decode_workspace_bytes(int B, int H, int d_v, int num_splits) {
   return (size_t)B * H * num_splits * 2 * diffattn::kPartialStride * sizeof(float);
 }
 
-int diffattn_fwd_decode_ex(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,
-                           const void* k2, const void* v, const diffattn_strides* cache_strides,
-                           const int32_t* seqlens, int B, int L, int H, int d_qk, int d_v, float lambda,
-                           const float* lambda_per_head, const float* gain, float gn_eps, float scale,
-                           int num_splits, void* workspace, size_t workspace_bytes, void* out, int out_dtype,
-                           float* o_pre, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by diffattn_fwd_decode_ex (the caller's workspace) and
+// diffattn_fwd_decode_noalloc (scratch: the library's per-device array, whose
+// address is looked up only once every argument has passed validation).
+int decode_impl(const diffattn_options* opt, const void* q1, const void* q2, const void* k1, const void* k2,
+                const void* v, const diffattn_strides* cache_strides, const int32_t* seqlens, int B, int L, int H,
+                int d_qk, int d_v, float lambda, const float* lambda_per_head, const float* gain, float gn_eps,
+                float scale, int num_splits, void* workspace, size_t workspace_bytes, bool scratch, void* out,
+                int out_dtype, float* o_pre, void* stream) {
   if (!q1 || !q2 || !k1 || !k2 || !v || !gain || !out) return DIFFATTN_ERR_NULL;
   int rc = check_common(B, H, d_qk, d_v, lambda, gn_eps, scale, out_dtype);
   if (rc != DIFFATTN_OK) return rc;
@@ -393,12 +399,22 @@ int diffattn_fwd_decode_ex(const diffattn_options* opt, const void* q1, const vo
   for (const void* p : ptrs)
     if (!aligned16(p)) return DIFFATTN_ERR_LAYOUT;
   if (!aligned16(out) || !aligned16(gain) || (o_pre && !aligned16(o_pre))) return DIFFATTN_ERR_LAYOUT;
-  if (!workspace || !aligned16(workspace)) return DIFFATTN_ERR_WORKSPACE;
-  if (workspace_bytes < diffattn_decode_workspace_bytes(B, H, d_v, num_splits)) return DIFFATTN_ERR_WORKSPACE;
+  if (scratch) {
+    if (diffattn_decode_workspace_bytes(B, H, d_v, num_splits) > diffattn::kDecodeScratchBytes)
+      return DIFFATTN_ERR_WORKSPACE;
+  } else {
+    if (!workspace || !aligned16(workspace)) return DIFFATTN_ERR_WORKSPACE;
+    if (workspace_bytes < diffattn_decode_workspace_bytes(B, H, d_v, num_splits)) return DIFFATTN_ERR_WORKSPACE;
+  }
   diffattn_strides st[3];
   for (int i = 0; i < 3; ++i) {
     st[i] = cache_strides ? cache_strides[i] : contiguous(L, H, i == 2 ? d_v : d_qk);
     if (!strides_ok(st[i])) return DIFFATTN_ERR_LAYOUT;
+  }
+  if (scratch) {
+    float* p = nullptr;
+    if (diffattn::decode_scratch(&p) != hipSuccess) return DIFFATTN_ERR_HIP;
+    workspace = p;
   }
 
   diffattn::DecodeArgs a{};
@@ -430,6 +446,30 @@ int diffattn_fwd_decode_ex(const diffattn_options* opt, const void* q1, const vo
   a.o_pre = o_pre;
   if (diffattn::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
   return DIFFATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int diffattn_fwd_decode_ex(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,
+                           const void* k2, const void* v, const diffattn_strides* cache_strides,
+                           const int32_t* seqlens, int B, int L, int H, int d_qk, int d_v, float lambda,
+                           const float* lambda_per_head, const float* gain, float gn_eps, float scale,
+                           int num_splits, void* workspace, size_t workspace_bytes, void* out, int out_dtype,
+                           float* o_pre, void* stream) {
+  return decode_impl(opt, q1, q2, k1, k2, v, cache_strides, seqlens, B, L, H, d_qk, d_v, lambda, lambda_per_head,
+                     gain, gn_eps, scale, num_splits, workspace, workspace_bytes, false, out, out_dtype, o_pre,
+                     stream);
+}
+
+int diffattn_fwd_decode_noalloc(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,
+                                const void* k2, const void* v, const diffattn_strides* cache_strides,
+                                const int32_t* seqlens, int B, int L, int H, int d_qk, int d_v, float lambda,
+                                const float* lambda_per_head, const float* gain, float gn_eps, float scale,
+                                int num_splits, void* out, int out_dtype, float* o_pre, void* stream) {
+  return decode_impl(opt, q1, q2, k1, k2, v, cache_strides, seqlens, B, L, H, d_qk, d_v, lambda, lambda_per_head,
+                     gain, gn_eps, scale, num_splits, nullptr, 0, true, out, out_dtype, o_pre, stream);
 }
 
 int diffattn_fwd_decode(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,

@@ -16,10 +16,37 @@
 // lanes per 256-byte V row.  Scores are kept in base-2 units (c = scale log2 e).
 // Every cache byte is read exactly once, so the cache loads are non-temporal:
 // they stream past the caches instead of evicting other data.
+#include <mutex>
+
 #include "kernels.h"
 #include "rope.h"
 
 namespace diffattn {
+
+// The split partials of diffattn_fwd_decode_noalloc.  In host code `scratch`
+// names a host-side stand-in, not the device array: kernels and copies get
+// the address decode_scratch() looked up.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -192,6 +192,13 @@ inline hipError_t launch_kernel(void (*f)(A), dim3 grid, dim3 block, hipStream_t
 bool prefill_window_kernel_fits(const PrefillArgs& a);
 hipError_t launch_prefill_window(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Split partials of the no-allocation decode: a file-scope device array of
+// this many bytes (decode.hip), one per device, shared by every such call.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+// Device address of the current device's array, looked up with
+// hipGetSymbolAddress on the first call on that device and kept per device.
+hipError_t decode_scratch(float** ptr);
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t stream);
 hipError_t launch_rope_keys(const RopeKeysArgs& a, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);

@@ -234,6 +234,32 @@ DIFFATTN_API int diffattn_fwd_decode_ex(const diffattn_options* opt, const void*
                                         void* stream);
 
 /*
+ * diffattn_fwd_decode_ex without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  It makes no allocation of any
+ * kind.  The split partials live in a buffer the library holds on each device
+ * (a file-scope device array of DIFFATTN_DECODE_SCRATCH_BYTES, kept until the
+ * process ends), so B * H * num_splits * 2 * (d_v + 2) * 4 bytes (the value
+ * of diffattn_decode_workspace_bytes) must not exceed it:
+ * DIFFATTN_ERR_WORKSPACE otherwise, before any HIP call.  The first call on a
+ * device looks the buffer's address up there (DIFFATTN_ERR_HIP if that fails).
+ * Every call on one device shares that device's buffer and the buffer keeps
+ * the last call's contents; each call writes every record it reads, so none
+ * needs clearing.  Calls that overlap on one device (different streams, or
+ * threads with no ordering between them) race on the buffer and give wrong
+ * results; calls in order on one stream are safe.  Otherwise as
+ * diffattn_fwd_decode_ex, with the same arguments, results and errors.
+ */
+#define DIFFATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+DIFFATTN_API int diffattn_fwd_decode_noalloc(const diffattn_options* opt, const void* q1, const void* q2,
+                                             const void* k1, const void* k2, const void* v,
+                                             const diffattn_strides* cache_strides, const int32_t* seqlens,
+                                             int B, int L, int H, int d_qk, int d_v, float lambda,
+                                             const float* lambda_per_head, const float* gain, float gn_eps,
+                                             float scale, int num_splits, void* out, int out_dtype,
+                                             float* o_pre, void* stream);
+
+/*
  * Rotary embedding of a bf16 [B, T, H, 64] tensor, the same rotation the *_ex
  * entry points apply (see diffattn_options.rope), for writing rotated keys
  * into a decode cache.  Token t of batch row b sits at position

@@ -25,6 +25,7 @@ def test_header_symbols_exported():
     names = _declared()
     assert set(names) == {"diffattn_fwd_prefill", "diffattn_fwd_decode", "diffattn_decode_workspace_bytes",
                           "diffattn_fwd_prefill_ex", "diffattn_fwd_decode_ex", "diffattn_rope_apply",
+                          "diffattn_fwd_decode_noalloc",
                           "diffattn_fwd_prefill_train", "diffattn_bwd_workspace_bytes", "diffattn_bwd_prefill",
                           "diffattn_grouped_workspace_bytes", "diffattn_fwd_grouped",
                           "diffattn_prefill_workspace_bytes", "diffattn_fwd_prefill_ws",
@@ -32,7 +33,7 @@ def test_header_symbols_exported():
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 106
+    assert da.diffattn_abi_version() == 107
 
 
 def test_status_strings():
@@ -306,3 +307,26 @@ def test_rows_extent_bytes_host(tmp_path):
     for (stride, k0, kend, row), got in zip(cases, out):
         exact = 0 if kend <= k0 else ((kend - k0 - 1) * stride + row) * 2
         assert int(got) == min(exact, 0xFFFFFFFF), (stride, k0, kend, row, got)
+
+
+def _decode_noalloc(**kw):
+    args = dict(opt=ctypes.byref(da._Options()), q1=A, q2=A, k1=A, k2=A, v=A, st=None, sl=None, B=4, L=100, H=2,
+                dqk=64, dv=128, lam=0.8, lamh=None, gain=A, eps=1e-5, scale=0.0, splits=8, out=A, odt=0, opre=None,
+                stream=None)
+    args.update(kw)
+    return da._lib.diffattn_fwd_decode_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(q1=None), ENULL), (dict(out=None), ENULL), (dict(L=0), ESHAPE), (dict(dv=64), EUNSUP),
+    (dict(splits=65), EVALUE), (dict(k1=A + 6), ELAYOUT), (dict(lam=float("nan")), EVALUE),
+    # partials beyond the library's buffer: B*H*splits*2*130*4 > 16 MiB
+    (dict(B=64, H=16, splits=64), EWS), (dict(B=4096, H=1, splits=8), EWS),
+    # within the buffer, stopped by another invalid argument before any HIP call
+    (dict(B=64, H=16, splits=8, odt=5), EVALUE),
+])
+def test_decode_noalloc_rejects(kw, rc):
+    assert _decode_noalloc(**kw) == rc
+    if rc == EWS:
+        B, H, s = kw["B"], kw["H"], kw["splits"]
+        assert da.diffattn_decode_workspace_bytes(B, H, 128, s) > da.DECODE_SCRATCH_BYTES
