@@ -51,9 +51,9 @@ BATCH_WL = "batch_b8_t4096_h16"
 LONGCTX_WL = "longctx_b1_t16384_h16"
 ROPE_THETA = 500000.0        # Motif 2.6B's RoPE base
 CSRC = os.path.join(ROOT, "differential_attention_causal_amd", "csrc")
-PREFILL_PMC = os.path.join(ROOT, "profiles", "prefill_kernel_b1_t4096_h16_hbm_counters.txt")
+PREFILL_PMC = os.path.join(ROOT, "profiles", "prefill_pp_kernel_prefill_b1_t4096_h16_hbm_counters.txt")
 PREFILL_SOURCES = [os.path.join(CSRC, f) for f in ("prefill.hip", "prefill_tiles.h", "kernels.h", "rope.h", "tile.h")]
-DECODE_PMC = os.path.join(ROOT, "profiles", "decode_split_kernel_b64_l4096_h16_hbm_counters.txt")
+DECODE_PMC = os.path.join(ROOT, "profiles", "decode_split_kernel_decode_b64_l4096_h16_hbm_counters.txt")
 DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode.hip", "kernels.h", "rope.h")]
 
 
@@ -351,6 +351,44 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     return rec
 
 
+def one_workload(args, da, torch, np, synth, to_dev, f32_dev) -> int:
+    """Settle, warm-up and timed calls of one workload alone (a profiling
+    harness target): prints {workload, kernel us_mean/us_min, rate}."""
+    wl = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    if wl.kind == "prefill":
+        x = synth.make_prefill_inputs(wl)
+        t = {n: to_dev(x[n], dev) for n in ("q1", "q2", "k1", "k2", "v")}
+        gain = f32_dev(x["gain"], dev)
+        lam = f32_dev(x["lam"], dev) if wl.lam_range is not None else wl.lam
+        out = torch.empty((wl.B, wl.T, wl.H, wl.d_v), dtype=torch.bfloat16, device=dev)
+
+        def call():
+            da.diffattn_fwd_prefill_ex(t["q1"], t["q2"], t["k1"], t["k2"], t["v"], lam, gain, eps=wl.eps,
+                                       scale=wl.scale, out=out, window=wl.window)
+        work = {"flop": wl.causal_pairs * FLOP_PER_PAIR, "bytes": swa_prefill_bytes(wl)}
+    else:
+        x = synth.make_decode_inputs(wl)
+        t = {n: to_dev(x[n], dev) for n in ("q1", "q2", "k1", "k2", "v")}
+        gain = f32_dev(x["gain"], dev)
+        out = torch.empty((wl.B, wl.H, wl.d_v), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(da.diffattn_decode_workspace_bytes(wl.B, wl.H, wl.d_v, wl.num_splits), dtype=torch.uint8,
+                         device=dev)
+
+        def call():
+            da.diffattn_fwd_decode_ex(t["q1"], t["q2"], t["k1"], t["k2"], t["v"], wl.lam, gain, eps=wl.eps,
+                                      scale=wl.scale, num_splits=wl.num_splits, workspace=ws, out=out,
+                                      window=wl.window)
+        work = {"flop": wl.causal_pairs * FLOP_PER_PAIR, "bytes": decode_bytes(wl)}
+    settle(torch, call, args.settle)
+    us, us_min = _time_calls(torch, np, call, args.warmup, args.steps)
+    assert bool(torch.isfinite(out.float()).all())
+    print(json.dumps({"workload": wl.name, "us_mean": round(us, 2), "us_min": round(us_min, 2),
+                      "tflops": round(work["flop"] / us / 1e6, 2), "gbs": round(work["bytes"] / us / 1e3, 1),
+                      "calls": args.warmup + args.steps, "settle_s": args.settle}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,6 +399,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the variant timings")
+    ap.add_argument("--workload", default="",
+                    help="time only this prefill or decode workload (for profiling runs); prints its own JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -383,6 +423,9 @@ def main() -> int:
 
     def f32_dev(a, device):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    if args.workload:
+        return one_workload(args, da, torch, np, synth, to_dev, f32_dev)
 
     dev = "cuda"
     pw = synth.WORKLOADS[PREFILL_WL]
