@@ -101,7 +101,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 107; }
+int diffattn_abi_version(void) { return 108; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -124,6 +124,11 @@ namespace {
 // workspace (256-byte aligned slices).
 size_t rope_keys_bytes(int B, int T, int H) {
   return ((size_t)B * T * H * diffattn::kDqk * 2 + 255) & ~size_t(255);
+}
+
+// Bytes of the fp16 V^T tiles in the prefill workspace (vtiles.hip).
+size_t vtiles_bytes(int B, int T, int H) {
+  return (size_t)B * H * ((T + 31) / 32) * diffattn::kVtTileBytes;
 }
 
 // Shared by diffattn_fwd_prefill_ex, _ws and _train; `train` holds the three
@@ -184,11 +189,15 @@ int prefill_impl(const diffattn_options* opt, const void* q1, const void* q2, co
     a.lse = train[2];
   }
   const hipStream_t hs = static_cast<hipStream_t>(stream);
+  // Workspace: [rotated K1, K2 (with rope)] [V^T tiles]; checked before any launch.
+  const size_t rope_part = a.rope.mode != 0 ? 2 * rope_keys_bytes(B, T, H) : 0;
+  if (ws != nullptr &&
+      (ws_bytes < rope_part + vtiles_bytes(B, T, H) || reinterpret_cast<uintptr_t>(ws) % 256 != 0))
+    return DIFFATTN_ERR_WORKSPACE;
   if (ws != nullptr && a.rope.mode != 0) {
     // Rotate both key tensors once into the workspace (fp16, C-contiguous);
     // the prefill then stages them like plain keys.
     const size_t one = rope_keys_bytes(B, T, H);
-    if (ws_bytes < 2 * one || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return DIFFATTN_ERR_WORKSPACE;
     diffattn::RopeKeysArgs r{};
     r.k1 = a.k1;
     r.k2 = a.k2;
@@ -208,6 +217,20 @@ int prefill_impl(const diffattn_options* opt, const void* q1, const void* q2, co
     a.sk2 = kc;
     a.keys_rotated = 1;
   }
+  if (ws != nullptr && diffattn::prefill_takes_vt(a)) {
+    // V converted and transposed once into fp16 V^T tiles that the prefill
+    // kernels move into LDS by DMA.
+    diffattn::VTilesArgs t{};
+    t.v = a.v;
+    t.sv = a.sv;
+    t.B = B;
+    t.T = T;
+    t.H = H;
+    t.ntiles = (T + 31) / 32;
+    t.out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + rope_part);
+    if (diffattn::launch_vtiles(t, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
+    a.vt = t.out;
+  }
   if (diffattn::launch_prefill(a, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
   return DIFFATTN_OK;
 }
@@ -224,8 +247,9 @@ int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void* q1, const v
 
 size_t diffattn_prefill_workspace_bytes(const diffattn_options* opt, int B, int T, int H) {
   if (B <= 0 || T <= 0 || H <= 0 || (int64_t)B * H > (1 << 24) || T > (1 << 22)) return 0;
-  if (!opt || opt->rope == DIFFATTN_ROPE_NONE) return 0;
-  return 2 * rope_keys_bytes(B, T, H);
+  if ((int64_t)((T + 127) / 128) * B * H > kMaxWorkgroups) return 0;
+  const size_t rope_part = opt && opt->rope != DIFFATTN_ROPE_NONE ? 2 * rope_keys_bytes(B, T, H) : 0;
+  return rope_part + vtiles_bytes(B, T, H);
 }
 
 int diffattn_fwd_prefill_ws(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,

@@ -47,6 +47,9 @@ struct PrefillArgs {
   float* o1n;
   float* o2n;
   float* lse;
+  // The values as fp16 V^T tiles (vtiles.hip), or null: the kernels then
+  // convert and transpose V while staging it.
+  const uint16_t* vt;
 };
 
 struct DecodeArgs {
@@ -168,6 +171,21 @@ constexpr int kBwdRowsPerChunk = 64;
 void rope_phases(float theta, RopeArgs& r);
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Whether the kernel launch_prefill picks for `a` reads V^T tiles (a.vt).
+bool prefill_takes_vt(const PrefillArgs& a);
+
+// V of a prefill as fp16 V^T tiles, each the exact LDS image the prefill
+// kernels read: per (b, h) and 32-key tile, 128 channel rows of 64 bytes,
+// keys in the score accumulator's order, 16-byte chunks swizzled by row.
+constexpr int kVtTileBytes = 128 * 32 * 2;
+struct VTilesArgs {
+  const uint16_t* v;  // [B, T, H, kDv] bf16 with strides
+  Strides sv;
+  int B, T, H;
+  int ntiles;         // ceil(T / 32)
+  uint16_t* out;      // [B * H][ntiles][kVtTileBytes / 2]
+};
+hipError_t launch_vtiles(const VTilesArgs& a, hipStream_t stream);
 
 // Compute units of the current device, queried once per device and cached.
 int device_cu_count();

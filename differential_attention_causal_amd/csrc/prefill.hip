@@ -73,6 +73,99 @@ __device__ __forceinline__ void pp_load_v(Staged& st, const KeyRes& r, const Sta
     st.v[i] = __builtin_amdgcn_raw_buffer_load_b64(r.v, off.v + (uint32_t)(kbase + i) * r.vs, 0, 0);
 }
 
+// The matrix phase of a ping-pong step with V^T tiles when the wave has both a
+// current tile (16 P V products) and a next one (8 score products): every
+// product's LDS operand is read two reads ahead, so no product waits for a
+// full LDS round trip.  The scheduling groups pin that order (LDS reads
+// interleaved with the products, the key DMA after the fourth product).
+template <bool kF16>
+__device__ __forceinline__ void pp_matrix_vt(const char* cur, const char* nxt, int lq, int hf, int ksw,
+                                             const bf16x8 (&qa)[4], const bf16x8 (&qb2)[4], const f16x8& p1a,
+                                             const f16x8& p1b, const f16x8& p2a, const f16x8& p2b, f32x16 (&O1)[4],
+                                             f32x16 (&O2)[4], f32x16& s1, f32x16& s2, const KeyRes& res,
+                                             const StageOffsets& soff, char* kdst, int kbase, int wq) {
+  const char* vt = cur + 2 * kKBytes;
+  // V^T operands in order of use: (cb, s) = (0,0) (1,0) (0,1) (1,1) (2,0) (3,0) (2,1) (3,1)
+  auto vop = [&](int i) __attribute__((always_inline)) { return vt_operand(vt, lq, hf, (i & 1) + 2 * (i >> 2), (i >> 1) & 1); };
+  const int krow = lq * kKRow;
+  // K operands: map m's chunk s, in order (s, m) = (0,1) (0,2) (1,1) ...
+  auto kop = [&](int i) __attribute__((always_inline)) {
+    const int s = i >> 1;
+    const int off = krow + (((2 * s + hf) ^ ksw) << 4) + (i & 1) * kKBytes;
+    return *reinterpret_cast<const bf16x8*>(nxt + off);
+  };
+  auto pv = [&](int i, const f16x8& v) __attribute__((always_inline)) {
+    const int cb = (i & 1) + 2 * (i >> 2);
+    const bool second = (i >> 1) & 1;
+    O1[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v, second ? p1b : p1a, O1[cb], 0, 0, 0);
+    O2[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v, second ? p2b : p2a, O2[cb], 0, 0, 0);
+  };
+  auto sc = [&](int i, const bf16x8& k) __attribute__((always_inline)) {
+    const int s = i >> 1;
+    f32x16& acc = (i & 1) ? s2 : s1;
+    const bf16x8& q = (i & 1) ? qb2[s] : qa[s];
+    const f32x16 c0 = s == 0 ? f32x16{} : acc;
+    if constexpr (kF16)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, k), __builtin_bit_cast(f16x8, q), c0, 0,
+                                                   0, 0);
+    else
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, q, c0, 0, 0, 0);
+  };
+  // Region 1: three reads, two product pairs, each followed by the next read.
+  f16x8 va = vop(0), vb = vop(1), vc = vop(2);
+  pv(0, va);
+  va = vop(3);
+  pv(1, vb);
+  vb = vop(4);
+  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // (masks: 0x100 LDS read, 0x008 matrix product)
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  pp_dma_k(res, soff, kdst, kbase, wq);
+  __builtin_amdgcn_sched_barrier(0);
+  // Region 2: the other six product pairs and the eight score products, each
+  // followed by the read two ahead of it.
+  pv(2, vc);
+  vc = vop(5);
+  pv(3, va);
+  va = vop(6);
+  pv(4, vb);
+  vb = vop(7);
+  pv(5, vc);
+  bf16x8 ka = kop(0);
+  pv(6, va);
+  bf16x8 kb = kop(1);
+  pv(7, vb);
+  bf16x8 kc = kop(2);
+  sc(0, ka);
+  ka = kop(3);
+  sc(1, kb);
+  kb = kop(4);
+  sc(2, kc);
+  kc = kop(5);
+  sc(3, ka);
+  ka = kop(6);
+  sc(4, kb);
+  kb = kop(7);
+  sc(5, kc);
+  sc(6, ka);
+  sc(7, kb);
+#pragma unroll
+  for (int g = 0; g < 6; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int g = 0; g < 5; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Ping-pong split-key kernel (two groups of four waves, one wave of each group
 // per SIMD).  Each group runs a two-phase step: a matrix phase (O += V P for
 // its current tile, then S = K Q^T for its next tile) and a vector phase
@@ -83,14 +176,37 @@ __device__ __forceinline__ void pp_load_v(Staged& st, const KeyRes& r, const Sta
 // in slot x % 2.  In the matrix phase of step x the group reads V(x) and
 // K(x + 1) while the DMA of K(x + 2) fills slot x % 2; V(x + 1) is stored in
 // the vector phase of step x from registers loaded a step earlier.
-constexpr int kPPStage = 2 * kTile;
-constexpr int kPPSmem = 2 * kPPStage + kDv * 4 + 16;
+// With V^T tiles (kVT, vtiles.hip) the values come by DMA as well, and each
+// group cycles through kVtSlots slots: tile x sits in slot x % kVtSlots, K(x +
+// kVtSlots) goes into slot x's key half in the matrix phase of step x (K(x)
+// was read in the step before) and V(x + kVtSlots) into its value half in the
+// vector phase (the matrix phase has read V(x)).  The deeper prefetch hides
+// the memory latency of the tiles, which two slots did not.
+constexpr int kVtSlots = 4;
+template <bool kVT>
+constexpr int pp_stage_bytes() { return 2 * (kVT ? kTileVT : kTile); }
+template <bool kVT>
+constexpr int pp_stages() { return kVT ? kVtSlots : 2; }
+// LDS: the stages (or the merge buffer, which reuses them), then the head's
+// gain and lambda.
+template <bool kVT>
+constexpr int pp_gain_offset() {
+  return pp_stages<kVT>() * pp_stage_bytes<kVT>() > kMergeOutBytes ? pp_stages<kVT>() * pp_stage_bytes<kVT>()
+                                                                     : kMergeOutBytes;
+}
+// Vector-memory instructions issued after K(x + 2) by the time the vector
+// phase of step x ends: V(x + 2), then K(y), V(y) for y = x + 3 .. x + slots
+// (two instructions each).
+constexpr int kVtYounger = 2 + 4 * (kVtSlots - 2);
+template <bool kVT>
+constexpr int pp_smem_bytes() { return pp_gain_offset<kVT>() + kDv * 4 + 16; }
 
-template <bool kTrain, bool kRopeQ>
+template <bool kTrain, bool kRopeQ, bool kVT>
 __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int item) {
-  constexpr int kStage = kPPStage;
-  f32x4* const gain_s = reinterpret_cast<f32x4*>(smem + 2 * kStage);
-  float* const lam_s = reinterpret_cast<float*>(smem + 2 * kStage + kDv * 4);
+  constexpr int kStage = pp_stage_bytes<kVT>();
+  constexpr int kTileB = kVT ? kTileVT : kTile;
+  f32x4* const gain_s = reinterpret_cast<f32x4*>(smem + pp_gain_offset<kVT>());
+  float* const lam_s = reinterpret_cast<float*>(smem + pp_gain_offset<kVT>() + kDv * 4);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -155,7 +271,11 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
   res.ks2 = (uint32_t)(a.sk2.t * 2);
   res.vs = (uint32_t)(a.sv.t * 2);
   auto key0 = [&](int x) { return (tile0 + 2 * x + grp) * kBN; };  // first key of the group's tile of step x
-  char* const slot0 = smem + grp * kTile;                          // the group's tile in stage 0
+  char* const slot0 = smem + grp * kTileB;                         // the group's tile in stage 0
+  const __amdgpu_buffer_rsrc_t rvt = vt_rsrc(a, b, head);  // used with V^T tiles only
+  // DMA of the group's V^T tile of step x into stage s
+  auto dma_v = [&](int x, int s) { dma_vt(rvt, slot0 + s * kStage + 2 * kKBytes, tile0 + 2 * x + grp, wq, lane); };
+  auto vslot = [&](int x) { return slot0 + (x % kVtSlots) * kStage; };  // tile x's slot (V^T tiles)
   auto live = [&](int j) { return wave_live && j >= wave_first_tile && j <= wave_last_tile; };
 
   // The epilogue's gain and lambda, fetched while the first tiles load.
@@ -165,16 +285,28 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
   if (tid == kDv / 4) lpre = a.lambda_h ? a.lambda_h[head] : a.lambda;
 
   // Prologue: tile 0 complete in slot 0, K(1) in slot 1, V(1) in registers
-  // (wait: everything but the four V(1) loads).
+  // (wait: everything but the four V(1) loads); with V^T tiles, V(1) is on its
+  // way to slot 1 instead (its two DMAs may still be in flight).
   Staged st;
-  pp_dma_k(res, soff, slot0, key0(0), wq);
-  pp_load_v(st, res, soff, key0(0));
-  pp_dma_k(res, soff, slot0 + kStage, key0(1), wq);
-  stage_store<0>(st, smem, tid, nullptr);
-  pp_load_v(st, res, soff, key0(1));
-  if (tid < kDv / 4) gain_s[tid] = gpre;
-  if (tid == kDv / 4) *lam_s = lpre;
-  wait_vm<4>();
+  if constexpr (kVT) {
+#pragma unroll
+    for (int x = 0; x < kVtSlots; ++x) {
+      pp_dma_k(res, soff, slot0 + x * kStage, key0(x), wq);
+      dma_v(x, x);
+    }
+    if (tid < kDv / 4) gain_s[tid] = gpre;
+    if (tid == kDv / 4) *lam_s = lpre;
+    wait_vm<kVtYounger>();  // K(0), V(0), K(1) have landed
+  } else {
+    pp_dma_k(res, soff, slot0, key0(0), wq);
+    pp_load_v(st, res, soff, key0(0));
+    pp_dma_k(res, soff, slot0 + kStage, key0(1), wq);
+    stage_store<0>(st, smem, tid, nullptr);
+    pp_load_v(st, res, soff, key0(1));
+    if (tid < kDv / 4) gain_s[tid] = gpre;
+    if (tid == kDv / 4) *lam_s = lpre;
+    wait_vm<4>();
+  }
   wait_lds();
   phase_barrier();
 
@@ -183,7 +315,7 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
     const int j = tile0 + grp;
     if (live(j)) {
       f32x16 s1, s2;
-      scores_tile<kRopeQ>(smem + grp * kTile, lq, hf, ksw, qa, qb2, s1, s2);
+      scores_tile<kRopeQ>(slot0, lq, hf, ksw, qa, qb2, s1, s2);
       mask_tile(a, s1, s2, j, wave_last_tile, q_first, q, hf);
       softmax_step(s1, c, m1, l1, O1, p1a, p1b);
       softmax_step(s2, c, m2, l2, O2, p2a, p2b);
@@ -193,39 +325,94 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
   phase_barrier();
   if (grp == 1) phase_barrier();  // group 1 starts one phase late
 
-  for (int it = 0; it < nsteps; ++it) {
-    char* cur = smem + (it & 1) * kStage + grp * kTile;
-    char* nxt = smem + ((it + 1) & 1) * kStage + grp * kTile;
+  // One step of the group with V^T tiles.  piped: the wave has both a live
+  // current tile and a live next one, and the matrix phase runs
+  // pp_matrix_vt; otherwise the products it has go one after another.  The
+  // two forms run in separate loops (the steps of a wave where both tiles are
+  // live come first, without a window), so each loop body holds one of them.
+  auto step = [&](int it, auto piped) __attribute__((always_inline)) {
+    char* cur = vslot(it);
+    char* nxt = vslot(it + 1);
     const int j = tile0 + 2 * it + grp;
     const bool next = it + 1 < nsteps && live(j + 2);
     // Matrix phase (raised issue priority: its products go first whenever
     // both waves of a SIMD are ready).
     __builtin_amdgcn_s_setprio(1);
     f32x16 s1, s2;
-    const bool lj = live(j);
-    if (lj) pv_pair(cur, lq, hf, 0, p1a, p1b, p2a, p2b, O1, O2);
-    // K(it + 2) into slot it % 2, issued once the first products are queued.
-    // Unconditional: past the last tile the loads read zeros (rows past kend)
-    // into a slot nobody reads again, and the wait counts stay the same on
-    // every iteration.
-    __builtin_amdgcn_sched_barrier(0);
-    pp_dma_k(res, soff, slot0 + (it & 1) * kStage, key0(it + 2), wq);
-    __builtin_amdgcn_sched_barrier(0);
-    if (lj) pv_pair(cur, lq, hf, 2, p1a, p1b, p2a, p2b, O1, O2);
-    if (next) scores_tile<kRopeQ>(nxt, lq, hf, ksw, qa, qb2, s1, s2);
+    if constexpr (decltype(piped)::value) {
+      pp_matrix_vt<kRopeQ>(cur, nxt, lq, hf, ksw, qa, qb2, p1a, p1b, p2a, p2b, O1, O2, s1, s2, res, soff, cur,
+                           key0(it + kVtSlots), wq);
+    } else {
+      const bool lj = live(j);
+      if (lj) pv_pair<kVT>(cur, lq, hf, 0, p1a, p1b, p2a, p2b, O1, O2);
+      // K(it + 2) into slot it % 2, issued once the first products are queued.
+      // Unconditional: past the last tile the loads read zeros (rows past kend)
+      // into a slot nobody reads again, and the wait counts stay the same on
+      // every iteration.
+      __builtin_amdgcn_sched_barrier(0);
+      pp_dma_k(res, soff, cur, key0(it + kVtSlots), wq);
+      __builtin_amdgcn_sched_barrier(0);
+      if (lj) pv_pair<kVT>(cur, lq, hf, 2, p1a, p1b, p2a, p2b, O1, O2);
+      if (next) scores_tile<kRopeQ>(nxt, lq, hf, ksw, qa, qb2, s1, s2);
+    }
     __builtin_amdgcn_s_setprio(0);
     phase_barrier();
-    // Vector phase.
-    if (it + 1 < nsteps) stage_store<0>(st, smem + ((it + 1) & 1) * kStage, tid, nullptr);
-    pp_load_v(st, res, soff, key0(it + 2));
-    if (next) {
+    // Vector phase.  V(it + slots) into tile it's slot: every wave of the group
+    // has read V(it).  Unconditional like the key DMA (tiles past the last
+    // read as zero).
+    dma_v(it + kVtSlots, it % kVtSlots);
+    if (decltype(piped)::value || next) {
       mask_tile(a, s1, s2, j + 2, wave_last_tile, q_first, q, hf);
       softmax_step(s1, c, m1, l1, O1, p1a, p1b);
       softmax_step(s2, c, m2, l2, O2, p2a, p2b);
     }
-    wait_vm<4>();  // K(it + 2) has landed; only the four V(it + 2) loads may be in flight
-    wait_lds();    // V(it + 1) stored
+    wait_vm<kVtYounger>();  // K(it + 2) and V(it + 1) have landed
     phase_barrier();
+  };
+  if constexpr (kVT) {
+    // Steps 0 .. n_piped-1 have both tiles live (no window): tile
+    // j = tile0 + 2 it + grp and j + 2 at most the wave's diagonal tile, and
+    // a next step.
+    const int span = wave_last_tile - tile0 - grp - 2;  // j + 2 <= diagonal  <=>  2 it <= span
+    const int n_piped = a.window > 0 || !wave_live || span < 0 ? 0 : min(nsteps - 1, span / 2 + 1);
+    int it = 0;
+    for (; it < n_piped; ++it) step(it, std::true_type{});
+    for (; it < nsteps; ++it) step(it, std::false_type{});
+  } else {
+    for (int it = 0; it < nsteps; ++it) {
+      char* cur = smem + (it & 1) * kStage + grp * kTile;
+      char* nxt = smem + ((it + 1) & 1) * kStage + grp * kTile;
+      const int j = tile0 + 2 * it + grp;
+      const bool next = it + 1 < nsteps && live(j + 2);
+      // Matrix phase (raised issue priority: its products go first whenever
+      // both waves of a SIMD are ready).
+      __builtin_amdgcn_s_setprio(1);
+      f32x16 s1, s2;
+      const bool lj = live(j);
+      if (lj) pv_pair(cur, lq, hf, 0, p1a, p1b, p2a, p2b, O1, O2);
+      // K(it + 2) into slot it % 2, issued once the first products are queued.
+      // Unconditional: past the last tile the loads read zeros (rows past kend)
+      // into a slot nobody reads again, and the wait counts stay the same on
+      // every iteration.
+      __builtin_amdgcn_sched_barrier(0);
+      pp_dma_k(res, soff, slot0 + (it & 1) * kStage, key0(it + 2), wq);
+      __builtin_amdgcn_sched_barrier(0);
+      if (lj) pv_pair(cur, lq, hf, 2, p1a, p1b, p2a, p2b, O1, O2);
+      if (next) scores_tile<kRopeQ>(nxt, lq, hf, ksw, qa, qb2, s1, s2);
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+      // Vector phase.
+      if (it + 1 < nsteps) stage_store<0>(st, smem + ((it + 1) & 1) * kStage, tid, nullptr);
+      pp_load_v(st, res, soff, key0(it + 2));
+      if (next) {
+        mask_tile(a, s1, s2, j + 2, wave_last_tile, q_first, q, hf);
+        softmax_step(s1, c, m1, l1, O1, p1a, p1b);
+        softmax_step(s2, c, m2, l2, O2, p2a, p2b);
+      }
+      wait_vm<4>();  // K(it + 2) has landed; only the four V(it + 2) loads may be in flight
+      wait_lds();    // V(it + 1) stored
+      phase_barrier();
+    }
   }
   if (grp == 0) phase_barrier();
   wait_vm<0>();  // the zero-filling DMAs past the last tile, before the merge reuses the stages
@@ -241,20 +428,20 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
 // back to back: the longest block with the shortest, so one workgroup per CU
 // carries the same work everywhere, and a head's blocks stay on the XCD that
 // holds its keys in L2 (B*H a multiple of 8).  An odd middle row runs alone.
-template <bool kTrain, bool kRopeQ>
+template <bool kTrain, bool kRopeQ, bool kVT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_pp_kernel(PrefillArgs a) {
   // One LDS object (the stages, then the epilogue's gain and lambda): the
   // compiler then has no per-object alias scopes to go on and adds no waits
   // of its own for the key DMA before LDS reads; the explicit waits order them.
-  __shared__ __attribute__((aligned(16))) char smem[kPPSmem];
+  __shared__ __attribute__((aligned(16))) char smem[pp_smem_bytes<kVT>()];
   const int BH = a.B * a.H;
   const int nqb = (a.T + kBM - 1) / kBM;
   const int r = (int)blockIdx.x / BH, bh = (int)blockIdx.x % BH;
-  pp_item<kTrain, kRopeQ>(a, smem, (int)blockIdx.x);
+  pp_item<kTrain, kRopeQ, kVT>(a, smem, (int)blockIdx.x);
   if (nqb - 1 - r > r) {
     __syncthreads();  // the first block's epilogue is done with LDS
-    pp_item<kTrain, kRopeQ>(a, smem, (nqb - 1 - r) * BH + bh);
+    pp_item<kTrain, kRopeQ, kVT>(a, smem, (nqb - 1 - r) * BH + bh);
   }
 }
 
@@ -265,11 +452,15 @@ prefill_pp_kernel(PrefillArgs a) {
 // carries none of its registers: 0 none; 1 split-half and 2 interleaved, with
 // the key tiles rotated while staged; 3 keys rotated beforehand (fp16 copies
 // moved by DMA like plain keys), the query rotated here in mode a.rope.mode.
-template <int kGroups, int kRope>
+// kVT (kRope 0 or 3): the values come as fp16 V^T tiles (vtiles.hip) by DMA.
+template <int kGroups, int kRope, bool kVT = false>
 __global__ void __launch_bounds__(64 * kGroupWaves * kGroups) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillArgs a) {
-  constexpr int kStage = kGroups * kTile;  // one step: a tile for each group
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  static_assert(!kVT || kRope == 0 || kRope == 3, "V^T tiles go with keys moved by DMA");
+  constexpr int kTileB = kVT ? kTileVT : kTile;
+  constexpr int kStage = kGroups * kTileB;  // one step: a tile for each group
+  constexpr int kSmem = kGroups == 2 && kMergeBytes > 2 * kStage ? kMergeBytes : 2 * kStage;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   __shared__ uint64_t rope_tab[32];
 
   const int tid = threadIdx.x;
@@ -340,9 +531,14 @@ prefill_kernel(PrefillArgs a) {
   const StageOffsets soff = stage_offsets<kRope>(a, tid);
 
   Staged st;
-  if constexpr (kRope == 0 || kRope == 3) stage_dma_k(a, kb1, kb2, soff, smem, tile0 * kBN, kend, tid);
-  stage_load<kRope>(st, a, kb1, kb2, vbase, soff, tile0 * kBN, kend, tid);
-  stage_store<kRope>(st, smem, tid, rope_tab);
+  const __amdgpu_buffer_rsrc_t rvt = vt_rsrc(a, b, head);  // used with V^T tiles only
+  if constexpr (kRope == 0 || kRope == 3) stage_dma_k<kTileB>(a, kb1, kb2, soff, smem, tile0 * kBN, kend, tid);
+  if constexpr (kVT) {
+    dma_vt(rvt, smem + grp * kTileB + 2 * kKBytes, tile0 + grp, wq, lane);
+  } else {
+    stage_load<kRope>(st, a, kb1, kb2, vbase, soff, tile0 * kBN, kend, tid);
+    stage_store<kRope>(st, smem, tid, rope_tab);
+  }
   if constexpr (kRope == 0 || kRope == 3) wait_dma();
   __syncthreads();
 
@@ -352,13 +548,16 @@ prefill_kernel(PrefillArgs a) {
     const bool more = it + 1 < nsteps;
     if (more) {
       if constexpr (kRope == 0 || kRope == 3)
-        stage_dma_k(a, kb1, kb2, soff, nxt, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
-      stage_load<kRope>(st, a, kb1, kb2, vbase, soff, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
+        stage_dma_k<kTileB>(a, kb1, kb2, soff, nxt, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
+      if constexpr (kVT)
+        dma_vt(rvt, nxt + grp * kTileB + 2 * kKBytes, tile0 + (it + 1) * kGroups + grp, wq, lane);
+      else
+        stage_load<kRope>(st, a, kb1, kb2, vbase, soff, (tile0 + (it + 1) * kGroups) * kBN, kend, tid);
     }
 
     const int j = tile0 + it * kGroups + grp;  // this group's tile
     if (wave_live && j >= wave_first_tile && j <= wave_last_tile) {
-      const char* kt = cur + grp * kTile;
+      const char* kt = cur + grp * kTileB;
       f32x16 s1 = f32x16{}, s2 = f32x16{};
       const int krow = lq * kKRow;
 #pragma unroll
@@ -407,8 +606,10 @@ prefill_kernel(PrefillArgs a) {
       const char* vt = kt + 2 * kKBytes + lq * kVRow + hf * 16;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const f16x8 va0 = *reinterpret_cast<const f16x8*>(vt + cb * 32 * kVRow);
-        const f16x8 va1 = *reinterpret_cast<const f16x8*>(vt + cb * 32 * kVRow + 32);
+        const f16x8 va0 = kVT ? vt_operand(kt + 2 * kKBytes, lq, hf, cb, 0)
+                              : *reinterpret_cast<const f16x8*>(vt + cb * 32 * kVRow);
+        const f16x8 va1 = kVT ? vt_operand(kt + 2 * kKBytes, lq, hf, cb, 1)
+                              : *reinterpret_cast<const f16x8*>(vt + cb * 32 * kVRow + 32);
         O1[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va0, p1a, O1[cb], 0, 0, 0);
         O2[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va0, p2a, O2[cb], 0, 0, 0);
         O1[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va1, p1b, O1[cb], 0, 0, 0);
@@ -416,7 +617,7 @@ prefill_kernel(PrefillArgs a) {
       }
     }
 
-    if (more) stage_store<kRope>(st, nxt, tid, rope_tab);
+    if (more && !kVT) stage_store<kRope>(st, nxt, tid, rope_tab);
     if constexpr (kRope == 0 || kRope == 3) wait_dma();
     __syncthreads();
   }
@@ -434,38 +635,73 @@ prefill_kernel(PrefillArgs a) {
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  const int nqb = (a.T + kBM - 1) / kBM;
-  const int64_t grid = (int64_t)nqb * a.B * a.H;
+namespace {
+
+// The launch shape of a prefill (see launch_prefill).
+struct PrefillPlan {
+  int nqb;
+  int64_t grid;
+  bool split;     // the grid fits on the chip in one round
+  bool prerot;    // keys rotated beforehand (fp16 copies)
+  bool pingpong;  // prefill_pp_kernel
+  bool window;    // the streaming window kernel (window.hip)
+  bool takes_vt;  // the chosen kernel can read V^T tiles (vtiles.hip)
+};
+
+PrefillPlan plan_prefill(const PrefillArgs& a) {
+  PrefillPlan p;
+  p.nqb = (a.T + kBM - 1) / kBM;
+  p.grid = (int64_t)p.nqb * a.B * a.H;
   // A grid that fits on the chip in one round (two 4-wave workgroups per CU)
   // leaves the CUs holding the longest query blocks working alone at the end;
   // splitting each workgroup's key range over two wave groups halves that
   // tail.  Larger grids balance by themselves in longest-first order and run
   // better as independent 4-wave workgroups.
-  const int cus = device_cu_count();
-  const bool split = grid <= 2 * (int64_t)cus;
+  p.split = p.grid <= 2 * (int64_t)device_cu_count();
   const int64_t row_max = std::max(std::max(a.sk1.t, a.sk2.t), a.sv.t);
   // Keys already rotated (fp16 copies): they are staged like plain keys, and
   // only the queries turn inside the kernels.
-  const bool prerot = a.rope.mode != 0 && a.keys_rotated;
+  p.prerot = a.rope.mode != 0 && a.keys_rotated;
   // The ping-pong kernel addresses a (b, h)'s key rows from one buffer base
   // with 32-bit offsets (up to about T + 192 rows).
-  const bool pingpong = split && (a.rope.mode == 0 || prerot) && !(prerot && a.o1n != nullptr) &&
-                        (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31);
+  p.pingpong = p.split && (a.rope.mode == 0 || p.prerot) && !(p.prerot && a.o1n != nullptr) &&
+               (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31);
   // Windowed prefill without the rotary embedding or training outputs, at
   // most four tiles before the diagonal: the streaming kernel (window.hip).
-  if (prefill_window_kernel_fits(a)) return launch_prefill_window(a, stream);
-  if (pingpong) {
+  p.window = prefill_window_kernel_fits(a);
+  // V^T tiles go with the kernels that move keys by DMA, without training
+  // outputs: the ping-pong kernel and the four-wave kernel; the lock-step
+  // two-group kernel and key rotation while staging keep V in registers.
+  p.takes_vt = !p.window && a.o1n == nullptr && (a.rope.mode == 0 || p.prerot) && (p.pingpong || !p.split);
+  return p;
+}
+
+}  // namespace
+
+bool prefill_takes_vt(const PrefillArgs& a) { return plan_prefill(a).takes_vt; }
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  const PrefillPlan p = plan_prefill(a);
+  if (p.window) return launch_prefill_window(a, stream);
+  const bool vt = a.vt != nullptr && p.takes_vt;
+  const int nqb = p.nqb;
+  if (p.pingpong) {
     const dim3 gp((unsigned)((int64_t)((nqb + 1) / 2) * a.B * a.H));
-    if (prerot) return launch_kernel(prefill_pp_kernel<false, true>, gp, dim3(512), stream, a);
-    if (a.o1n != nullptr) return launch_kernel(prefill_pp_kernel<true, false>, gp, dim3(512), stream, a);
-    return launch_kernel(prefill_pp_kernel<false, false>, gp, dim3(512), stream, a);
+    if (p.prerot)
+      return vt ? launch_kernel(prefill_pp_kernel<false, true, true>, gp, dim3(512), stream, a)
+                : launch_kernel(prefill_pp_kernel<false, true, false>, gp, dim3(512), stream, a);
+    if (a.o1n != nullptr) return launch_kernel(prefill_pp_kernel<true, false, false>, gp, dim3(512), stream, a);
+    return vt ? launch_kernel(prefill_pp_kernel<false, false, true>, gp, dim3(512), stream, a)
+              : launch_kernel(prefill_pp_kernel<false, false, false>, gp, dim3(512), stream, a);
   }
-  const dim3 g((unsigned)grid), b1(64 * kGroupWaves), b2(64 * kGroupWaves * 2);
-  if (prerot)
-    return split ? launch_kernel(prefill_kernel<2, 3>, g, b2, stream, a)
-                 : launch_kernel(prefill_kernel<1, 3>, g, b1, stream, a);
-  switch (a.rope.mode * 2 + (split ? 1 : 0)) {
+  const dim3 g((unsigned)p.grid), b1(64 * kGroupWaves), b2(64 * kGroupWaves * 2);
+  if (p.prerot) {
+    if (p.split) return launch_kernel(prefill_kernel<2, 3>, g, b2, stream, a);
+    return vt ? launch_kernel(prefill_kernel<1, 3, true>, g, b1, stream, a)
+              : launch_kernel(prefill_kernel<1, 3>, g, b1, stream, a);
+  }
+  if (vt) return launch_kernel(prefill_kernel<1, 0, true>, g, b1, stream, a);
+  switch (a.rope.mode * 2 + (p.split ? 1 : 0)) {
     case 0: return launch_kernel(prefill_kernel<1, 0>, g, b1, stream, a);
     case 1: return launch_kernel(prefill_kernel<2, 0>, g, b2, stream, a);
     case 2: return launch_kernel(prefill_kernel<1, 1>, g, b1, stream, a);

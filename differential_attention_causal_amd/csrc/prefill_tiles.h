@@ -25,7 +25,11 @@ constexpr int kKBytes = kBN * kKRow;        // 4 KiB per K tile
 constexpr int kVRow = (kBN + 8) * 2;        // 80 bytes per V^T channel row (16-byte pad)
 constexpr int kVBytes = kDv * kVRow;        // 10 KiB per V^T tile
 constexpr int kTile = 2 * kKBytes + kVBytes;
+constexpr int kTileVT = 2 * kKBytes + kVtTileBytes;  // with V^T tiles moved by DMA (vtiles.hip)
 constexpr int kTileThreads = 256;           // threads that stage one tile
+// merge_out's buffer: one map's O^T of four waves, then (m1, l1, m2, l2) of
+// both groups' eight waves
+constexpr int kMergeOutBytes = kMergeO + 8 * 64 * 16;
 static_assert(kMergeBytes <= 2 * 2 * kTile, "merge buffer must fit in the stage memory");
 
 
@@ -65,16 +69,44 @@ __device__ __forceinline__ StageOffsets stage_offsets(const PrefillArgs& a, int 
 // Memory -> LDS for the key tiles of one step (no registers involved): each
 // wave moves 64 chunks of K1 and of K2 into its quarter of its group's tile.
 // Completion is counted by vmcnt; the step's barrier follows a wait for it.
+// kTileBytes: the stage's bytes per tile (kTile, or kTileVT with V^T tiles).
+template <int kTileBytes = kTile>
 __device__ __forceinline__ void stage_dma_k(const PrefillArgs& a, const uint16_t* kb1, const uint16_t* kb2,
                                             const StageOffsets& off, char* stage, int k0, int kend, int tid) {
   const int tile = __builtin_amdgcn_readfirstlane(tid / kTileThreads);
   const int part = __builtin_amdgcn_readfirstlane((tid % kTileThreads) >> 6);  // wave within the tile's group
   const int kbase = k0 + tile * kBN;
-  char* dst = stage + tile * kTile + part * 1024;
+  char* dst = stage + tile * kTileBytes + part * 1024;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(kb1, a.sk1.t, kbase, kend, kDqk), (lds_ptr_t)dst, 16, off.k1,
                                            0, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(kb2, a.sk2.t, kbase, kend, kDqk), (lds_ptr_t)(dst + kKBytes),
                                            16, off.k2, 0, 0, 0);
+}
+
+// Buffer resource over one (b, h)'s fp16 V^T tiles (vtiles.hip): tiles past
+// the last read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t vt_rsrc(const PrefillArgs& a, int b, int head) {
+  const int nt = (a.T + kBN - 1) / kBN;
+  const uint16_t* p = a.vt + ((int64_t)b * a.H + head) * nt * (kVtTileBytes / 2);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)rows_extent_bytes(kVtTileBytes / 2, 0, nt, kVtTileBytes / 2),
+                                           0x00020000);
+}
+
+// Memory -> LDS of one 8 KiB V^T tile by the four waves that stage it: wave
+// `part` moves bytes 2048 part .. +2047 (two loads of 64 lanes x 16 bytes).
+// The instruction's immediate offset would move the LDS destination as well,
+// so the second half's 1 KiB step goes into the per-lane offset.
+__device__ __forceinline__ void dma_vt(__amdgpu_buffer_rsrc_t r, char* vt_lds, int tile, int part, int lane) {
+  char* dst = vt_lds + part * 2048;
+  const uint32_t off = (uint32_t)tile * kVtTileBytes + part * 2048 + lane * 16;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 1024), 16, off + 1024, 0, 0, 0);
+}
+
+// The V^T operand of one P V product from a DMA'd tile: channel row
+// 32 cb + lq, keys 16 s .. 16 s + 15, lane half hf's eight (one swizzled chunk).
+__device__ __forceinline__ f16x8 vt_operand(const char* vt, int lq, int hf, int cb, int s) {
+  return *reinterpret_cast<const f16x8*>(vt + (32 * cb + lq) * 64 + (((2 * s + hf) ^ ((lq >> 2) & 3)) << 4));
 }
 
 __device__ __forceinline__ u32x4 load_krow(__amdgpu_buffer_rsrc_t r, uint32_t off, bool split) {
@@ -538,9 +570,27 @@ __device__ __forceinline__ void mask_tile(const PrefillArgs& a, f32x16& s1, f32x
 }
 
 // Two 32-channel blocks of O += V P for both maps, ordered so that
-// consecutive products never share an accumulator.
+// consecutive products never share an accumulator.  kVT: the tile's V^T came
+// by DMA in the vtiles.hip layout; otherwise it was staged in kVRow rows.
+template <bool kVT = false>
 __device__ __forceinline__ void pv_pair(const char* kt, int lq, int hf, int cb, const f16x8& p1a, const f16x8& p1b,
                                         const f16x8& p2a, const f16x8& p2b, f32x16 (&O1)[4], f32x16 (&O2)[4]) {
+  if constexpr (kVT) {
+    const char* vt = kt + 2 * kKBytes;
+    const f16x8 a0 = vt_operand(vt, lq, hf, cb, 0);
+    const f16x8 b0 = vt_operand(vt, lq, hf, cb + 1, 0);
+    O1[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, p1a, O1[cb], 0, 0, 0);
+    O2[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, p2a, O2[cb], 0, 0, 0);
+    O1[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, p1a, O1[cb + 1], 0, 0, 0);
+    O2[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, p2a, O2[cb + 1], 0, 0, 0);
+    const f16x8 a1 = vt_operand(vt, lq, hf, cb, 1);
+    const f16x8 b1 = vt_operand(vt, lq, hf, cb + 1, 1);
+    O1[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, p1b, O1[cb], 0, 0, 0);
+    O2[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, p2b, O2[cb], 0, 0, 0);
+    O1[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, p1b, O1[cb + 1], 0, 0, 0);
+    O2[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, p2b, O2[cb + 1], 0, 0, 0);
+    return;
+  }
   const char* vt = kt + 2 * kKBytes + lq * kVRow + hf * 16 + cb * 32 * kVRow;
   const f16x8 a0 = *reinterpret_cast<const f16x8*>(vt);
   const f16x8 b0 = *reinterpret_cast<const f16x8*>(vt + 32 * kVRow);

@@ -194,23 +194,29 @@ DIFFATTN_API int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void
 /*
  * Bytes of device workspace diffattn_fwd_prefill_ws needs for these options
  * and sizes: with rope on, one fp16 copy of each of K1 and K2, rotated once
- * (2 * B * T * H * 64 * 2 bytes, rounded up to 256-byte slices); 0 without
- * rope (and for invalid sizes).
+ * (2 * B * T * H * 64 * 2 bytes, rounded up to 256-byte slices); then V as
+ * fp16 V^T tiles, B * H * ceil(T / 32) * 8192 bytes.  0 for invalid sizes.
  */
 DIFFATTN_API size_t diffattn_prefill_workspace_bytes(const diffattn_options* opt, int B, int T, int H);
 
 /*
- * diffattn_fwd_prefill_ex with a workspace.  With rope on, K1 and K2 are first
- * rotated into the workspace, each key once (the same fp32 rotation and fp16
- * rounding the kernels of diffattn_fwd_prefill_ex apply to every key tile they
- * stage), and the prefill then reads those copies: the query blocks no longer
- * repeat the rotation of the keys they share.  Without rope the workspace is
- * not used (may be NULL).
+ * diffattn_fwd_prefill_ex with a workspace, the fast path.  With rope on, K1
+ * and K2 are first rotated into the workspace, each key once (the same fp32
+ * rotation and fp16 rounding the kernels of diffattn_fwd_prefill_ex apply to
+ * every key tile they stage), and the prefill then reads those copies: the
+ * query blocks no longer repeat the rotation of the keys they share.  V is
+ * converted once to fp16 (the same exact conversion the kernels otherwise
+ * apply while staging each tile) into transposed 32-key tiles that the
+ * prefill kernels move into LDS by DMA.  The results equal those of
+ * diffattn_fwd_prefill_ex bit for bit (same products, same order); a sliding
+ * window of at most 129 keys uses the workspace only for the rotated keys.
+ * Without rope the workspace may be NULL (then it is the plain entry point).
  *   workspace : >= diffattn_prefill_workspace_bytes(opt, B, T, H) bytes,
  *               256-byte aligned; contents need no initialisation
- * Errors as for diffattn_fwd_prefill_ex, plus DIFFATTN_ERR_WORKSPACE (rope on
- * with a missing, misaligned or too small workspace).  The workspace is
- * overwritten on the stream: calls that share one must not overlap.
+ * Errors as for diffattn_fwd_prefill_ex, plus DIFFATTN_ERR_WORKSPACE (a
+ * missing workspace with rope on, or a misaligned or too small one).  The
+ * workspace is overwritten on the stream: calls that share one must not
+ * overlap.
  */
 DIFFATTN_API int diffattn_fwd_prefill_ws(const diffattn_options* opt, const void* q1, const void* q2,
                                          const void* k1, const void* k2, const void* v,
@@ -361,7 +367,9 @@ DIFFATTN_API const char* diffattn_status_string(int status);
  * 102 the rotary embedding (diffattn_options.rope, diffattn_rope_apply), 103
  * the training forward and the backward pass, 104 grouped attention, 105 the
  * prefill workspace entry points (keys rotated once), 106 a larger backward
- * workspace (fp16 input copies; query diffattn_bwd_workspace_bytes again). */
+ * workspace (fp16 input copies; query diffattn_bwd_workspace_bytes again),
+ * 107 diffattn_fwd_decode_noalloc, 108 V^T tiles in the prefill workspace
+ * (query diffattn_prefill_workspace_bytes again). */
 DIFFATTN_API int diffattn_abi_version(void);
 
 #ifdef __cplusplus

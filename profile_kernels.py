@@ -113,6 +113,18 @@ def _workload_rate(name):
     return wl, "hbm", bench.decode_bytes(wl), wl.causal_pairs * bench.FLOP_PER_PAIR
 
 
+def vtiles_bytes(wl):
+    """Bytes the V^T pre-pass moves: V read (bf16), the tiles written (fp16,
+    32-key tiles)."""
+    return wl.B * wl.T * wl.H * wl.d_v * 2 + wl.B * wl.H * (-(-wl.T // 32)) * 32 * wl.d_v * 2
+
+
+def _vtiles_roof(wl, avg):
+    b = vtiles_bytes(wl)
+    return "%.0f GB/s = %.4f of %.0f (HBM, %d B/launch)" % (b / avg / 1e3, b / avg / 1e3 / bench.HBM_PEAK_GBS,
+                                                           bench.HBM_PEAK_GBS, b)
+
+
 def _stats_table(rows):
     out = []
     for r in rows:
@@ -128,7 +140,7 @@ def _sources_digest(kernel):
     if kernel.startswith("prefill_swa"):
         files = ("window.hip", "prefill_tiles.h", "kernels.h", "rope.h", "tile.h")
         return (bench.kernel_source_digest([os.path.join(bench.CSRC, f) for f in files]), " + ".join(files))
-    return bench.kernel_source_digest(), "prefill.hip + prefill_tiles.h + kernels.h + rope.h + tile.h"
+    return bench.kernel_source_digest(), "prefill.hip + prefill_tiles.h + kernels.h + rope.h + tile.h + vtiles.hip"
 
 
 def cmd_step():
@@ -151,6 +163,8 @@ def cmd_step():
         if name.startswith("prefill_pp_kernel"):
             roof = "%.1f TFLOP/s = %.4f of %.1f (bf16 MFMA, %d FLOP/launch)" % (
                 flop / avg / 1e6, flop / avg / 1e6 / bench.MFMA_PEAK_TFLOPS, bench.MFMA_PEAK_TFLOPS, flop)
+        elif name.startswith("vtiles_kernel"):
+            roof = _vtiles_roof(pw, avg)
         elif name.startswith("decode_split_kernel"):
             b = bench.decode_bytes(dw)
             roof = "%.0f GB/s = %.4f of %.0f (HBM, %d B/launch, split kernel alone)" % (
@@ -190,6 +204,8 @@ def cmd_trace(name):
             else:
                 roof = "%.0f GB/s = %.4f of %.0f (HBM, %d B/launch)" % (
                     work / avg / 1e3, work / avg / 1e3 / bench.HBM_PEAK_GBS, bench.HBM_PEAK_GBS, work)
+        elif kname.startswith("vtiles_kernel"):
+            roof = _vtiles_roof(wl, avg)
         lines.append("%s | %d | %.2f | %.2f | %.2f | %s" % (kname, calls, avg, mn, mx, roof))
     lines += ["",
               "# HIP-event timing of the same command without the profiler, same session:",

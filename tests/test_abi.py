@@ -33,7 +33,7 @@ def test_header_symbols_exported():
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 107
+    assert da.diffattn_abi_version() == 108
 
 
 def test_status_strings():
@@ -141,14 +141,19 @@ def _prefill_ws(opt, ws=A, wsb=1 << 30, **kw):
     return da._lib.diffattn_fwd_prefill_ws(ctypes.byref(o), *args.values(), ws, wsb, None)
 
 
+def _vt_bytes(B, T, H):
+    return B * H * (-(-T // 32)) * 8192  # fp16 V^T tiles of 32 keys x 128 channels
+
+
 def test_prefill_workspace_bytes():
     one = -(-1 * 4096 * 16 * 64 * 2 // 256) * 256
-    assert da.diffattn_prefill_workspace_bytes(1, 4096, 16, rope=1) == 2 * one
-    assert da.diffattn_prefill_workspace_bytes(2, 77, 3, rope=2) == 2 * (-(-2 * 77 * 3 * 128 // 256) * 256)
-    assert da.diffattn_prefill_workspace_bytes(1, 4096, 16) == 0  # no rope: nothing to rotate
+    assert da.diffattn_prefill_workspace_bytes(1, 4096, 16, rope=1) == 2 * one + _vt_bytes(1, 4096, 16)
+    assert da.diffattn_prefill_workspace_bytes(2, 77, 3, rope=2) == (2 * (-(-2 * 77 * 3 * 128 // 256) * 256)
+                                                                    + _vt_bytes(2, 77, 3))
+    assert da.diffattn_prefill_workspace_bytes(1, 4096, 16) == _vt_bytes(1, 4096, 16)  # no rope: V^T tiles only
     assert da.diffattn_prefill_workspace_bytes(0, 4096, 16, rope=1) == 0
     assert da.diffattn_prefill_workspace_bytes(1, (1 << 22) + 1, 16, rope=1) == 0
-    assert da._lib.diffattn_prefill_workspace_bytes(None, 1, 128, 2) == 0
+    assert da._lib.diffattn_prefill_workspace_bytes(None, 1, 128, 2) == _vt_bytes(1, 128, 2)  # NULL options: plain
 
 
 @pytest.mark.parametrize("opt,kw,rc", [
