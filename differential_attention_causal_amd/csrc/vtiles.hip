@@ -19,39 +19,55 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One workgroup per tile.  Thread t converts keys 4kg .. 4kg+3 (kg = t % 8) of
-// channels 4cg .. 4cg+3 (cg = t / 8): four 8-byte loads, four 8-byte stores of
-// four keys of one channel each.  A wave's stores cover eight 64-byte rows.
+// One workgroup per tile, 16-byte accesses both ways with the transposition
+// in LDS.  Loads: the tile's 32 key rows are 512 16-byte chunks (8 channels
+// each), chunks t and t + 256 for thread t, consecutive threads on
+// consecutive chunks of a row.  Each thread writes its 2 x 8 converted values
+// into LDS at [channel][key position] (rows padded to 68 bytes, which spreads
+// the 16 channels a wave writes at once over distinct banks), then reads
+// back two 16-byte output chunks (eight keys of one channel, four 4-byte
+// reads) and stores them to consecutive addresses.
+constexpr int kLdsRow = 68;  // bytes per channel row in LDS: 64 + 4 of padding
+
 __global__ void __launch_bounds__(kThreads) vtiles_kernel(VTilesArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kDv * kLdsRow];
   const int64_t g = blockIdx.x;
   const int j = (int)(g % a.ntiles);
   const int64_t bh = g / a.ntiles;
   const int h = (int)(bh % a.H);
   const int b = (int)(bh / a.H);
-  const int t = threadIdx.x, kg = t & 7, cg = t >> 3;
-  const uint16_t* src = a.v + (int64_t)b * a.sv.b + (int64_t)h * a.sv.h + 4 * cg;
-  u32x2 w[4];
+  const int t = threadIdx.x;
+  const uint16_t* src = a.v + (int64_t)b * a.sv.b + (int64_t)h * a.sv.h;
+  u32x4 w[2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int key = 32 * j + 4 * kg + r;
-    w[r] = key < a.T ? *reinterpret_cast<const u32x2*>(src + (int64_t)key * a.sv.t) : u32x2{0, 0};
+  for (int u = 0; u < 2; ++u) {
+    const int c = t + 256 * u;
+    const int key = 32 * j + (c >> 4);
+    w[u] = key < a.T ? *reinterpret_cast<const u32x4*>(src + (int64_t)key * a.sv.t + 8 * (c & 15))
+                     : u32x4{0, 0, 0, 0};
   }
-  float e[4][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    e[r][0] = bf16_lo(w[r].x);
-    e[r][1] = bf16_hi(w[r].x);
-    e[r][2] = bf16_lo(w[r].y);
-    e[r][3] = bf16_hi(w[r].y);
+  for (int u = 0; u < 2; ++u) {
+    const int c = t + 256 * u;
+    const int kr = c >> 4, ch0 = 8 * (c & 15);
+    // position of key kr in its row: bits 2 and 3 swapped (see the file header)
+    const int pos = (kr & 16) | ((kr & 4) << 1) | ((kr & 8) >> 1) | (kr & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 lo = (_Float16)bf16_lo(w[u][i]), hi = (_Float16)bf16_hi(w[u][i]);
+      *reinterpret_cast<_Float16*>(lds + (ch0 + 2 * i) * kLdsRow + pos * 2) = lo;
+      *reinterpret_cast<_Float16*>(lds + (ch0 + 2 * i + 1) * kLdsRow + pos * 2) = hi;
+    }
   }
+  __syncthreads();
   char* dst = reinterpret_cast<char*>(a.out) + g * kVtTileBytes;
-  const int pos4 = kVPos(kg);  // position of the four keys, in units of 4
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int row = 4 * cg + c;
-    const int chunk = (pos4 >> 1) ^ ((row >> 2) & 3);
-    f16x4 hv = {(_Float16)e[0][c], (_Float16)e[1][c], (_Float16)e[2][c], (_Float16)e[3][c]};
-    *reinterpret_cast<f16x4*>(dst + row * 64 + chunk * 16 + (pos4 & 1) * 8) = hv;
+  for (int u = 0; u < 2; ++u) {
+    const int q = t + 256 * u;                   // output chunk: row q / 4, stored chunk q % 4
+    const int row = q >> 2;
+    const int lc = (q & 3) ^ ((row >> 2) & 3);   // the logical chunk stored there
+    const uint32_t* r = reinterpret_cast<const uint32_t*>(lds + row * kLdsRow + lc * 16);
+    *reinterpret_cast<u32x4*>(dst + q * 16) = u32x4{r[0], r[1], r[2], r[3]};
   }
 }
 
