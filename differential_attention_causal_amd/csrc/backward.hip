@@ -14,9 +14,9 @@
 // product serves both maps.
 //
 // Kernels (all deterministic, no atomics):
-//   bwd_pre_kernel     per row: do (fp16), D_1, D_2; gain/lambda partials
+//   bwd_pre_kernel     per row: do (fp16), D_1, D_2; gain/lambda partials; the
+//                      fp16 copies of Q_1, Q_2, K_1, K_2, V in the workspace
 //   bwd_reduce_kernel  per head: sum of the partials
-//   bwd_cast_kernel    fp16 copies of Q_1, Q_2, K_1, K_2, V in the workspace
 //   bwd_dq_kernel      queries own lanes (the forward's orientation): recompute
 //                      S^T, P^T from the saved log-sum-exp, dP^T = V dO^T,
 //                      dQ^T += K^T dS^T
@@ -60,8 +60,8 @@ __device__ __forceinline__ int swz8(int r) { return (((r >> 1) & 1) << 2) | ((r 
 
 // ---------------------------------------------------------------------------
 // Per row: the GroupNorm backward, do, D_1 = rowsum(do O_1),
-// D_2 = rowsum(-lambda do O_2), and partial sums of dgain and dlambda over a
-// chunk of kBwdRowsPerChunk rows of one head.  Sixteen lanes per row (eight
+// D_2 = rowsum(-lambda do O_2), partial sums of dgain and dlambda over a
+// chunk of kBwdRowsPerChunk rows of one head, and the row's fp16 input copies.  Sixteen lanes per row (eight
 // channels each), four rows per wave at a time; row sums are reduced within
 // the 16-lane DPP row in four steps.
 
@@ -105,6 +105,36 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BackwardArgs a) {
     const int rbt = chunk * kBwdRowsPerChunk + pass * kRowsPerPass + wave * 4 + grp;
     if (rbt >= BT) continue;  // per-lane; the DPP rows of a wave are independent
     const int64_t off = ((int64_t)rbt * a.H + h) * kDv + 8 * li;
+    // fp16 copies of this row's inputs for the product kernels (exact for |x|
+    // in [2^-14, 65504), like every fp16 operand of the products): V's eight
+    // channels 8li.., and two 8-dim chunks of Q_1, Q_2, K_1 or K_2 (tensor
+    // li / 4, chunks li % 4 and li % 4 + 4).
+    {
+      const int bb = rbt / a.T, tt = rbt - bb * a.T;
+      const int64_t row = (int64_t)rbt * a.H + h;
+      const int m = li >> 2, c0 = li & 3;
+      const uint16_t* base = m == 0 ? a.q1 : m == 1 ? a.q2 : m == 2 ? a.k1 : a.k2;
+      const Strides& st = m == 0 ? a.sq1 : m == 1 ? a.sq2 : m == 2 ? a.sk1 : a.sk2;
+      uint16_t* dst = m == 0 ? a.q1h : m == 1 ? a.q2h : m == 2 ? a.k1h : a.k2h;
+      const uint16_t* src = base + (int64_t)bb * st.b + (int64_t)tt * st.t + (int64_t)h * st.h;
+      const uint16_t* vsrc = a.v + (int64_t)bb * a.sv.b + (int64_t)tt * a.sv.t + (int64_t)h * a.sv.h + 8 * li;
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(src + 8 * c0);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 8 * (c0 + 4));
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(vsrc);
+      f16x8 h0, h1, hv8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h0[2 * i] = (_Float16)bf16_lo(w0[i]);
+        h0[2 * i + 1] = (_Float16)bf16_hi(w0[i]);
+        h1[2 * i] = (_Float16)bf16_lo(w1[i]);
+        h1[2 * i + 1] = (_Float16)bf16_hi(w1[i]);
+        hv8[2 * i] = (_Float16)bf16_lo(wv[i]);
+        hv8[2 * i + 1] = (_Float16)bf16_hi(wv[i]);
+      }
+      *reinterpret_cast<f16x8*>(dst + row * kDqk + 8 * c0) = h0;
+      *reinterpret_cast<f16x8*>(dst + row * kDqk + 8 * (c0 + 4)) = h1;
+      *reinterpret_cast<f16x8*>(a.vh + row * kDv + 8 * li) = hv8;
+    }
     float o1[8], o2[8], dy[8], x[8];
     {
       const f32x4 a0 = *reinterpret_cast<const f32x4*>(a.o1n + off), a1 = *reinterpret_cast<const f32x4*>(a.o1n + off + 4);
@@ -205,37 +235,6 @@ __global__ void __launch_bounds__(192) bwd_reduce_kernel(BackwardArgs a) {
     a.dgain[(int64_t)h * kDv + t] = s;
   else
     a.dlam[h] = s;
-}
-
-// fp16 copies of Q_1, Q_2, K_1, K_2 and V, contiguous [B, T, H, d] (exact for
-// |x| in [2^-14, 65504), like every fp16 operand of the products).  blockIdx.y
-// picks the tensor (0 .. 3 the 64-dim inputs, 4 V), so a wave streams
-// consecutive 16-byte chunks of one tensor: 8 chunks per (b, t, h) row of a
-// 64-dim input, 16 of V; one thread converts 8 elements.
-__global__ void __launch_bounds__(256) bwd_cast_kernel(BackwardArgs a) {
-  const int m = (int)blockIdx.y;
-  const int per_row = m < 4 ? 8 : 16;  // chunks per row
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t rows = (int64_t)a.B * a.T * a.H;
-  if (g >= rows * per_row) return;
-  const int64_t row = g / per_row;
-  const int ch = (int)(g - row * per_row);
-  const int h = (int)(row % a.H);
-  const int64_t bt = row / a.H;
-  const int t = (int)(bt % a.T), b = (int)(bt / a.T);
-  const uint16_t* base = m == 0 ? a.q1 : m == 1 ? a.q2 : m == 2 ? a.k1 : m == 3 ? a.k2 : a.v;
-  const Strides& st = m == 0 ? a.sq1 : m == 1 ? a.sq2 : m == 2 ? a.sk1 : m == 3 ? a.sk2 : a.sv;
-  uint16_t* out = m == 0 ? a.q1h : m == 1 ? a.q2h : m == 2 ? a.k1h : m == 3 ? a.k2h : a.vh;
-  const uint16_t* src = base + (int64_t)b * st.b + (int64_t)t * st.t + (int64_t)h * st.h + 8 * ch;
-  uint16_t* dst = out + row * (8 * per_row) + 8 * ch;
-  const u32x4 w = *reinterpret_cast<const u32x4*>(src);
-  f16x8 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[2 * i] = (_Float16)bf16_lo(w[i]);
-    o[2 * i + 1] = (_Float16)bf16_hi(w[i]);
-  }
-  *reinterpret_cast<f16x8*>(dst) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -704,9 +703,6 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   hipError_t e = launch_kernel(bwd_pre_kernel, dim3((unsigned)a.nchunks, (unsigned)a.H), dim3(256), stream, a);
   if (e != hipSuccess) return e;
   if ((e = launch_kernel(bwd_reduce_kernel, dim3((unsigned)a.H), dim3(192), stream, a)) != hipSuccess) return e;
-  const int64_t chunks = (int64_t)a.B * a.T * a.H * 16;  // the most of any tensor (V)
-  e = launch_kernel(bwd_cast_kernel, dim3((unsigned)((chunks + 255) / 256), 5), dim3(256), stream, a);
-  if (e != hipSuccess) return e;
   const int64_t nqb = (a.T + kRows - 1) / kRows;
   const int64_t blocks = nqb * a.B * a.H;
   e = launch_kernel(bwd_dq_kernel, dim3((unsigned)((nqb + 1) / 2 * a.B * a.H)), dim3(512), stream, a);
