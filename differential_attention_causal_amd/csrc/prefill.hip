@@ -418,9 +418,14 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
   wait_vm<0>();  // the zero-filling DMAs past the last tile, before the merge reuses the stages
   __syncthreads();
 
-  merge_out<kTrain>(a, smem, grp, wq, lane, wave_live, *lam_s, b, head, q, hf, m1, l1, m2, l2, O1, O2);
-  if (grp != 0 || !wave_live) return;
-  norm_store(a, b, head, q, hf, O1, reinterpret_cast<const float*>(gain_s));
+  if constexpr (kTrain) {
+    merge_out<kTrain>(a, smem, grp, wq, lane, wave_live, *lam_s, b, head, q, hf, m1, l1, m2, l2, O1, O2);
+    if (grp != 0 || !wave_live) return;
+    norm_store(a, b, head, q, hf, O1, reinterpret_cast<const float*>(gain_s));
+  } else {
+    merge_norm_split(a, smem, grp, wq, lane, wave_live, *lam_s, b, head, q, hf, m1, l1, m2, l2, O1, O2,
+                     reinterpret_cast<const float*>(gain_s));
+  }
 }
 
 // Persistent form: workgroup w = r * B*H + bh runs the query blocks of row r

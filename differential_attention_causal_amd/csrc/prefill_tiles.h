@@ -261,6 +261,44 @@ __device__ __forceinline__ void rope_query(bf16x8 (&q1)[4], bf16x8 (&q2)[4], int
   }
 }
 
+// GroupNorm statistics of a query's 128 channels, taken as two halves of 64:
+// channel blocks 2h and 2h + 1 (cb) of the lane pair holding the query.
+// half_stats: the half's mean and sum of squared deviations from it
+// (two-pass), added over the lane pair.  combine_halves: the mean and the
+// variance of all 128 by the pairwise update for two equal halves, var * 128
+// = M2_0 + M2_1 + 32 (mu_0 - mu_1)^2, whose operations are symmetric in the
+// halves.  Every kernel normalises with these two, so outputs that agree
+// before the norm agree after it bit for bit, whichever kernel (or wave group,
+// when two groups finish one half each) took the statistics.
+template <int h>
+__device__ __forceinline__ f32x2 half_stats(const f32x16 (&O)[4]) {
+  float sum = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += O[2 * h + blk][i];
+  sum += __shfl_xor(sum, 32);
+  const float mu = sum * (1.0f / 64);
+  float m2 = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float d = O[2 * h + blk][i] - mu;
+      m2 += d * d;
+    }
+  m2 += __shfl_xor(m2, 32);
+  return f32x2{mu, m2};
+}
+
+// (mean, 1 / sqrt(var + eps)) from the two halves' statistics (either order).
+__device__ __forceinline__ f32x2 combine_halves(f32x2 x, f32x2 y, float eps) {
+  const float dmu = x[0] - y[0];
+  const float mean = (x[0] + y[0]) * 0.5f;
+  const float var = (x[1] + y[1] + 32.0f * (dmu * dmu)) * (1.0f / kDv);
+  return f32x2{mean, 1.0f / __builtin_sqrtf(var + eps)};
+}
+
 // GroupNorm over the 128 channels of the query (o in O, lane (hf, lq)
 // holding channels 32cb + 8(i/4) + 4hf + i%4, its partner lane the other 64),
 // then the stores.  gain(cb, r4): the head's gain of channels 32cb + 8r4 + 4hf
@@ -268,24 +306,8 @@ __device__ __forceinline__ void rope_query(bf16x8 (&q1)[4], bf16x8 (&q2)[4], int
 template <class GainFn>
 __device__ __forceinline__ void norm_store_g(const PrefillArgs& a, int b, int head, int q, int hf, f32x16 (&O)[4],
                                              GainFn gain) {
-  float sum = 0.f;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sum += O[cb][i];
-  sum += __shfl_xor(sum, 32);
-  const float mu = sum * (1.0f / kDv);
-  float ss = 0.f;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float d = O[cb][i] - mu;
-      ss += d * d;
-    }
-  }
-  ss += __shfl_xor(ss, 32);
-  const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / kDv) + a.eps);
+  const f32x2 mi = combine_halves(half_stats<0>(O), half_stats<1>(O), a.eps);
+  const float mu = mi[0], inv = mi[1];
 
   if (q >= a.T) return;
   const int64_t row = (((int64_t)b * a.T + q) * a.H + head) * kDv;
@@ -450,6 +472,127 @@ __device__ __forceinline__ void merge_out(const PrefillArgs& a, char* smem, int 
 #pragma unroll
       for (int i = 0; i < 16; ++i) O1[cb][i] += mo[slot(cb, i)];
   }
+}
+
+// merge_out and the GroupNorm epilogue (inference outputs) with the work split
+// between the two wave groups by channel: group g finishes channel blocks
+// cb = 2g, 2g + 1 of its queries.  After the (m, l) exchange each group forms
+// its own weighted part of o for all four blocks, as merge_out does; the two
+// blocks it does not finish cross LDS to the other group as 16-byte vectors,
+// and each group adds the other's part into its two blocks (the same sums as
+// merge_out's, in commutative order).  GroupNorm then needs the statistics of
+// all 128 channels: each group takes its half's (half_stats), the groups
+// exchange them once, and both combine them (combine_halves, symmetric in the
+// halves), so both get the statistics norm_store_g would, bit for bit.  Each
+// group then normalises and stores its 64 channels.  Every thread calls it
+// (the barriers are unconditional).
+__device__ __forceinline__ void merge_norm_split(const PrefillArgs& a, char* smem, int grp, int wq, int lane,
+                                                 bool live, float lam, int b, int head, int q, int hf, float m1,
+                                                 float l1, float m2, float l2, f32x16 (&O1)[4],
+                                                 const f32x16 (&O2)[4], const float* gain_s) {
+  f32x4* xo = reinterpret_cast<f32x4*>(smem);            // [sender][wave][block][r4][lane]
+  f32x4* ml = reinterpret_cast<f32x4*>(smem + kMergeO);  // [group][wave][lane]: m1, l1, m2, l2
+  f32x2* st = reinterpret_cast<f32x2*>(smem + kMergeO);  // reused: [group][wave][lane]: mean, M2
+  static_assert(2 * 4 * 2 * 4 * 64 * 16 <= kMergeO, "exchange buffer");
+  auto xslot = [&](int sender, int blk, int r4) { return (((sender * 4 + wq) * 2 + blk) * 4 + r4) * 64 + lane; };
+  // The register blocks are indexed with compile-time constants only (a
+  // runtime index would move the accumulators to scratch memory): each part
+  // that depends on the group runs as one of two instantiations.
+  typedef std::integral_constant<int, 0> G0;
+  typedef std::integral_constant<int, 1> G1;
+  auto send = [&](auto G) __attribute__((always_inline)) {
+    constexpr int g = decltype(G)::value;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x16& o = O1[2 * (1 - g) + blk];
+        xo[xslot(g, blk, r4)] = f32x4{o[4 * r4], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
+      }
+  };
+  // adds the other group's part and returns the 64-channel (mean, M2)
+  auto gather = [&](auto G) __attribute__((always_inline)) {
+    constexpr int g = decltype(G)::value;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 o = xo[xslot(1 - g, blk, r4)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O1[2 * g + blk][4 * r4 + r] += o[r];
+      }
+    return half_stats<g>(O1);
+  };
+  auto store = [&](auto G, float mean, float inv) __attribute__((always_inline)) {
+    constexpr int g = decltype(G)::value;
+    const int64_t row = (((int64_t)b * a.T + q) * a.H + head) * kDv;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int cb = 2 * g + blk;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ch = 32 * cb + 8 * r4 + 4 * hf;
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(gain_s + ch);
+        f32x4 o, y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          o[r] = O1[cb][4 * r4 + r];
+          y[r] = (o[r] - mean) * inv * gv[r];
+        }
+        if (a.o_pre) *reinterpret_cast<f32x4*>(a.o_pre + row + ch) = o;
+        if (a.out_f32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row + ch) = y;
+        } else {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 yb = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+          *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(a.out) + row + ch) = yb;
+        }
+      }
+    }
+  };
+
+  if (live) ml[(grp * 4 + wq) * 64 + lane] = f32x4{m1, l1, m2, l2};
+  __syncthreads();
+  if (live) {
+    const f32x4 ot = ml[((grp ^ 1) * 4 + wq) * 64 + lane];
+    const float M1 = fmaxf(m1, ot[0]);
+    const float M2 = fmaxf(m2, ot[2]);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - M1);
+    const float a2 = __builtin_amdgcn_exp2f(m2 - M2);
+    float L1 = l1 * a1 + ot[1] * __builtin_amdgcn_exp2f(ot[0] - M1);
+    float L2 = l2 * a2 + ot[3] * __builtin_amdgcn_exp2f(ot[2] - M2);
+    L1 += __shfl_xor(L1, 32);
+    L2 += __shfl_xor(L2, 32);
+    const float w1 = a1 / L1, w2 = lam * a2 / L2;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        // both products rounded before the subtraction (no FMA contraction):
+        // two identical maps at lambda = 1 cancel to exactly zero
+#pragma clang fp contract(off)
+        O1[cb][i] = O1[cb][i] * w1 - O2[cb][i] * w2;
+      }
+    if (grp == 0)
+      send(G0{});
+    else
+      send(G1{});
+  }
+  __syncthreads();  // every wave has read ml and written its blocks
+  f32x2 mine = f32x2{0.f, 0.f};
+  if (live) {
+    mine = grp == 0 ? gather(G0{}) : gather(G1{});
+    st[(grp * 4 + wq) * 64 + lane] = mine;
+  }
+  __syncthreads();
+  if (!live) return;
+  const f32x2 mi = combine_halves(mine, st[((grp ^ 1) * 4 + wq) * 64 + lane], a.eps);
+  const float mean = mi[0], inv = mi[1];
+  if (q >= a.T) return;
+  if (grp == 0)
+    store(G0{}, mean, inv);
+  else
+    store(G1{}, mean, inv);
 }
 
 // o = O1 / l1 - lam O2 / l2 into O1 (l1, l2: the row's full sums).

@@ -78,7 +78,9 @@ constexpr float kSlack = 8.0f;
 // Probabilities 2^(c s - m) of a tile as the two f16 operands of the P^T V^T
 // product, and the running sum l += their sum, taken over the rounded f16
 // values the product uses, two per instruction (dot product with (1, 1), fp32
-// accumulation).
+// accumulation).  The sixteen values go into two interleaved chains of four
+// dependent instructions, not one of eight: the wave issues in order, and the
+// end of the softmax phase otherwise waits on that chain's latency.
 __device__ __forceinline__ void softmax_probs(const f32x16& s, float c, float m, float& l, f16x8& p0, f16x8& p1) {
   float p[16];
 #pragma unroll
@@ -89,13 +91,18 @@ __device__ __forceinline__ void softmax_probs(const f32x16& s, float c, float m,
     p1[j] = (_Float16)p[8 + j];
   }
   const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-  float sum = l;
+  float d0 = l, d1 = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sum = __builtin_amdgcn_fdot2(f16x2{p0[2 * j], p0[2 * j + 1]}, one, sum, false);
-    sum = __builtin_amdgcn_fdot2(f16x2{p1[2 * j], p1[2 * j + 1]}, one, sum, false);
+  for (int j = 0; j < 4; j += 2) {
+    d0 = __builtin_amdgcn_fdot2(f16x2{p0[2 * j], p0[2 * j + 1]}, one, d0, false);
+    d1 = __builtin_amdgcn_fdot2(f16x2{p0[2 * j + 2], p0[2 * j + 3]}, one, d1, false);
   }
-  l = sum;
+#pragma unroll
+  for (int j = 0; j < 4; j += 2) {
+    d0 = __builtin_amdgcn_fdot2(f16x2{p1[2 * j], p1[2 * j + 1]}, one, d0, false);
+    d1 = __builtin_amdgcn_fdot2(f16x2{p1[2 * j + 2], p1[2 * j + 3]}, one, d1, false);
+  }
+  l = d0 + d1;
 }
 
 __device__ __forceinline__ float tile_max(const f32x16& s) {
