@@ -5,6 +5,7 @@ summaries kept under profiles/.
     python3 profile_kernels.py step            # the benchmark step (prefill + decode)
     python3 profile_kernels.py trace NAME      # one workload (bench.py --workload NAME)
     python3 profile_kernels.py pmc NAME        # HBM counters of one workload's kernel
+    python3 profile_kernels.py core NAME       # matrix-core busy, LDS and issue counters of its kernel
 
 Every profiled program is `python3 bench.py ...`, launched directly after
 rocprofv3's `--` by this process, which itself never touches the GPU.  Raw
@@ -15,7 +16,10 @@ and head against the dense bf16/fp16 MFMA peak (2516.6 TFLOP/s); decode and
 windowed kernels by the bytes they must move against 8 TB/s (bench.py's
 definitions).  Counter bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
 each scaled by what the same counter reads for a plain device copy of 1 GiB
-(bench.py --copy-calibration) measured in the same session.
+(bench.py --copy-calibration) measured in the same session.  Matrix-core
+utilisation: SQ_VALU_MFMA_BUSY_CYCLES (busy cycles summed over the SIMDs)
+over the dispatch's active cycles times the SIMD count, where the active
+cycles are GRBM_GUI_ACTIVE, which rocprofv3 reports summed over the XCDs.
 """
 from __future__ import annotations
 
@@ -284,6 +288,61 @@ def cmd_pmc(name):
     _write("%s_%s_hbm_counters.txt" % (kfile, name), lines)
 
 
+# Counter passes of `core` (at most 8 SQ counters and a GRBM one per pass).
+CORE_PASSES = (
+    ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_ANY",
+     "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"),
+    ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS",
+     "SQ_WAVES", "GRBM_GUI_ACTIVE"),
+)
+MI355X_XCDS = 8
+MI355X_SIMDS = 4 * 256
+MFMA_32X32X16_CYCLES = 32  # busy cycles per v_mfma_f32_32x32x16 (the prefill kernels' main product)
+
+
+def cmd_core(name):
+    wl, bound, work, _ = _workload_rate(name)
+    prog = ["python3", "bench.py", "--workload", name, "--steps", "3", "--warmup", "1", "--settle", "0"]
+    vals, cmds, durs = {}, [], {}
+    for i, counters in enumerate(CORE_PASSES):
+        d = os.path.join(OUT, "core_%s_%d" % (name, i))
+        _, cmd = _rocprof(["--pmc"] + list(counters), d, prog)
+        cmds.append(cmd)
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if "diffattn" not in r["Kernel_Name"]:
+                continue
+            k = short_name(r["Kernel_Name"])
+            key = (i, r.get("Dispatch_Id"))
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], {}).setdefault(key, 0.0)
+            vals[k][r["Counter_Name"]][key] += float(r["Counter_Value"])
+            durs.setdefault(k, {})[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    main = max(vals, key=lambda k: sum(durs[k].values()) / len(durs[k]))
+    v = {c: sum(d.values()) / len(d) for c, d in vals[main].items()}
+    dur = sum(durs[main].values()) / len(durs[main])
+    active = v["GRBM_GUI_ACTIVE"] / MI355X_XCDS  # cycles per XCD
+    util = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * MI355X_SIMDS)
+    lds_conf = v["SQ_LDS_BANK_CONFLICT"] / max(1.0, v["SQ_LDS_IDX_ACTIVE"] - v["SQ_LDS_BANK_CONFLICT"])
+    digest, what = _sources_digest(main)
+    lines = ["# matrix-core, LDS and issue counters of %s per dispatch, workload %s (B=%d T=%d H=%d window=%d), "
+             "from %d rocprofv3 --pmc passes" % (main, name, wl.B, wl.T, wl.H, wl.window, len(CORE_PASSES))]
+    lines += ["command_%d: %s" % (i, " ".join(c)) for i, c in enumerate(cmds)]
+    lines += ["%s: %.0f" % (c, v[c]) for c in sorted(v)]
+    lines += ["dispatch_us_under_counters: %.2f" % (dur * 1e6),
+              "active_cycles_per_xcd: %.0f (GRBM_GUI_ACTIVE / %d XCDs)" % (active, MI355X_XCDS),
+              "clock_mhz_under_counters: %.0f" % (active / dur / 1e6),
+              "mfma_busy_cycles_per_instruction: %.2f (SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_MFMA; %d for the "
+              "32x32x16 product)" % (v["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, v["SQ_INSTS_MFMA"]),
+                                     MFMA_32X32X16_CYCLES),
+              "mfma_utilisation: %.4f (busy cycles / (active cycles x %d SIMDs))" % (util, MI355X_SIMDS),
+              "lds_bank_conflict_cycles_per_access: %.4f" % lds_conf,
+              "vector_issue_per_instruction: %.2f (SQ_ACTIVE_INST_VALU / SQ_INSTS_VALU in the counters' own units, "
+              "both counting the matrix products)" % (v["SQ_ACTIVE_INST_VALU"] / max(1.0, v["SQ_INSTS_VALU"])),
+              "# kernel sources hashed: " + what,
+              "kernel_source_sha256_16: %s" % digest]
+    kfile = re.sub(r"<.*", "", main)
+    _write("%s_%s_core_counters.txt" % (kfile, name), lines)
+
+
 def _write(fname, lines):
     lines = ["# made by: python3 profile_kernels.py " + " ".join(sys.argv[1:])] + lines
     os.makedirs(PROFILES, exist_ok=True)
@@ -297,7 +356,7 @@ def _write(fname, lines):
 
 
 def main(argv):
-    if len(argv) < 2 or argv[1] not in ("step", "trace", "pmc"):
+    if len(argv) < 2 or argv[1] not in ("step", "trace", "pmc", "core"):
         print(__doc__)
         return 2
     os.makedirs(OUT, exist_ok=True)
@@ -306,9 +365,12 @@ def main(argv):
     elif argv[1] == "trace":
         for name in argv[2:]:
             cmd_trace(name)
-    else:
+    elif argv[1] == "pmc":
         for name in argv[2:]:
             cmd_pmc(name)
+    else:
+        for name in argv[2:]:
+            cmd_core(name)
     return 0
 
 
