@@ -64,7 +64,8 @@ class _Strides(ctypes.Structure):
 
 class _Options(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("kv_ring", ctypes.c_int32), ("rope", ctypes.c_int32),
-                ("rope_pos0", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("reserved", ctypes.c_int32 * 3)]
+                ("rope_pos0", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("ws_prepared", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -84,6 +85,9 @@ _lib.diffattn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(_Options), _I, 
 _lib.diffattn_fwd_prefill_ws.restype = _I
 _lib.diffattn_fwd_prefill_ws.argtypes = ([ctypes.POINTER(_Options)] + _lib.diffattn_fwd_prefill.argtypes[:-1]
                                          + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
+_lib.diffattn_prefill_prepare.restype = _I
+_lib.diffattn_prefill_prepare.argtypes = [ctypes.POINTER(_Options), _P, _P, _P, ctypes.POINTER(_Strides), _I, _I, _I,
+                                          _I, _I, _P, ctypes.c_size_t, _P]
 _lib.diffattn_fwd_decode_ex.restype = _I
 _lib.diffattn_fwd_decode_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffattn_fwd_decode.argtypes
 _lib.diffattn_fwd_decode_noalloc.restype = _I
@@ -201,12 +205,37 @@ def diffattn_fwd_prefill_ex(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, o
 
 def diffattn_fwd_prefill_ws(q1, q2, k1, k2, v, lam, gain, workspace, eps=1e-5, scale=0.0, out=None,
                             out_dtype=torch.bfloat16, o_pre=None, stream=None, window=0, rope=ROPE_NONE,
-                            rope_theta=0.0, rope_pos0=0):
+                            rope_theta=0.0, rope_pos0=0, prepared=False):
     """diffattn_fwd_prefill_ex with a caller's workspace (uint8 device tensor of
-    diffattn_prefill_workspace_bytes(...) bytes; may be None without rope)."""
-    opt = _Options(window=int(window), rope=int(rope), rope_pos0=int(rope_pos0), rope_theta=float(rope_theta))
+    diffattn_prefill_workspace_bytes(...) bytes; may be None without rope).
+    prepared: the workspace already holds what diffattn_prefill_prepare wrote
+    for these keys, values and options; only the prefill kernel runs."""
+    opt = _Options(window=int(window), rope=int(rope), rope_pos0=int(rope_pos0), rope_theta=float(rope_theta),
+                   ws_prepared=1 if prepared else 0)
     return _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream,
                     ws=workspace if workspace is not None else False)
+
+
+def diffattn_prefill_prepare(k1, k2, v, workspace, stream=None, window=0, rope=ROPE_NONE, rope_theta=0.0,
+                             rope_pos0=0):
+    """The pre-pass of diffattn_fwd_prefill_ws alone (rotated keys with rope,
+    fp16 V^T tiles) into `workspace`, for later calls with prepared=True on
+    the same k1, k2, v and options."""
+    B, T, H, d_qk = k1.shape
+    d_v = v.shape[3]
+    for t in (k1, k2, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError("k1, k2, v must be bf16 device tensors")
+    if tuple(k2.shape) != (B, T, H, d_qk) or tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError("k1, k2 must share one shape and v be [B, T, H, d_v]")
+    if workspace is None or workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise ValueError("workspace must be a uint8 device tensor")
+    opt = _Options(window=int(window), rope=int(rope), rope_pos0=int(rope_pos0), rope_theta=float(rope_theta))
+    st = (_Strides * 5)(*([_strides4(k1)] * 2 + [_strides4(t) for t in (k1, k2, v)]))
+    rc = _lib.diffattn_prefill_prepare(ctypes.byref(opt), _ptr(k1), _ptr(k2), _ptr(v), st, B, T, H, d_qk, d_v,
+                                       _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc)
+    return workspace
 
 
 def diffattn_prefill_workspace_bytes(B, T, H, rope=ROPE_NONE):

@@ -53,6 +53,7 @@ int check_common(int B, int H, int d_qk, int d_v, float lambda, float eps, float
 int check_options(const diffattn_options* opt) {
   if (!opt) return DIFFATTN_OK;
   if (opt->window < 0) return DIFFATTN_ERR_VALUE;
+  if (opt->ws_prepared != 0 && opt->ws_prepared != 1) return DIFFATTN_ERR_VALUE;
   for (int r : opt->reserved)
     if (r != 0) return DIFFATTN_ERR_VALUE;
   if (opt->rope < DIFFATTN_ROPE_NONE || opt->rope > DIFFATTN_ROPE_INTERLEAVED) return DIFFATTN_ERR_VALUE;
@@ -101,7 +102,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 108; }
+int diffattn_abi_version(void) { return 109; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -129,6 +130,57 @@ size_t rope_keys_bytes(int B, int T, int H) {
 // Bytes of the fp16 V^T tiles in the prefill workspace (vtiles.hip).
 size_t vtiles_bytes(int B, int T, int H) {
   return (size_t)B * H * ((T + 31) / 32) * diffattn::kVtTileBytes;
+}
+
+// The prefill workspace, [rotated K1, K2 (with rope)] [V^T tiles]: its size and
+// alignment checked, its pre-pass kernels launched when `launch` (else the
+// caller vouches that diffattn_prefill_prepare wrote it for these arguments),
+// and the prefill's arguments pointed at it.  The V^T tiles exist when the
+// launch plan of `a` takes them, a function of the sizes, the key and value
+// strides and the options only.
+int ws_pre_pass(diffattn::PrefillArgs& a, void* ws, size_t ws_bytes, hipStream_t hs, bool launch) {
+  const int B = a.B, T = a.T, H = a.H;
+  const size_t rope_part = a.rope.mode != 0 ? 2 * rope_keys_bytes(B, T, H) : 0;
+  if (ws_bytes < rope_part + vtiles_bytes(B, T, H) || reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return DIFFATTN_ERR_WORKSPACE;
+  if (a.rope.mode != 0) {
+    // Rotate both key tensors once into the workspace (fp16, C-contiguous);
+    // the prefill then stages them like plain keys.
+    const size_t one = rope_keys_bytes(B, T, H);
+    diffattn::RopeKeysArgs r{};
+    r.k1 = a.k1;
+    r.k2 = a.k2;
+    r.s1 = a.sk1;
+    r.s2 = a.sk2;
+    r.out1 = static_cast<uint16_t*>(ws);
+    r.out2 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + one);
+    r.B = B;
+    r.T = T;
+    r.H = H;
+    r.rope = a.rope;
+    if (launch && diffattn::launch_rope_keys(r, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
+    const diffattn::Strides kc = to_internal(contiguous(T, H, kDqk));
+    a.k1 = r.out1;
+    a.k2 = r.out2;
+    a.sk1 = kc;
+    a.sk2 = kc;
+    a.keys_rotated = 1;
+  }
+  if (diffattn::prefill_takes_vt(a)) {
+    // V converted and transposed once into fp16 V^T tiles that the prefill
+    // kernels move into LDS by DMA.
+    diffattn::VTilesArgs t{};
+    t.v = a.v;
+    t.sv = a.sv;
+    t.B = B;
+    t.T = T;
+    t.H = H;
+    t.ntiles = (T + 31) / 32;
+    t.out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + rope_part);
+    if (launch && diffattn::launch_vtiles(t, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
+    a.vt = t.out;
+  }
+  return DIFFATTN_OK;
 }
 
 // Shared by diffattn_fwd_prefill_ex, _ws and _train; `train` holds the three
@@ -189,47 +241,10 @@ int prefill_impl(const diffattn_options* opt, const void* q1, const void* q2, co
     a.lse = train[2];
   }
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  // Workspace: [rotated K1, K2 (with rope)] [V^T tiles]; checked before any launch.
-  const size_t rope_part = a.rope.mode != 0 ? 2 * rope_keys_bytes(B, T, H) : 0;
-  if (ws != nullptr &&
-      (ws_bytes < rope_part + vtiles_bytes(B, T, H) || reinterpret_cast<uintptr_t>(ws) % 256 != 0))
-    return DIFFATTN_ERR_WORKSPACE;
-  if (ws != nullptr && a.rope.mode != 0) {
-    // Rotate both key tensors once into the workspace (fp16, C-contiguous);
-    // the prefill then stages them like plain keys.
-    const size_t one = rope_keys_bytes(B, T, H);
-    diffattn::RopeKeysArgs r{};
-    r.k1 = a.k1;
-    r.k2 = a.k2;
-    r.s1 = a.sk1;
-    r.s2 = a.sk2;
-    r.out1 = static_cast<uint16_t*>(ws);
-    r.out2 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + one);
-    r.B = B;
-    r.T = T;
-    r.H = H;
-    r.rope = a.rope;
-    if (diffattn::launch_rope_keys(r, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
-    const diffattn::Strides kc = to_internal(contiguous(T, H, d_qk));
-    a.k1 = r.out1;
-    a.k2 = r.out2;
-    a.sk1 = kc;
-    a.sk2 = kc;
-    a.keys_rotated = 1;
-  }
-  if (ws != nullptr && diffattn::prefill_takes_vt(a)) {
-    // V converted and transposed once into fp16 V^T tiles that the prefill
-    // kernels move into LDS by DMA.
-    diffattn::VTilesArgs t{};
-    t.v = a.v;
-    t.sv = a.sv;
-    t.B = B;
-    t.T = T;
-    t.H = H;
-    t.ntiles = (T + 31) / 32;
-    t.out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + rope_part);
-    if (diffattn::launch_vtiles(t, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
-    a.vt = t.out;
+  if (opt && opt->ws_prepared && ws == nullptr) return DIFFATTN_ERR_WORKSPACE;
+  if (ws != nullptr) {
+    rc = ws_pre_pass(a, ws, ws_bytes, hs, !(opt && opt->ws_prepared));
+    if (rc != DIFFATTN_OK) return rc;
   }
   if (diffattn::launch_prefill(a, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
   return DIFFATTN_OK;
@@ -241,6 +256,7 @@ int diffattn_fwd_prefill_ex(const diffattn_options* opt, const void* q1, const v
                             const void* k2, const void* v, const diffattn_strides* strides, int B, int T, int H,
                             int d_qk, int d_v, float lambda, const float* lambda_per_head, const float* gain,
                             float gn_eps, float scale, void* out, int out_dtype, float* o_pre, void* stream) {
+  if (opt && opt->ws_prepared != 0) return DIFFATTN_ERR_VALUE;  // a workspace entry point's option
   return prefill_impl(opt, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head, gain, gn_eps,
                       scale, out, out_dtype, o_pre, nullptr, stream);
 }
@@ -260,6 +276,40 @@ int diffattn_fwd_prefill_ws(const diffattn_options* opt, const void* q1, const v
   if (opt && opt->rope != DIFFATTN_ROPE_NONE && workspace == nullptr) return DIFFATTN_ERR_WORKSPACE;
   return prefill_impl(opt, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head, gain, gn_eps,
                       scale, out, out_dtype, o_pre, nullptr, stream, workspace, workspace_bytes);
+}
+
+int diffattn_prefill_prepare(const diffattn_options* opt, const void* k1, const void* k2, const void* v,
+                             const diffattn_strides* strides, int B, int T, int H, int d_qk, int d_v, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!k1 || !k2 || !v) return DIFFATTN_ERR_NULL;
+  if (workspace == nullptr) return DIFFATTN_ERR_WORKSPACE;
+  int rc = check_common(B, H, d_qk, d_v, 0.0f, 0.0f, 0.0f, DIFFATTN_OUT_BF16);
+  if (rc != DIFFATTN_OK) return rc;
+  rc = check_options(opt);
+  if (rc != DIFFATTN_OK) return rc;
+  if (opt && (opt->kv_ring != 0 || opt->ws_prepared != 0)) return DIFFATTN_ERR_VALUE;
+  if (T <= 0 || T > (1 << 22)) return DIFFATTN_ERR_SHAPE;
+  if ((int64_t)((T + 127) / 128) * B * H > kMaxWorkgroups) return DIFFATTN_ERR_SHAPE;
+  if (!aligned16(k1) || !aligned16(k2) || !aligned16(v)) return DIFFATTN_ERR_LAYOUT;
+  diffattn_strides st[5];
+  for (int i = 2; i < 5; ++i) {
+    st[i] = strides ? strides[i] : contiguous(T, H, i == 4 ? d_v : d_qk);
+    if (!strides_ok(st[i])) return DIFFATTN_ERR_LAYOUT;
+  }
+  // The arguments the workspace depends on, as prefill_impl fills them.
+  diffattn::PrefillArgs a{};
+  a.k1 = static_cast<const uint16_t*>(k1);
+  a.k2 = static_cast<const uint16_t*>(k2);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sk1 = to_internal(st[2]);
+  a.sk2 = to_internal(st[3]);
+  a.sv = to_internal(st[4]);
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.window = opt ? opt->window : 0;
+  a.rope = rope_args(opt);
+  return ws_pre_pass(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream), true);
 }
 
 int diffattn_fwd_prefill_train(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
@@ -413,6 +463,7 @@ int decode_impl(const diffattn_options* opt, const void* q1, const void* q2, con
   if (rc != DIFFATTN_OK) return rc;
   rc = check_options(opt);
   if (rc != DIFFATTN_OK) return rc;
+  if (opt && opt->ws_prepared != 0) return DIFFATTN_ERR_VALUE;  // a prefill workspace option
   if (L <= 0 || L > (1 << 26)) return DIFFATTN_ERR_SHAPE;
   const bool ring = opt && opt->kv_ring != 0;
   if (ring && opt->window > L) return DIFFATTN_ERR_VALUE;

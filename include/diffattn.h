@@ -113,6 +113,11 @@ enum diffattn_rope {
  *                must hold keys already rotated (diffattn_rope_apply).
  *   rope_theta : base, finite and > 0 when rope is on.
  *   rope_pos0  : >= 0; positions must stay below 2^32.
+ *   ws_prepared: diffattn_fwd_prefill_ws only (0 or 1; must be 0 for every
+ *                other entry point).  1: the workspace already holds what
+ *                diffattn_prefill_prepare wrote for the same K1, K2, V,
+ *                strides, sizes and options, so the call skips its pre-pass
+ *                and runs the prefill kernel alone.
  *   reserved   : must be zero.
  */
 typedef struct {
@@ -121,7 +126,8 @@ typedef struct {
     int32_t rope;
     int32_t rope_pos0;
     float rope_theta;
-    int32_t reserved[3];
+    int32_t ws_prepared;
+    int32_t reserved[2];
 } diffattn_options;
 
 /* Element strides of the three outer dimensions of a [B, T, H, D] tensor. */
@@ -225,6 +231,22 @@ DIFFATTN_API int diffattn_fwd_prefill_ws(const diffattn_options* opt, const void
                                          const float* gain, float gn_eps, float scale, void* out,
                                          int out_dtype, float* o_pre, void* workspace,
                                          size_t workspace_bytes, void* stream);
+
+/*
+ * The pre-pass of diffattn_fwd_prefill_ws alone: the rotated key copies
+ * (rope on) and the fp16 V^T tiles, written to the workspace exactly as that
+ * call writes them.  A caller that runs several prefills over the same keys
+ * and values (query chunks against one cache, repeated calls) prepares once
+ * and passes opt->ws_prepared = 1 to each diffattn_fwd_prefill_ws, which then
+ * launches the prefill kernel alone.  Arguments as for diffattn_fwd_prefill_ws
+ * (strides: the five entries, of which those of K1, K2 and V are used; opt
+ * with ws_prepared 0).  Results of the prepared calls equal those of
+ * unprepared ones bit for bit.  Errors as for diffattn_fwd_prefill_ws.
+ */
+DIFFATTN_API int diffattn_prefill_prepare(const diffattn_options* opt, const void* k1, const void* k2,
+                                          const void* v, const diffattn_strides* strides, int B, int T, int H,
+                                          int d_qk, int d_v, void* workspace, size_t workspace_bytes,
+                                          void* stream);
 
 /* diffattn_fwd_decode with variants (opt may be NULL: every cached position).
  * Errors as for diffattn_fwd_prefill_ex, and DIFFATTN_ERR_VALUE for a ring
@@ -368,7 +390,8 @@ DIFFATTN_API const char* diffattn_status_string(int status);
  * the training forward and the backward pass, 104 grouped attention, 105 the
  * prefill workspace entry points (keys rotated once), 106 a larger backward
  * workspace (fp16 input copies; query diffattn_bwd_workspace_bytes again),
- * 107 diffattn_fwd_decode_noalloc, 108 V^T tiles in the prefill workspace
+ * 107 diffattn_fwd_decode_noalloc, 108 V^T tiles in the prefill workspace,
+ * 109 diffattn_prefill_prepare and diffattn_options.ws_prepared
  * (query diffattn_prefill_workspace_bytes again). */
 DIFFATTN_API int diffattn_abi_version(void);
 

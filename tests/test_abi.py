@@ -28,12 +28,12 @@ def test_header_symbols_exported():
                           "diffattn_fwd_decode_noalloc",
                           "diffattn_fwd_prefill_train", "diffattn_bwd_workspace_bytes", "diffattn_bwd_prefill",
                           "diffattn_grouped_workspace_bytes", "diffattn_fwd_grouped",
-                          "diffattn_prefill_workspace_bytes", "diffattn_fwd_prefill_ws",
+                          "diffattn_prefill_workspace_bytes", "diffattn_fwd_prefill_ws", "diffattn_prefill_prepare",
                           "diffattn_status_string", "diffattn_abi_version"}
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 108
+    assert da.diffattn_abi_version() == 109
 
 
 def test_status_strings():
@@ -112,7 +112,7 @@ def test_workspace_bytes():
 # given an invalid shape instead, so every call stops before any HIP call.
 @pytest.mark.parametrize("opt,rc", [
     (dict(window=-1), EVALUE), (dict(rope=3), EVALUE), (dict(rope=-1), EVALUE),
-    (dict(kv_ring=1), EVALUE), (dict(reserved=(0, 0, 1)), EVALUE),
+    (dict(kv_ring=1), EVALUE), (dict(reserved=(0, 1)), EVALUE), (dict(ws_prepared=1), EVALUE),
     (dict(rope=1), EVALUE), (dict(rope=2, rope_theta=-1.0), EVALUE), (dict(rope=1, rope_theta=float("inf")), EVALUE),
     (dict(rope=1, rope_theta=float("nan")), EVALUE), (dict(rope=1, rope_theta=1e4, rope_pos0=-1), EVALUE),
     (dict(window=5), ESHAPE), (dict(window=1 << 30), ESHAPE), ("null", ESHAPE), (dict(), ESHAPE),
@@ -123,7 +123,7 @@ def test_prefill_ex_options(opt, rc):
 
 
 @pytest.mark.parametrize("opt,rc", [
-    (dict(window=-7), EVALUE), (dict(rope=9), EVALUE), (dict(reserved=(2, 0, 0)), EVALUE),
+    (dict(window=-7), EVALUE), (dict(rope=9), EVALUE), (dict(reserved=(2, 0)), EVALUE), (dict(ws_prepared=1), EVALUE),
     (dict(kv_ring=1, window=101), EVALUE),
     (dict(rope=1, rope_theta=0.0), EVALUE),
     (dict(window=3), ESHAPE), (dict(kv_ring=1), ESHAPE), (dict(kv_ring=1, window=100), ESHAPE), ("null", ESHAPE),
@@ -164,20 +164,42 @@ def test_prefill_workspace_bytes():
     (dict(rope=1, rope_theta=-1.0), dict(), EVALUE),
     (dict(rope=1, rope_theta=5e5), dict(k1=A + 2), ELAYOUT),
     (dict(), dict(ws=None, T=0), ESHAPE),                        # no rope: the workspace is not needed
+    (dict(ws_prepared=1), dict(ws=None), EWS),                   # a prepared workspace must be given
+    (dict(ws_prepared=2), dict(), EVALUE),
+    (dict(ws_prepared=1), dict(wsb=_vt_bytes(1, 128, 2) - 1), EWS),
 ])
 def test_prefill_ws_rejects(opt, kw, rc):
     assert _prefill_ws(opt, **kw) == rc
 
 
+def _prepare(opt=None, **kw):
+    args = dict(k1=A, k2=A, v=A, st=None, B=1, T=128, H=2, dqk=64, dv=128, ws=A, wsb=1 << 30, stream=None)
+    args.update(kw)
+    o = None if opt is None else ctypes.byref(da._Options(**opt))
+    return da._lib.diffattn_prefill_prepare(o, *args.values())
+
+
+@pytest.mark.parametrize("opt,kw,rc", [
+    (None, dict(k2=None), ENULL), (None, dict(v=None), ENULL), (None, dict(ws=None), EWS),
+    (None, dict(T=0), ESHAPE), (None, dict(B=0), ESHAPE), (None, dict(dqk=32), EUNSUP),
+    (None, dict(v=A + 8), ELAYOUT), (None, dict(ws=A + 16), EWS), (None, dict(wsb=_vt_bytes(1, 128, 2) - 1), EWS),
+    (dict(rope=1, rope_theta=5e5), dict(wsb=_vt_bytes(1, 128, 2)), EWS),  # rotated keys need room too
+    (dict(ws_prepared=1), dict(), EVALUE), (dict(kv_ring=1), dict(), EVALUE), (dict(rope=1), dict(), EVALUE),
+    (dict(window=-2), dict(), EVALUE),
+])
+def test_prepare_rejects(opt, kw, rc):
+    assert _prepare(opt, **kw) == rc
+
+
 def test_options_layout():
-    # The C struct: five 4-byte fields then int32 reserved[3], 32 bytes.
+    # The C struct: six 4-byte fields then int32 reserved[2], 32 bytes.
     assert ctypes.sizeof(da._Options) == 32
     assert [f[0] for f in da._Options._fields_] == ["window", "kv_ring", "rope", "rope_pos0", "rope_theta",
-                                                    "reserved"]
+                                                    "ws_prepared", "reserved"]
     txt = open(HEADER).read()
     body = txt[txt.index("typedef struct {\n    int32_t window;"):txt.index("} diffattn_options;")]
     assert re.findall(r"(\w+)(?:\[\d\])?;", body) == ["window", "kv_ring", "rope", "rope_pos0", "rope_theta",
-                                                       "reserved"]
+                                                       "ws_prepared", "reserved"]
 
 
 def _rope_apply(**kw):

@@ -107,3 +107,31 @@ def test_vtiles_workspace_refused_when_short():
     ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
     with pytest.raises(RuntimeError, match="workspace"):
         da.diffattn_fwd_prefill_ws(q1, q2, k1, k2, v, 0.8, f32_dev(x["gain"]), ws)
+
+
+@pytest.mark.parametrize("B,T,H,window,rope", [(1, 300, 4, 0, da.ROPE_NONE), (2, 1000, 3, 0, da.ROPE_HALF),
+                                               (1, 4096, 2, 1000, da.ROPE_NONE),
+                                               (1, 129, 2, 300, da.ROPE_INTERLEAVED)])
+def test_prepared_workspace(B, T, H, window, rope):
+    """diffattn_prefill_prepare then diffattn_fwd_prefill_ws with the prepared
+    flag equals the unprepared call bit for bit, and one preparation serves
+    several calls with other queries over the same keys and values."""
+    _say("prepared workspace", B, T, H, "window", window, "rope", rope)
+    wl = Workload("vtp", "prefill", B=B, T=T, H=H, seed=700 + T + rope, lam=0.6)
+    x = synth.make_prefill_inputs(wl)
+    q1, q2, k1, k2, v = _dev_inputs(x)
+    gain = f32_dev(x["gain"])
+    kw = dict(eps=x["eps"], scale=x["scale"], out_dtype=torch.float32, window=window, rope=rope,
+              rope_theta=5e5 if rope else 0.0, rope_pos0=3 if rope else 0)
+    need = da.diffattn_prefill_workspace_bytes(B, T, H, rope=rope)
+    ref_ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+    da.diffattn_prefill_prepare(k1, k2, v, ws, window=window, rope=rope, rope_theta=kw["rope_theta"],
+                                rope_pos0=kw["rope_pos0"])
+    for qa, qb in ((q1, q2), (q2, q1), (q1, q1)):
+        pre_a = torch.empty((B, T, H, 128), dtype=torch.float32, device="cuda")
+        pre_b = torch.empty_like(pre_a)
+        ref = da.diffattn_fwd_prefill_ws(qa, qb, k1, k2, v, 0.6, gain, ref_ws, o_pre=pre_a, **kw)
+        got = da.diffattn_fwd_prefill_ws(qa, qb, k1, k2, v, 0.6, gain, ws, o_pre=pre_b, prepared=True, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref) and torch.equal(pre_b, pre_a)
