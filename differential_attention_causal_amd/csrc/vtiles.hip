@@ -20,13 +20,15 @@ namespace {
 constexpr int kThreads = 256;
 
 // One workgroup per tile, 16-byte accesses both ways with the transposition
-// in LDS.  Loads: the tile's 32 key rows are 512 16-byte chunks (8 channels
-// each), chunks t and t + 256 for thread t, consecutive threads on
-// consecutive chunks of a row.  Each thread writes its 2 x 8 converted values
-// into LDS at [channel][key position] (rows padded to 68 bytes, which spreads
-// the 16 channels a wave writes at once over distinct banks), then reads
-// back two 16-byte output chunks (eight keys of one channel, four 4-byte
-// reads) and stores them to consecutive addresses.
+// in LDS.  Loads: thread t takes the 16-byte chunk (t % 16) (channels
+// 8 (t % 16) .. + 7) of key rows 2 (t / 16) and 2 (t / 16) + 1, a key pair
+// that sits at adjacent positions of the tile (position bit 0 is key bit 0),
+// so each of its channels becomes one 4-byte word of two fp16 keys, written
+// into LDS at [channel][key position] (rows padded to 68 bytes: the words a
+// wave writes at once fall on distinct banks but for pairs of channels 64
+// apart).  Then each thread reads back two 16-byte output chunks (eight keys
+// of one channel, four 4-byte reads) and stores them to consecutive
+// addresses.
 constexpr int kLdsRow = 68;  // bytes per channel row in LDS: 64 + 4 of padding
 
 __global__ void __launch_bounds__(kThreads) vtiles_kernel(VTilesArgs a) {
@@ -38,26 +40,22 @@ __global__ void __launch_bounds__(kThreads) vtiles_kernel(VTilesArgs a) {
   const int b = (int)(bh / a.H);
   const int t = threadIdx.x;
   const uint16_t* src = a.v + (int64_t)b * a.sv.b + (int64_t)h * a.sv.h;
+  const int kr = 2 * (t >> 4), ch0 = 8 * (t & 15);  // key rows kr, kr + 1 of the tile; first channel
   u32x4 w[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int c = t + 256 * u;
-    const int key = 32 * j + (c >> 4);
-    w[u] = key < a.T ? *reinterpret_cast<const u32x4*>(src + (int64_t)key * a.sv.t + 8 * (c & 15))
-                     : u32x4{0, 0, 0, 0};
+    const int key = 32 * j + kr + u;
+    w[u] = key < a.T ? *reinterpret_cast<const u32x4*>(src + (int64_t)key * a.sv.t + ch0) : u32x4{0, 0, 0, 0};
   }
+  // position of key kr in its row: bits 2 and 3 swapped (see the file header); kr + 1 follows it
+  const int pos = (kr & 16) | ((kr & 4) << 1) | ((kr & 8) >> 1) | (kr & 3);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = t + 256 * u;
-    const int kr = c >> 4, ch0 = 8 * (c & 15);
-    // position of key kr in its row: bits 2 and 3 swapped (see the file header)
-    const int pos = (kr & 16) | ((kr & 4) << 1) | ((kr & 8) >> 1) | (kr & 3);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const _Float16 lo = (_Float16)bf16_lo(w[u][i]), hi = (_Float16)bf16_hi(w[u][i]);
-      *reinterpret_cast<_Float16*>(lds + (ch0 + 2 * i) * kLdsRow + pos * 2) = lo;
-      *reinterpret_cast<_Float16*>(lds + (ch0 + 2 * i + 1) * kLdsRow + pos * 2) = hi;
-    }
+  for (int i = 0; i < 4; ++i) {
+    // channels ch0 + 2i (low halves) and ch0 + 2i + 1 (high halves) of both keys
+    const f16x2 lo = {(_Float16)bf16_lo(w[0][i]), (_Float16)bf16_lo(w[1][i])};
+    const f16x2 hi = {(_Float16)bf16_hi(w[0][i]), (_Float16)bf16_hi(w[1][i])};
+    *reinterpret_cast<f16x2*>(lds + (ch0 + 2 * i) * kLdsRow + pos * 2) = lo;
+    *reinterpret_cast<f16x2*>(lds + (ch0 + 2 * i + 1) * kLdsRow + pos * 2) = hi;
   }
   __syncthreads();
   char* dst = reinterpret_cast<char*>(a.out) + g * kVtTileBytes;
