@@ -120,3 +120,82 @@ def test_identical_maps_cancel():
     np.testing.assert_allclose(g["dq1"], -g["dq2"], rtol=0, atol=1e-12)
     np.testing.assert_allclose(g["dk1"], -g["dk2"], rtol=0, atol=1e-12)
     np.testing.assert_allclose(g["dv"], 0, atol=1e-12)
+
+
+# Rotary embedding and sliding window (Motif 2.6B explainer, "The block";
+# picx.dev summary of the Motif 3 report, section 2.1).
+VARIANTS = [dict(window=4), dict(rope=1, rope_theta=500.0, rope_pos0=3), dict(rope=2, rope_theta=50.0),
+            dict(window=3, rope=1, rope_theta=1e4, rope_pos0=11)]
+
+
+@pytest.mark.parametrize("var", VARIANTS)
+def test_forward_variants_match_c_oracle(var):
+    x = _inputs(B=2, T=14, H=2, seed=77)
+    g = bwd.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"], x["dy"],
+                     **var)
+    o, y = oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"],
+                          **var)
+    np.testing.assert_allclose(g["o"], o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["y"], y, rtol=0, atol=1e-10)
+
+
+def test_rope_torch_matches_c_rotation():
+    x = _inputs(B=1, T=9, H=2, seed=78)
+    for mode in (1, 2):
+        r = bwd.rope_torch(bwd._f64(x["q1"]), mode, 500.0, 7).numpy()
+        np.testing.assert_allclose(r, oracle.rope(x["q1"], mode, 500.0, pos0=7), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("var", VARIANTS)
+def test_variant_gradients_match_central_differences(var):
+    x = _inputs(B=1, T=9, H=2, seed=79)
+    g = bwd.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"], x["dy"],
+                     **var)
+    rng = np.random.default_rng(9)
+    base = {n: bwd._f64(x[n]) for n in ("q1", "q2", "k1", "k2", "v")}
+    lam = torch.tensor(x["lam"], dtype=torch.float64)
+    gain = torch.tensor(np.asarray(x["gain"], np.float64))
+    dy = torch.from_numpy(x["dy"])
+
+    def f(t):
+        y, _ = bwd.forward_torch(t["q1"], t["q2"], t["k1"], t["k2"], t["v"], lam, gain, x["eps"], x["scale"], **var)
+        return float((y * dy).sum())
+
+    h = 1e-6
+    for name in ("q1", "q2", "k1", "k2", "v"):
+        d = torch.from_numpy(rng.standard_normal(base[name].shape))
+        fd = (f(dict(base, **{name: base[name] + h * d})) - f(dict(base, **{name: base[name] - h * d}))) / (2 * h)
+        an = float((torch.from_numpy(g["d" + name]) * d).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+@pytest.mark.parametrize("var", [VARIANTS[0], VARIANTS[3]])
+def test_variant_gradient_matches_c_oracle_difference_quotient(var):
+    # As test_gradient_matches_c_oracle_difference_quotient, through the C
+    # oracle's own rotation and window.
+    x = _inputs(B=1, T=10, H=2, seed=80)
+    g = bwd.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"], x["dy"],
+                     **var)
+    for name, idx in (("k2", (0, 3, 1, 5)), ("q1", (0, 7, 0, 2)), ("k1", (0, 6, 0, 1)), ("v", (0, 4, 1, 9))):
+        bits = x[name][idx]
+        up, dn = x[name].copy(), x[name].copy()
+        up[idx], dn[idx] = bits + 1, bits - 1
+        vals = synth.bf16_bits_to_f32(np.array([dn[idx], up[idx]], np.uint16)).astype(np.float64)
+
+        def loss(xx):
+            _, y = oracle.prefill(xx["q1"], xx["q2"], xx["k1"], xx["k2"], xx["v"], x["lam"], x["gain"], x["eps"],
+                                  x["scale"], **var)
+            return float((y * x["dy"]).sum())
+
+        fd = (loss(dict(x, **{name: up})) - loss(dict(x, **{name: dn}))) / (vals[1] - vals[0])
+        an = g["d" + name][idx]
+        assert abs(fd - an) <= 2e-3 * max(1.0, abs(an)), (name, var, fd, an)
+
+
+def test_window_covering_everything_equals_causal():
+    x = _inputs(B=1, T=8, H=2, seed=81)
+    a = _grads(x)
+    b = bwd.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"], x["dy"],
+                     window=8)
+    for n in ("dq1", "dq2", "dk1", "dk2", "dv", "dlam", "dgain"):
+        np.testing.assert_array_equal(a[n], b[n])
