@@ -99,12 +99,16 @@ _lib.diffattn_rope_apply.argtypes = [_P, ctypes.POINTER(_Strides), _P, ctypes.PO
                                      _I, ctypes.c_float, _I, _P, _P]
 _lib.diffattn_fwd_prefill_train.restype = _I
 _lib.diffattn_fwd_prefill_train.argtypes = _lib.diffattn_fwd_prefill.argtypes[:-1] + [_P, _P, _P, _P]
+_lib.diffattn_fwd_prefill_train_ex.restype = _I
+_lib.diffattn_fwd_prefill_train_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffattn_fwd_prefill_train.argtypes
 _lib.diffattn_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.diffattn_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
 _lib.diffattn_bwd_prefill.restype = _I
 _lib.diffattn_bwd_prefill.argtypes = ([_P, _P, _P, _P, _P, ctypes.POINTER(_Strides), _I, _I, _I, _I, _I, ctypes.c_float,
                                       _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P, _I]
                                      + [_P] * 7 + [_P, ctypes.c_size_t, _P])
+_lib.diffattn_bwd_prefill_ex.restype = _I
+_lib.diffattn_bwd_prefill_ex.argtypes = [ctypes.POINTER(_Options)] + _lib.diffattn_bwd_prefill.argtypes
 _lib.diffattn_grouped_workspace_bytes.restype = ctypes.c_size_t
 _lib.diffattn_grouped_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.diffattn_fwd_grouped.restype = _I
@@ -277,7 +281,9 @@ def _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pr
     st = (_Strides * 5)(*[_strides4(t) for t in (q1, q2, k1, k2, v)])
     args = (_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, B, T, H, d_qk, d_v, lam_v, _ptr(lam_t),
             _ptr(gain), float(eps), float(scale), _ptr(out), _out_code(out.dtype), _ptr(o_pre), _stream(stream))
-    if train is not None:
+    if train is not None and opt is not None:
+        rc = _lib.diffattn_fwd_prefill_train_ex(ctypes.byref(opt), *args[:-1], *(_ptr(t) for t in train), args[-1])
+    elif train is not None:
         rc = _lib.diffattn_fwd_prefill_train(*args[:-1], *(_ptr(t) for t in train), args[-1])
     elif opt is None:
         rc = _lib.diffattn_fwd_prefill(*args)
@@ -399,17 +405,27 @@ def diffattn_rope_apply(x, mode, theta, pos0=0, pos_start=None, out=None, stream
     return out
 
 
+def _variant_options(window, rope, rope_theta, rope_pos0):
+    if int(window) == 0 and int(rope) == ROPE_NONE:
+        return None
+    return _Options(window=int(window), rope=int(rope), rope_pos0=int(rope_pos0), rope_theta=float(rope_theta))
+
+
 def diffattn_fwd_prefill_train(q1, q2, k1, k2, v, lam, gain, eps=1e-5, scale=0.0, out=None,
-                               out_dtype=torch.bfloat16, o_pre=None, stream=None):
+                               out_dtype=torch.bfloat16, o_pre=None, stream=None, window=0, rope=ROPE_NONE,
+                               rope_theta=0.0, rope_pos0=0):
     """Causal prefill that also returns what diffattn_bwd_prefill needs:
     (out, o1, o2, lse) with o1, o2 fp32 [B, T, H, 128] (each map's normalised
-    output) and lse fp32 [B, T, H, 2] (base-2 log-sum-exp per map)."""
+    output) and lse fp32 [B, T, H, 2] (base-2 log-sum-exp per map).  window,
+    rope, rope_theta, rope_pos0: the variants (diffattn_fwd_prefill_train_ex);
+    give the backward the same ones."""
+    opt = _variant_options(window, rope, rope_theta, rope_pos0)
     B, T, H, _ = q1.shape
     with _alloc_on(stream):
         o1 = torch.empty((B, T, H, D_V), dtype=torch.float32, device=q1.device)
         o2 = torch.empty_like(o1)
         lse = torch.empty((B, T, H, 2), dtype=torch.float32, device=q1.device)
-    out = _prefill(None, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream,
+    out = _prefill(opt, q1, q2, k1, k2, v, lam, gain, eps, scale, out, out_dtype, o_pre, stream,
                    train=(o1, o2, lse))
     return out, o1, o2, lse
 
@@ -419,12 +435,15 @@ def diffattn_bwd_workspace_bytes(B: int, T: int, H: int, d_v: int = D_V) -> int:
 
 
 def diffattn_bwd_prefill(q1, q2, k1, k2, v, lam, gain, o1, o2, lse, dy, eps=1e-5, scale=0.0, workspace=None,
-                         grads=None, stream=None):
+                         grads=None, stream=None, window=0, rope=ROPE_NONE, rope_theta=0.0, rope_pos0=0):
     """Gradients of sum(y * dy) for the causal prefill.  dy: bf16 or fp32
     [B, T, H, 128], contiguous.  o1, o2, lse: diffattn_fwd_prefill_train's
-    outputs.  Returns a dict of fp32 tensors dq1, dq2, dk1, dk2 ([B, T, H, 64]),
-    dv ([B, T, H, 128]), dlam ([H], per head) and dgain ([H, 128]); pass
-    `grads` (such a dict) to write into preallocated tensors."""
+    outputs (run with the same window and rope options).  Returns a dict of
+    fp32 tensors dq1, dq2, dk1, dk2 ([B, T, H, 64], the gradients of the
+    unrotated inputs), dv ([B, T, H, 128]), dlam ([H], per head) and dgain
+    ([H, 128]); pass `grads` (such a dict) to write into preallocated
+    tensors."""
+    opt = _variant_options(window, rope, rope_theta, rope_pos0)
     B, T, H, d_qk = q1.shape
     d_v = v.shape[3]
     for t in (q1, q2, k1, k2, v):
@@ -451,11 +470,14 @@ def diffattn_bwd_prefill(q1, q2, k1, k2, v, lam, gain, o1, o2, lse, dy, eps=1e-5
     lam_v, lam_t = _lambda_args(lam, H, q1.device)
     st = (_Strides * 5)(*[_strides4(t) for t in (q1, q2, k1, k2, v)])
     g = grads
-    rc = _lib.diffattn_bwd_prefill(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, B, T, H, d_qk, d_v, lam_v,
-                                   _ptr(lam_t), _ptr(gain), float(eps), float(scale), _ptr(o1), _ptr(o2), _ptr(lse),
-                                   _ptr(dy), _out_code(dy.dtype), _ptr(g["dq1"]), _ptr(g["dq2"]), _ptr(g["dk1"]),
-                                   _ptr(g["dk2"]), _ptr(g["dv"]), _ptr(g["dlam"]), _ptr(g["dgain"]),
-                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    args = (_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), st, B, T, H, d_qk, d_v, lam_v, _ptr(lam_t), _ptr(gain),
+            float(eps), float(scale), _ptr(o1), _ptr(o2), _ptr(lse), _ptr(dy), _out_code(dy.dtype), _ptr(g["dq1"]),
+            _ptr(g["dq2"]), _ptr(g["dk1"]), _ptr(g["dk2"]), _ptr(g["dv"]), _ptr(g["dlam"]), _ptr(g["dgain"]),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if opt is None:
+        rc = _lib.diffattn_bwd_prefill(*args)
+    else:
+        rc = _lib.diffattn_bwd_prefill_ex(ctypes.byref(opt), *args)
     _check(rc)
     return grads
 

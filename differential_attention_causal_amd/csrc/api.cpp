@@ -102,7 +102,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 109; }
+int diffattn_abi_version(void) { return 110; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -317,11 +317,22 @@ int diffattn_fwd_prefill_train(const void* q1, const void* q2, const void* k1, c
                                float lambda, const float* lambda_per_head, const float* gain, float gn_eps,
                                float scale, void* out, int out_dtype, float* o_pre, float* o1, float* o2,
                                float* lse, void* stream) {
+  return diffattn_fwd_prefill_train_ex(nullptr, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda,
+                                       lambda_per_head, gain, gn_eps, scale, out, out_dtype, o_pre, o1, o2, lse,
+                                       stream);
+}
+
+int diffattn_fwd_prefill_train_ex(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,
+                                  const void* k2, const void* v, const diffattn_strides* strides, int B, int T,
+                                  int H, int d_qk, int d_v, float lambda, const float* lambda_per_head,
+                                  const float* gain, float gn_eps, float scale, void* out, int out_dtype,
+                                  float* o_pre, float* o1, float* o2, float* lse, void* stream) {
   if (!o1 || !o2 || !lse) return DIFFATTN_ERR_NULL;
   if (!aligned16(o1) || !aligned16(o2) || !aligned16(lse)) return DIFFATTN_ERR_LAYOUT;
+  if (opt && opt->ws_prepared != 0) return DIFFATTN_ERR_VALUE;  // a workspace entry point's option
   float* const train[3] = {o1, o2, lse};
-  return prefill_impl(nullptr, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head, gain,
-                      gn_eps, scale, out, out_dtype, o_pre, train, stream);
+  return prefill_impl(opt, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head, gain, gn_eps,
+                      scale, out, out_dtype, o_pre, train, stream);
 }
 
 namespace {
@@ -366,11 +377,25 @@ int diffattn_bwd_prefill(const void* q1, const void* q2, const void* k1, const v
                          const float* o2, const float* lse, const void* dy, int dy_dtype, float* dq1, float* dq2,
                          float* dk1, float* dk2, float* dv, float* dlambda, float* dgain, void* workspace,
                          size_t workspace_bytes, void* stream) {
+  return diffattn_bwd_prefill_ex(nullptr, q1, q2, k1, k2, v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head,
+                                 gain, gn_eps, scale, o1, o2, lse, dy, dy_dtype, dq1, dq2, dk1, dk2, dv, dlambda,
+                                 dgain, workspace, workspace_bytes, stream);
+}
+
+int diffattn_bwd_prefill_ex(const diffattn_options* opt, const void* q1, const void* q2, const void* k1,
+                            const void* k2, const void* v, const diffattn_strides* strides, int B, int T, int H,
+                            int d_qk, int d_v, float lambda, const float* lambda_per_head, const float* gain,
+                            float gn_eps, float scale, const float* o1, const float* o2, const float* lse,
+                            const void* dy, int dy_dtype, float* dq1, float* dq2, float* dk1, float* dk2, float* dv,
+                            float* dlambda, float* dgain, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q1 || !q2 || !k1 || !k2 || !v || !gain || !o1 || !o2 || !lse || !dy || !dq1 || !dq2 || !dk1 || !dk2 ||
       !dv || !dlambda || !dgain)
     return DIFFATTN_ERR_NULL;
   int rc = check_common(B, H, d_qk, d_v, lambda, gn_eps, scale, dy_dtype);
   if (rc != DIFFATTN_OK) return rc;
+  rc = check_options(opt);
+  if (rc != DIFFATTN_OK) return rc;
+  if (opt && (opt->kv_ring != 0 || opt->ws_prepared != 0)) return DIFFATTN_ERR_VALUE;
   if (T <= 0 || T > (1 << 22)) return DIFFATTN_ERR_SHAPE;
   if ((int64_t)((T + 127) / 128) * B * H > kMaxWorkgroups) return DIFFATTN_ERR_SHAPE;
   const void* ptrs[] = {q1, q2, k1, k2, v, gain, o1, o2, lse, dy, dq1, dq2, dk1, dk2, dv, dgain};
@@ -427,6 +452,8 @@ int diffattn_bwd_prefill(const void* q1, const void* q2, const void* k1, const v
   a.dstat = reinterpret_cast<float*>(ws + lay.dstat);
   a.partial = reinterpret_cast<float*>(ws + lay.partial);
   a.nchunks = lay.nchunks;
+  a.window = opt ? opt->window : 0;
+  a.rope = rope_args(opt);
   if (diffattn::launch_backward(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
   return DIFFATTN_OK;
 }

@@ -32,6 +32,7 @@
 // [2^-14, 65504)), so the scores are the same products of the inputs as the
 // forward's bf16 ones; P, dS and dO are rounded to fp16; fp32 accumulation.
 #include "kernels.h"
+#include "rope.h"
 #include "tile.h"
 
 namespace diffattn {
@@ -83,6 +84,11 @@ __device__ __forceinline__ float sum16(float x) {
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BackwardArgs a) {
   constexpr int kRowsPerPass = 4 * kWaves;  // 16: four per wave
   __shared__ float red[kRowsPerPass][kDv + 1];
+  __shared__ uint64_t rope_tab[32];
+  if (a.rope.mode != 0) {
+    if (threadIdx.x < 32) rope_tab[threadIdx.x] = rope_phase_at(a.rope, (int)threadIdx.x);
+    __syncthreads();
+  }
   const int chunk = blockIdx.x, h = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = lane >> 4, li = lane & 15;  // row within the wave's four, lane within the row
@@ -121,13 +127,42 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BackwardArgs a) {
       const u32x4 w0 = *reinterpret_cast<const u32x4*>(src + 8 * c0);
       const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 8 * (c0 + 4));
       const u32x4 wv = *reinterpret_cast<const u32x4*>(vsrc);
+      float x0[8], x1[8];
+      rope_unpack(w0, x0);
+      rope_unpack(w1, x1);
+      if (a.rope.mode != 0) {
+        // The rotary embedding at position pos0 + t, in fp32 with the
+        // forward's arithmetic (each pair (u, w) -> (u cos - w sin,
+        // u sin + w cos)), then rounded to fp16 like the forward's rotated
+        // score operands: chunk c0 pairs with chunk c0 + 4 in split-half
+        // mode, each chunk with itself in interleaved mode.
+        const uint32_t pos = a.rope.pos0 + (uint32_t)tt;
+        auto turn = [&](float& u, float& w, int pair) __attribute__((always_inline)) {
+          float cs, sn;
+          rope_cos_sin(pos, rope_tab[pair], cs, sn);
+          const float uu = u, ww = w;
+          u = uu * cs - ww * sn;
+          w = uu * sn + ww * cs;
+        };
+        if (a.rope.mode == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) turn(x0[e], x1[e], 8 * c0 + e);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            turn(x0[2 * i], x0[2 * i + 1], 4 * c0 + i);
+            turn(x1[2 * i], x1[2 * i + 1], 4 * (c0 + 4) + i);
+          }
+        }
+      }
       f16x8 h0, h1, hv8;
 #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        h0[i] = (_Float16)x0[i];
+        h1[i] = (_Float16)x1[i];
+      }
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        h0[2 * i] = (_Float16)bf16_lo(w0[i]);
-        h0[2 * i + 1] = (_Float16)bf16_hi(w0[i]);
-        h1[2 * i] = (_Float16)bf16_lo(w1[i]);
-        h1[2 * i + 1] = (_Float16)bf16_hi(w1[i]);
         hv8[2 * i] = (_Float16)bf16_lo(wv[i]);
         hv8[2 * i + 1] = (_Float16)bf16_hi(wv[i]);
       }
@@ -326,6 +361,40 @@ __device__ __forceinline__ f32x16 mfma_tr(const char* tile, int blk, int lane, c
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(tr_operand<kRowBytes>(tile, blk, 1, lane), p1, acc, 0, 0, 0);
 }
 
+// The gradient of an unrotated query or key from that of its rotated copy
+// (the rotary embedding R at the row's position pos is orthogonal, so the
+// gradient is R^T times it): each pair (g_u, g_w) -> (g_u cos + g_w sin,
+// -g_u sin + g_w cos), in fp32.  g0, g1 hold dims 8 (i / 4) + 4 hf + i % 4
+// and 32 more in register i, so both members of every pair are in the lane.
+__device__ __forceinline__ void unrotate_grad(f32x16& g0, f32x16& g1, int hf, uint32_t pos, const RopeArgs& r) {
+  // pair (u, w) = (x[iu], y[iw])
+  auto turn_back = [&](f32x16& x, int iu, f32x16& y, int iw, uint64_t phase) __attribute__((always_inline)) {
+    float cs, sn;
+    rope_cos_sin(pos, phase, cs, sn);
+    const float u = x[iu], w = y[iw];
+    x[iu] = u * cs + w * sn;
+    y[iw] = w * cs - u * sn;
+  };
+  if (r.mode == 1) {
+    // pair c = dims c, c + 32 (c = 8 r4 + 4 hf + e)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        turn_back(g0, 4 * r4 + e, g1, 4 * r4 + e, hf ? r.phase[8 * r4 + 4 + e] : r.phase[8 * r4 + e]);
+  } else {
+    // pair c = dims 2c, 2c + 1 (2c = 32 blk + 8 r4 + 4 hf + 2 e)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int c0 = 4 * r4 + e;
+        turn_back(g0, 4 * r4 + 2 * e, g0, 4 * r4 + 2 * e + 1, hf ? r.phase[c0 + 2] : r.phase[c0]);
+        turn_back(g1, 4 * r4 + 2 * e, g1, 4 * r4 + 2 * e + 1, hf ? r.phase[16 + c0 + 2] : r.phase[16 + c0]);
+      }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dQ_1, dQ_2: 128 queries of one (b, h) per work item; wave w of a group
 // queries 32w .. 32w+31, lane (hf, lq) query lq.  Two groups of four waves
@@ -349,9 +418,14 @@ __device__ __forceinline__ void dq_item(const BackwardArgs& a, char* smem, int i
   const int q_first = qb * kRows + 32 * wq, q = q_first + lq;
   const bool wave_live = q_first < a.T, ok = q < a.T;
   const int ntiles = min(qb * (kRows / 32) + kRows / 32, (a.T + 31) / 32);
-  const int nsteps = (ntiles + 1) / 2;
   const int kend = min(a.T, ntiles * 32);
   const int last_tile = q_first / 32;
+  // With a sliding window, the key tiles below every query's window are
+  // skipped (the forward's tile range).
+  const int W = a.window;
+  const int tile0 = W > 0 ? max(0, qb * kRows - W + 1) / 32 : 0;
+  const int first_tile = W > 0 ? max(0, q_first - W + 1) / 32 : 0;
+  const int nsteps = (ntiles - tile0 + 1) / 2;
 
   // Operands held for the whole item: Q_m^T (score B operands) and dO^T
   // (dP^T B operand), fp16, both for this lane's query.
@@ -387,7 +461,7 @@ __device__ __forceinline__ void dq_item(const BackwardArgs& a, char* smem, int i
   // Each group stages its own tile of the step (tile 2 it + grp; past the
   // last tile the rows read as zero).
   auto stage_issue = [&](int it, char* st) {
-    const int j = 2 * it + grp;
+    const int j = tile0 + 2 * it + grp;
     char* t = st + grp * kDqTile;
     dma_qk(kb1, kb2, sk, sk, 32 * j, kend, t, rt);
     dma_do(vb, sv, 32 * j, kend, t + 2 * kQKTile, rt);
@@ -398,8 +472,8 @@ __device__ __forceinline__ void dq_item(const BackwardArgs& a, char* smem, int i
 
   for (int it = 0; it < nsteps; ++it) {
     char* cur = smem + (it & 1) * kDqStage + grp * kDqTile;
-    const int j = 2 * it + grp;
-    const bool act = wave_live && j <= last_tile;
+    const int j = tile0 + 2 * it + grp;
+    const bool act = wave_live && j >= first_tile && j <= last_tile;
     // K_m^T operands of the dQ products, read transposed before the next
     // tile's DMA goes out: the compiler orders transposed LDS reads behind
     // every LDS DMA in flight, which would make these products wait for the
@@ -438,6 +512,13 @@ __device__ __forceinline__ void dq_item(const BackwardArgs& a, char* smem, int i
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (8 * (i >> 2) + 4 * hf + (i & 3) > lq) s1[i] = s2[i] = -__builtin_inff();  // P = 0, dS = 0
+      }
+      if (W > 0 && 32 * j < q_first + 32 - W) {
+        // lower window edge: key 32 j + kr is visible to query q iff it is > q - W
+        const int lim = q - W - 32 * j;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + 4 * hf + (i & 3) <= lim) s1[i] = s2[i] = -__builtin_inff();
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -482,6 +563,11 @@ __device__ __forceinline__ void dq_item(const BackwardArgs& a, char* smem, int i
       dq1[1][i] += mo[slot(1, i)];
       dq2[0][i] += mo[slot(2, i)];
       dq2[1][i] += mo[slot(3, i)];
+    }
+    if (a.rope.mode != 0) {
+      const uint32_t pos = a.rope.pos0 + (uint32_t)q;
+      unrotate_grad(dq1[0], dq1[1], hf, pos, a.rope);
+      unrotate_grad(dq2[0], dq2[1], hf, pos, a.rope);
     }
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -568,8 +654,14 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
   const int bh = (int)(blockIdx.x % BH), head = bh % a.H, b = bh / a.H;
   const int k_first = kb * kRows + 32 * rw, key = k_first + lk;
   const bool wave_live = k_first < a.T, ok = key < a.T;
-  const int nqt = (a.T + 31) / 32, qt0 = kb * (kRows / 32);
+  const int qt0 = kb * (kRows / 32);
   const int diag = k_first / 32;  // this wave's first (diagonal) query tile
+  // With a sliding window of W keys, query q sees key k iff q < k + W: the
+  // query tiles past the last that sees one of the workgroup's keys are
+  // skipped, and a wave stops at the last tile that sees one of its own.
+  const int W = a.window;
+  const int nqt = W > 0 ? min((a.T + 31) / 32, (kb * kRows + kRows - 1 + W - 1) / 32 + 1) : (a.T + 31) / 32;
+  const int wave_last = W > 0 ? (k_first + 31 + W - 1) / 32 : nqt - 1;
 
   const int64_t rk = ((int64_t)b * a.T + key) * a.H + head;
   f16x8 k1t[4], k2t[4];
@@ -608,7 +700,7 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
     char* nxt = smem + ((it + 1) & 1) * kDkvStage;
     const bool more = qt + 1 < nqt;
     if (more) stage_issue(qt + 1, nxt);
-    if (wave_live && qt >= diag) {
+    if (wave_live && qt >= diag && qt <= wave_last) {
       f32x16 s1 = scores_qk(cur, k1t, lk, hf);
       f32x16 s2 = scores_qk(cur + kQKTile, k2t, lk, hf);
       const float* stats = reinterpret_cast<const float*>(cur + kOffSt);
@@ -616,6 +708,11 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (lk > 8 * (i >> 2) + 4 * hf + (i & 3)) s1[i] = s2[i] = -__builtin_inff();  // P = 0
+      }
+      if (W > 0 && 32 * qt + 31 >= k_first + W) {  // queries past the window of this lane's key
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * qt + 8 * (i >> 2) + 4 * hf + (i & 3) >= key + W) s1[i] = s2[i] = -__builtin_inff();
       }
       if constexpr (!kDV) {
         // dP = dO V^T (32 queries x 32 keys)
@@ -677,6 +774,11 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
   }
   if (!ok) return;
   if constexpr (!kDV) {
+    if (a.rope.mode != 0) {
+      const uint32_t pos = a.rope.pos0 + (uint32_t)key;
+      unrotate_grad(acc[0], acc[1], hf, pos, a.rope);
+      unrotate_grad(acc[2], acc[3], hf, pos, a.rope);
+    }
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       store_col(a.dk1 + rk * kDqk, acc[blk], blk, hf, a.scale);

@@ -143,6 +143,8 @@ struct BackwardArgs {
   float* dstat;           // [B, T, H, 2]: D_m = rowsum(dO_m * O_m) per map
   float* partial;         // [H, nchunks, kDv + 1]: gain and lambda gradient partials
   int nchunks;
+  int window;             // > 0: sliding window of that many keys (as the forward's)
+  RopeArgs rope;          // rotary embedding of Q1, Q2, K1, K2 (mode 0: none)
 };
 
 // Grouped differential attention with token-wise lambda and output gate:

@@ -303,8 +303,9 @@ DIFFATTN_API int diffattn_rope_apply(const void* x, const diffattn_strides* x_st
                                      float theta, int pos0, const int32_t* pos_start, void* stream);
 
 /*
- * Training forward: diffattn_fwd_prefill (plain causal: no window, no RoPE)
- * that also saves what the backward pass needs.
+ * Training forward: diffattn_fwd_prefill (plain causal; for windows and RoPE
+ * see diffattn_fwd_prefill_train_ex) that also saves what the backward pass
+ * needs.
  *   o1, o2 : fp32 [B, T, H, d_v], each map's normalised output
  *            softmax(Q_m K_m^T * scale) V (so o = o1 - lambda o2)
  *   lse    : fp32 [B, T, H, 2], each map's log-sum-exp of its scaled scores
@@ -319,6 +320,23 @@ DIFFATTN_API int diffattn_fwd_prefill_train(const void* q1, const void* q2, cons
                                             float* o_pre, float* o1, float* o2, float* lse, void* stream);
 
 /*
+ * diffattn_fwd_prefill_train with variants: opt->window (a sliding window)
+ * and opt->rope, rope_theta, rope_pos0 (the rotary embedding of Q1, Q2, K1,
+ * K2, rotated inside the kernels as diffattn_fwd_prefill_ex does), the
+ * training outputs then being those of the rotated, windowed operation (lse
+ * over each query's visible keys).  kv_ring and ws_prepared must be 0
+ * (DIFFATTN_ERR_VALUE).  opt may be NULL.  Pass the same options to
+ * diffattn_bwd_prefill_ex.
+ */
+DIFFATTN_API int diffattn_fwd_prefill_train_ex(const diffattn_options* opt, const void* q1, const void* q2,
+                                               const void* k1, const void* k2, const void* v,
+                                               const diffattn_strides* strides, int B, int T, int H, int d_qk,
+                                               int d_v, float lambda, const float* lambda_per_head,
+                                               const float* gain, float gn_eps, float scale, void* out,
+                                               int out_dtype, float* o_pre, float* o1, float* o2, float* lse,
+                                               void* stream);
+
+/*
  * Bytes of device workspace diffattn_bwd_prefill needs (256-byte aligned
  * buffer): fp16 copies of q1, q2, k1, k2 and v, the pre-norm output gradient
  * in fp16, two row statistics and the gain/lambda partial sums (about
@@ -329,7 +347,8 @@ DIFFATTN_API size_t diffattn_bwd_workspace_bytes(int B, int T, int H, int d_v);
 /*
  * Backward pass of the causal prefill: the gradients of sum(y * dy) for the
  * operation above (the calculus of the definition on the Motif 2.6B
- * explainer, section "Differential attention"; plain causal only).
+ * explainer, section "Differential attention"; plain causal, and see
+ * diffattn_bwd_prefill_ex for windows and RoPE).
  *   q1 .. v, strides, B, T, H, d_qk, d_v, lambda, lambda_per_head, gain,
  *   gn_eps, scale : the forward's arguments
  *   o1, o2, lse   : the forward's training outputs (diffattn_fwd_prefill_train)
@@ -349,6 +368,28 @@ DIFFATTN_API int diffattn_bwd_prefill(const void* q1, const void* q2, const void
                                       const float* o2, const float* lse, const void* dy, int dy_dtype, float* dq1,
                                       float* dq2, float* dk1, float* dk2, float* dv, float* dlambda,
                                       float* dgain, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * diffattn_bwd_prefill with variants, for the forward diffattn_fwd_prefill_train_ex
+ * ran with the same options (its o1, o2, lse):
+ *   opt->window > 0: the sliding window (picx.dev summary of the Motif 3
+ *     report, section 2.1); the gradients flow through the visible pairs only.
+ *   opt->rope: the rotary embedding (Motif 2.6B explainer, section "The
+ *     block"); dq1, dq2, dk1, dk2 are the gradients of the unrotated inputs:
+ *     the rotated copies' gradients turned back by the inverse rotation of
+ *     their position (the rotation is orthogonal), in fp32.
+ * kv_ring and ws_prepared must be 0 (DIFFATTN_ERR_VALUE).  opt may be NULL
+ * (then it is diffattn_bwd_prefill).  Other arguments, outputs and errors as
+ * for diffattn_bwd_prefill.
+ */
+DIFFATTN_API int diffattn_bwd_prefill_ex(const diffattn_options* opt, const void* q1, const void* q2,
+                                         const void* k1, const void* k2, const void* v,
+                                         const diffattn_strides* strides, int B, int T, int H, int d_qk, int d_v,
+                                         float lambda, const float* lambda_per_head, const float* gain,
+                                         float gn_eps, float scale, const float* o1, const float* o2,
+                                         const float* lse, const void* dy, int dy_dtype, float* dq1, float* dq2,
+                                         float* dk1, float* dk2, float* dv, float* dlambda, float* dgain,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Grouped differential attention with a token-wise lambda and an output gate
@@ -391,7 +432,8 @@ DIFFATTN_API const char* diffattn_status_string(int status);
  * prefill workspace entry points (keys rotated once), 106 a larger backward
  * workspace (fp16 input copies; query diffattn_bwd_workspace_bytes again),
  * 107 diffattn_fwd_decode_noalloc, 108 V^T tiles in the prefill workspace,
- * 109 diffattn_prefill_prepare and diffattn_options.ws_prepared
+ * 109 diffattn_prefill_prepare and diffattn_options.ws_prepared, 110 the
+ * training forward and backward with windows and RoPE (_train_ex, _bwd_prefill_ex)
  * (query diffattn_prefill_workspace_bytes again). */
 DIFFATTN_API int diffattn_abi_version(void);
 

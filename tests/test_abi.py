@@ -27,13 +27,14 @@ def test_header_symbols_exported():
                           "diffattn_fwd_prefill_ex", "diffattn_fwd_decode_ex", "diffattn_rope_apply",
                           "diffattn_fwd_decode_noalloc",
                           "diffattn_fwd_prefill_train", "diffattn_bwd_workspace_bytes", "diffattn_bwd_prefill",
+                          "diffattn_fwd_prefill_train_ex", "diffattn_bwd_prefill_ex",
                           "diffattn_grouped_workspace_bytes", "diffattn_fwd_grouped",
                           "diffattn_prefill_workspace_bytes", "diffattn_fwd_prefill_ws", "diffattn_prefill_prepare",
                           "diffattn_status_string", "diffattn_abi_version"}
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 109
+    assert da.diffattn_abi_version() == 110
 
 
 def test_status_strings():
@@ -254,6 +255,33 @@ def _bwd(**kw):
 ])
 def test_bwd_rejects(kw, rc):
     assert _bwd(**kw) == rc
+
+
+# The variants of the training forward and backward: options checked like
+# the forward's (invalid shapes elsewhere, so every call stops before HIP).
+@pytest.mark.parametrize("opt,rc", [
+    (dict(window=-1), EVALUE), (dict(rope=5), EVALUE), (dict(rope=1, rope_theta=0.0), EVALUE),
+    (dict(kv_ring=1), EVALUE), (dict(ws_prepared=1), EVALUE), (dict(reserved=(0, 3)), EVALUE),
+    (dict(window=64, rope=2, rope_theta=5e5, rope_pos0=9), ESHAPE), ("null", ESHAPE),
+])
+def test_train_and_bwd_ex_options(opt, rc):
+    def call(fn, args):
+        if opt == "null":
+            return fn(None, *args)
+        o = da._Options(**{k: v for k, v in opt.items() if k != "reserved"})
+        for i, r in enumerate(opt.get("reserved", ())):
+            o.reserved[i] = r
+        return fn(ctypes.byref(o), *args)
+
+    targs = dict(q1=A, q2=A, k1=A, k2=A, v=A, st=None, B=1, T=128, H=2, dqk=64, dv=128, lam=0.5, lamh=None,
+                 gain=A, eps=1e-5, scale=0.0, out=A, odt=0, opre=None, o1=A, o2=A, lse=A, stream=None)
+    bargs = dict(q1=A, q2=A, k1=A, k2=A, v=A, st=None, B=1, T=128, H=2, dqk=64, dv=128, lam=0.5, lamh=None,
+                 gain=A, eps=1e-5, scale=0.0, o1=A, o2=A, lse=A, dy=A, dyt=0, dq1=A, dq2=A, dk1=A, dk2=A, dv_=A,
+                 dlam=A, dgain=A, ws=A, wsb=1 << 30, stream=None)
+    if rc == ESHAPE:
+        targs["T"] = bargs["T"] = 0
+    assert call(da._lib.diffattn_fwd_prefill_train_ex, list(targs.values())) == rc
+    assert call(da._lib.diffattn_bwd_prefill_ex, list(bargs.values())) == rc
 
 
 def test_bwd_workspace_bytes():

@@ -47,14 +47,16 @@ def _inputs(B, T, H, seed, lam_range=(0.2, 0.9)):
     return x
 
 
-def _gpu(x, dy_f32=False):
+def _gpu(x, dy_f32=False, **var):
     q1, q2, k1, k2, v = (to_dev(x[n]) for n in ("q1", "q2", "k1", "k2", "v"))
     gain, lam = f32_dev(x["gain"]), f32_dev(x["lam"])
-    out, o1, o2, lse = da.diffattn_fwd_prefill_train(q1, q2, k1, k2, v, lam, gain, eps=x["eps"], scale=x["scale"])
+    out, o1, o2, lse = da.diffattn_fwd_prefill_train(q1, q2, k1, k2, v, lam, gain, eps=x["eps"], scale=x["scale"],
+                                                     **var)
     dy = to_dev(x["dy"])
     if dy_f32:
         dy = dy.float()
-    g = da.diffattn_bwd_prefill(q1, q2, k1, k2, v, lam, gain, o1, o2, lse, dy, eps=x["eps"], scale=x["scale"])
+    g = da.diffattn_bwd_prefill(q1, q2, k1, k2, v, lam, gain, o1, o2, lse, dy, eps=x["eps"], scale=x["scale"],
+                                **var)
     torch.cuda.synchronize()
     return {n: g[n].cpu().numpy().astype(np.float64) for n in NAMES}, (out, o1, o2, lse)
 
@@ -63,9 +65,9 @@ def _rel(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
-def _check(x, g, what):
+def _check(x, g, what, **var):
     ref = bwd.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"],
-                       synth.bf16_bits_to_f32(x["dy"]).astype(np.float64))
+                       synth.bf16_bits_to_f32(x["dy"]).astype(np.float64), **var)
     _compare(g, ref, what)
 
 
@@ -189,3 +191,58 @@ def test_backward_full_layer_h16(B, seed):
     else:
         names = ("dq1", "dq2", "dk1", "dk2", "dv")
     _compare(gs, ref, ("full layer", B), names)
+
+
+# The variants (diffattn_fwd_prefill_train_ex + diffattn_bwd_prefill_ex): the
+# rotary embedding with both pairings (Motif 2.6B explainer, "The block"), the
+# sliding window (picx.dev summary of the Motif 3 report, section 2.1), both
+# together; ragged lengths, windows narrower and wider than a tile, a last
+# case at T=4096 with the 128-token window of the Motif 3 sliding layers.
+VARIANTS = [
+    (1, 100, 2, dict(rope=da.ROPE_HALF, rope_theta=1e4, rope_pos0=5)),
+    (2, 300, 2, dict(rope=da.ROPE_INTERLEAVED, rope_theta=5e5)),
+    (1, 515, 2, dict(window=64)),
+    (1, 257, 2, dict(window=2)),
+    (1, 700, 3, dict(window=200, rope=da.ROPE_HALF, rope_theta=1e4)),
+    (2, 1000, 2, dict(window=33, rope=da.ROPE_INTERLEAVED, rope_theta=1e4, rope_pos0=100)),
+    (1, 4096, 2, dict(window=128, rope=da.ROPE_HALF, rope_theta=5e5)),
+]
+
+
+@pytest.mark.parametrize("B,T,H,var", VARIANTS)
+def test_backward_variants(B, T, H, var):
+    _say("backward variant", B, T, H, var)
+    x = _inputs(B, T, H, seed=900 + T + var.get("window", 0))
+    g, _ = _gpu(x, **var)
+    _check(x, g, (B, T, H, var), **var)
+
+
+def test_backward_rope_window_wide_equals_causal():
+    # a window covering every key is the causal backward, bit for bit
+    _say("backward window >= T equals causal")
+    x = _inputs(1, 300, 2, seed=31)
+    g0, _ = _gpu(x, rope=da.ROPE_HALF, rope_theta=5e5)
+    g1, _ = _gpu(x, rope=da.ROPE_HALF, rope_theta=5e5, window=300)
+    for n in NAMES:
+        assert np.array_equal(g0[n], g1[n]), n
+
+
+def test_backward_single_key_window():
+    """window = 1: every softmax covers one key (P = 1), so the exact dQ and
+    dK vanish; what the kernels leave is the difference of two fp32
+    evaluations of the same row dot product (D from the fp32 forward output,
+    dP from the fp16 operands), a few 1e-4 of the gradients' natural scale,
+    bounded here by 1e-3 of dV's RMS.  dV and dgain keep the usual bounds;
+    dlambda, a sum over B*T*128 signed products that nearly cancel, is held
+    to a relative 2e-2."""
+    _say("backward window 1")
+    x = _inputs(1, 257, 2, seed=1258)
+    g, _ = _gpu(x, window=1)
+    ref = bwd.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"], x["scale"],
+                       synth.bf16_bits_to_f32(x["dy"]).astype(np.float64), window=1)
+    _compare(g, ref, "window 1", names=("dv", "dgain"))
+    scale = float(np.sqrt(np.mean(ref["dv"] ** 2)))
+    for n in ("dq1", "dq2", "dk1", "dk2"):
+        assert np.abs(ref[n]).max() <= 1e-12 * scale, n
+        assert np.abs(g[n]).max() <= 1e-3 * scale, (n, np.abs(g[n]).max(), scale)
+    assert _rel(g["dlam"], ref["dlam"]) <= 2e-2, (g["dlam"], ref["dlam"])
