@@ -98,6 +98,16 @@ def decode_bytes(wl) -> int:
     return cache + q + out + gain
 
 
+def grouped_decode_bytes(wl, n_signal) -> int:
+    """Bytes the grouped decode must move: every head's K and V cache
+    positions once, the queries, each signal head's lambda, gate (bf16) and
+    output (bf16)."""
+    cache = wl.B * wl.T * wl.H * (wl.d_qk + wl.d_v) * 2
+    q = wl.B * wl.H * wl.d_qk * 2
+    per_signal = wl.B * n_signal * (4 + 2 * wl.d_v * 2)
+    return cache + q + per_signal
+
+
 def swa_prefill_bytes(wl) -> int:
     """Bytes a prefill must move: Q1, Q2, K1, K2, V read once, the bf16 output
     written once, and the gain."""
@@ -288,6 +298,19 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     def grouped():
         da.diffattn_fwd_grouped(gq, gk, gv, 3, glam, gate=ggate, out=gout, workspace=gws)
 
+    # grouped decode over the decode workload's full 4096-long caches: one K and
+    # one V cache per head (16 heads: 12 signal, 4 noise, g = 3)
+    gdw = synth.WORKLOADS[DECODE_WL]
+    gd_lam = torch.from_numpy(synth.uniform_f32(gdw.seed, 7, (gdw.B, 12), 0.0, 1.0)).to(dev)
+    gd_gate = to_dev(synth.f32_to_bf16_bits(synth.normal_f32(gdw.seed, 8, (gdw.B, 12, gdw.d_v), std=2.0)), dev)
+    gd_ws = torch.empty(da.diffattn_grouped_decode_workspace_bytes(gdw.B, gdw.H, gdw.d_v, 8), dtype=torch.uint8,
+                        device=dev)
+    gd_out = torch.empty((gdw.B, 12, gdw.d_v), dtype=torch.bfloat16, device=dev)
+
+    def grouped_decode():
+        da.diffattn_fwd_grouped_decode(D["q1"], D["k1"], D["v"], 3, gd_lam, gate=gd_gate, num_splits=8, out=gd_out,
+                                       workspace=gd_ws)
+
     # the two other full-attention workloads: the training-shaped batch
     # (B=8, lambda per head) and the long-context layer (T=16384)
     big = {}
@@ -318,6 +341,9 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
     r_us, r_min = _time_calls(torch, np, prefill_rope, warmup, iters)
     bw_us, bw_min = _time_calls(torch, np, backward, warmup // 3, iters)
     g_us, g_min = _time_calls(torch, np, grouped, warmup, iters)
+    gd_us, gd_min = _time_calls(torch, np, grouped_decode, warmup // 3, iters)
+    assert bool(torch.isfinite(gd_out.float()).all())
+    gd_bytes = grouped_decode_bytes(gdw, 12)
     assert bool(torch.isfinite(gout.float()).all())
     g_flop = rw.causal_pairs * GROUPED_FLOP_PER_PAIR_HEAD  # causal_pairs already counts the 16 heads
     assert all(bool(torch.isfinite(t).all()) for t in bgr.values())
@@ -334,6 +360,10 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
                     "us_mean": round(g_us, 2), "us_min": round(g_min, 2),
                     "tflops": round(g_flop / g_us / 1e6, 2),
                     "frac_mfma_peak": round(g_flop / g_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},
+        "grouped_decode": {"workload": "B=64 L=4096 16 heads (12 signal, 4 noise, g=3), token-wise lambda, gate",
+                           "bound": "hbm", "us_mean": round(gd_us, 2), "us_min": round(gd_min, 2),
+                           "bytes": gd_bytes, "gbs": round(gd_bytes / gd_us / 1e3, 1),
+                           "frac_hbm_peak": round(gd_bytes / gd_us / 1e3 / HBM_PEAK_GBS, 4), "splits": 8},
         "backward": {"workload": PREFILL_WL, "us_mean": round(bw_us, 2), "us_min": round(bw_min, 2),
                      "flop_per_pair": BWD_FLOP_PER_PAIR, "tflops": round(bw_flop / bw_us / 1e6, 2),
                      "frac_mfma_peak": round(bw_flop / bw_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},

@@ -114,6 +114,12 @@ _lib.diffattn_grouped_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.diffattn_fwd_grouped.restype = _I
 _lib.diffattn_fwd_grouped.argtypes = [_P, _P, _P, ctypes.POINTER(_Strides), _I, _I, _I, _I, _I, _I, _P, _P,
                                       ctypes.c_float, _P, _I, _P, ctypes.c_size_t, _P]
+_lib.diffattn_grouped_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.diffattn_grouped_decode_workspace_bytes.argtypes = [_I, _I, _I, _I]
+_lib.diffattn_fwd_grouped_decode.restype = _I
+_lib.diffattn_fwd_grouped_decode.argtypes = [ctypes.POINTER(_Options), _P, _P, _P, ctypes.POINTER(_Strides), _P, _I,
+                                             _I, _I, _I, _I, _I, _P, _P, ctypes.c_float, _I, _P, ctypes.c_size_t,
+                                             _P, _I, _P]
 _lib.diffattn_status_string.restype = ctypes.c_char_p
 _lib.diffattn_status_string.argtypes = [_I]
 _lib.diffattn_abi_version.restype = _I
@@ -516,6 +522,54 @@ def diffattn_fwd_grouped(q, k, v, group, lambda_t, gate=None, scale=0.0, out=Non
     rc = _lib.diffattn_fwd_grouped(_ptr(q), _ptr(k), _ptr(v), st, B, T, n_heads, int(group), d_qk, d_v,
                                    _ptr(lambda_t), _ptr(gate), float(scale), _ptr(out), _out_code(out.dtype),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+    return out
+
+
+def diffattn_grouped_decode_workspace_bytes(B, n_heads, d_v=D_V, num_splits=0):
+    return int(_lib.diffattn_grouped_decode_workspace_bytes(int(B), int(n_heads), int(d_v), int(num_splits)))
+
+
+def diffattn_fwd_grouped_decode(q, k, v, group, lambda_t, gate=None, scale=0.0, seqlens=None, num_splits=0,
+                                out=None, out_dtype=torch.bfloat16, workspace=None, stream=None, window=0,
+                                kv_ring=False):
+    """Single-query decode of grouped differential attention: q bf16
+    [B, n_heads, 64] (each sequence's newest token), caches k bf16
+    [B, L, n_heads, 64] and v bf16 [B, L, n_heads, 128], seqlens optional
+    int32 [B] device tensor, lambda_t fp32 [B, n_S], optional gate bf16
+    [B, n_S, 128] logits.  Returns out [B, n_S, 128]."""
+    B, n_heads, d_qk = q.shape
+    L = k.shape[1]
+    d_v = v.shape[3]
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError("q, k, v must be bf16 device tensors")
+    if not q.is_contiguous() or tuple(k.shape) != (B, L, n_heads, d_qk) or tuple(v.shape[:3]) != (B, L, n_heads):
+        raise ValueError("q must be a contiguous [B, n_heads, d_qk] tensor and k, v [B, L, n_heads, d] caches")
+    if group < 1 or n_heads % (group + 1):
+        raise ValueError("n_heads must be a multiple of group + 1")
+    n_S = group * (n_heads // (group + 1))
+    if lambda_t.dtype != torch.float32 or tuple(lambda_t.shape) != (B, n_S) or not lambda_t.is_contiguous():
+        raise ValueError("lambda_t must be a contiguous fp32 [B, n_S] tensor")
+    if gate is not None and (gate.dtype != torch.bfloat16 or tuple(gate.shape) != (B, n_S, d_v)
+                             or not gate.is_contiguous()):
+        raise ValueError("gate must be a contiguous bf16 [B, n_S, d_v] tensor")
+    if seqlens is not None and (seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,) or not seqlens.is_cuda):
+        raise ValueError("seqlens must be an int32 [B] device tensor")
+    if out is None:
+        with _alloc_on(stream):
+            out = torch.empty((B, n_S, d_v), dtype=out_dtype, device=q.device)
+    need = diffattn_grouped_decode_workspace_bytes(B, n_heads, d_v, num_splits)
+    if workspace is None:
+        with _alloc_on(stream):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    opt = _Options(window=int(window), kv_ring=int(bool(kv_ring)))
+    st = (_Strides * 2)(*[_strides4(t) for t in (k, v)])
+    rc = _lib.diffattn_fwd_grouped_decode(ctypes.byref(opt), _ptr(q), _ptr(k), _ptr(v), st, _ptr(seqlens), B, L,
+                                          n_heads, int(group), d_qk, d_v, _ptr(lambda_t), _ptr(gate), float(scale),
+                                          int(num_splits), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _ptr(out),
+                                          _out_code(out.dtype), _stream(stream))
     _check(rc)
     return out
 

@@ -28,7 +28,8 @@ COMMON = [
     # with VALU ops, and AGPR accumulators cost a copy each way per key tile
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
-SOURCES = ["prefill.hip", "window.hip", "decode.hip", "rope.hip", "vtiles.hip", "backward.hip", "grouped.hip", "api.cpp"]
+SOURCES = ["prefill.hip", "window.hip", "decode.hip", "rope.hip", "vtiles.hip", "backward.hip", "grouped.hip",
+           "gdecode.hip", "api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -102,7 +102,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 110; }
+int diffattn_abi_version(void) { return 111; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -661,6 +661,73 @@ int diffattn_fwd_grouped(const void* q, const void* k, const void* v, const diff
   a.out_f32 = out_dtype == DIFFATTN_OUT_F32;
   a.hw = static_cast<float*>(workspace);
   if (diffattn::launch_grouped(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
+  return DIFFATTN_OK;
+}
+
+size_t diffattn_grouped_decode_workspace_bytes(int B, int n_heads, int d_v, int num_splits) {
+  if (num_splits <= 0) num_splits = kDefaultSplits;
+  if (B <= 0 || n_heads <= 0 || d_v != kDv || num_splits > kMaxSplits) return 0;
+  if ((int64_t)B * n_heads > (int64_t(1) << 24)) return 0;
+  return (size_t)B * n_heads * num_splits * (kDv + 2) * sizeof(float);
+}
+
+int diffattn_fwd_grouped_decode(const diffattn_options* opt, const void* q, const void* k, const void* v,
+                                const diffattn_strides* strides, const int32_t* seqlens, int B, int L, int n_heads,
+                                int group, int d_qk, int d_v, const float* lambda_t, const void* gate, float scale,
+                                int num_splits, void* workspace, size_t workspace_bytes, void* out, int out_dtype,
+                                void* stream) {
+  if (!q || !k || !v || !lambda_t || !out) return DIFFATTN_ERR_NULL;
+  int rc = check_options(opt);
+  if (rc != DIFFATTN_OK) return rc;
+  if (opt && (opt->rope != DIFFATTN_ROPE_NONE || opt->ws_prepared != 0)) return DIFFATTN_ERR_VALUE;
+  if (B <= 0 || L <= 0 || L > (1 << 26) || n_heads <= 0 || group <= 0) return DIFFATTN_ERR_SHAPE;
+  if (n_heads % (group + 1) != 0) return DIFFATTN_ERR_SHAPE;
+  if ((int64_t)B * n_heads > (int64_t(1) << 24)) return DIFFATTN_ERR_SHAPE;
+  if (d_qk != kDqk || d_v != kDv) return DIFFATTN_ERR_UNSUPPORTED;
+  if (std::isnan(scale) || std::isinf(scale)) return DIFFATTN_ERR_VALUE;
+  if (out_dtype != DIFFATTN_OUT_BF16 && out_dtype != DIFFATTN_OUT_F32) return DIFFATTN_ERR_VALUE;
+  const bool ring = opt && opt->kv_ring != 0;
+  if (ring && opt->window > L) return DIFFATTN_ERR_VALUE;
+  if (num_splits <= 0) num_splits = kDefaultSplits;
+  if (num_splits > kMaxSplits) return DIFFATTN_ERR_VALUE;
+  if ((int64_t)B * n_heads * num_splits > kMaxWorkgroups) return DIFFATTN_ERR_SHAPE;
+  const void* ptrs[] = {q, k, v, lambda_t, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return DIFFATTN_ERR_LAYOUT;
+  if (gate && (reinterpret_cast<uintptr_t>(gate) & 7u) != 0) return DIFFATTN_ERR_LAYOUT;
+  if (seqlens && (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0) return DIFFATTN_ERR_LAYOUT;
+  diffattn_strides st[2];
+  for (int i = 0; i < 2; ++i) {
+    st[i] = strides ? strides[i] : contiguous(L, n_heads, i == 1 ? d_v : d_qk);
+    if (!strides_ok(st[i])) return DIFFATTN_ERR_LAYOUT;
+  }
+  if (!workspace || !aligned16(workspace)) return DIFFATTN_ERR_WORKSPACE;
+  if (workspace_bytes < diffattn_grouped_decode_workspace_bytes(B, n_heads, d_v, num_splits))
+    return DIFFATTN_ERR_WORKSPACE;
+  diffattn::GroupedDecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.sk = to_internal(st[0]);
+  a.sv = to_internal(st[1]);
+  a.seqlens = seqlens;
+  a.B = B;
+  a.L = L;
+  a.nH = n_heads;
+  a.g = group;
+  a.nN = n_heads / (group + 1);
+  a.nS = group * a.nN;
+  a.splits = num_splits;
+  a.window = opt ? opt->window : 0;
+  a.ring = ring ? 1 : 0;
+  if (ring && a.window == 0) a.window = L;  // a ring holds the last L positions
+  a.c = score_factor(scale);
+  a.lam = lambda_t;
+  a.gate = static_cast<const uint16_t*>(gate);
+  a.partial = static_cast<float*>(workspace);
+  a.out = out;
+  a.out_f32 = out_dtype == DIFFATTN_OUT_F32;
+  if (diffattn::launch_grouped_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
   return DIFFATTN_OK;
 }
 

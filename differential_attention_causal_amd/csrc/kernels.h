@@ -166,6 +166,28 @@ struct GroupedArgs {
 
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream);
 
+// Single-query decode of the grouped form: head h's query q[b, h] against its
+// own cache rows (n_H heads, each plain softmax attention), then signal head
+// s combined with noise head nS + s / g as the prefill does.
+struct GroupedDecodeArgs {
+  const uint16_t* q;       // [B, nH, kDqk]
+  const uint16_t* k;       // [B, L, nH, kDqk] with strides
+  const uint16_t* v;       // [B, L, nH, kDv] with strides
+  Strides sk, sv;
+  const int32_t* seqlens;  // [B] or null (L each)
+  int B, L, nH, g, nN, nS, splits;
+  int window;              // > 0: the last `window` positions
+  int ring;                // cache of L slots is a ring: position p in slot p % L
+  float c;                 // scale * log2(e)
+  const float* lam;        // [B, nS] fp32
+  const uint16_t* gate;    // [B, nS, kDv] bf16 logits, or null
+  float* partial;          // [B, nH, splits, kDv + 2] fp32 workspace
+  void* out;               // [B, nS, kDv] bf16 or fp32
+  int out_f32;
+};
+
+hipError_t launch_grouped_decode(const GroupedDecodeArgs& a, hipStream_t stream);
+
 // Rows (b, t) of one head per workgroup of the backward's first kernel.
 constexpr int kBwdRowsPerChunk = 64;
 

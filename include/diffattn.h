@@ -423,6 +423,39 @@ DIFFATTN_API int diffattn_fwd_grouped(const void* q, const void* k, const void* 
                                       void* out, int out_dtype, void* workspace, size_t workspace_bytes,
                                       void* stream);
 
+/*
+ * Single-query decode of the grouped form above (picx.dev summary of the
+ * Motif 3 report, section 2.2, and its note on KV-cache reduction for
+ * long-context inference): the query of each sequence's newest token against
+ * its cache, per head H_h = softmax(q_h K_h^T * scale) V_h over the cached
+ * positions, and
+ *   out_s = sigmoid(G_s) * (H_s - lambda_t[s] * H_(n_S + s / group)),
+ * no GroupNorm.  Each noise head is computed once per sequence.
+ *   opt         : window (the last `window` positions) and kv_ring as for
+ *                 diffattn_fwd_decode_ex; rope and ws_prepared must be 0
+ *                 (DIFFATTN_ERR_VALUE); may be NULL
+ *   q           : bf16 [B, n_heads, d_qk], C-contiguous
+ *   k, v        : bf16 caches [B, L, n_heads, d_qk] and [B, L, n_heads, d_v]
+ *   strides     : 2 entries (k, v) or NULL (C-contiguous)
+ *   seqlens     : device int32 [B] cached positions per sequence (as
+ *                 diffattn_fwd_decode), or NULL for L each; 0 gives 0 output
+ *   lambda_t    : device fp32 [B, n_S], the newest token's lambda per signal head
+ *   gate        : device bf16 [B, n_S, d_v] gate logits, 8-byte aligned, or NULL
+ *   num_splits  : key ranges per (b, head), 1 .. 64; <= 0 selects 8
+ *   workspace   : >= diffattn_grouped_decode_workspace_bytes() bytes, 16-byte
+ *                 aligned: each (b, head, split)'s softmax state
+ *   out         : [B, n_S, d_v] bf16 or fp32 per out_dtype
+ * Errors as for diffattn_fwd_decode_ex, and DIFFATTN_ERR_SHAPE when n_heads
+ * is not a multiple of group + 1.
+ */
+DIFFATTN_API size_t diffattn_grouped_decode_workspace_bytes(int B, int n_heads, int d_v, int num_splits);
+DIFFATTN_API int diffattn_fwd_grouped_decode(const diffattn_options* opt, const void* q, const void* k,
+                                             const void* v, const diffattn_strides* strides,
+                                             const int32_t* seqlens, int B, int L, int n_heads, int group,
+                                             int d_qk, int d_v, const float* lambda_t, const void* gate,
+                                             float scale, int num_splits, void* workspace,
+                                             size_t workspace_bytes, void* out, int out_dtype, void* stream);
+
 /* Static text for a status code (never NULL). */
 DIFFATTN_API const char* diffattn_status_string(int status);
 
@@ -433,7 +466,8 @@ DIFFATTN_API const char* diffattn_status_string(int status);
  * workspace (fp16 input copies; query diffattn_bwd_workspace_bytes again),
  * 107 diffattn_fwd_decode_noalloc, 108 V^T tiles in the prefill workspace,
  * 109 diffattn_prefill_prepare and diffattn_options.ws_prepared, 110 the
- * training forward and backward with windows and RoPE (_train_ex, _bwd_prefill_ex)
+ * training forward and backward with windows and RoPE (_train_ex, _bwd_prefill_ex),
+ * 111 the grouped decode (diffattn_fwd_grouped_decode)
  * (query diffattn_prefill_workspace_bytes again). */
 DIFFATTN_API int diffattn_abi_version(void);
 

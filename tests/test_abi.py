@@ -28,13 +28,14 @@ def test_header_symbols_exported():
                           "diffattn_fwd_decode_noalloc",
                           "diffattn_fwd_prefill_train", "diffattn_bwd_workspace_bytes", "diffattn_bwd_prefill",
                           "diffattn_fwd_prefill_train_ex", "diffattn_bwd_prefill_ex",
+                          "diffattn_grouped_decode_workspace_bytes", "diffattn_fwd_grouped_decode",
                           "diffattn_grouped_workspace_bytes", "diffattn_fwd_grouped",
                           "diffattn_prefill_workspace_bytes", "diffattn_fwd_prefill_ws", "diffattn_prefill_prepare",
                           "diffattn_status_string", "diffattn_abi_version"}
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 110
+    assert da.diffattn_abi_version() == 111
 
 
 def test_status_strings():
@@ -385,3 +386,33 @@ def test_decode_noalloc_rejects(kw, rc):
     if rc == EWS:
         B, H, s = kw["B"], kw["H"], kw["splits"]
         assert da.diffattn_decode_workspace_bytes(B, H, 128, s) > da.DECODE_SCRATCH_BYTES
+
+
+def _gdec(opt=None, **kw):
+    need = da.diffattn_grouped_decode_workspace_bytes(2, 4, 128, 8)
+    args = dict(q=A, k=A, v=A, st=None, sl=None, B=2, L=100, nh=4, g=1, dqk=64, dv=128, lam=A, gate=None, scale=0.0,
+                splits=8, ws=A, wsb=need, out=A, odt=0, stream=None)
+    args.update(kw)
+    o = None if opt is None else ctypes.byref(da._Options(**opt))
+    return da._lib.diffattn_fwd_grouped_decode(o, *args.values())
+
+
+@pytest.mark.parametrize("opt,kw,rc", [
+    (None, dict(q=None), ENULL), (None, dict(lam=None), ENULL), (None, dict(out=None), ENULL),
+    (None, dict(B=0), ESHAPE), (None, dict(L=0), ESHAPE), (None, dict(nh=5), ESHAPE), (None, dict(g=0), ESHAPE),
+    (None, dict(dqk=32), EUNSUP), (None, dict(dv=64), EUNSUP), (None, dict(splits=65), EVALUE),
+    (None, dict(odt=2), EVALUE), (None, dict(scale=float("nan")), EVALUE), (None, dict(k=A + 2), ELAYOUT),
+    (None, dict(gate=A + 4), ELAYOUT), (None, dict(sl=A + 2), ELAYOUT), (None, dict(ws=None), EWS),
+    (None, dict(wsb=16), EWS), (dict(rope=1, rope_theta=5e5), dict(), EVALUE), (dict(ws_prepared=1), dict(), EVALUE),
+    (dict(kv_ring=1, window=101), dict(), EVALUE), (dict(window=-3), dict(), EVALUE),
+])
+def test_grouped_decode_rejects(opt, kw, rc):
+    assert _gdec(opt, **kw) == rc
+
+
+def test_grouped_decode_workspace_bytes():
+    assert da.diffattn_grouped_decode_workspace_bytes(64, 16, 128, 8) == 64 * 16 * 8 * 130 * 4
+    assert da.diffattn_grouped_decode_workspace_bytes(64, 16, 128, 0) == 64 * 16 * 8 * 130 * 4
+    assert da.diffattn_grouped_decode_workspace_bytes(0, 16, 128, 8) == 0
+    assert da.diffattn_grouped_decode_workspace_bytes(1, 16, 64, 8) == 0
+    assert da.diffattn_grouped_decode_workspace_bytes(1, 16, 128, 65) == 0
