@@ -333,7 +333,7 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
         big[key] = {"workload": name, "B": w.B, "T": w.T, "H": w.H, "us_mean": round(us, 2),
                     "us_min": round(us_min, 2), "tflops": round(flop / us / 1e6, 2),
                     "frac_mfma_peak": round(flop / us / 1e6 / MFMA_PEAK_TFLOPS, 4),
-                    "kernels": "vtiles_kernel + prefill_kernel<1, 0, true>"}
+                    "kernels": "vtiles_kernel + prefill_pp_kernel<false, false, true>"}
         del W, w_out, w_ws
 
     p_us, p_min = _time_calls(torch, np, prefill, warmup, iters)

@@ -14,11 +14,11 @@
 //     of the causal range (group 0 the even ones, group 1 the odd ones), each
 //     with its own softmax states and accumulators, merged through LDS at the
 //     end; group 1 runs half a step behind group 0, so that on every SIMD one
-//     wave's matrix products run while the other wave does its softmax.  Used
-//     for grids that fit on the chip in one round, without the rotary
-//     embedding; each workgroup runs two query blocks of one (b, h) back to
-//     back (the longest with the shortest), so one workgroup per CU carries
-//     the same work everywhere;
+//     wave's matrix products run while the other wave does its softmax.  Each
+//     workgroup runs two query blocks of one (b, h) back to back (the longest
+//     with the shortest), so every workgroup carries the same work.  Used
+//     with V^T tiles at every grid size, and with V in registers for grids
+//     that fit on the chip in one round; not with keys rotated while staged;
 //   - one group (4 waves, prefill_kernel<1, .>): two workgroups share a CU,
 //     and a grid larger than the chip balances itself in longest-first order;
 //   - two groups in lock step (prefill_kernel<2, .>): the split of the
@@ -233,22 +233,6 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
   const int wave_last_tile = q_first / kBN;
   const int wave_first_tile = a.window > 0 ? max(0, q_first - a.window + 1) / kBN : 0;
 
-  bf16x8 qa[4], qb2[4];
-  {
-    const bool ok = q < a.T;
-    const uint16_t* p1 = a.q1 + (int64_t)b * a.sq1.b + (int64_t)q * a.sq1.t + (int64_t)head * a.sq1.h + 8 * hf;
-    const uint16_t* p2 = a.q2 + (int64_t)b * a.sq2.b + (int64_t)q * a.sq2.t + (int64_t)head * a.sq2.h + 8 * hf;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 x1 = ok ? load16(p1 + 16 * s) : u32x4{0, 0, 0, 0};
-      u32x4 x2 = ok ? load16(p2 + 16 * s) : u32x4{0, 0, 0, 0};
-      qa[s] = __builtin_bit_cast(bf16x8, x1);
-      qb2[s] = __builtin_bit_cast(bf16x8, x2);
-    }
-  }
-  // With pre-rotated keys, the query is rotated here (fp16 operands).
-  if constexpr (kRopeQ) rope_query(qa, qb2, hf, a.rope.pos0 + (uint32_t)q, a.rope.mode, a.rope);
-
   f32x16 O1[4], O2[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
@@ -278,25 +262,50 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
   auto vslot = [&](int x) { return slot0 + (x % kVtSlots) * kStage; };  // tile x's slot (V^T tiles)
   auto live = [&](int j) { return wave_live && j >= wave_first_tile && j <= wave_last_tile; };
 
+  // Prologue: tile 0 complete in slot 0, K(1) in slot 1, V(1) in registers
+  // (wait: everything but the four V(1) loads); with V^T tiles, V(1) is on its
+  // way to slot 1 instead (its two DMAs may still be in flight).  With V^T
+  // tiles the first three tiles' DMAs go out before anything else, so that
+  // the query loads, the gain and lambda fetches (and the scalar loads they
+  // wait on) run under their latency instead of ahead of it.
+  if constexpr (kVT) {
+    pp_dma_k(res, soff, slot0, key0(0), wq);
+    dma_v(0, 0);
+    pp_dma_k(res, soff, slot0 + kStage, key0(1), wq);
+  }
+  bf16x8 qa[4], qb2[4];
+  {
+    const bool ok = q < a.T;
+    const uint16_t* p1 = a.q1 + (int64_t)b * a.sq1.b + (int64_t)q * a.sq1.t + (int64_t)head * a.sq1.h + 8 * hf;
+    const uint16_t* p2 = a.q2 + (int64_t)b * a.sq2.b + (int64_t)q * a.sq2.t + (int64_t)head * a.sq2.h + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 x1 = ok ? load16(p1 + 16 * s) : u32x4{0, 0, 0, 0};
+      u32x4 x2 = ok ? load16(p2 + 16 * s) : u32x4{0, 0, 0, 0};
+      qa[s] = __builtin_bit_cast(bf16x8, x1);
+      qb2[s] = __builtin_bit_cast(bf16x8, x2);
+    }
+  }
+  // With pre-rotated keys, the query is rotated here (fp16 operands).
+  if constexpr (kRopeQ) rope_query(qa, qb2, hf, a.rope.pos0 + (uint32_t)q, a.rope.mode, a.rope);
+
   // The epilogue's gain and lambda, fetched while the first tiles load.
   f32x4 gpre = f32x4{};
   float lpre = 0.f;
   if (tid < kDv / 4) gpre = *reinterpret_cast<const f32x4*>(a.gain + (int64_t)head * kDv + 4 * tid);
   if (tid == kDv / 4) lpre = a.lambda_h ? a.lambda_h[head] : a.lambda;
 
-  // Prologue: tile 0 complete in slot 0, K(1) in slot 1, V(1) in registers
-  // (wait: everything but the four V(1) loads); with V^T tiles, V(1) is on its
-  // way to slot 1 instead (its two DMAs may still be in flight).
   Staged st;
   if constexpr (kVT) {
+    dma_v(1, 1);
 #pragma unroll
-    for (int x = 0; x < kVtSlots; ++x) {
+    for (int x = 2; x < kVtSlots; ++x) {
       pp_dma_k(res, soff, slot0 + x * kStage, key0(x), wq);
       dma_v(x, x);
     }
     if (tid < kDv / 4) gain_s[tid] = gpre;
     if (tid == kDv / 4) *lam_s = lpre;
-    wait_vm<kVtYounger>();  // K(0), V(0), K(1) have landed
+    wait_vm<kVtYounger>();  // K(0), V(0), K(1), the queries and the gain have landed
   } else {
     pp_dma_k(res, soff, slot0, key0(0), wq);
     pp_load_v(st, res, soff, key0(0));
@@ -648,7 +657,7 @@ struct PrefillPlan {
   int64_t grid;
   bool split;     // the grid fits on the chip in one round
   bool prerot;    // keys rotated beforehand (fp16 copies)
-  bool pingpong;  // prefill_pp_kernel
+  bool pp_fits;   // prefill_pp_kernel can take this call
   bool window;    // the streaming window kernel (window.hip)
   bool takes_vt;  // the chosen kernel can read V^T tiles (vtiles.hip)
 };
@@ -660,8 +669,8 @@ PrefillPlan plan_prefill(const PrefillArgs& a) {
   // A grid that fits on the chip in one round (two 4-wave workgroups per CU)
   // leaves the CUs holding the longest query blocks working alone at the end;
   // splitting each workgroup's key range over two wave groups halves that
-  // tail.  Larger grids balance by themselves in longest-first order and run
-  // better as independent 4-wave workgroups.
+  // tail.  Larger grids with V in registers balance by themselves in
+  // longest-first order and run better as independent 4-wave workgroups.
   p.split = p.grid <= 2 * (int64_t)device_cu_count();
   const int64_t row_max = std::max(std::max(a.sk1.t, a.sk2.t), a.sv.t);
   // Keys already rotated (fp16 copies): they are staged like plain keys, and
@@ -669,15 +678,15 @@ PrefillPlan plan_prefill(const PrefillArgs& a) {
   p.prerot = a.rope.mode != 0 && a.keys_rotated;
   // The ping-pong kernel addresses a (b, h)'s key rows from one buffer base
   // with 32-bit offsets (up to about T + 192 rows).
-  p.pingpong = p.split && (a.rope.mode == 0 || p.prerot) && !(p.prerot && a.o1n != nullptr) &&
-               (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31);
+  p.pp_fits = (a.rope.mode == 0 || p.prerot) && !(p.prerot && a.o1n != nullptr) &&
+              (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31);
   // Windowed prefill without the rotary embedding or training outputs, at
   // most four tiles before the diagonal: the streaming kernel (window.hip).
   p.window = prefill_window_kernel_fits(a);
   // V^T tiles go with the kernels that move keys by DMA, without training
   // outputs: the ping-pong kernel and the four-wave kernel; the lock-step
   // two-group kernel and key rotation while staging keep V in registers.
-  p.takes_vt = !p.window && a.o1n == nullptr && (a.rope.mode == 0 || p.prerot) && (p.pingpong || !p.split);
+  p.takes_vt = !p.window && a.o1n == nullptr && (a.rope.mode == 0 || p.prerot) && (p.pp_fits || !p.split);
   return p;
 }
 
@@ -690,7 +699,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (p.window) return launch_prefill_window(a, stream);
   const bool vt = a.vt != nullptr && p.takes_vt;
   const int nqb = p.nqb;
-  if (p.pingpong) {
+  // With V^T tiles the persistent ping-pong kernel runs every grid size: its
+  // workgroups carry equal work (a long query block with a short one), so a
+  // grid of several rounds stays balanced, and it beats the four-wave kernel
+  // there too (B=1, T=16384, H=16: 11% faster).  With V in registers the
+  // four-wave kernel is the faster one once the grid exceeds one round.
+  if (p.pp_fits && (p.split || vt)) {
     const dim3 gp((unsigned)((int64_t)((nqb + 1) / 2) * a.B * a.H));
     if (p.prerot)
       return vt ? launch_kernel(prefill_pp_kernel<false, true, true>, gp, dim3(512), stream, a)

@@ -1,13 +1,16 @@
 """The prefill's workspace path (diffattn_fwd_prefill_ws without rope: V
 converted once into fp16 V^T tiles that the kernels move by DMA) against the
-plain entry point, through the C ABI.  Both run the same products on the same
-fp16 operands in the same order, so their outputs must agree bit for bit, on
-every launch shape: the ping-pong kernel (grids that fit the chip), the
-four-wave kernel (larger grids), a sliding window wider than the streaming
-kernel takes, per-head lambda, a fused strided layout, ragged lengths that
-leave part of the last V^T tile past T.  The full-size workloads are also
-checked against the oracle on sampled rows.  Every case prints its name
-first."""
+plain entry point, through the C ABI.  On grids that fit the chip in one
+round both run the ping-pong kernel, the same products on the same fp16
+operands in the same order, so their outputs must agree bit for bit: small
+and ragged lengths that leave part of the last V^T tile past T, a sliding
+window wider than the streaming kernel takes, per-head lambda, a fused
+strided layout.  On larger grids the workspace path keeps the persistent
+ping-pong kernel while the plain path runs the four-wave kernel: two wave
+groups with their own reference maxima round P differently, so there the
+two are held to the oracle's bounds and to each other within the fp16
+rounding of P.  The full-size workloads are also checked against the oracle
+on sampled rows.  Every case prints its name first."""
 import numpy as np
 import pytest
 
@@ -37,6 +40,24 @@ def _dev_inputs(x, strided=False):
     return tuple(to_dev(x[n]) for n in ("q1", "q2", "k1", "k2", "v"))
 
 
+def _same_kernel(B, T, H):
+    """Both entry points run the ping-pong kernel: the grid of 128-query
+    blocks fits the chip in one round (two blocks per CU)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return (T + 127) // 128 * B * H <= 2 * cus
+
+
+def _agree(plain, pre_a, fast, pre_b, B, T, H):
+    if _same_kernel(B, T, H):
+        assert torch.equal(fast, plain) and torch.equal(pre_b, pre_a)
+        return
+    # different wave splits: the pre-norm outputs differ by the fp16 rounding
+    # of P (relative 2^-11 per probability), averaged over the keys
+    d = float(torch.linalg.vector_norm(pre_b - pre_a) / torch.linalg.vector_norm(pre_a))
+    _say("workspace vs plain (different kernels): pre-norm rel-F %.3g" % d)
+    assert d <= 1e-3
+
+
 def _both(x, lam, window=0, strided=False, out_dtype=torch.float32):
     q1, q2, k1, k2, v = _dev_inputs(x, strided)
     gain = f32_dev(x["gain"])
@@ -63,8 +84,8 @@ def test_vtiles_bitwise_equal_plain(B, T, H, window):
     x = synth.make_prefill_inputs(wl)
     lam = f32_dev(x["lam"])
     plain, pre_a, fast, pre_b = _both(x, lam, window=window)
-    assert torch.equal(fast, plain) and torch.equal(pre_b, pre_a)
-    if T <= 1100:
+    _agree(plain, pre_a, fast, pre_b, B, T, H)
+    if T <= 1100 or not _same_kernel(B, T, H):
         o_ref, y_ref = oracle.prefill(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], x["gain"], x["eps"],
                                       x["scale"], window=window)
         assert_parity(metrics(fast.cpu().numpy(), y_ref, pre_b.cpu().numpy(), o_ref), (B, T, H, window))
@@ -85,7 +106,7 @@ def test_vtiles_workloads(name):
     x = synth.make_prefill_inputs(wl)
     lam = f32_dev(x["lam"]) if wl.lam_range is not None else wl.lam
     plain, pre_a, fast, pre_b = _both(x, lam, out_dtype=torch.bfloat16)
-    assert torch.equal(fast, plain) and torch.equal(pre_b, pre_a)
+    _agree(plain, pre_a, fast, pre_b, wl.B, wl.T, wl.H)
     rng = np.random.default_rng(wl.seed)
     rows = sorted({(b, i, h) for b in {0, wl.B - 1} for h in {0, wl.H - 1} for i in (0, 31, 32, wl.T // 2, wl.T - 1)}
                   | {(int(rng.integers(wl.B)), int(rng.integers(wl.T)), int(rng.integers(wl.H))) for _ in range(24)})
