@@ -3,6 +3,7 @@ traffic from the FETCH_SIZE / WRITE_SIZE counters, written as the text
 summaries kept under profiles/.
 
     python3 profile_kernels.py step            # the benchmark step (prefill + decode)
+    python3 profile_kernels.py variants        # one full bench run: every kernel of the step and the variants
     python3 profile_kernels.py trace NAME      # one workload (bench.py --workload NAME)
     python3 profile_kernels.py pmc NAME        # HBM counters of one workload's kernel
     python3 profile_kernels.py core NAME       # matrix-core busy, LDS and issue counters of its kernel
@@ -185,6 +186,25 @@ def cmd_step():
     _write("prefill_decode_step_kernel_trace.txt", lines)
 
 
+def cmd_variants():
+    """Kernel trace of one full bench run: the step and every variant
+    (backward, RoPE, grouped prefill and decode, windowed prefill and decode,
+    the larger prefills), one line per kernel."""
+    prog = ["python3", "bench.py", "--no-cpu-baseline", "--steps", "20", "--warmup", "5", "--settle", "1"]
+    _, cmd = _rocprof(["--kernel-trace", "--stats"], os.path.join(OUT, "variants"), prog)
+    table = _stats_table(_csv_rows(os.path.join(OUT, "variants"), "kernel_stats.csv"))
+    lines = ["# rocprofv3 kernel-trace summary of one full bench.py run (the step and every variant) on MI355X (gfx950)",
+             "command: " + " ".join(cmd),
+             "# averages over every dispatch of the run, warm-up ones included; a kernel that runs in several",
+             "# variants averages over all of them (prefill_pp_kernel<false, false, true>: the step's prefill and",
+             "# the B=8 and T=16384 prefills; vtiles_kernel: every workspace prefill)",
+             "kernel | calls | avg_us | min_us | max_us"]
+    for name, calls, avg, mn, mx in table:
+        lines.append("%s | %d | %.2f | %.2f | %.2f" % (name, calls, avg, mn, mx))
+    lines.append("kernel_source_sha256_16: %s" % bench.kernel_source_digest())
+    _write("variants_kernel_trace.txt", lines)
+
+
 def cmd_trace(name):
     wl, bound, work, _ = _workload_rate(name)
     prog = ["python3", "bench.py", "--workload", name, "--steps", "50", "--warmup", "20", "--settle", "1"]
@@ -356,12 +376,14 @@ def _write(fname, lines):
 
 
 def main(argv):
-    if len(argv) < 2 or argv[1] not in ("step", "trace", "pmc", "core"):
+    if len(argv) < 2 or argv[1] not in ("step", "variants", "trace", "pmc", "core"):
         print(__doc__)
         return 2
     os.makedirs(OUT, exist_ok=True)
     if argv[1] == "step":
         cmd_step()
+    elif argv[1] == "variants":
+        cmd_variants()
     elif argv[1] == "trace":
         for name in argv[2:]:
             cmd_trace(name)
