@@ -437,11 +437,11 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
   }
 }
 
-// Persistent form: workgroup w = r * B*H + bh runs the query blocks of row r
-// and of row nqb - 1 - r of the longest-first order, both of (b, h) = bh,
-// back to back: the longest block with the shortest, so one workgroup per CU
-// carries the same work everywhere, and a head's blocks stay on the XCD that
-// holds its keys in L2 (B*H a multiple of 8).  An odd middle row runs alone.
+// Persistent form: each workgroup runs the query blocks of row r and of row
+// nqb - 1 - r of the longest-first order, both of one (b, h) = bh, back to
+// back: the longest block with the shortest, so every workgroup carries the
+// same work, and a head's blocks stay on the XCD that holds its keys in L2
+// (B*H a multiple of 8).  An odd middle row runs alone.
 template <bool kTrain, bool kRopeQ, bool kVT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_pp_kernel(PrefillArgs a) {
@@ -451,8 +451,23 @@ prefill_pp_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[pp_smem_bytes<kVT>()];
   const int BH = a.B * a.H;
   const int nqb = (a.T + kBM - 1) / kBM;
-  const int r = (int)blockIdx.x / BH, bh = (int)blockIdx.x % BH;
-  pp_item<kTrain, kRopeQ, kVT>(a, smem, (int)blockIdx.x);
+  const int rows = (nqb + 1) / 2;  // workgroups per (b, h)
+  const int w = (int)blockIdx.x;
+  int r, bh;
+  if (BH % 8 == 0) {
+    // Workgroup w runs on XCD w % 8, which serves heads xcd, xcd + 8, ...
+    // one head after another, all its rows before the next: each XCD's L2
+    // then holds the keys and values of about two heads at a time, where
+    // walking the rows across every head (as dispatched) spreads a round
+    // over all of them (B=8, H=16: 128 heads, 256 MB of K and V).
+    const int xcd = w & 7, s = w >> 3;
+    bh = (s / rows) * 8 + xcd;
+    r = s % rows;
+  } else {
+    r = w / BH;
+    bh = w % BH;
+  }
+  pp_item<kTrain, kRopeQ, kVT>(a, smem, r * BH + bh);
   if (nqb - 1 - r > r) {
     __syncthreads();  // the first block's epilogue is done with LDS
     pp_item<kTrain, kRopeQ, kVT>(a, smem, (nqb - 1 - r) * BH + bh);
