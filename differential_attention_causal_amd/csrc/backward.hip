@@ -645,7 +645,7 @@ constexpr int kDkvStage = 2 * kQKTile + kD16Tile + 4 * 32 * 4;
 constexpr int kOffDo = 2 * kQKTile, kOffSt = kOffDo + kD16Tile;
 
 template <bool kDV>
-__device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int tid) {
+__device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, char* stage1, int tid) {
   const int rt = tid & 255;                                   // thread within its role
   const int rw = __builtin_amdgcn_readfirstlane(rt >> 6);     // wave within its role
   const int lane = tid & 63, hf = lane >> 5, lk = lane & 31;
@@ -688,16 +688,16 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
     if constexpr (kDV) stage_stats(a, b, head, 32 * qt, reinterpret_cast<float*>(st + kOffSt), rt);
   };
   if (qt0 < nqt) {
-    stage_issue(qt0, smem);
-    stage_store(qt0, smem);
+    stage_issue(qt0, stage0);
+    stage_store(qt0, stage0);
   }
   wait_dma();
   __syncthreads();
 
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int it = qt - qt0;
-    char* cur = smem + (it & 1) * kDkvStage;
-    char* nxt = smem + ((it + 1) & 1) * kDkvStage;
+  // The two stages are separate LDS objects and the loop is unrolled by two,
+  // so every step names the stage it reads and the one the next tile's DMA
+  // fills.
+  auto step = [&](int qt, char* cur, char* nxt) __attribute__((always_inline)) {
     const bool more = qt + 1 < nqt;
     if (more) stage_issue(qt + 1, nxt);
     if (wave_live && qt >= diag && qt <= wave_last) {
@@ -771,6 +771,10 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
     if (more) stage_store(qt + 1, nxt);
     wait_dma();
     __syncthreads();
+  };
+  for (int qt = qt0; qt < nqt; qt += 2) {
+    step(qt, stage0, stage1);
+    if (qt + 1 < nqt) step(qt + 1, stage1, stage0);
   }
   if (!ok) return;
   if constexpr (!kDV) {
@@ -791,12 +795,13 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* smem, int 
 }
 
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dkv_kernel(BackwardArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kDkvStage];
+  __shared__ __attribute__((aligned(16))) char stage0[kDkvStage];
+  __shared__ __attribute__((aligned(16))) char stage1[kDkvStage];
   const int tid = threadIdx.x;
   if (__builtin_amdgcn_readfirstlane(tid >> 6) >= kWaves)
-    dkv_role<true>(a, smem, tid);
+    dkv_role<true>(a, stage0, stage1, tid);
   else
-    dkv_role<false>(a, smem, tid);
+    dkv_role<false>(a, stage0, stage1, tid);
 }
 
 }  // namespace
