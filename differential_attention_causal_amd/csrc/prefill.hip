@@ -320,19 +320,46 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
   phase_barrier();
 
   f16x8 p1a, p1b, p2a, p2b;
-  {
+  if constexpr (kVT) {
+    // The ping-pong from the first tile on: group 0 takes its first scores
+    // (matrix), then its softmax beside group 1's first scores, then its
+    // step 0 matrix phase beside group 1's first softmax; each group reads
+    // its slot 0's keys before the barrier that precedes its refill.
     const int j = tile0 + grp;
-    if (live(j)) {
-      f32x16 s1, s2;
-      scores_tile<kRopeQ>(slot0, lq, hf, ksw, qa, qb2, s1, s2);
+    const bool lj = live(j);
+    f32x16 s1, s2;
+    if (grp == 0 && lj) scores_tile<kRopeQ>(slot0, lq, hf, ksw, qa, qb2, s1, s2);
+    phase_barrier();
+    if (grp == 1 && lj) scores_tile<kRopeQ>(slot0, lq, hf, ksw, qa, qb2, s1, s2);
+    if (grp == 0 && lj) {
       mask_tile(a, s1, s2, j, wave_last_tile, q_first, q, hf);
       softmax_step(s1, c, m1, l1, O1, p1a, p1b);
       softmax_step(s2, c, m2, l2, O2, p2a, p2b);
     }
+    phase_barrier();
+    if (grp == 1) {
+      if (lj) {
+        mask_tile(a, s1, s2, j, wave_last_tile, q_first, q, hf);
+        softmax_step(s1, c, m1, l1, O1, p1a, p1b);
+        softmax_step(s2, c, m2, l2, O2, p2a, p2b);
+      }
+      phase_barrier();  // group 0's step 0 matrix phase is done
+    }
+  } else {
+    {
+      const int j = tile0 + grp;
+      if (live(j)) {
+        f32x16 s1, s2;
+        scores_tile<kRopeQ>(slot0, lq, hf, ksw, qa, qb2, s1, s2);
+        mask_tile(a, s1, s2, j, wave_last_tile, q_first, q, hf);
+        softmax_step(s1, c, m1, l1, O1, p1a, p1b);
+        softmax_step(s2, c, m2, l2, O2, p2a, p2b);
+      }
+    }
+    // Every wave is done reading slot 0's keys before step 0 refills them.
+    phase_barrier();
+    if (grp == 1) phase_barrier();  // group 1 starts one phase late
   }
-  // Every wave is done reading slot 0's keys before step 0 refills them.
-  phase_barrier();
-  if (grp == 1) phase_barrier();  // group 1 starts one phase late
 
   // One step of the group with V^T tiles.  piped: the wave has both a live
   // current tile and a live next one, and the matrix phase runs
@@ -432,8 +459,13 @@ __device__ __forceinline__ void pp_item(const PrefillArgs& a, char* smem, int it
     if (grp != 0 || !wave_live) return;
     norm_store(a, b, head, q, hf, O1, reinterpret_cast<const float*>(gain_s));
   } else {
+    // Group 1 issues first in the epilogue: at equal priority the arbiter
+    // favours group 0's waves, and group 1's half of the epilogue finished
+    // last.
+    if (grp == 1) __builtin_amdgcn_s_setprio(1);
     merge_norm_split(a, smem, grp, wq, lane, wave_live, *lam_s, b, head, q, hf, m1, l1, m2, l2, O1, O2,
                      reinterpret_cast<const float*>(gain_s));
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
