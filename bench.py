@@ -368,6 +368,7 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
                      "flop_per_pair": BWD_FLOP_PER_PAIR, "tflops": round(bw_flop / bw_us / 1e6, 2),
                      "frac_mfma_peak": round(bw_flop / bw_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},
         "rope_prefill": {"workload": PREFILL_WL, "rope": "split-half", "theta": ROPE_THETA,
+                         "kernels": "prepass_kernel + prefill_pp_kernel<false, true, true>",
                          "us_mean": round(r_us, 2), "us_min": round(r_min, 2),
                          "tflops": round(r_flop / r_us / 1e6, 2),
                          "frac_mfma_peak": round(r_flop / r_us / 1e6 / MFMA_PEAK_TFLOPS, 4)},

@@ -143,11 +143,12 @@ int ws_pre_pass(diffattn::PrefillArgs& a, void* ws, size_t ws_bytes, hipStream_t
   const size_t rope_part = a.rope.mode != 0 ? 2 * rope_keys_bytes(B, T, H) : 0;
   if (ws_bytes < rope_part + vtiles_bytes(B, T, H) || reinterpret_cast<uintptr_t>(ws) % 256 != 0)
     return DIFFATTN_ERR_WORKSPACE;
-  if (a.rope.mode != 0) {
+  const bool rope = a.rope.mode != 0;
+  diffattn::RopeKeysArgs r{};
+  if (rope) {
     // Rotate both key tensors once into the workspace (fp16, C-contiguous);
     // the prefill then stages them like plain keys.
     const size_t one = rope_keys_bytes(B, T, H);
-    diffattn::RopeKeysArgs r{};
     r.k1 = a.k1;
     r.k2 = a.k2;
     r.s1 = a.sk1;
@@ -158,7 +159,6 @@ int ws_pre_pass(diffattn::PrefillArgs& a, void* ws, size_t ws_bytes, hipStream_t
     r.T = T;
     r.H = H;
     r.rope = a.rope;
-    if (launch && diffattn::launch_rope_keys(r, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
     const diffattn::Strides kc = to_internal(contiguous(T, H, kDqk));
     a.k1 = r.out1;
     a.k2 = r.out2;
@@ -166,20 +166,34 @@ int ws_pre_pass(diffattn::PrefillArgs& a, void* ws, size_t ws_bytes, hipStream_t
     a.sk2 = kc;
     a.keys_rotated = 1;
   }
-  if (diffattn::prefill_takes_vt(a)) {
-    // V converted and transposed once into fp16 V^T tiles that the prefill
-    // kernels move into LDS by DMA.
-    diffattn::VTilesArgs t{};
-    t.v = a.v;
-    t.sv = a.sv;
-    t.B = B;
-    t.T = T;
-    t.H = H;
-    t.ntiles = (T + 31) / 32;
-    t.out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + rope_part);
-    if (launch && diffattn::launch_vtiles(t, hs) != hipSuccess) return DIFFATTN_ERR_HIP;
-    a.vt = t.out;
+  // V converted and transposed once into fp16 V^T tiles that the prefill
+  // kernels move into LDS by DMA (the kernel choice depends on the rotated
+  // keys, so this is asked after the fields above are set).
+  const bool vt = diffattn::prefill_takes_vt(a);
+  diffattn::VTilesArgs t{};
+  t.v = a.v;
+  t.sv = a.sv;
+  t.B = B;
+  t.T = T;
+  t.H = H;
+  t.ntiles = (T + 31) / 32;
+  t.out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + rope_part);
+  // one launch of 256-thread workgroups covers every key vector (32 per
+  // workgroup) and every V^T tile: its work-items must fit 32 bits
+  const int64_t blocks = (rope ? ((int64_t)B * T * H + 31) / 32 : 0) + (vt ? (int64_t)B * H * t.ntiles : 0);
+  if (blocks * 256 > (int64_t)UINT32_MAX) return DIFFATTN_ERR_SHAPE;
+  if (launch) {
+    // with both pre-passes, one launch does the two
+    hipError_t e = hipSuccess;
+    if (rope && vt)
+      e = diffattn::launch_prepass(r, t, hs);
+    else if (rope)
+      e = diffattn::launch_rope_keys(r, hs);
+    else if (vt)
+      e = diffattn::launch_vtiles(t, hs);
+    if (e != hipSuccess) return DIFFATTN_ERR_HIP;
   }
+  if (vt) a.vt = t.out;
   return DIFFATTN_OK;
 }
 

@@ -210,6 +210,9 @@ struct VTilesArgs {
   uint16_t* out;      // [B * H][ntiles][kVtTileBytes / 2]
 };
 hipError_t launch_vtiles(const VTilesArgs& a, hipStream_t stream);
+// The key rotation and the V^T tiles of one rotary prefill in one launch
+// (both results exactly as launch_rope_keys and launch_vtiles give them).
+hipError_t launch_prepass(const RopeKeysArgs& r, const VTilesArgs& t, hipStream_t stream);
 
 // Compute units of the current device, queried once per device and cached.
 int device_cu_count();

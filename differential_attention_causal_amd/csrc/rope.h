@@ -123,6 +123,31 @@ __device__ __forceinline__ void rope_chunks(rope_u32x4 (&v)[kVecs], int ch, uint
   for (int k = 0; k < kVecs; ++k) v[k] = rope_pack<kOutF16>(x[k]);
 }
 
+// One workgroup (256 threads) of the prefill's key pre-pass: key vectors
+// 32 blk .. 32 blk + 31 of the flattened [B, T, H] index, K1 and K2 of one
+// token in the same lanes (they share the angles), rounded to fp16 as the
+// prefill's score products take them and stored C-contiguous.  tab: the 32
+// phases, already in memory the whole workgroup reads.
+__device__ __forceinline__ void rope_keys_block(const RopeKeysArgs& a, int64_t blk, int tid, const uint64_t* tab) {
+  const int64_t vec = blk * 32 + (tid >> 3);
+  const int ch = tid & 7;
+  const int64_t nvec = (int64_t)a.B * a.T * a.H;
+  const bool live = vec < nvec;
+  const int h = live ? (int)(vec % a.H) : 0;
+  const int64_t t = live ? (vec / a.H) % a.T : 0;
+  const int b = live ? (int)(vec / ((int64_t)a.H * a.T)) : 0;
+  rope_u32x4 v[2] = {rope_u32x4{0, 0, 0, 0}, rope_u32x4{0, 0, 0, 0}};
+  if (live) {
+    v[0] = *reinterpret_cast<const rope_u32x4*>(a.k1 + b * a.s1.b + t * a.s1.t + h * a.s1.h + 8 * ch);
+    v[1] = *reinterpret_cast<const rope_u32x4*>(a.k2 + b * a.s2.b + t * a.s2.t + h * a.s2.h + 8 * ch);
+  }
+  rope_chunks<2, true>(v, ch, a.rope.pos0 + (uint32_t)t, a.rope.mode, tab);
+  if (live) {
+    *reinterpret_cast<rope_u32x4*>(a.out1 + vec * 64 + 8 * ch) = v[0];
+    *reinterpret_cast<rope_u32x4*>(a.out2 + vec * 64 + 8 * ch) = v[1];
+  }
+}
+
 // The same on fp32 chunks (no rounding of the result).
 template <int kVecs>
 __device__ __forceinline__ void rope_floats(float (&x)[kVecs][8], int ch, uint32_t pos, int mode,

@@ -50,23 +50,7 @@ __global__ void __launch_bounds__(kThreads) rope_keys_kernel(RopeKeysArgs a) {
   __shared__ uint64_t tab[32];
   if (threadIdx.x < 32) tab[threadIdx.x] = rope_phase_at(a.rope, (int)threadIdx.x);
   __syncthreads();
-  const int64_t vec = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
-  const int ch = threadIdx.x & 7;
-  const int64_t nvec = (int64_t)a.B * a.T * a.H;
-  const bool live = vec < nvec;
-  const int h = live ? (int)(vec % a.H) : 0;
-  const int64_t t = live ? (vec / a.H) % a.T : 0;
-  const int b = live ? (int)(vec / ((int64_t)a.H * a.T)) : 0;
-  rope_u32x4 v[2] = {rope_u32x4{0, 0, 0, 0}, rope_u32x4{0, 0, 0, 0}};
-  if (live) {
-    v[0] = *reinterpret_cast<const rope_u32x4*>(a.k1 + b * a.s1.b + t * a.s1.t + h * a.s1.h + 8 * ch);
-    v[1] = *reinterpret_cast<const rope_u32x4*>(a.k2 + b * a.s2.b + t * a.s2.t + h * a.s2.h + 8 * ch);
-  }
-  rope_chunks<2, true>(v, ch, a.rope.pos0 + (uint32_t)t, a.rope.mode, tab);
-  if (live) {
-    *reinterpret_cast<rope_u32x4*>(a.out1 + vec * 64 + 8 * ch) = v[0];
-    *reinterpret_cast<rope_u32x4*>(a.out2 + vec * 64 + 8 * ch) = v[1];
-  }
+  rope_keys_block(a, (int64_t)blockIdx.x, (int)threadIdx.x, tab);
 }
 
 }  // namespace

@@ -12,6 +12,7 @@
 // distinct bank groups.  Keys at or past T are zero (their probabilities are
 // zero, and zero values keep 0 * v finite).
 #include "kernels.h"
+#include "rope.h"
 #include "tile.h"
 
 namespace diffattn {
@@ -31,14 +32,13 @@ constexpr int kThreads = 256;
 // addresses.
 constexpr int kLdsRow = 68;  // bytes per channel row in LDS: 64 + 4 of padding
 
-__global__ void __launch_bounds__(kThreads) vtiles_kernel(VTilesArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kDv * kLdsRow];
-  const int64_t g = blockIdx.x;
+// Tile g (flattened over (b, h, tile)) by the 256 threads of one workgroup;
+// lds: kDv * kLdsRow bytes, 16-byte aligned.
+__device__ __forceinline__ void vtiles_tile(const VTilesArgs& a, int64_t g, int t, char* lds) {
   const int j = (int)(g % a.ntiles);
   const int64_t bh = g / a.ntiles;
   const int h = (int)(bh % a.H);
   const int b = (int)(bh / a.H);
-  const int t = threadIdx.x;
   const uint16_t* src = a.v + (int64_t)b * a.sv.b + (int64_t)h * a.sv.h;
   const int kr = 2 * (t >> 4), ch0 = 8 * (t & 15);  // key rows kr, kr + 1 of the tile; first channel
   u32x4 w[2];
@@ -69,11 +69,46 @@ __global__ void __launch_bounds__(kThreads) vtiles_kernel(VTilesArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(kThreads) vtiles_kernel(VTilesArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kDv * kLdsRow];
+  vtiles_tile(a, (int64_t)blockIdx.x, (int)threadIdx.x, lds);
+}
+
+// Both workspace pre-passes of a rotary prefill in one launch: workgroups
+// below rope_blocks rotate the keys (32 key vectors each), the rest build one
+// V^T tile each.  The two share no data, so one launch lets their memory
+// traffic overlap and saves the gap between two launches; each workgroup
+// computes exactly what the separate kernels compute.
+struct PrepassArgs {
+  RopeKeysArgs r;
+  VTilesArgs t;
+  int64_t rope_blocks;
+};
+
+__global__ void __launch_bounds__(kThreads) prepass_kernel(PrepassArgs p) {
+  __shared__ __attribute__((aligned(16))) char lds[kDv * kLdsRow];
+  const int64_t g = blockIdx.x;
+  if (g < p.rope_blocks) {
+    uint64_t* tab = reinterpret_cast<uint64_t*>(lds);
+    if (threadIdx.x < 32) tab[threadIdx.x] = rope_phase_at(p.r.rope, (int)threadIdx.x);
+    __syncthreads();
+    rope_keys_block(p.r, g, (int)threadIdx.x, tab);
+  } else {
+    vtiles_tile(p.t, g - p.rope_blocks, (int)threadIdx.x, lds);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_vtiles(const VTilesArgs& a, hipStream_t stream) {
   const int64_t tiles = (int64_t)a.B * a.H * a.ntiles;
   return launch_kernel(vtiles_kernel, dim3((unsigned)tiles), dim3(kThreads), stream, a);
+}
+
+hipError_t launch_prepass(const RopeKeysArgs& r, const VTilesArgs& t, hipStream_t stream) {
+  PrepassArgs p{r, t, ((int64_t)r.B * r.T * r.H + 31) / 32};
+  const int64_t tiles = (int64_t)t.B * t.H * t.ntiles;
+  return launch_kernel(prepass_kernel, dim3((unsigned)(p.rope_blocks + tiles)), dim3(kThreads), stream, p);
 }
 
 }  // namespace diffattn

@@ -213,14 +213,21 @@ DIFFATTN_API size_t diffattn_prefill_workspace_bytes(const diffattn_options* opt
  * query blocks no longer repeat the rotation of the keys they share.  V is
  * converted once to fp16 (the same exact conversion the kernels otherwise
  * apply while staging each tile) into transposed 32-key tiles that the
- * prefill kernels move into LDS by DMA.  The results equal those of
- * diffattn_fwd_prefill_ex bit for bit (same products, same order); a sliding
- * window of at most 129 keys uses the workspace only for the rotated keys.
- * Without rope the workspace may be NULL (then it is the plain entry point).
+ * prefill kernels move into LDS by DMA; with rope, one launch does both
+ * pre-passes.  Where the grid of 128-query blocks fits the chip in one round
+ * (two per compute unit) both entry points run the same kernel and the
+ * results equal those of diffattn_fwd_prefill_ex bit for bit (same products,
+ * same order); on larger grids the workspace path keeps the persistent
+ * two-group kernel, whose per-group reference maxima round P to fp16
+ * differently, so the two differ within that rounding.  A sliding window of
+ * at most 129 keys uses the workspace only for the rotated keys.  Without
+ * rope the workspace may be NULL (then it is the plain entry point).
  *   workspace : >= diffattn_prefill_workspace_bytes(opt, B, T, H) bytes,
  *               256-byte aligned; contents need no initialisation
  * Errors as for diffattn_fwd_prefill_ex, plus DIFFATTN_ERR_WORKSPACE (a
- * missing workspace with rope on, or a misaligned or too small one).  The
+ * missing workspace with rope on, or a misaligned or too small one) and
+ * DIFFATTN_ERR_SHAPE when the pre-pass launch would exceed 2^32 work-items
+ * (256 per V^T tile and per 32 rotated key vectors).  The
  * workspace is overwritten on the stream: calls that share one must not
  * overlap.
  */

@@ -163,6 +163,39 @@ def test_prefill_rope_large_sampled(mode, B, T, H, ws):
     assert_parity(m, (mode, B, T, H))
 
 
+@pytest.mark.parametrize("mode,B,T,H,pos0", [(1, 1, 100, 3, 0), (2, 2, 1000, 4, 17), (1, 1, 4096, 16, 0)])
+def test_prepared_rope_workspace_contents(mode, B, T, H, pos0):
+    """The pre-pass alone (diffattn_prefill_prepare with rope: the key
+    rotation and the V^T tiles in one launch).  The rotated keys at the head
+    of the workspace (fp16, C-contiguous, K1 then K2 at 256-byte aligned
+    offsets) are held to the fp64 rotation within fp16 rounding; the V^T tiles
+    after them equal, byte for byte, those that the preparation without rope
+    writes (the two workspaces start from different fill bytes, so equal
+    bytes mean both were written)."""
+    _say("prepared rope workspace contents", mode, B, T, H, "pos0", pos0)
+    wl = Workload("rws", "prefill", B=B, T=T, H=H, seed=900 + T + mode, lam=0.5)
+    x = synth.make_prefill_inputs(wl)
+    k1, k2, v = to_dev(x["k1"]), to_dev(x["k2"]), to_dev(x["v"])
+    need_r = da.diffattn_prefill_workspace_bytes(B, T, H, rope=mode)
+    need_p = da.diffattn_prefill_workspace_bytes(B, T, H)
+    one = (B * T * H * 64 * 2 + 255) // 256 * 256
+    assert need_r == 2 * one + need_p
+    ws_r = torch.full((need_r,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws_p = torch.full((need_p,), 0xA5, dtype=torch.uint8, device="cuda")
+    da.diffattn_prefill_prepare(k1, k2, v, ws_r, rope=mode, rope_theta=THETA, rope_pos0=pos0)
+    da.diffattn_prefill_prepare(k1, k2, v, ws_p)
+    torch.cuda.synchronize()
+    assert torch.equal(ws_r[2 * one:], ws_p)
+    n = B * T * H * 64
+    for i, name in enumerate(("k1", "k2")):
+        got = ws_r[i * one:i * one + 2 * n].view(torch.float16).float().cpu().numpy().astype(np.float64)
+        ref = oracle.rope(x[name], mode, THETA, pos0=pos0).reshape(-1)
+        err = np.abs(got - ref)
+        _say(name, "max err", float(err.max()))
+        # fp16 rounding (half an ulp, 2^-11 relative) plus the angle's error
+        assert (err <= np.abs(ref) * 2.0 ** -10 + 2e-5).all(), (name, float(err.max()))
+
+
 def test_prefill_rope_shift_invariance():
     _say("prefill rope: moving every token leaves the result (up to rounding)")
     x = _inputs(1, 400, 2, seed=9)
