@@ -102,7 +102,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int diffattn_abi_version(void) { return 111; }
+int diffattn_abi_version(void) { return 112; }
 
 const char* diffattn_status_string(int status) {
   switch (status) {
@@ -629,7 +629,7 @@ int diffattn_rope_apply(const void* x, const diffattn_strides* x_strides, void* 
 
 size_t diffattn_grouped_workspace_bytes(int B, int T, int n_heads, int group, int d_v) {
   if (B <= 0 || T <= 0 || n_heads <= 0 || group <= 0 || n_heads % (group + 1) != 0 || d_v != kDv) return 0;
-  return (size_t)B * T * n_heads * kDv * sizeof(float);
+  return (size_t)B * T * n_heads * kDv * sizeof(float) + vtiles_bytes(B, T, n_heads);
 }
 
 int diffattn_fwd_grouped(const void* q, const void* k, const void* v, const diffattn_strides* strides, int B, int T,
@@ -674,6 +674,12 @@ int diffattn_fwd_grouped(const void* q, const void* k, const void* v, const diff
   a.out = out;
   a.out_f32 = out_dtype == DIFFATTN_OUT_F32;
   a.hw = static_cast<float*>(workspace);
+  // fp16 V^T tiles after the head outputs, for the ping-pong kernel, which
+  // addresses a head's key rows with 32-bit offsets (up to about T + 320
+  // rows) and whose pre-pass covers every tile with one 256-thread workgroup
+  const int64_t tiles = (int64_t)B * n_heads * ((T + 31) / 32);
+  if ((int64_t)(T + 320) * a.sk.t * 2 < (int64_t(1) << 31) && tiles * 256 <= (int64_t)UINT32_MAX)
+    a.vt = reinterpret_cast<const uint16_t*>(static_cast<char*>(workspace) + (size_t)B * T * n_heads * kDv * 4);
   if (diffattn::launch_grouped(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DIFFATTN_ERR_HIP;
   return DIFFATTN_OK;
 }

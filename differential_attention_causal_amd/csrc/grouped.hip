@@ -331,6 +331,216 @@ grouped_pp_kernel(GroupedArgs a) {
   }
 }
 
+// The same ping-pong form with fp16 V^T tiles (vtiles.hip): keys and values
+// both come by DMA, and no V conversion is left in the key loop.
+// Each group cycles through kVtGSlots slots: tile x sits in slot x % kVtGSlots,
+// K(x + kVtGSlots) goes into slot x's key half in the matrix phase of step x
+// (K(x) was read in the step before) and V(x + kVtGSlots) into its value half
+// in the vector phase (the matrix phase has read V(x)).  Workgroups run
+// query-block rows r and nqb - 1 - r of one (b, head) back to back.
+constexpr int kVtGTile = kKBytes + kVtTileBytes;  // a group's key and V^T tiles
+constexpr int kVtGStage = 2 * kVtGTile;             // one slot of both groups
+constexpr int kVtGSlots = 4;
+constexpr int kVtGSmem = kVtGSlots * kVtGStage > kMergeBytes ? kVtGSlots * kVtGStage : kMergeBytes;
+// Vector-memory instructions issued after K(x + 2) by the time the vector
+// phase of step x ends: V(x + 2), then K(y), V(y) for y = x + 3 .. x + slots
+// (one key instruction, two value instructions per tile).
+constexpr int kVtGYounger = 2 + 3 * (kVtGSlots - 2);
+
+__device__ __forceinline__ void gppvt_block(const GroupedArgs& a, char* smem, int item) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / 4, wq = wave % 4;
+  const int lane = tid & 63, hf = lane >> 5, lq = lane & 31, rt = tid & 255;
+  const int nqb = (a.T + kBM - 1) / kBM, BH = a.B * a.nH;
+  const int qb = nqb - 1 - item / BH;
+  const int bh = item % BH, head = bh % a.nH, b = bh / a.nH;
+  const int q_first = qb * kBM + 32 * wq, q = q_first + lq;
+  const bool wave_live = q_first < a.T, ok = q < a.T;
+  const int ntiles = min(qb * (kBM / kBN) + kBM / kBN, (a.T + kBN - 1) / kBN);
+  const int nsteps = (ntiles + 1) / 2;
+  const int kend = min(a.T, ntiles * kBN);
+  const int last_tile = q_first / kBN;
+  auto live = [&](int j) { return wave_live && j <= last_tile; };
+
+  const uint16_t* kb = a.k + (int64_t)b * a.sk.b + (int64_t)head * a.sk.h;
+  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kb, a.sk.t, 0, kend, kDqk);
+  const __amdgpu_buffer_rsrc_t rvt = vt_tiles_rsrc(a.vt, (int64_t)b * a.nH + head, a.T);
+  const uint32_t ks = (uint32_t)(a.sk.t * 2);
+  // DMA: thread rt of the group fetches key row rt / 8, logical chunk
+  // (rt % 8) ^ kSwz(row), landing at chunk position rt of the group's tile.
+  const int kr = rt >> 3;
+  const uint32_t koff = (uint32_t)((kr * a.sk.t + 8 * ((rt & 7) ^ kSwz(kr))) * 2);
+  auto key0 = [&](int x) { return (2 * x + grp) * kBN; };  // first key of the group's tile of step x
+  char* const slot0 = smem + grp * kVtGTile;
+  auto slot = [&](int x) { return slot0 + (x % kVtGSlots) * kVtGStage; };
+  auto dma_k = [&](int x) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(slot(x) + wq * 1024), 16, koff + (uint32_t)key0(x) * ks,
+                                             0, 0, 0);
+  };
+  auto dma_v = [&](int x) { dma_vt(rvt, slot(x) + kKBytes, 2 * x + grp, wq, lane); };
+
+  // Prologue: the first three tiles' DMAs go out first, the queries load
+  // under their latency, then the rest of the slots fill; the wait leaves
+  // only V(1) .. V(slots - 1) and K(2) .. K(slots - 1) in flight.
+  dma_k(0);
+  dma_v(0);
+  dma_k(1);
+  bf16x8 qa[4];
+  {
+    const uint16_t* p = a.q + (int64_t)b * a.sq.b + (int64_t)q * a.sq.t + (int64_t)head * a.sq.h + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = ok ? *reinterpret_cast<const bf16x8*>(p + 16 * s) : bf16x8{};
+  }
+  dma_v(1);
+#pragma unroll
+  for (int x = 2; x < kVtGSlots; ++x) {
+    dma_k(x);
+    dma_v(x);
+  }
+  wait_vm<kVtGYounger>();
+  wait_lds();
+  phase_barrier();
+
+  f32x16 O[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  float m = kNoMax, l = 0.f;
+  const float c = a.c;
+  const int ksw = kSwz(lq);
+  auto scores = [&](const char* kt) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(kt + lq * kKRow + (((2 * k + hf) ^ ksw) << 4)), qa[k], s, 0, 0, 0);
+    return s;
+  };
+  auto mask = [&](f32x16& s, int j) {
+    if (j == last_tile) {
+      // key row 8(i/4) + 4hf + i%4 of tile j is key 32j + row: visible iff <= q
+      const int hi = q - j * kBN - 4 * hf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) > hi) s[i] = -__builtin_inff();
+    }
+  };
+  // O += V^T P for channel blocks cb, cb + 1 (consecutive products on
+  // different accumulators).
+  auto pv_pair = [&](const char* st, int cb, const f16x8& pa, const f16x8& pb) {
+    const char* vt = st + kKBytes;
+    const f16x8 a0 = vt_operand(vt, lq, hf, cb, 0), b0 = vt_operand(vt, lq, hf, cb + 1, 0);
+    O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, pa, O[cb], 0, 0, 0);
+    O[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, pa, O[cb + 1], 0, 0, 0);
+    const f16x8 a1 = vt_operand(vt, lq, hf, cb, 1), b1 = vt_operand(vt, lq, hf, cb + 1, 1);
+    O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, pb, O[cb], 0, 0, 0);
+    O[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, pb, O[cb + 1], 0, 0, 0);
+  };
+
+  // The ping-pong from the first tile: group 0 takes its first scores, then
+  // its softmax beside group 1's first scores, then its step 0 matrix phase
+  // beside group 1's first softmax.  Each group reads its slot 0's keys
+  // before the barrier that precedes their refill.
+  f16x8 pa, pb;
+  {
+    const bool l0 = live(grp);
+    f32x16 s;
+    if (grp == 0 && l0) s = scores(slot(0));
+    phase_barrier();
+    if (grp == 1 && l0) s = scores(slot(0));
+    if (grp == 0 && l0) {
+      mask(s, 0);
+      softmax_step(s, c, m, l, O, pa, pb);
+    }
+    phase_barrier();
+    if (grp == 1) {
+      if (l0) {
+        mask(s, 1);
+        softmax_step(s, c, m, l, O, pa, pb);
+      }
+      phase_barrier();  // group 0's step 0 matrix phase is done
+    }
+  }
+
+  for (int it = 0; it < nsteps; ++it) {
+    char* cur = slot(it);
+    char* nxt = slot(it + 1);
+    const int j = 2 * it + grp;
+    const bool next = it + 1 < nsteps && live(j + 2);
+    // Matrix phase (raised issue priority: its products go first whenever
+    // both waves of a SIMD are ready).
+    __builtin_amdgcn_s_setprio(1);
+    f32x16 s;
+    const bool lj = live(j);
+    if (lj) pv_pair(cur, 0, pa, pb);
+    // K(it + slots) into slot it's key half, issued once the first products
+    // are queued.  Unconditional: past the last tile the loads read zeros
+    // into a slot nobody reads again, and the wait counts stay the same on
+    // every iteration.
+    __builtin_amdgcn_sched_barrier(0);
+    dma_k(it + kVtGSlots);
+    __builtin_amdgcn_sched_barrier(0);
+    if (lj) pv_pair(cur, 2, pa, pb);
+    if (next) s = scores(nxt);
+    __builtin_amdgcn_s_setprio(0);
+    phase_barrier();
+    // Vector phase: V(it + slots) into slot it's value half (every wave of
+    // the group has read V(it)), then the softmax of the next tile.
+    dma_v(it + kVtGSlots);
+    if (next) {
+      mask(s, j + 2);
+      softmax_step(s, c, m, l, O, pa, pb);
+    }
+    wait_vm<kVtGYounger>();  // K(it + 2) and V(it + 1) have landed
+    phase_barrier();
+  }
+  if (grp == 0) phase_barrier();
+  wait_vm<0>();  // the zero-filling loads past the last tile, before the merge reuses LDS
+  __syncthreads();
+
+  merge_map(smem, grp, wq, lane, wave_live, m, l, O);
+  if (grp != 0) return;
+  l += __shfl_xor(l, 32);
+  if (!ok) return;
+  const float r = 1.0f / l;
+  float* dst = a.hw + (((int64_t)b * a.T + q) * a.nH + head) * kDv;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = O[cb][4 * r4 + i] * r;
+      *reinterpret_cast<f32x4*>(dst + 32 * cb + 8 * r4 + 4 * hf) = o;
+    }
+}
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+grouped_ppvt_kernel(GroupedArgs a) {
+  // One LDS object: no per-object alias scopes, so the compiler adds no waits
+  // of its own for the DMAs before LDS reads (the explicit ones order them).
+  __shared__ __attribute__((aligned(16))) char smem[kVtGSmem];
+  const int BH = a.B * a.nH;
+  const int nqb = (a.T + kBM - 1) / kBM;
+  const int rows = (nqb + 1) / 2;
+  // Workgroup w runs on XCD w % 8.  With B * nH a multiple of 8, XCD x takes
+  // heads x, x + 8, ... one after another, every row of a head before the
+  // next, so its L2 holds the keys and values of few heads at a time.
+  const int w = (int)blockIdx.x;
+  int r, bh;
+  if (BH % 8 == 0) {
+    const int xcd = w & 7, s = w >> 3;
+    bh = (s / rows) * 8 + xcd;
+    r = s % rows;
+  } else {
+    r = w / BH;
+    bh = w % BH;
+  }
+  gppvt_block(a, smem, r * BH + bh);
+  if (nqb - 1 - r > r) {
+    __syncthreads();  // the first block's epilogue is done with LDS
+    gppvt_block(a, smem, (nqb - 1 - r) * BH + bh);
+  }
+}
+
 // out_s = sigmoid(G_s) * (H_s - lambda_t,s * H_(nS + s / g)): 32 threads per
 // (b, t, s) row, four channels each.
 __global__ void __launch_bounds__(256) grouped_combine_kernel(GroupedArgs a) {
@@ -363,18 +573,40 @@ __global__ void __launch_bounds__(256) grouped_combine_kernel(GroupedArgs a) {
 }  // namespace
 
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream) {
-  const int64_t grid = (int64_t)((a.T + kBM - 1) / kBM) * a.B * a.nH;
-  const int cus = device_cu_count();
-  const bool split = grid <= 2 * (int64_t)cus;
-  // The ping-pong form addresses a head's key rows from one buffer base with
-  // 32-bit offsets (up to about T + 192 rows).
-  const int64_t row_max = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
+  const int64_t nqb = (a.T + kBM - 1) / kBM;
+  const int64_t grid = nqb * a.B * a.nH;
+  const int64_t cus = device_cu_count();
+  const int64_t pairs = (nqb + 1) / 2 * a.B * a.nH;
+  // The V^T form's workgroups all carry equal work (a long block with a
+  // short one), so its grid must fill its rounds (a last round nearly empty
+  // costs a whole round), and its pre-pass (V read and written once) pays
+  // off against a one-round grid of the register-staged ping-pong kernel
+  // only for long sequences.  Measured, 16 heads: B=1, T=16384 1071 against
+  // 1285 us (four-wave kernel); B=1, T=4096 97.7 against 95.3 us; B=4,
+  // T=1100 (288 pairs: two rounds, the second an eighth full) 81 against 57.
+  const int64_t rounds = (pairs + cus - 1) / cus;
+  const bool filled = pairs * 10 >= rounds * cus * 9;
+  const bool one_round = grid <= 2 * cus;
   hipError_t e;
-  if (split && (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31)) {
-    const int64_t nqb = (a.T + kBM - 1) / kBM;
-    e = launch_kernel(grouped_pp_kernel, dim3((unsigned)((nqb + 1) / 2 * a.B * a.nH)), dim3(512), stream, a);
-  } else if (split) {
-    e = launch_kernel(grouped_attn_kernel<2>, dim3((unsigned)grid), dim3(512), stream, a);
+  if (a.vt != nullptr && filled && (!one_round || a.T >= 8192)) {
+    VTilesArgs t{};
+    t.v = a.v;
+    t.sv = a.sv;
+    t.B = a.B;
+    t.T = a.T;
+    t.H = a.nH;
+    t.ntiles = (a.T + kBN - 1) / kBN;
+    t.out = const_cast<uint16_t*>(a.vt);
+    if ((e = launch_vtiles(t, stream)) != hipSuccess) return e;
+    e = launch_kernel(grouped_ppvt_kernel, dim3((unsigned)pairs), dim3(512), stream, a);
+  } else if (one_round) {
+    // The register-staged ping-pong form addresses a head's key and value
+    // rows from one buffer base with 32-bit offsets (up to about T + 192 rows).
+    const int64_t row_max = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
+    if ((int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31))
+      e = launch_kernel(grouped_pp_kernel, dim3((unsigned)pairs), dim3(512), stream, a);
+    else
+      e = launch_kernel(grouped_attn_kernel<2>, dim3((unsigned)grid), dim3(512), stream, a);
   } else {
     e = launch_kernel(grouped_attn_kernel<1>, dim3((unsigned)grid), dim3(256), stream, a);
   }

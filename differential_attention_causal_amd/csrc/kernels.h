@@ -162,6 +162,7 @@ struct GroupedArgs {
   void* out;             // [B, T, nS, kDv] bf16 or fp32
   int out_f32;
   float* hw;             // workspace [B, T, nH, kDv] fp32: every head's normalised output
+  const uint16_t* vt;    // workspace for fp16 V^T tiles (vtiles.hip) of every (b, head), or null
 };
 
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream);

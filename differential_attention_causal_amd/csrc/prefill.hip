@@ -707,6 +707,7 @@ struct PrefillPlan {
   bool pp_fits;   // prefill_pp_kernel can take this call
   bool window;    // the streaming window kernel (window.hip)
   bool takes_vt;  // the chosen kernel can read V^T tiles (vtiles.hip)
+  bool filled;    // the ping-pong kernel's pairs fill their rounds (>= 90%)
 };
 
 PrefillPlan plan_prefill(const PrefillArgs& a) {
@@ -718,7 +719,11 @@ PrefillPlan plan_prefill(const PrefillArgs& a) {
   // splitting each workgroup's key range over two wave groups halves that
   // tail.  Larger grids with V in registers balance by themselves in
   // longest-first order and run better as independent 4-wave workgroups.
-  p.split = p.grid <= 2 * (int64_t)device_cu_count();
+  const int64_t cus = device_cu_count();
+  p.split = p.grid <= 2 * cus;
+  const int64_t pairs = (int64_t)((p.nqb + 1) / 2) * a.B * a.H;
+  const int64_t rounds = (pairs + cus - 1) / cus;
+  p.filled = pairs * 10 >= rounds * cus * 9;
   const int64_t row_max = std::max(std::max(a.sk1.t, a.sk2.t), a.sv.t);
   // Keys already rotated (fp16 copies): they are staged like plain keys, and
   // only the queries turn inside the kernels.
@@ -746,12 +751,16 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (p.window) return launch_prefill_window(a, stream);
   const bool vt = a.vt != nullptr && p.takes_vt;
   const int nqb = p.nqb;
-  // With V^T tiles the persistent ping-pong kernel runs every grid size: its
-  // workgroups carry equal work (a long query block with a short one), so a
-  // grid of several rounds stays balanced, and it beats the four-wave kernel
-  // there too (B=1, T=16384, H=16: 11% faster).  With V in registers the
-  // four-wave kernel is the faster one once the grid exceeds one round.
-  if (p.pp_fits && (p.split || vt)) {
+  // With V^T tiles the persistent ping-pong kernel also runs grids of several
+  // rounds whose pairs fill them: its workgroups carry equal work (a long
+  // query block with a short one), so such a grid stays balanced, and it
+  // beats the four-wave kernel there (B=1, T=16384, H=16: 11% faster; B=2,
+  // T=6000: 10%).  A last round left mostly empty costs a whole round of
+  // equal workgroups, while the four-wave kernel's longest-first blocks fill
+  // it with the short ones (B=4, T=1100, H=16, 320 pairs on 256 CUs: 96
+  // against 55 us).  With V in registers the four-wave kernel is the faster
+  // one once the grid exceeds one round.
+  if (p.pp_fits && (p.split || (vt && p.filled))) {
     const dim3 gp((unsigned)((int64_t)((nqb + 1) / 2) * a.B * a.H));
     if (p.prerot)
       return vt ? launch_kernel(prefill_pp_kernel<false, true, true>, gp, dim3(512), stream, a)

@@ -83,30 +83,9 @@ __device__ __forceinline__ void stage_dma_k(const PrefillArgs& a, const uint16_t
                                            16, off.k2, 0, 0, 0);
 }
 
-// Buffer resource over one (b, h)'s fp16 V^T tiles (vtiles.hip): tiles past
-// the last read as zero.
+// Buffer resource over one (b, h)'s fp16 V^T tiles (vtiles.hip).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t vt_rsrc(const PrefillArgs& a, int b, int head) {
-  const int nt = (a.T + kBN - 1) / kBN;
-  const uint16_t* p = a.vt + ((int64_t)b * a.H + head) * nt * (kVtTileBytes / 2);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)rows_extent_bytes(kVtTileBytes / 2, 0, nt, kVtTileBytes / 2),
-                                           0x00020000);
-}
-
-// Memory -> LDS of one 8 KiB V^T tile by the four waves that stage it: wave
-// `part` moves bytes 2048 part .. +2047 (two loads of 64 lanes x 16 bytes).
-// The instruction's immediate offset would move the LDS destination as well,
-// so the second half's 1 KiB step goes into the per-lane offset.
-__device__ __forceinline__ void dma_vt(__amdgpu_buffer_rsrc_t r, char* vt_lds, int tile, int part, int lane) {
-  char* dst = vt_lds + part * 2048;
-  const uint32_t off = (uint32_t)tile * kVtTileBytes + part * 2048 + lane * 16;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 1024), 16, off + 1024, 0, 0, 0);
-}
-
-// The V^T operand of one P V product from a DMA'd tile: channel row
-// 32 cb + lq, keys 16 s .. 16 s + 15, lane half hf's eight (one swizzled chunk).
-__device__ __forceinline__ f16x8 vt_operand(const char* vt, int lq, int hf, int cb, int s) {
-  return *reinterpret_cast<const f16x8*>(vt + (32 * cb + lq) * 64 + (((2 * s + hf) ^ ((lq >> 2) & 3)) << 4));
+  return vt_tiles_rsrc(a.vt, (int64_t)b * a.H + head, a.T);
 }
 
 __device__ __forceinline__ u32x4 load_krow(__amdgpu_buffer_rsrc_t r, uint32_t off, bool split) {

@@ -47,6 +47,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, nrec, 0x00020000);
 }
 
+// Buffer resource over the fp16 V^T tiles (vtiles.hip) of the bh-th (b, h)
+// of a T-key tensor: tiles past the last read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t vt_tiles_rsrc(const uint16_t* vt, int64_t bh, int T) {
+  const int nt = (T + 31) / 32;
+  const uint16_t* p = vt + bh * nt * (kVtTileBytes / 2);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0,
+                                           (int)rows_extent_bytes(kVtTileBytes / 2, 0, nt, kVtTileBytes / 2),
+                                           0x00020000);
+}
+
+// Memory -> LDS of one 8 KiB V^T tile by the four waves that stage it: wave
+// `part` moves bytes 2048 part .. +2047 (two loads of 64 lanes x 16 bytes).
+// The instruction's immediate offset would move the LDS destination as well,
+// so the second half's 1 KiB step goes into the per-lane offset.
+__device__ __forceinline__ void dma_vt(__amdgpu_buffer_rsrc_t r, char* vt_lds, int tile, int part, int lane) {
+  char* dst = vt_lds + part * 2048;
+  const uint32_t off = (uint32_t)tile * kVtTileBytes + part * 2048 + lane * 16;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 1024), 16, off + 1024, 0, 0, 0);
+}
+
+// The V^T operand of one P V product from a DMA'd tile: channel row
+// 32 cb + lq, keys 16 s .. 16 s + 15, lane half hf's eight (one swizzled chunk).
+__device__ __forceinline__ f16x8 vt_operand(const char* vt, int lq, int hf, int cb, int s) {
+  return *reinterpret_cast<const f16x8*>(vt + (32 * cb + lq) * 64 + (((2 * s + hf) ^ ((lq >> 2) & 3)) << 4));
+}
+
 // Waits for this wave's outstanding memory loads, the LDS-destination ones
 // included (vmcnt 0; export and LDS counters left alone).
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -217,9 +217,11 @@ DIFFATTN_API size_t diffattn_prefill_workspace_bytes(const diffattn_options* opt
  * pre-passes.  Where the grid of 128-query blocks fits the chip in one round
  * (two per compute unit) both entry points run the same kernel and the
  * results equal those of diffattn_fwd_prefill_ex bit for bit (same products,
- * same order); on larger grids the workspace path keeps the persistent
- * two-group kernel, whose per-group reference maxima round P to fp16
- * differently, so the two differ within that rounding.  A sliding window of
+ * same order); on larger grids whose long/short query-block pairs fill
+ * their rounds of the chip the workspace path keeps the persistent two-group
+ * kernel, whose per-group reference maxima round P to fp16 differently, so
+ * the two differ within that rounding (other grids run the four-wave kernel
+ * on both paths).  A sliding window of
  * at most 129 keys uses the workspace only for the rotated keys.  Without
  * rope the workspace may be NULL (then it is the plain entry point).
  *   workspace : >= diffattn_prefill_workspace_bytes(opt, B, T, H) bytes,
@@ -419,8 +421,12 @@ DIFFATTN_API int diffattn_bwd_prefill_ex(const diffattn_options* opt, const void
  *   scale       : score factor; <= 0 selects 1/sqrt(d_qk)
  *   out         : [B, T, n_S, d_v] bf16 or fp32 per out_dtype
  *   workspace   : >= diffattn_grouped_workspace_bytes() bytes, 16-byte
- *                 aligned: every head's normalised output (fp32), each noise
- *                 head's computed once
+ *                 aligned, contents need no initialisation: every head's
+ *                 normalised output (fp32, B * T * n_heads * d_v * 4 bytes),
+ *                 each noise head's computed once, then V converted once into
+ *                 fp16 transposed 32-key tiles that the attention kernel
+ *                 moves into LDS by DMA (B * n_heads * ceil(T / 32) * 8192
+ *                 bytes)
  * Errors: DIFFATTN_ERR_SHAPE also when n_heads is not a multiple of group + 1.
  */
 DIFFATTN_API size_t diffattn_grouped_workspace_bytes(int B, int T, int n_heads, int group, int d_v);
@@ -474,7 +480,8 @@ DIFFATTN_API const char* diffattn_status_string(int status);
  * 107 diffattn_fwd_decode_noalloc, 108 V^T tiles in the prefill workspace,
  * 109 diffattn_prefill_prepare and diffattn_options.ws_prepared, 110 the
  * training forward and backward with windows and RoPE (_train_ex, _bwd_prefill_ex),
- * 111 the grouped decode (diffattn_fwd_grouped_decode)
+ * 111 the grouped decode (diffattn_fwd_grouped_decode), 112 V^T tiles in the
+ * grouped prefill's workspace (query diffattn_grouped_workspace_bytes again)
  * (query diffattn_prefill_workspace_bytes again). */
 DIFFATTN_API int diffattn_abi_version(void);
 

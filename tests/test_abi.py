@@ -35,7 +35,7 @@ def test_header_symbols_exported():
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da.diffattn_abi_version() == 111
+    assert da.diffattn_abi_version() == 112
 
 
 def test_status_strings():
@@ -315,7 +315,8 @@ def test_grouped_rejects(kw, rc):
 
 
 def test_grouped_workspace_bytes():
-    assert da.diffattn_grouped_workspace_bytes(2, 100, 8, 3, 128) == 2 * 100 * 8 * 128 * 4
+    # fp32 head outputs, then 8 KiB fp16 V^T tiles per (b, head) and 32 keys
+    assert da.diffattn_grouped_workspace_bytes(2, 100, 8, 3, 128) == 2 * 100 * 8 * 128 * 4 + 2 * 8 * 4 * 8192
     assert da.diffattn_grouped_workspace_bytes(2, 100, 8, 2, 128) == 0
     assert da.diffattn_grouped_workspace_bytes(2, 100, 8, 3, 64) == 0
 

@@ -101,9 +101,9 @@ def test_grouped_motif3_shape_every_row():
 
 
 def test_grouped_large_grid_sampled():
-    # B=4, T=1100, 16 heads: 9 query blocks x 64 (b, head) = 576 workgroups, more
-    # than two per CU, so the four-wave kernel runs instead of the ping-pong one
-    _say("grouped B=4 T=1100 n_H=16 g=3 (four-wave grid)")
+    # B=4, T=1100, 16 heads: 9 query blocks x 64 (b, head) = 576 blocks, more
+    # than two per CU: the persistent ping-pong kernel runs several rounds
+    _say("grouped B=4 T=1100 n_H=16 g=3 (grid of several rounds)")
     x = _inputs(4, 1100, 16, 3, seed=33)
     out = _gpu(x, 3)
     rng = np.random.default_rng(4)
@@ -125,3 +125,39 @@ def test_grouped_structure():
     assert np.array_equal(a[:, :, :3], b[:, :, :3])
     assert np.abs(a[:, :, 3:] - b[:, :, 3:]).max() > 1e-3
     assert np.array_equal(a, _gpu(x, 3))
+
+
+@pytest.mark.parametrize("T,n_H", [(300, 8), (200, 260)])
+def test_grouped_wide_key_stride(T, n_H):
+    """A key row stride of 2^21 elements puts a head's key span past 2^31
+    bytes: the ping-pong kernel's 32-bit offsets do not reach, and the
+    register-staged kernels run instead (T=300, 8 heads: the two-group form;
+    T=200, 260 heads: 520 blocks, more than two per CU, the four-wave form).
+    Every output row against the oracle."""
+    _say("grouped wide key stride", T, n_H)
+    g = 3
+    x = _inputs(1, T, n_H, g, seed=700 + n_H)
+    st = 1 << 21
+    base = torch.empty((T - 1) * st + n_H * 64, dtype=torch.bfloat16, device="cuda")
+    k = base.as_strided((1, T, n_H, 64), (T * st, st, 64, 1))
+    k.copy_(to_dev(x["k"]))
+    q, v = to_dev(x["q"]), to_dev(x["v"])
+    lam = torch.from_numpy(x["lam"]).cuda()
+    gate = to_dev(x["gate"])
+    out = da.diffattn_fwd_grouped(q, k, v, g, lam, gate=gate, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _assert_close(out.cpu().numpy(), _ref(x, g), "fp32 out")
+    del base, k
+
+
+@pytest.mark.parametrize("B,T,n_H", [(1, 8192, 8), (8, 1000, 16), (2, 4096, 16)])
+def test_grouped_vt_tiles_every_row(B, T, n_H):
+    """Shapes that take the V^T form on a 256-CU chip (V converted once into
+    fp16 V^T tiles, moved by DMA): a one-round grid of a long sequence
+    (T=8192), and two full rounds of pairs with a ragged last key tile
+    (T=1000) or a whole one (T=4096).  Every output row against the oracle."""
+    _say("grouped V^T form", B, T, n_H)
+    x = _inputs(B, T, n_H, 3, seed=800 + T + n_H)
+    ref = _ref(x, 3)
+    _assert_close(_gpu(x, 3), ref, "fp32 out")
+    _assert_close(_gpu(x, 3, torch.bfloat16), ref, "bf16 out", bf16=True)

@@ -5,12 +5,15 @@ round both run the ping-pong kernel, the same products on the same fp16
 operands in the same order, so their outputs must agree bit for bit: small
 and ragged lengths that leave part of the last V^T tile past T, a sliding
 window wider than the streaming kernel takes, per-head lambda, a fused
-strided layout.  On larger grids the workspace path keeps the persistent
-ping-pong kernel while the plain path runs the four-wave kernel: two wave
-groups with their own reference maxima round P differently, so there the
-two are held to the oracle's bounds and to each other within the fp16
-rounding of P.  The full-size workloads are also checked against the oracle
-on sampled rows.  Every case prints its name first."""
+strided layout.  On larger grids whose long/short pairs fill their rounds of
+the chip (B=8 and T=16384 at 16 heads) the workspace path keeps the
+persistent ping-pong kernel while the plain path runs the four-wave kernel:
+two wave groups with their own reference maxima round P differently, so
+there the two are held to the oracle's bounds and to each other within the
+fp16 rounding of P.  Other larger grids (B=1, T=2048, 40 heads: 320 pairs on
+256 CUs) run the four-wave kernel on both paths, with V^T tiles on the
+workspace path.  The full-size workloads are also checked against the
+oracle on sampled rows.  Every case prints its name first."""
 import numpy as np
 import pytest
 
