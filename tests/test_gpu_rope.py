@@ -146,8 +146,11 @@ def _rows(B, T, H, rng, n_random=40):
     return sorted(rows)
 
 
+# (2, 1, 2048, 40, True): 320 long/short pairs on 256 CUs do not fill two
+# rounds, so the workspace path runs the four-wave kernel with V^T tiles and
+# pre-rotated keys; T=8192 at 16 heads fills two rounds (ping-pong kernel).
 @pytest.mark.parametrize("mode,B,T,H,ws", [(1, 1, 4096, 16, True), (2, 1, 4096, 16, True), (1, 1, 8192, 16, True),
-                                         (2, 1, 8192, 16, False)])
+                                         (2, 1, 8192, 16, False), (2, 1, 2048, 40, True)])
 def test_prefill_rope_large_sampled(mode, B, T, H, ws):
     _say("prefill rope sampled rows", mode, B, T, H, ws)
     x = _inputs(B, T, H, seed=T + mode)
