@@ -638,14 +638,21 @@ __device__ __forceinline__ void load_row16(f16x8 (&r)[kN], const uint16_t* base,
 // SIMD holds one wave of each kind and every query tile is staged once for
 // both: Q_1, Q_2 and dO row-major fp16 by DMA (issued by the dK waves; Q^T and
 // dO^T come from the same tiles by transposed reads) and the per-query
-// statistics (stored by the dV waves).  Each role runs its own copy of the
-// loop (same trip count, one barrier per query tile), so its registers are
-// allocated for that role alone.
-constexpr int kDkvStage = 2 * kQKTile + kD16Tile + 4 * 32 * 4;
-constexpr int kOffDo = 2 * kQKTile, kOffSt = kOffDo + kD16Tile;
+// statistics (stored by the dV waves).  The dV wave of a tile computes the
+// scores and both maps' probabilities, takes P_1 - lambda P_2 for dV and
+// leaves P_1 and P_2 (fp32) in the tile's stage; the dK wave of the same keys
+// takes them one step later, with dP = dO V^T, for dS and dK.  Each kind then
+// carries 16 products per tile.  Three stages keep a tile staged for the step
+// after its own.  Each role runs its own copy of the loop (same trip count, one barrier
+// per query tile), so its registers are allocated for that role alone.
+// A stage: Q_1, Q_2, dO, the statistics, then the tile's P_1, P_2 as the dV
+// waves leave them ([dK wave][f32x4 index 0..7][lane]).
+constexpr int kDkvP = 4 * 8 * 64 * 16;
+constexpr int kDkvStage = 2 * kQKTile + kD16Tile + 4 * 32 * 4 + kDkvP;
+constexpr int kOffDo = 2 * kQKTile, kOffSt = kOffDo + kD16Tile, kOffP = kOffSt + 4 * 32 * 4;
 
 template <bool kDV>
-__device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, char* stage1, int tid) {
+__device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, char* stage1, char* stage2, int tid) {
   const int rt = tid & 255;                                   // thread within its role
   const int rw = __builtin_amdgcn_readfirstlane(rt >> 6);     // wave within its role
   const int lane = tid & 63, hf = lane >> 5, lk = lane & 31;
@@ -662,13 +669,16 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
   const int W = a.window;
   const int nqt = W > 0 ? min((a.T + 31) / 32, (kb * kRows + kRows - 1 + W - 1) / 32 + 1) : (a.T + 31) / 32;
   const int wave_last = W > 0 ? (k_first + 31 + W - 1) / 32 : nqt - 1;
+  auto live = [&](int qt) { return wave_live && qt >= diag && qt <= wave_last; };
 
   const int64_t rk = ((int64_t)b * a.T + key) * a.H + head;
-  f16x8 k1t[4], k2t[4];
-  load_row16(k1t, a.k1h, rk, ok, hf);
-  load_row16(k2t, a.k2h, rk, ok, hf);
-  f16x8 vt[kDV ? 1 : 8];
-  if constexpr (!kDV) load_row16(vt, a.vh, rk, ok, hf);
+  f16x8 k1t[kDV ? 4 : 1], k2t[kDV ? 4 : 1], vt[kDV ? 1 : 8];
+  if constexpr (kDV) {
+    load_row16(k1t, a.k1h, rk, ok, hf);
+    load_row16(k2t, a.k2h, rk, ok, hf);
+  } else {
+    load_row16(vt, a.vh, rk, ok, hf);
+  }
   const float lam = a.lambda_h ? a.lambda_h[head] : a.lambda;
   const float c = a.c;
   const int64_t row0 = (int64_t)b * a.T * a.H + head;  // (b, t = 0, head)
@@ -676,6 +686,7 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
   const uint16_t* qb2 = a.q2h + row0 * kDqk;
   const uint16_t* dob = a.dO + row0 * kDv;
   const int64_t sq = (int64_t)a.H * kDqk, sdo = (int64_t)a.H * kDv;
+  auto pslot = [&](char* st, int j) { return reinterpret_cast<f32x4*>(st + kOffP) + (rw * 8 + j) * 64 + lane; };
 
   f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};  // dK_1 (0, 1), dK_2 (2, 3) or dV^T (0 .. 3)
   auto stage_issue = [&](int qt, char* st) {
@@ -687,6 +698,48 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
   auto stage_store = [&](int qt, char* st) {
     if constexpr (kDV) stage_stats(a, b, head, 32 * qt, reinterpret_cast<float*>(st + kOffSt), rt);
   };
+  // dK wave: dS of the tile staged in st from its P and dP, then dK += Q^T dS
+  auto dk_tile = [&](char* st) __attribute__((always_inline)) {
+    f32x16 p1, p2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 x = *pslot(st, j), y = *pslot(st, 4 + j);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p1[4 * j + r] = x[r];
+        p2[4 * j + r] = y[r];
+      }
+    }
+    // dP = dO V^T (32 queries x 32 keys)
+    f32x16 dp = f32x16{};
+    const char* dt = st + kOffDo + lk * kD16Row;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8*>(dt + (((2 * s + hf) ^ swz16(lk)) << 4)),
+                                                  vt[s], dp, 0, 0, 0);
+    const float* stats = reinterpret_cast<const float*>(st + kOffSt);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r0 = 8 * g + 4 * hf;
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(stats + 64 + r0);
+      const f32x4 d2 = *reinterpret_cast<const f32x4*>(stats + 96 + r0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;
+        p1[i] = p1[i] * (dp[i] - d1[r]);
+        p2[i] = p2[i] * (-lam * dp[i] - d2[r]);
+      }
+    }
+    f16x8 a0, a1, b0, b1;
+    pack16(p1, a0, a1);
+    pack16(p2, b0, b1);
+    // dK_m^T += Q_m^T dS_m, Q_m^T read transposed from the query tiles
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      acc[blk] = mfma_tr<kKRow>(st, blk, lane, a0, a1, acc[blk]);
+      acc[2 + blk] = mfma_tr<kKRow>(st + kQKTile, blk, lane, b0, b1, acc[2 + blk]);
+    }
+  };
   if (qt0 < nqt) {
     stage_issue(qt0, stage0);
     stage_store(qt0, stage0);
@@ -694,87 +747,76 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
   wait_dma();
   __syncthreads();
 
-  // The two stages are separate LDS objects and the loop is unrolled by two,
-  // so every step names the stage it reads and the one the next tile's DMA
-  // fills.
-  auto step = [&](int qt, char* cur, char* nxt) __attribute__((always_inline)) {
+  // The three stages are separate LDS objects and the loop is unrolled by
+  // three, so every step names the stage it reads, the one the next tile's
+  // DMA fills and the previous tile's (the compiler then adds no wait for a
+  // DMA into another object before the transposed reads).
+  auto step = [&](int qt, char* cur, char* nxt, char* prev) __attribute__((always_inline)) {
     const bool more = qt + 1 < nqt;
     if (more) stage_issue(qt + 1, nxt);
-    if (wave_live && qt >= diag && qt <= wave_last) {
-      f32x16 s1 = scores_qk(cur, k1t, lk, hf);
-      f32x16 s2 = scores_qk(cur + kQKTile, k2t, lk, hf);
-      const float* stats = reinterpret_cast<const float*>(cur + kOffSt);
-      if (qt == diag) {  // rows are queries 8(i/4) + 4hf + i%4 of the tile, the column key lk
+    if constexpr (kDV) {
+      if (live(qt)) {
+        f32x16 s1 = scores_qk(cur, k1t, lk, hf);
+        f32x16 s2 = scores_qk(cur + kQKTile, k2t, lk, hf);
+        const float* stats = reinterpret_cast<const float*>(cur + kOffSt);
+        if (qt == diag) {  // rows are queries 8(i/4) + 4hf + i%4 of the tile, the column key lk
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (lk > 8 * (i >> 2) + 4 * hf + (i & 3)) s1[i] = s2[i] = -__builtin_inff();  // P = 0
-      }
-      if (W > 0 && 32 * qt + 31 >= k_first + W) {  // queries past the window of this lane's key
+          for (int i = 0; i < 16; ++i)
+            if (lk > 8 * (i >> 2) + 4 * hf + (i & 3)) s1[i] = s2[i] = -__builtin_inff();  // P = 0
+        }
+        if (W > 0 && 32 * qt + 31 >= k_first + W) {  // queries past the window of this lane's key
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * qt + 8 * (i >> 2) + 4 * hf + (i & 3) >= key + W) s1[i] = s2[i] = -__builtin_inff();
-      }
-      if constexpr (!kDV) {
-        // dP = dO V^T (32 queries x 32 keys)
-        f32x16 dp = f32x16{};
-        const char* dt = cur + kOffDo + lk * kD16Row;
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              *reinterpret_cast<const f16x8*>(dt + (((2 * s + hf) ^ swz16(lk)) << 4)), vt[s], dp, 0, 0, 0);
+          for (int i = 0; i < 16; ++i)
+            if (32 * qt + 8 * (i >> 2) + 4 * hf + (i & 3) >= key + W) s1[i] = s2[i] = -__builtin_inff();
+        }
+        f32x16 pv;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int r0 = 8 * g + 4 * hf;
           const f32x4 l1 = *reinterpret_cast<const f32x4*>(stats + r0);
           const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 32 + r0);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(stats + 64 + r0);
-          const f32x4 d2 = *reinterpret_cast<const f32x4*>(stats + 96 + r0);
+          f32x4 x, y;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * g + r;
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r]));
             const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r]));
-            s1[i] = p1 * (dp[i] - d1[r]);
-            s2[i] = p2 * (-lam * dp[i] - d2[r]);
+            x[r] = p1;
+            y[r] = p2;
+            pv[i] = p1 - lam * p2;
           }
-        }
-        f16x8 a0, a1, b0, b1;
-        pack16(s1, a0, a1);
-        pack16(s2, b0, b1);
-        // dK_m^T += Q_m^T dS_m, Q_m^T read transposed from the query tiles
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          acc[blk] = mfma_tr<kKRow>(cur, blk, lane, a0, a1, acc[blk]);
-          acc[2 + blk] = mfma_tr<kKRow>(cur + kQKTile, blk, lane, b0, b1, acc[2 + blk]);
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r0 = 8 * g + 4 * hf;
-          const f32x4 l1 = *reinterpret_cast<const f32x4*>(stats + r0);
-          const f32x4 l2 = *reinterpret_cast<const f32x4*>(stats + 32 + r0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * g + r;
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -l1[r]));
-            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -l2[r]));
-            s1[i] = p1 - lam * p2;
-          }
+          *pslot(cur, g) = x;
+          *pslot(cur, 4 + g) = y;
         }
         f16x8 p0, p1;
-        pack16(s1, p0, p1);
+        pack16(pv, p0, p1);
         // dV^T += dO^T (P_1 - lambda P_2), dO^T read transposed from the dO tile
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) acc[blk] = mfma_tr<kD16Row>(cur + kOffDo, blk, lane, p0, p1, acc[blk]);
       }
+    } else {
+      // the previous tile, whose P the dV wave of these keys left a step ago
+      if (qt > qt0 && live(qt - 1)) dk_tile(prev);
     }
     if (more) stage_store(qt + 1, nxt);
     wait_dma();
     __syncthreads();
   };
-  for (int qt = qt0; qt < nqt; qt += 2) {
-    step(qt, stage0, stage1);
-    if (qt + 1 < nqt) step(qt + 1, stage1, stage0);
+  int qt = qt0;
+  for (; qt + 2 < nqt; qt += 3) {
+    step(qt, stage0, stage1, stage2);
+    step(qt + 1, stage1, stage2, stage0);
+    step(qt + 2, stage2, stage0, stage1);
+  }
+  if (qt < nqt) step(qt, stage0, stage1, stage2);
+  if (qt + 1 < nqt) step(qt + 1, stage1, stage2, stage0);
+  if constexpr (!kDV) {
+    // the last tile, staged in stage (nqt - 1 - qt0) % 3
+    const int ql = nqt - 1;
+    if (ql >= qt0 && live(ql)) {
+      const int k = (ql - qt0) % 3;
+      dk_tile(k == 0 ? stage0 : (k == 1 ? stage1 : stage2));
+    }
   }
   if (!ok) return;
   if constexpr (!kDV) {
@@ -797,11 +839,12 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dkv_kernel(BackwardArgs a) {
   __shared__ __attribute__((aligned(16))) char stage0[kDkvStage];
   __shared__ __attribute__((aligned(16))) char stage1[kDkvStage];
+  __shared__ __attribute__((aligned(16))) char stage2[kDkvStage];
   const int tid = threadIdx.x;
   if (__builtin_amdgcn_readfirstlane(tid >> 6) >= kWaves)
-    dkv_role<true>(a, stage0, stage1, tid);
+    dkv_role<true>(a, stage0, stage1, stage2, tid);
   else
-    dkv_role<false>(a, stage0, stage1, tid);
+    dkv_role<false>(a, stage0, stage1, stage2, tid);
 }
 
 }  // namespace
