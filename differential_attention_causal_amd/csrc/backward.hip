@@ -595,21 +595,29 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 // stream through LDS.  Scores are S = Q K^T (32 queries x 32 keys), so the
 // accumulator's columns are this lane's key and its rows queries.
 
-// Per-query statistics of a query tile in LDS: [lse_1, lse_2, D_1, D_2][32].
-// Rows past T get lse = +inf, so their probabilities are 0.
-__device__ __forceinline__ void stage_stats(const BackwardArgs& a, int b, int head, int q0, float* st, int tid) {
+// Per-query statistics of a query tile in LDS: [lse_1, lse_2, D_1, D_2][32],
+// in two parts: threads 0..31 load their query's values into registers (at
+// the start of a step, so the loads run under its products), then store them
+// (at its end).  Rows past T get lse = +inf, so their probabilities are 0.
+struct QueryStats {
+  f32x2 l, d;
+};
+__device__ __forceinline__ QueryStats load_stats(const BackwardArgs& a, int b, int head, int q0, int tid) {
+  QueryStats r{{__builtin_inff(), __builtin_inff()}, {0.f, 0.f}};
+  const int q = q0 + tid;
+  if (tid < 32 && q < a.T) {
+    const int64_t row = ((int64_t)b * a.T + q) * a.H + head;
+    r.l = *reinterpret_cast<const f32x2*>(a.lse + row * 2);
+    r.d = *reinterpret_cast<const f32x2*>(a.dstat + row * 2);
+  }
+  return r;
+}
+__device__ __forceinline__ void store_stats(const QueryStats& v, float* st, int tid) {
   if (tid < 32) {
-    const int q = q0 + tid;
-    f32x2 l = {__builtin_inff(), __builtin_inff()}, d = {0.f, 0.f};
-    if (q < a.T) {
-      const int64_t r = ((int64_t)b * a.T + q) * a.H + head;
-      l = *reinterpret_cast<const f32x2*>(a.lse + r * 2);
-      d = *reinterpret_cast<const f32x2*>(a.dstat + r * 2);
-    }
-    st[tid] = l.x;
-    st[32 + tid] = l.y;
-    st[64 + tid] = d.x;
-    st[96 + tid] = d.y;
+    st[tid] = v.l.x;
+    st[32 + tid] = v.l.y;
+    st[64 + tid] = v.d.x;
+    st[96 + tid] = v.d.y;
   }
 }
 
@@ -695,8 +703,12 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
       dma_do(dob, sdo, 32 * qt, a.T, st + kOffDo, rt);
     }
   };
-  auto stage_store = [&](int qt, char* st) {
-    if constexpr (kDV) stage_stats(a, b, head, 32 * qt, reinterpret_cast<float*>(st + kOffSt), rt);
+  QueryStats nst;  // the next tile's statistics (dV role), loaded at the start of a step
+  auto stats_load = [&](int qt) {
+    if constexpr (kDV) nst = load_stats(a, b, head, 32 * qt, rt);
+  };
+  auto stats_store = [&](char* st) {
+    if constexpr (kDV) store_stats(nst, reinterpret_cast<float*>(st + kOffSt), rt);
   };
   // dK wave: dS of the tile staged in st from its P and dP, then dK += Q^T dS
   auto dk_tile = [&](char* st) __attribute__((always_inline)) {
@@ -742,7 +754,8 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
   };
   if (qt0 < nqt) {
     stage_issue(qt0, stage0);
-    stage_store(qt0, stage0);
+    stats_load(qt0);
+    stats_store(stage0);
   }
   wait_dma();
   __syncthreads();
@@ -753,7 +766,10 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
   // DMA into another object before the transposed reads).
   auto step = [&](int qt, char* cur, char* nxt, char* prev) __attribute__((always_inline)) {
     const bool more = qt + 1 < nqt;
-    if (more) stage_issue(qt + 1, nxt);
+    if (more) {
+      stage_issue(qt + 1, nxt);
+      stats_load(qt + 1);
+    }
     if constexpr (kDV) {
       if (live(qt)) {
         f32x16 s1 = scores_qk(cur, k1t, lk, hf);
@@ -798,7 +814,7 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
       // the previous tile, whose P the dV wave of these keys left a step ago
       if (qt > qt0 && live(qt - 1)) dk_tile(prev);
     }
-    if (more) stage_store(qt + 1, nxt);
+    if (more) stats_store(nxt);
     wait_dma();
     __syncthreads();
   };
