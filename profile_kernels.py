@@ -197,7 +197,8 @@ def cmd_variants():
              "command: " + " ".join(cmd),
              "# averages over every dispatch of the run, warm-up ones included; a kernel that runs in several",
              "# variants averages over all of them (prefill_pp_kernel<false, false, true>: the step's prefill and",
-             "# the B=8 and T=16384 prefills; vtiles_kernel: every workspace prefill)",
+             "# the B=8 and T=16384 prefills; vtiles_kernel: every workspace prefill without RoPE, prepass_kernel:",
+             "# the RoPE prefill's key rotation and V^T tiles in one launch)",
              "kernel | calls | avg_us | min_us | max_us"]
     for name, calls, avg, mn, mx in table:
         lines.append("%s | %d | %.2f | %.2f | %.2f" % (name, calls, avg, mn, mx))
