@@ -710,47 +710,48 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
   auto stats_store = [&](char* st) {
     if constexpr (kDV) store_stats(nst, reinterpret_cast<float*>(st + kOffSt), rt);
   };
-  // dK wave: dS of the tile staged in st from its P and dP, then dK += Q^T dS
-  auto dk_tile = [&](char* st) __attribute__((always_inline)) {
+  // dK wave, in this order within a step, so that its vector work comes while
+  // the dV wave of its SIMD runs the score products and its products while
+  // that wave computes the exponentials: dS of the previous tile (from the P
+  // the dV wave left in its stage and the dP computed a step ago), then
+  // dK += Q^T dS of the previous tile and dP = dO V^T of the current one.
+  f32x16 dp;               // dP of the last tile this wave computed it for
+  f16x8 a0, a1, b0, b1;    // dS_1, dS_2 of the previous tile, as fp16 operands
+  auto dk_ds = [&](const char* st) __attribute__((always_inline)) {
+    const float* stats = reinterpret_cast<const float*>(st + kOffSt);
     f32x16 p1, p2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 x = *pslot(st, j), y = *pslot(st, 4 + j);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p1[4 * j + r] = x[r];
-        p2[4 * j + r] = y[r];
-      }
-    }
-    // dP = dO V^T (32 queries x 32 keys)
-    f32x16 dp = f32x16{};
-    const char* dt = st + kOffDo + lk * kD16Row;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8*>(dt + (((2 * s + hf) ^ swz16(lk)) << 4)),
-                                                  vt[s], dp, 0, 0, 0);
-    const float* stats = reinterpret_cast<const float*>(st + kOffSt);
-#pragma unroll
     for (int g = 0; g < 4; ++g) {
+      const f32x4 x = *pslot(const_cast<char*>(st), g), y = *pslot(const_cast<char*>(st), 4 + g);
       const int r0 = 8 * g + 4 * hf;
       const f32x4 d1 = *reinterpret_cast<const f32x4*>(stats + 64 + r0);
       const f32x4 d2 = *reinterpret_cast<const f32x4*>(stats + 96 + r0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * g + r;
-        p1[i] = p1[i] * (dp[i] - d1[r]);
-        p2[i] = p2[i] * (-lam * dp[i] - d2[r]);
+        p1[i] = x[r] * (dp[i] - d1[r]);
+        p2[i] = y[r] * (-lam * dp[i] - d2[r]);
       }
     }
-    f16x8 a0, a1, b0, b1;
     pack16(p1, a0, a1);
     pack16(p2, b0, b1);
+  };
+  auto dk_products = [&](const char* st) __attribute__((always_inline)) {
     // dK_m^T += Q_m^T dS_m, Q_m^T read transposed from the query tiles
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       acc[blk] = mfma_tr<kKRow>(st, blk, lane, a0, a1, acc[blk]);
       acc[2 + blk] = mfma_tr<kKRow>(st + kQKTile, blk, lane, b0, b1, acc[2 + blk]);
     }
+  };
+  auto dk_dp = [&](const char* st) __attribute__((always_inline)) {
+    // dP = dO V^T (32 queries x 32 keys)
+    dp = f32x16{};
+    const char* dt = st + kOffDo + lk * kD16Row;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8*>(dt + (((2 * s + hf) ^ swz16(lk)) << 4)),
+                                                  vt[s], dp, 0, 0, 0);
   };
   if (qt0 < nqt) {
     stage_issue(qt0, stage0);
@@ -771,7 +772,7 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
       stats_load(qt + 1);
     }
     if constexpr (kDV) {
-      if (live(qt)) {
+      if (qt < nqt && live(qt)) {
         f32x16 s1 = scores_qk(cur, k1t, lk, hf);
         f32x16 s2 = scores_qk(cur + kQKTile, k2t, lk, hf);
         const float* stats = reinterpret_cast<const float*>(cur + kOffSt);
@@ -811,29 +812,26 @@ __device__ __forceinline__ void dkv_role(const BackwardArgs& a, char* stage0, ch
         for (int blk = 0; blk < 4; ++blk) acc[blk] = mfma_tr<kD16Row>(cur + kOffDo, blk, lane, p0, p1, acc[blk]);
       }
     } else {
-      // the previous tile, whose P the dV wave of these keys left a step ago
-      if (qt > qt0 && live(qt - 1)) dk_tile(prev);
+      // the previous tile, whose P the dV wave of these keys left a step ago,
+      // then the current tile's dP
+      const bool lp = qt > qt0 && live(qt - 1);
+      if (lp) dk_ds(prev);
+      if (lp) dk_products(prev);
+      if (qt < nqt && live(qt)) dk_dp(cur);
     }
     if (more) stats_store(nxt);
     wait_dma();
     __syncthreads();
   };
+  // steps qt0 .. nqt: the last one finishes tile nqt - 1's dK
   int qt = qt0;
-  for (; qt + 2 < nqt; qt += 3) {
+  for (; qt + 2 <= nqt; qt += 3) {
     step(qt, stage0, stage1, stage2);
     step(qt + 1, stage1, stage2, stage0);
     step(qt + 2, stage2, stage0, stage1);
   }
-  if (qt < nqt) step(qt, stage0, stage1, stage2);
-  if (qt + 1 < nqt) step(qt + 1, stage1, stage2, stage0);
-  if constexpr (!kDV) {
-    // the last tile, staged in stage (nqt - 1 - qt0) % 3
-    const int ql = nqt - 1;
-    if (ql >= qt0 && live(ql)) {
-      const int k = (ql - qt0) % 3;
-      dk_tile(k == 0 ? stage0 : (k == 1 ? stage1 : stage2));
-    }
-  }
+  if (qt <= nqt) step(qt, stage0, stage1, stage2);
+  if (qt + 1 <= nqt) step(qt + 1, stage1, stage2, stage0);
   if (!ok) return;
   if constexpr (!kDV) {
     if (a.rope.mode != 0) {
