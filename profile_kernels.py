@@ -10,7 +10,8 @@ summaries kept under profiles/.
 
 Every profiled program is `python3 bench.py ...`, launched directly after
 rocprofv3's `--` by this process, which itself never touches the GPU.  Raw
-output goes to gpurun_out/prof/; the summaries go to profiles/.
+output goes to the run-output directory OUT_REL; the summaries go to
+profiles/.
 
 Rates: prefill kernels are priced at 768 FLOP per visible (query, key) pair
 and head against the dense bf16/fp16 MFMA peak (2516.6 TFLOP/s); decode and
@@ -370,7 +371,7 @@ def _write(fname, lines):
     path = os.path.join(PROFILES, fname)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
-    # a copy travels back with gpurun_out/ as well
+    # and a copy beside the raw output
     os.makedirs(OUT, exist_ok=True)
     shutil.copy(path, os.path.join(OUT, fname))
     print("[prof] wrote " + path, flush=True)
