@@ -170,14 +170,8 @@ int ws_pre_pass(diffattn::PrefillArgs& a, void* ws, size_t ws_bytes, hipStream_t
   // kernels move into LDS by DMA (the kernel choice depends on the rotated
   // keys, so this is asked after the fields above are set).
   const bool vt = diffattn::prefill_takes_vt(a);
-  diffattn::VTilesArgs t{};
-  t.v = a.v;
-  t.sv = a.sv;
-  t.B = B;
-  t.T = T;
-  t.H = H;
-  t.ntiles = (T + 31) / 32;
-  t.out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + rope_part);
+  const diffattn::VTilesArgs t = diffattn::make_vtiles_args(
+      a.v, a.sv, B, T, H, reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + rope_part));
   // one launch of 256-thread workgroups covers every key vector (32 per
   // workgroup) and every V^T tile: its work-items must fit 32 bits
   const int64_t blocks = (rope ? ((int64_t)B * T * H + 31) / 32 : 0) + (vt ? (int64_t)B * H * t.ntiles : 0);

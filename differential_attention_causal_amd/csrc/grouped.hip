@@ -589,15 +589,9 @@ hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream) {
   const bool one_round = grid <= 2 * cus;
   hipError_t e;
   if (a.vt != nullptr && filled && (!one_round || a.T >= 8192)) {
-    VTilesArgs t{};
-    t.v = a.v;
-    t.sv = a.sv;
-    t.B = a.B;
-    t.T = a.T;
-    t.H = a.nH;
-    t.ntiles = (a.T + kBN - 1) / kBN;
-    t.out = const_cast<uint16_t*>(a.vt);
-    if ((e = launch_vtiles(t, stream)) != hipSuccess) return e;
+    if ((e = launch_vtiles(make_vtiles_args(a.v, a.sv, a.B, a.T, a.nH, const_cast<uint16_t*>(a.vt)), stream)) !=
+        hipSuccess)
+      return e;
     e = launch_kernel(grouped_ppvt_kernel, dim3((unsigned)pairs), dim3(512), stream, a);
   } else if (one_round) {
     // The register-staged ping-pong form addresses a head's key and value

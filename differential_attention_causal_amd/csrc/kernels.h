@@ -210,6 +210,18 @@ struct VTilesArgs {
   int ntiles;         // ceil(T / 32)
   uint16_t* out;      // [B * H][ntiles][kVtTileBytes / 2]
 };
+// The pre-pass arguments for V ([B, T, H, kDv] bf16 with strides sv) into out.
+inline VTilesArgs make_vtiles_args(const uint16_t* v, const Strides& sv, int B, int T, int H, uint16_t* out) {
+  VTilesArgs t{};
+  t.v = v;
+  t.sv = sv;
+  t.B = B;
+  t.T = T;
+  t.H = H;
+  t.ntiles = (T + 31) / 32;
+  t.out = out;
+  return t;
+}
 hipError_t launch_vtiles(const VTilesArgs& a, hipStream_t stream);
 // The key rotation and the V^T tiles of one rotary prefill in one launch
 // (both results exactly as launch_rope_keys and launch_vtiles give them).
