@@ -20,8 +20,7 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One workgroup per tile, 16-byte accesses both ways with the transposition
-// in LDS.  Loads: thread t takes the 16-byte chunk (t % 16) (channels
+// 16-byte accesses both ways with the transposition in LDS.  Loads: thread t takes the 16-byte chunk (t % 16) (channels
 // 8 (t % 16) .. + 7) of key rows 2 (t / 16) and 2 (t / 16) + 1, a key pair
 // that sits at adjacent positions of the tile (position bit 0 is key bit 0),
 // so each of its channels becomes one 4-byte word of two fp16 keys, written
@@ -32,21 +31,26 @@ constexpr int kThreads = 256;
 // addresses.
 constexpr int kLdsRow = 68;  // bytes per channel row in LDS: 64 + 4 of padding
 
-// Tile g (flattened over (b, h, tile)) by the 256 threads of one workgroup;
-// lds: kDv * kLdsRow bytes, 16-byte aligned.
-__device__ __forceinline__ void vtiles_tile(const VTilesArgs& a, int64_t g, int t, char* lds) {
+// Loads of tile g (flattened over (b, h, tile)) by thread t of the 256 of a
+// workgroup: key rows kr, kr + 1 of the tile, channels ch0 .. ch0 + 7.
+__device__ __forceinline__ void vtiles_load(const VTilesArgs& a, int64_t g, int t, u32x4 (&w)[2]) {
   const int j = (int)(g % a.ntiles);
   const int64_t bh = g / a.ntiles;
   const int h = (int)(bh % a.H);
   const int b = (int)(bh / a.H);
   const uint16_t* src = a.v + (int64_t)b * a.sv.b + (int64_t)h * a.sv.h;
   const int kr = 2 * (t >> 4), ch0 = 8 * (t & 15);  // key rows kr, kr + 1 of the tile; first channel
-  u32x4 w[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int key = 32 * j + kr + u;
     w[u] = key < a.T ? *reinterpret_cast<const u32x4*>(src + (int64_t)key * a.sv.t + ch0) : u32x4{0, 0, 0, 0};
   }
+}
+
+// The loaded rows into lds (kDv * kLdsRow bytes, 16-byte aligned) as fp16
+// words of two keys.
+__device__ __forceinline__ void vtiles_transpose(const u32x4 (&w)[2], int t, char* lds) {
+  const int kr = 2 * (t >> 4), ch0 = 8 * (t & 15);
   // position of key kr in its row: bits 2 and 3 swapped (see the file header); kr + 1 follows it
   const int pos = (kr & 16) | ((kr & 4) << 1) | ((kr & 8) >> 1) | (kr & 3);
 #pragma unroll
@@ -57,7 +61,10 @@ __device__ __forceinline__ void vtiles_tile(const VTilesArgs& a, int64_t g, int 
     *reinterpret_cast<f16x2*>(lds + (ch0 + 2 * i) * kLdsRow + pos * 2) = lo;
     *reinterpret_cast<f16x2*>(lds + (ch0 + 2 * i + 1) * kLdsRow + pos * 2) = hi;
   }
-  __syncthreads();
+}
+
+// Tile g's output chunks from lds (after a barrier) to the workspace.
+__device__ __forceinline__ void vtiles_store(const VTilesArgs& a, int64_t g, int t, const char* lds) {
   char* dst = reinterpret_cast<char*>(a.out) + g * kVtTileBytes;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -69,9 +76,37 @@ __device__ __forceinline__ void vtiles_tile(const VTilesArgs& a, int64_t g, int 
   }
 }
 
+// Tile g by the 256 threads of one workgroup.
+__device__ __forceinline__ void vtiles_tile(const VTilesArgs& a, int64_t g, int t, char* lds) {
+  u32x4 w[2];
+  vtiles_load(a, g, t, w);
+  vtiles_transpose(w, t, lds);
+  __syncthreads();
+  vtiles_store(a, g, t, lds);
+}
+
+// Two tiles per workgroup, every load of both issued before the first
+// conversion (one workgroup per tile: 46.0 against 42.8 us at B=8, T=4096,
+// H=16; the same bytes).
+constexpr int kTilesPerGroup = 2;
 __global__ void __launch_bounds__(kThreads) vtiles_kernel(VTilesArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kDv * kLdsRow];
-  vtiles_tile(a, (int64_t)blockIdx.x, (int)threadIdx.x, lds);
+  __shared__ __attribute__((aligned(16))) char lds[kTilesPerGroup][kDv * kLdsRow];
+  const int64_t tiles = (int64_t)a.B * a.H * a.ntiles;
+  const int t = (int)threadIdx.x;
+  u32x4 w[kTilesPerGroup][2];
+#pragma unroll
+  for (int x = 0; x < kTilesPerGroup; ++x) {
+    const int64_t g = (int64_t)blockIdx.x * kTilesPerGroup + x;
+    vtiles_load(a, g < tiles ? g : tiles - 1, t, w[x]);  // a last odd tile loads a valid tile twice
+  }
+#pragma unroll
+  for (int x = 0; x < kTilesPerGroup; ++x) vtiles_transpose(w[x], t, lds[x]);
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < kTilesPerGroup; ++x) {
+    const int64_t g = (int64_t)blockIdx.x * kTilesPerGroup + x;
+    if (g < tiles) vtiles_store(a, g, t, lds[x]);
+  }
 }
 
 // Both workspace pre-passes of a rotary prefill in one launch: workgroups
@@ -102,7 +137,8 @@ __global__ void __launch_bounds__(kThreads) prepass_kernel(PrepassArgs p) {
 
 hipError_t launch_vtiles(const VTilesArgs& a, hipStream_t stream) {
   const int64_t tiles = (int64_t)a.B * a.H * a.ntiles;
-  return launch_kernel(vtiles_kernel, dim3((unsigned)tiles), dim3(kThreads), stream, a);
+  return launch_kernel(vtiles_kernel, dim3((unsigned)((tiles + kTilesPerGroup - 1) / kTilesPerGroup)),
+                       dim3(kThreads), stream, a);
 }
 
 hipError_t launch_prepass(const RopeKeysArgs& r, const VTilesArgs& t, hipStream_t stream) {

@@ -182,6 +182,7 @@ def cmd_step():
               "bench_prefill_us_min: %s" % plain.get("prefill", {}).get("us_min"),
               "bench_decode_us_mean (split + merge): %s" % plain.get("decode", {}).get("us_mean"),
               "bench_roofline_frac: %s" % plain.get("roofline", {}).get("frac"),
+              "bench_roofline_kernel_us_mean (back-to-back launches): %s" % plain.get("roofline", {}).get("kernel_us_mean"),
               "bench_sclk_mhz: %s" % json.dumps(plain.get("sclk_mhz")),
               "kernel_source_sha256_16: %s" % bench.kernel_source_digest()]
     _write("prefill_decode_step_kernel_trace.txt", lines)
