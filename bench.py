@@ -214,7 +214,11 @@ def copy_calibration(steps: int) -> None:
 
 
 def _time_calls(torch, np, fn, warmup: int, iters: int):
-    """Mean and minimum microseconds of fn() between events on the current stream."""
+    """Microseconds per call of fn() on the current stream, and the minimum of
+    single calls: per call, the smaller of the back-to-back median (b2b_median,
+    which the host's own time per call bounds for short kernels) and the mean
+    of single calls each between its own event pair (which adds the event
+    packets' dispatch latency)."""
     for _ in range(warmup):
         fn()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
@@ -224,19 +228,24 @@ def _time_calls(torch, np, fn, warmup: int, iters: int):
         b.record()
     torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(b) for a, b in ev])
-    return float(ms.mean()) * 1e3, float(ms.min()) * 1e3
+    b2b = b2b_median(torch, np, fn, max(20, iters // 5))
+    return min(float(ms.mean()), b2b) * 1e3, float(ms.min()) * 1e3
 
 
-def b2b_mean(torch, fn, n: int) -> float:
-    """Mean ms of fn over n back-to-back calls between two events."""
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(n):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n
+def b2b_median(torch, np, fn, n: int, repeats: int = 5) -> float:
+    """ms per call of fn: `repeats` times n back-to-back calls between two
+    events on the current stream, the median of the repeats."""
+    out = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / n)
+    return float(np.median(out))
 
 
 def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
@@ -541,12 +550,15 @@ def main() -> int:
     v_ms = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)])  # its V^T pre-pass
     d_ms = np.array([ev[k][2].elapsed_time(ev[k][3]) for k in range(K)])
     step_ms = ev[0][0].elapsed_time(ev[K - 1][3]) / K
-    # The main kernel once more on its own: K back-to-back launches between
-    # two events, right after the timed steps.  An event pair around a single
-    # launch (k1_ms) adds the dispatch latency of the event packets, 3-4 us,
-    # to the ~110 us kernel; the kernel is long enough that the host keeps
-    # the queue full.
-    k_ms = b2b_mean(torch, prefill_kernel, K)
+    # Sustained per-call times right after the timed steps: back-to-back
+    # calls of one kind between two events, median of five repeats.  They
+    # leave out the dispatch latency that an event pair around a single call
+    # adds (3-4 us), but a long run of the prefill alone, without the decode
+    # between, may hold the shader clock lower on a power-limited part.
+    n_b2b = max(20, K // 5)
+    p_b2b = b2b_median(torch, np, prefill, n_b2b)  # the whole prefill call (pre-pass + kernel)
+    k_b2b = b2b_median(torch, np, prefill_kernel, n_b2b)  # its main kernel alone
+    d_b2b = b2b_median(torch, np, decode, n_b2b)
     assert bool(torch.isfinite(p_out.float()).all()) and bool(torch.isfinite(d_out.float()).all())
 
     var = None if args.no_variants else variants(da, torch, np, to_dev, f32_dev, dev)
@@ -554,7 +566,7 @@ def main() -> int:
     p_flop = pw.causal_pairs * FLOP_PER_PAIR
     p_s = float(p_ms.mean()) / 1e3
     tflops = p_flop / p_s / 1e12
-    k_s = float(k_ms) / 1e3
+    k_s = float(k1_ms.mean()) / 1e3
     k_tflops = p_flop / k_s / 1e12
     d_bytes = decode_bytes(dw)
     d_s = float(d_ms.mean()) / 1e3
@@ -578,25 +590,26 @@ def main() -> int:
                    "lambda": pw.lam, "causal": True,
                    "entry_point": "diffattn_prefill_prepare + diffattn_fwd_prefill_ws (prepared)",
                    "step_also_runs": DECODE_WL},
-        # achieved: the ping-pong kernel's own launches, K of them back to
-        # back between two events after the timed steps (the V^T pre-pass is
-        # its own call, done once before them); value: the whole prefill
-        # call, both launches, per step; traffic: the ping-pong kernel's
-        # counters
+        # achieved: the ping-pong kernel's own launch, timed by the events
+        # that bracket it inside the step (the V^T pre-pass runs just before
+        # it as its own call); value: the whole prefill call, both launches;
+        # traffic: the ping-pong kernel's counters
         "roofline": {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(k_tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": "prefill_pp_kernel<false, false, true>", "kernel_us_mean": round(k_s * 1e6, 2),
-                     "timed": "prefill_pp_kernel alone (prepared workspace), %d back-to-back launches between two events" % K,
-                     "kernel_us_single_launch_events": round(float(k1_ms.mean()) * 1e3, 2),
+                     "timed": "prefill_pp_kernel alone (after diffattn_prefill_prepare), events in each step",
                      "algorithmic_flop_per_launch": p_flop},
+        "timing": "means of one event pair per launch inside each timed step; sustained: %d back-to-back calls "
+                  "of one kind between two events, median of 5 repeats, after the timed steps" % n_b2b,
         "prefill": {"us_mean": round(p_s * 1e6, 2), "us_min": round(float(p_ms.min()) * 1e3, 2),
                     "tflops": round(tflops, 2), "tflops_512_per_pair": round(pw.causal_pairs * 512 / p_s / 1e12, 2),
                     "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4),
                     "vtiles_us_mean": round(float(v_ms.mean()) * 1e3, 2), "kernel_us_mean": round(k_s * 1e6, 2),
-                    "kernel_us_mean_single_launch_events": round(float(k1_ms.mean()) * 1e3, 2)},
+                    "sustained": {"us": round(p_b2b * 1e3, 2), "kernel_us": round(k_b2b * 1e3, 2)}},
         "decode": {"workload": DECODE_WL, "us_mean": round(d_s * 1e6, 2), "us_min": round(float(d_ms.min()) * 1e3, 2),
                    "bytes": d_bytes, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                   "splits": dw.num_splits, "traffic": read_traffic(DECODE_PMC, DECODE_SOURCES)},
+                   "splits": dw.num_splits, "traffic": read_traffic(DECODE_PMC, DECODE_SOURCES),
+                   "sustained": {"us": round(d_b2b * 1e3, 2)}},
         "variants": var,
         "settle_s": round(settle_s, 3),
         "settle_steps": settle_steps,

@@ -178,11 +178,12 @@ def cmd_step():
         lines.append("%s | %d | %.2f | %.2f | %.2f | %s" % (name, calls, avg, mn, mx, roof))
     lines += ["",
               "# HIP-event timings of the same command without the profiler, same session:",
-              "bench_prefill_us_mean: %s" % plain.get("prefill", {}).get("us_mean"),
-              "bench_prefill_us_min: %s" % plain.get("prefill", {}).get("us_min"),
+              "bench_prefill_us_mean (pre-pass + kernel): %s" % plain.get("prefill", {}).get("us_mean"),
+              "bench_prefill_kernel_us_mean: %s" % plain.get("prefill", {}).get("kernel_us_mean"),
               "bench_decode_us_mean (split + merge): %s" % plain.get("decode", {}).get("us_mean"),
               "bench_roofline_frac: %s" % plain.get("roofline", {}).get("frac"),
-              "bench_roofline_kernel_us_mean (back-to-back launches): %s" % plain.get("roofline", {}).get("kernel_us_mean"),
+              "bench_sustained: prefill %s, decode %s" % (json.dumps(plain.get("prefill", {}).get("sustained")),
+                                                        json.dumps(plain.get("decode", {}).get("sustained"))),
               "bench_sclk_mhz: %s" % json.dumps(plain.get("sclk_mhz")),
               "kernel_source_sha256_16: %s" % bench.kernel_source_digest()]
     _write("prefill_decode_step_kernel_trace.txt", lines)
