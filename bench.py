@@ -278,6 +278,16 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
                                   scale=dw.scale, num_splits=dw.num_splits, workspace=ws, out=d_out,
                                   window=dw.window)
 
+    # the windowed layer with RoPE in front (keys rotated once into the
+    # workspace, each block's queries inside the streaming window kernel)
+    pr_ws = torch.empty(da.diffattn_prefill_workspace_bytes(pw.B, pw.T, pw.H, rope=da.ROPE_HALF), dtype=torch.uint8,
+                        device=dev)
+
+    def prefill_rope_window():
+        da.diffattn_fwd_prefill_ws(P["q1"], P["q2"], P["k1"], P["k2"], P["v"], pw.lam, pg, pr_ws, eps=pw.eps,
+                                   scale=pw.scale, out=p_out, window=pw.window, rope=da.ROPE_HALF,
+                                   rope_theta=ROPE_THETA)
+
     def prefill_rope():
         # the Motif 2.6B layer itself: RoPE with base 500,000 in front (keys
         # rotated once into the workspace, queries in the prefill's prologue)
@@ -358,6 +368,7 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
         del W, w_out, w_ws
 
     p_us, p_min = _time_calls(torch, np, prefill, warmup, iters)
+    pr_us, pr_min = _time_calls(torch, np, prefill_rope_window, warmup, iters)
     d_us, d_min = _time_calls(torch, np, decode, warmup, iters)
     r_us, r_min = _time_calls(torch, np, prefill_rope, warmup, iters)
     bw_us, bw_min = _time_calls(torch, np, backward, warmup // 3, iters)
@@ -400,6 +411,16 @@ def variants(da, torch, np, to_dev, f32_dev, dev, warmup=300, iters=100):
                         "bytes": p_bytes, "gbs": round(p_bytes / p_us / 1e3, 1),
                         "frac_hbm_peak": round(p_bytes / p_us / 1e3 / HBM_PEAK_GBS, 4),
                         "tflops": round(p_flop / p_us / 1e6, 2)},
+        # the same with RoPE: the key pre-pass (rope_keys_kernel) adds the
+        # keys' fp16 copies to the bytes moved (read 2 x 64 dims, write the
+        # same in fp16); priced on the algorithmic bytes of the layer itself
+        "swa_rope_prefill": {"workload": SWA_PREFILL_WL, "window": pw.window, "rope": "split-half",
+                             "theta": ROPE_THETA, "bound": "hbm",
+                             "kernels": "rope_keys_kernel + prefill_swa_kernel<true>",
+                             "us_mean": round(pr_us, 2), "us_min": round(pr_min, 2), "bytes": p_bytes,
+                             "gbs": round(p_bytes / pr_us / 1e3, 1),
+                             "frac_hbm_peak": round(p_bytes / pr_us / 1e3 / HBM_PEAK_GBS, 4),
+                             "tflops": round(p_flop / pr_us / 1e6, 2)},
         "swa_decode": {"workload": SWA_DECODE_WL, "window": dw.window, "bound": "hbm", "us_mean": round(d_us, 2),
                        "us_min": round(d_min, 2), "bytes": d_bytes, "gbs": round(d_bytes / d_us / 1e3, 1),
                        "frac_hbm_peak": round(d_bytes / d_us / 1e3 / HBM_PEAK_GBS, 4), "splits": dw.num_splits},

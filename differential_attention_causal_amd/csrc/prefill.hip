@@ -732,8 +732,9 @@ PrefillPlan plan_prefill(const PrefillArgs& a) {
   // with 32-bit offsets (up to about T + 192 rows).
   p.pp_fits = (a.rope.mode == 0 || p.prerot) && !(p.prerot && a.o1n != nullptr) &&
               (int64_t)(a.T + 256) * row_max * 2 < (int64_t(1) << 31);
-  // Windowed prefill without the rotary embedding or training outputs, at
-  // most four tiles before the diagonal: the streaming kernel (window.hip).
+  // Windowed prefill without training outputs, at most four tiles before the
+  // diagonal, with no rotary embedding or with the keys already rotated: the
+  // streaming kernel (window.hip).
   p.window = prefill_window_kernel_fits(a);
   // V^T tiles go with the kernels that move keys by DMA, without training
   // outputs: the ping-pong kernel and the four-wave kernel; the lock-step

@@ -190,6 +190,64 @@ __device__ __forceinline__ void stage_store(const Staged& st, char* stage, int t
 // as fp16 bits (the key tiles are rotated to fp16 as well, and the score
 // product then runs on fp16 operands: eight times finer than bf16, which keeps
 // the rounding of rotated operands well inside the error budget).
+// rope_query with a small working set: one pair of chunks (split-half) or
+// one chunk (interleaved) of both queries at a time, for kernels that call it
+// with most of their registers live.  The same rotation, element by element.
+__device__ __forceinline__ void rope_query_lean(bf16x8 (&q1)[4], bf16x8 (&q2)[4], int hf, uint32_t pos, int mode,
+                                                const RopeArgs& r) {
+  if (mode == 1) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float a1[8], b1[8], a2[8], b2[8];
+      rope_unpack(__builtin_bit_cast(rope_u32x4, q1[s]), a1);
+      rope_unpack(__builtin_bit_cast(rope_u32x4, q1[s + 2]), b1);
+      rope_unpack(__builtin_bit_cast(rope_u32x4, q2[s]), a2);
+      rope_unpack(__builtin_bit_cast(rope_u32x4, q2[s + 2]), b2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c0 = 16 * s + e;  // pair index in lane half 0; half 1 adds 8
+        float c, sn;
+        rope_cos_sin(pos, hf ? r.phase[c0 + 8] : r.phase[c0], c, sn);
+        float a = a1[e], b = b1[e];
+        a1[e] = a * c - b * sn;
+        b1[e] = a * sn + b * c;
+        a = a2[e];
+        b = b2[e];
+        a2[e] = a * c - b * sn;
+        b2[e] = a * sn + b * c;
+      }
+      q1[s] = __builtin_bit_cast(bf16x8, rope_pack<true>(a1));
+      q1[s + 2] = __builtin_bit_cast(bf16x8, rope_pack<true>(b1));
+      q2[s] = __builtin_bit_cast(bf16x8, rope_pack<true>(a2));
+      q2[s + 2] = __builtin_bit_cast(bf16x8, rope_pack<true>(b2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float x1[8], x2[8];
+      rope_unpack(__builtin_bit_cast(rope_u32x4, q1[s]), x1);
+      rope_unpack(__builtin_bit_cast(rope_u32x4, q2[s]), x2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c0 = 8 * s + e;  // pair index in lane half 0; half 1 adds 4
+        float c, sn;
+        rope_cos_sin(pos, hf ? r.phase[c0 + 4] : r.phase[c0], c, sn);
+        float a = x1[2 * e], b = x1[2 * e + 1];
+        x1[2 * e] = a * c - b * sn;
+        x1[2 * e + 1] = a * sn + b * c;
+        a = x2[2 * e];
+        b = x2[2 * e + 1];
+        x2[2 * e] = a * c - b * sn;
+        x2[2 * e + 1] = a * sn + b * c;
+      }
+      q1[s] = __builtin_bit_cast(bf16x8, rope_pack<true>(x1));
+      q2[s] = __builtin_bit_cast(bf16x8, rope_pack<true>(x2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 __device__ __forceinline__ void rope_query(bf16x8 (&q1)[4], bf16x8 (&q2)[4], int hf, uint32_t pos, int mode,
                                            const RopeArgs& r) {
   float x1[4][8], x2[4][8];

@@ -52,6 +52,10 @@ __device__ __forceinline__ void sw_store_v(const Staged& st, char* tile, int t) 
   }
 }
 
+// kRope: the keys arrive already rotated, as fp16 (the workspace pre-pass),
+// and each block's queries turn at their positions once loaded; the score
+// products then take fp16 operands, as in the other prefill kernels.
+template <bool kRope>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_swa_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSwSlots * kSwTile];
@@ -115,6 +119,20 @@ prefill_swa_kernel(PrefillArgs a) {
   }
   wait_dma();
   __syncthreads();
+  // With pre-rotated keys, a block's queries turn once they have landed (here
+  // for the first block, in the epilogue before it for the others), as fp16.
+  // The lane half goes in through an empty asm, which keeps the compiler from
+  // hoisting the lanes' selected phases (32 registers) out of the block loop,
+  // where they would stay live through every step (about 100 spilled
+  // registers).
+  auto rotate_q = [&](int qb) {
+    if constexpr (kRope) {
+      int h = hf;
+      asm volatile("" : "+v"(h));
+      rope_query_lean(qa, qb2, h, a.rope.pos0 + (uint32_t)(qb * kBM + 32 * wave + lq), a.rope.mode, a.rope);
+    }
+  };
+  rotate_q(qb0);
 
   f32x16 O1[4], O2[4];
   for (int qb = qb0; qb < qb1; ++qb) {
@@ -126,6 +144,7 @@ prefill_swa_kernel(PrefillArgs a) {
     float m1 = kNoMax, m2 = kNoMax, l1 = 0.f, l2 = 0.f;
     const int q_first = qb * kBM + 32 * wave, q = q_first + lq;
     const bool wave_live = q_first < a.T;
+
     const int wave_last_tile = q_first / kBN;
     for (int s = 0; s <= d; ++s) {
       const int t0 = 4 * qb - d + s;  // this step's first tile (wave w takes t0 + w)
@@ -143,9 +162,17 @@ prefill_swa_kernel(PrefillArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int off = lq * kKRow + (((2 * k + hf) ^ ksw) << 4);
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kt + off), qa[k], s1, 0, 0, 0);
-          s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kt + kKBytes + off), qb2[k],
-                                                       s2, 0, 0, 0);
+          const bf16x8 k1v = *reinterpret_cast<const bf16x8*>(kt + off);
+          const bf16x8 k2v = *reinterpret_cast<const bf16x8*>(kt + kKBytes + off);
+          if constexpr (kRope) {
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, k1v), __builtin_bit_cast(f16x8, qa[k]),
+                                                        s1, 0, 0, 0);
+            s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, k2v),
+                                                        __builtin_bit_cast(f16x8, qb2[k]), s2, 0, 0, 0);
+          } else {
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qa[k], s1, 0, 0, 0);
+            s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k2v, qb2[k], s2, 0, 0, 0);
+          }
         }
       }
       // The next tile's loads go out after the score products: a wait for the
@@ -187,6 +214,7 @@ prefill_swa_kernel(PrefillArgs a) {
     const f32x2 gl = load_lane_gain(a, head, lane);
     if (wave_live) combine_maps(lam, l1 + __shfl_xor(l1, 32), l2 + __shfl_xor(l2, 32), O1, O2);
     wait_vm<0>();
+    if (more) rotate_q(qb + 1);
     if (wave_live) norm_store_g(a, b, head, q, hf, O1, LaneGain{gl.x, gl.y, hf});
     if (more) {
       if (d < 3) {
@@ -207,14 +235,17 @@ prefill_swa_kernel(PrefillArgs a) {
 }  // namespace
 
 bool prefill_window_kernel_fits(const PrefillArgs& a) {
-  return a.window > 0 && a.rope.mode == 0 && a.o1n == nullptr && (a.window - 1 + kBN - 1) / kBN <= 4;
+  return a.window > 0 && (a.rope.mode == 0 || a.keys_rotated) && a.o1n == nullptr &&
+         (a.window - 1 + kBN - 1) / kBN <= 4;
 }
 
 hipError_t launch_prefill_window(const PrefillArgs& a, hipStream_t stream) {
   if (!prefill_window_kernel_fits(a)) return hipErrorInvalidValue;
   const int nqb = (a.T + kBM - 1) / kBM;
   const int64_t chunks = (nqb + kSwBlocks - 1) / kSwBlocks;
-  return launch_kernel(prefill_swa_kernel, dim3((unsigned)(chunks * a.B * a.H)), dim3(256), stream, a);
+  const dim3 grid((unsigned)(chunks * a.B * a.H));
+  if (a.rope.mode != 0) return launch_kernel(prefill_swa_kernel<true>, grid, dim3(256), stream, a);
+  return launch_kernel(prefill_swa_kernel<false>, grid, dim3(256), stream, a);
 }
 
 }  // namespace diffattn
