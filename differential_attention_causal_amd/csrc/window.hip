@@ -144,7 +144,6 @@ prefill_swa_kernel(PrefillArgs a) {
     float m1 = kNoMax, m2 = kNoMax, l1 = 0.f, l2 = 0.f;
     const int q_first = qb * kBM + 32 * wave, q = q_first + lq;
     const bool wave_live = q_first < a.T;
-
     const int wave_last_tile = q_first / kBN;
     for (int s = 0; s <= d; ++s) {
       const int t0 = 4 * qb - d + s;  // this step's first tile (wave w takes t0 + w)
